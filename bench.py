@@ -1,0 +1,254 @@
+"""Benchmark of the KDA mixer hot path on one MI355X.
+
+A step is one batched KDA decode step (B=64 sequences x 1 token, H=64, D=128, bf16
+activations, fp32 state updated in place, conv kernel 4): conv + SiLU + l2, the
+delta-rule scan, the gated RMSNorm and the ring roll, all in the library's fused
+decode kernel. Inputs are seeded synthetic data (gated_delta_rule_68_amd.synth)
+already resident in HBM; NBUF independent copies of every buffer are cycled so
+that the 268 MB of state cannot stay in the 256 MB last-level cache between steps.
+
+Prints ONE JSON line (rank 0). Extra legs: the single-sequence prefill (T=4626)
+and the oracle's CPU rate on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KDA tokens/s + achieved HBM GB/s (decode) / MFMA % (prefill), H=64 d=128"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+NBUF = 4
+RMS_EPS = 1e-5
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def decode_bytes(cfg) -> int:
+    """Algorithmic HBM bytes of one decode step: every input read once, every output
+    written once (state and ring both ways)."""
+    B, H, D, K, qkv = cfg.B, cfg.H, cfg.D, cfg.K, cfg.qkv
+    es = 2 if cfg.dtype == "bf16" else 4
+    state = 2 * B * H * D * D * 4
+    ring = 2 * B * 3 * qkv * (K - 1) * 4
+    acts_in = (5 * B * qkv + B * H) * es  # q, k, v, g, z + beta
+    out = B * qkv * es
+    params = 3 * qkv * K * 4 + D * 4
+    return state + ring + acts_in + out + params
+
+
+def prefill_bytes(cfg) -> int:
+    B, T, H, D, K, qkv = cfg.B, cfg.T, cfg.H, cfg.D, cfg.K, cfg.qkv
+    es = 2 if cfg.dtype == "bf16" else 4
+    gate = B * T * (H if cfg.gdn else qkv)
+    acts = (4 * B * T * qkv + gate + B * T * H) * es + B * T * qkv * es
+    state = 2 * B * H * D * D * 4
+    ring = 2 * B * 3 * qkv * (K - 1) * 4
+    return acts + state + ring + 3 * qkv * K * 4 + D * 4
+
+
+def chunk_flops(cfg, C=64) -> float:
+    """Dense-tile contraction FLOPs of the chunked form: 2(5CD + 3D^2) per token-head."""
+    return 2.0 * (5 * C * cfg.D + 3 * cfg.D * cfg.D) * cfg.B * cfg.T * cfg.H
+
+
+def traffic_from_profile(kernel_src: str, name: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = open(os.path.join(ROOT, "gated_delta_rule_68_amd", "csrc", kernel_src), "rb").read()
+    if rec.get("source_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, inp, budget_s: float = 12.0):
+    """The fp64 oracle on the host cores: whole decode steps of the same workload,
+    repeated until the budget is spent."""
+    import numpy as np
+    import oracle
+
+    threads = min(16, os.cpu_count() or 1)
+    arrs = [np.ascontiguousarray(getattr(inp, n), np.float64)
+            for n in ("q", "k", "v", "g", "beta", "conv_w", "ring", "state", "z", "norm_w")]
+    scale = 1.0 / math.sqrt(cfg.D)
+    oracle.mixer(*arrs, scale, RMS_EPS, gdn=cfg.gdn, threads=threads)  # warm
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.mixer(*arrs, scale, RMS_EPS, gdn=cfg.gdn, threads=threads)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or steps >= 400:
+            break
+    return {"value": cfg.B * cfg.T * steps / el, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{steps} full decode steps (B={cfg.B}, H={cfg.H}, D={cfg.D}) of the "
+                      f"same seeded inputs in {el:.1f} s, fp64, threads split the batch"}
+
+
+def run_decode(cfg, steps, warmup):
+    import torch
+
+    import gated_delta_rule_68_amd as kda
+    from gated_delta_rule_68_amd.synth import make_inputs
+    from gated_delta_rule_68_amd.torch_io import alloc_outputs, to_device
+
+    inp = make_inputs(cfg)
+    base = to_device(inp, "cuda")
+    sets = []
+    for _ in range(NBUF):
+        d = {n: t.clone() for n, t in base.items()}
+        d.update(alloc_outputs(cfg, 1, "cuda", o_core=False))
+        sets.append(d)
+    del base
+    scale = 1.0 / math.sqrt(cfg.D)
+
+    def step(i):
+        d = sets[i % NBUF]
+        kda.kda_decode(d["q"], d["k"], d["v"], d["g"], d["beta"], d["conv_w"], d["ring"],
+                       d["state"], d["state"], d["z"], d["norm_w"], d["out"], None,
+                       scale=scale, rms_eps=RMS_EPS)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record()
+        step(warmup + i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = sorted(a.elapsed_time(b) for a, b in ev)
+    return inp, wall, sum(kern_ms) / len(kern_ms), kern_ms[len(kern_ms) // 2]
+
+
+def run_prefill(cfg, mode, reps=5):
+    import torch
+
+    import gated_delta_rule_68_amd as kda
+    from gated_delta_rule_68_amd.synth import make_inputs
+    from gated_delta_rule_68_amd.torch_io import alloc_outputs, to_device
+
+    d = to_device(make_inputs(cfg), "cuda")
+    d.update(alloc_outputs(cfg, cfg.T, "cuda", o_core=False))
+    code = kda.KDA_DTYPE_BF16 if cfg.dtype == "bf16" else kda.KDA_DTYPE_F32
+    nb = kda.workspace_bytes(cfg.B, cfg.T, cfg.H, cfg.D, code, mode, gdn=cfg.gdn)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+    ring0, s_out = d["ring"].clone(), torch.empty_like(d["state"])
+    fn = kda.gdn_prefill if cfg.gdn else kda.kda_prefill
+    scale = 1.0 / math.sqrt(cfg.D)
+
+    def once():
+        d["ring"].copy_(ring0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn(d["q"], d["k"], d["v"], d["g"], d["beta"], d["conv_w"], d["ring"], d["state"], s_out,
+           d["z"], d["norm_w"], d["out"], None, scale=scale, rms_eps=RMS_EPS, mode=mode,
+           workspace=ws)
+        b.record()
+        return a, b
+
+    once()
+    torch.cuda.synchronize()
+    evs = [once() for _ in range(reps)]
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)[reps // 2]
+    arm = kda.prefill_arm(cfg.B, cfg.T, cfg.H, cfg.D, code, mode, gdn=cfg.gdn)
+    return ms, kda.ARM_NAMES.get(arm, str(arm))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the mixer shards by (sequence, head) with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from gated_delta_rule_68_amd import _lib
+    from gated_delta_rule_68_amd.synth import CONFIGS
+
+    if not os.path.exists(_lib.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    cfg = CONFIGS["kda_decode"]
+    log(f"decode: {cfg}")
+    inp, wall, kern_avg_ms, kern_med_ms = run_decode(cfg, args.steps, args.warmup)
+    ms_per_step = 1e3 * wall / args.steps
+    tokens_per_step = cfg.B * cfg.T
+    nbytes = decode_bytes(cfg)
+    achieved = nbytes / (kern_avg_ms * 1e-3) / 1e9
+    traffic = traffic_from_profile("kda_seq.hip", "seq_fused_decode")
+    line = {
+        "metric": METRIC,
+        "value": tokens_per_step / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 activations, fp32 state and math",
+        "data": "synthetic (seeded)",
+        "config": {"workload": "KDA batched decode step", "B": cfg.B, "T": cfg.T, "H": cfg.H,
+                   "D": cfg.D, "conv_kernel": cfg.K, "state": "fp32, in place",
+                   "buffers_cycled": NBUF, "arm": "seq_fused"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "seq_fused_kernel<128,bf16,kda>",
+                     "kernel_avg_us": kern_avg_ms * 1e3, "kernel_median_us": kern_med_ms * 1e3,
+                     "algorithmic_bytes": nbytes},
+    }
+    if not args.no_prefill:
+        import gated_delta_rule_68_amd as kda
+        pcfg = CONFIGS["kda_prefill"]
+        extra = {}
+        for mode in (kda.KDA_MODE_SEQUENTIAL, kda.KDA_MODE_CHUNKED):
+            if kda.prefill_arm(pcfg.B, pcfg.T, pcfg.H, pcfg.D, 1, mode) < 0:
+                continue
+            ms, arm = run_prefill(pcfg, mode)
+            rec = {"arm": arm, "ms": ms, "tokens_per_s": pcfg.B * pcfg.T / (ms * 1e-3),
+                   "hbm_gbs": prefill_bytes(pcfg) / (ms * 1e-3) / 1e9}
+            if arm == "chunked":
+                tf = chunk_flops(pcfg) / (ms * 1e-3) / 1e12
+                rec.update({"mfma_tflops": tf, "mfma_frac": tf / BF16_PEAK_TFLOPS})
+            extra[arm] = rec
+            log(f"prefill {arm}: {rec}")
+        line["prefill"] = {"workload": "KDA prefill B=1 T=4626 H=64 D=128 bf16", **extra}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, inp)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,7 @@
+"""MI355X (gfx950) KDA / GDN gated delta-rule mixer: a C-ABI HIP library
+(``libkda.so``, declared in include/kda.h) and its thin Python binding."""
+from ._lib import (  # noqa: F401
+    ARM_NAMES, EXPORTS, KDA_DTYPE_BF16, KDA_DTYPE_F32, KDA_MODE_AUTO, KDA_MODE_CHUNKED,
+    KDA_MODE_SEQUENTIAL, KdaError, gdn_decode, gdn_prefill, kda_decode, kda_prefill, lib,
+    prefill_arm, status_string, workspace_bytes,
+)

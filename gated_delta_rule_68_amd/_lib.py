@@ -1,0 +1,151 @@
+"""ctypes binding of ``libkda.so`` (the C ABI in include/kda.h).
+
+Argument marshalling only: shapes are read off the tensors, pointers and sizes are
+passed through, and every step of the mixer runs in the HIP library. There is no
+fallback: if the library is not built, loading it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libkda.so")
+
+KDA_DTYPE_F32, KDA_DTYPE_BF16 = 0, 1
+KDA_MODE_AUTO, KDA_MODE_SEQUENTIAL, KDA_MODE_CHUNKED = 0, 1, 2
+ARM_NAMES = {1: "seq_fused", 2: "seq_split", 3: "chunked"}
+
+_lib = None
+
+_vp, _fp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_PREFILL_ARGS = [_vp] * 5 + [_fp, _fp, _fp, _fp, _vp, _fp, _vp, _fp] + [_i] * 5 + [_f, _f, _i, _i, _vp, _sz, _vp]
+_DECODE_ARGS = [_vp] * 5 + [_fp, _fp, _fp, _fp, _vp, _fp, _vp, _fp] + [_i] * 5 + [_f, _f, _i, _vp]
+EXPORTS = ("kda_prefill", "kda_decode", "gdn_prefill", "gdn_decode",
+           "kda_prefill_workspace_bytes", "gdn_prefill_workspace_bytes",
+           "kda_prefill_arm", "gdn_prefill_arm", "kda_status_string")
+
+
+class KdaError(RuntimeError):
+    def __init__(self, rc: int, what: str):
+        self.rc = rc
+        super().__init__(f"{what} failed: rc {rc} ({status_string(rc)})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library. Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(the mixer has no non-HIP fallback)")
+        l = ctypes.CDLL(LIB_PATH)
+        for n in ("kda_prefill", "gdn_prefill"):
+            getattr(l, n).argtypes = _PREFILL_ARGS
+            getattr(l, n).restype = _i
+        for n in ("kda_decode", "gdn_decode"):
+            getattr(l, n).argtypes = _DECODE_ARGS
+            getattr(l, n).restype = _i
+        for n in ("kda_prefill_workspace_bytes", "gdn_prefill_workspace_bytes"):
+            getattr(l, n).argtypes = [_i] * 6
+            getattr(l, n).restype = _sz
+        for n in ("kda_prefill_arm", "gdn_prefill_arm"):
+            getattr(l, n).argtypes = [_i] * 6
+            getattr(l, n).restype = _i
+        l.kda_status_string.argtypes = [_i]
+        l.kda_status_string.restype = ctypes.c_char_p
+        _lib = l
+    return _lib
+
+
+def status_string(rc: int) -> str:
+    return lib().kda_status_string(rc).decode()
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return KDA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return KDA_DTYPE_F32
+    raise TypeError(f"activations must be float32 or bfloat16, got {t.dtype}")
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _geometry(q, state, conv_w):
+    B, T = q.shape[0], q.shape[1]
+    H, D = state.shape[1], state.shape[2]
+    return B, T, H, D, conv_w.shape[1]
+
+
+def workspace_bytes(B, T, H, D, dtype_code, mode=KDA_MODE_AUTO, gdn=False) -> int:
+    fn = lib().gdn_prefill_workspace_bytes if gdn else lib().kda_prefill_workspace_bytes
+    return int(fn(B, T, H, D, dtype_code, mode))
+
+
+def prefill_arm(B, T, H, D, dtype_code, mode=KDA_MODE_AUTO, gdn=False) -> int:
+    fn = lib().gdn_prefill_arm if gdn else lib().kda_prefill_arm
+    return int(fn(B, T, H, D, dtype_code, mode))
+
+
+def _prefill(name, q, k, v, g, beta, conv_w, conv_ring, state_in, state_out, z, norm_w, out,
+             o_core, scale, rms_eps, mode, workspace, stream, check):
+    B, T, H, D, K = _geometry(q, state_in, conv_w)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = getattr(lib(), name)(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(conv_w), _ptr(conv_ring),
+        _ptr(state_in), _ptr(state_out), _ptr(z), _ptr(norm_w), _ptr(out), _ptr(o_core),
+        B, T, H, D, K, float(scale), float(rms_eps), _dtype_code(q), int(mode),
+        _ptr(workspace), ws_bytes, _stream_handle(stream))
+    if check and rc != 0:
+        raise KdaError(rc, name)
+    return rc
+
+
+def _decode(name, q, k, v, g, beta, conv_w, conv_ring, state_in, state_out, z, norm_w, out,
+            o_core, scale, rms_eps, stream, check):
+    B, T, H, D, K = _geometry(q, state_in, conv_w)
+    rc = getattr(lib(), name)(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(conv_w), _ptr(conv_ring),
+        _ptr(state_in), _ptr(state_out), _ptr(z), _ptr(norm_w), _ptr(out), _ptr(o_core),
+        B, T, H, D, K, float(scale), float(rms_eps), _dtype_code(q), _stream_handle(stream))
+    if check and rc != 0:
+        raise KdaError(rc, name)
+    return rc
+
+
+def kda_prefill(q, k, v, g, beta, conv_w, conv_ring, state_in, state_out, z, norm_w, out,
+                o_core=None, *, scale, rms_eps, mode=KDA_MODE_AUTO, workspace=None,
+                stream=None, check=True):
+    """Tensors in the layouts of include/kda.h (all on the GPU). Returns the status."""
+    return _prefill("kda_prefill", q, k, v, g, beta, conv_w, conv_ring, state_in, state_out,
+                    z, norm_w, out, o_core, scale, rms_eps, mode, workspace, stream, check)
+
+
+def gdn_prefill(q, k, v, g, beta, conv_w, conv_ring, state_in, state_out, z, norm_w, out,
+                o_core=None, *, scale, rms_eps, mode=KDA_MODE_AUTO, workspace=None,
+                stream=None, check=True):
+    return _prefill("gdn_prefill", q, k, v, g, beta, conv_w, conv_ring, state_in, state_out,
+                    z, norm_w, out, o_core, scale, rms_eps, mode, workspace, stream, check)
+
+
+def kda_decode(q, k, v, g, beta, conv_w, conv_ring, state_in, state_out, z, norm_w, out,
+               o_core=None, *, scale, rms_eps, stream=None, check=True):
+    return _decode("kda_decode", q, k, v, g, beta, conv_w, conv_ring, state_in, state_out, z,
+                   norm_w, out, o_core, scale, rms_eps, stream, check)
+
+
+def gdn_decode(q, k, v, g, beta, conv_w, conv_ring, state_in, state_out, z, norm_w, out,
+               o_core=None, *, scale, rms_eps, stream=None, check=True):
+    return _decode("gdn_decode", q, k, v, g, beta, conv_w, conv_ring, state_in, state_out, z,
+                   norm_w, out, o_core, scale, rms_eps, stream, check)

@@ -1,0 +1,228 @@
+// Host side of the C ABI declared in include/kda.h: argument validation (all of
+// it before any launch, so a rejected call writes nothing on the device), arm
+// selection and dispatch to the HIP launchers.
+//
+// Status convention (memra-engine mla_ffi.rs, module header): 0 ok, 10000 + the
+// runtime error of a failing launch, 40000 + a contract violation.
+#include "kda.h"
+
+#include <stdint.h>
+#include <string.h>
+
+#include "kda_internal.h"
+
+namespace {
+
+using kda::MixerArgs;
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+    bool writable;
+    int id;
+};
+
+bool overlaps(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool head_dim_ok(int D) { return D == 16 || D == 128; }
+
+// Shape checks shared by the entry points and the workspace / arm queries.
+int check_shape(int B, int T, int H, int D, int K) {
+    if (B < 1 || T < 1 || H < 1) return KDA_ERR_SHAPE;
+    if (!head_dim_ok(D)) return KDA_ERR_HEAD_DIM;
+    if (K < 2 || K > 8) return KDA_ERR_CONV_KERNEL;
+    // Element counts are formed in 64-bit; keep every tensor below 2^40 elements and
+    // the (b, h) grid inside a launch dimension.
+    const double elems = (double)B * (double)T * (double)H * (double)D;
+    const double state = (double)B * (double)H * (double)D * (double)D;
+    if (elems > 1099511627776.0 || state > 1099511627776.0) return KDA_ERR_SHAPE;
+    if ((double)B * (double)H * 8.0 > 2147483647.0) return KDA_ERR_SHAPE;
+    return KDA_OK;
+}
+
+// Which arm runs. Sequential work needs many (b, h) pairs to fill the chip with one
+// fused workgroup per pair; below that the column-split pipeline is used, except for
+// very short prefills where its extra launches would dominate.
+int pick_arm(int B, int T, int H, int D, bool bf16, int mode) {
+    (void)bf16;
+    const bool chunk_ok = kda::kChunkedArmBuilt && D == 128;
+    if (mode == KDA_MODE_CHUNKED) return chunk_ok ? kda::ARM_CHUNKED : -1;
+    if (mode == KDA_MODE_AUTO && chunk_ok && T >= 128) return kda::ARM_CHUNKED;
+    if (mode != KDA_MODE_AUTO && mode != KDA_MODE_SEQUENTIAL) return -1;
+    if (T <= 16 || (long)B * H >= 1024) return kda::ARM_SEQ_FUSED;
+    return kda::ARM_SEQ_SPLIT;
+}
+
+size_t workspace_for(int B, int T, int H, int D, bool gdn, int arm) {
+    switch (arm) {
+        case kda::ARM_SEQ_SPLIT: return kda::split_workspace(B, T, H, D, gdn).total;
+        case kda::ARM_CHUNKED: return kda::chunked_workspace_bytes(B, T, H, D, gdn);
+        default: return 0;
+    }
+}
+
+int validate(const MixerArgs& a, bool decode, int mode, int* arm_out) {
+    if (!a.q || !a.k || !a.v || !a.g || !a.beta || !a.conv_w || !a.ring || !a.state_in ||
+        !a.state_out || !a.z || !a.norm_w || !a.out)
+        return KDA_ERR_NULL;
+    int rc = check_shape(a.B, a.T, a.H, a.D, a.K);
+    if (rc) return rc;
+    if (decode && a.T != 1) return KDA_ERR_DECODE_T;
+    const int arm = decode ? (int)kda::ARM_SEQ_FUSED : pick_arm(a.B, a.T, a.H, a.D, a.bf16, mode);
+    if (arm < 0) return KDA_ERR_DTYPE_MODE;
+
+    const void* ptrs[] = {a.q, a.k, a.v, a.g, a.beta, a.conv_w, a.ring, a.state_in,
+                          a.state_out, a.z, a.norm_w, a.out, a.o_core, a.ws};
+    for (const void* p : ptrs)
+        if (p && ((uintptr_t)p & 15u)) return KDA_ERR_ALIGN;
+
+    const size_t es = a.bf16 ? 2 : 4;
+    const size_t qkv = (size_t)a.H * a.D;
+    const size_t act = (size_t)a.B * a.T * qkv;
+    const size_t gate_n = a.gdn ? (size_t)a.B * a.T * a.H : act;
+    const size_t state_n = (size_t)a.B * a.H * a.D * a.D;
+    const size_t need_ws = workspace_for(a.B, a.T, a.H, a.D, a.gdn, arm);
+    if (need_ws > 0 && (!a.ws || a.ws_bytes < need_ws)) return KDA_ERR_WORKSPACE;
+
+    auto R = [](const void* p, size_t bytes, bool w, int id) {
+        return Range{(uintptr_t)p, (uintptr_t)p + bytes, w, id};
+    };
+    Range rs[14];
+    int n = 0;
+    rs[n++] = R(a.q, act * es, false, 0);
+    rs[n++] = R(a.k, act * es, false, 1);
+    rs[n++] = R(a.v, act * es, false, 2);
+    rs[n++] = R(a.g, gate_n * es, false, 3);
+    rs[n++] = R(a.beta, (size_t)a.B * a.T * a.H * es, false, 4);
+    rs[n++] = R(a.conv_w, 3 * qkv * a.K * 4, false, 5);
+    rs[n++] = R(a.ring, (size_t)a.B * 3 * qkv * (a.K - 1) * 4, true, 6);
+    rs[n++] = R(a.state_in, state_n * 4, false, 7);
+    rs[n++] = R(a.state_out, state_n * 4, true, 8);
+    rs[n++] = R(a.z, act * es, false, 9);
+    rs[n++] = R(a.norm_w, (size_t)a.D * 4, false, 10);
+    rs[n++] = R(a.out, act * es, true, 11);
+    if (a.o_core) rs[n++] = R(a.o_core, act * 4, true, 12);
+    if (need_ws > 0) rs[n++] = R(a.ws, need_ws, true, 13);
+    for (int i = 0; i < n; ++i)
+        for (int j = i + 1; j < n; ++j) {
+            if (!(rs[i].writable || rs[j].writable) || !overlaps(rs[i], rs[j])) continue;
+            const bool state_pair = (rs[i].id == 7 && rs[j].id == 8) && a.state_in == a.state_out;
+            if (!state_pair) return KDA_ERR_ALIAS;
+        }
+    *arm_out = arm;
+    return KDA_OK;
+}
+
+int run(const MixerArgs& a, int arm) {
+    hipError_t e;
+    switch (arm) {
+        case kda::ARM_SEQ_FUSED: e = kda::launch_seq_fused(a); break;
+        case kda::ARM_SEQ_SPLIT: e = kda::launch_seq_split(a); break;
+        case kda::ARM_CHUNKED: e = kda::launch_chunked(a); break;
+        default: return KDA_ERR_DTYPE_MODE;
+    }
+    return e == hipSuccess ? KDA_OK : KDA_ERR_RUNTIME_BASE + (int)e;
+}
+
+int entry(bool gdn, bool decode, const void* q, const void* k, const void* v, const void* g,
+          const void* beta, const float* conv_w, float* conv_ring, const float* state_in,
+          float* state_out, const void* z, const float* norm_w, void* out, float* o_core,
+          int B, int T, int H, int D, int K, float scale, float rms_eps, int dtype, int mode,
+          void* workspace, size_t workspace_bytes, void* stream) {
+    if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return KDA_ERR_DTYPE_MODE;
+    MixerArgs a{q, k, v, g, beta, conv_w, conv_ring, state_in, state_out, z, norm_w, out,
+                o_core, B, T, H, D, K, scale, rms_eps, dtype == KDA_DTYPE_BF16, gdn,
+                workspace, workspace_bytes, (hipStream_t)stream};
+    int arm = 0;
+    const int rc = validate(a, decode, mode, &arm);
+    if (rc) return rc;
+    return run(a, arm);
+}
+
+size_t ws_query(bool gdn, int B, int T, int H, int D, int dtype, int mode) {
+    if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return (size_t)-1;
+    if (check_shape(B, T, H, D, 4)) return (size_t)-1;
+    const int arm = pick_arm(B, T, H, D, dtype == KDA_DTYPE_BF16, mode);
+    if (arm < 0) return (size_t)-1;
+    return workspace_for(B, T, H, D, gdn, arm);
+}
+
+int arm_query(int B, int T, int H, int D, int dtype, int mode) {
+    if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return -1;
+    if (check_shape(B, T, H, D, 4)) return -1;
+    return pick_arm(B, T, H, D, dtype == KDA_DTYPE_BF16, mode);
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_prefill(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                const float* conv_w, float* conv_ring, const float* state_in, float* state_out,
+                const void* z, const float* norm_w, void* out, float* o_core, int B, int T,
+                int H, int D, int K, float scale, float rms_eps, int dtype, int mode,
+                void* workspace, size_t workspace_bytes, void* stream) {
+    return entry(false, false, q, k, v, g, beta, conv_w, conv_ring, state_in, state_out, z,
+                 norm_w, out, o_core, B, T, H, D, K, scale, rms_eps, dtype, mode, workspace,
+                 workspace_bytes, stream);
+}
+
+int gdn_prefill(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                const float* conv_w, float* conv_ring, const float* state_in, float* state_out,
+                const void* z, const float* norm_w, void* out, float* o_core, int B, int T,
+                int H, int D, int K, float scale, float rms_eps, int dtype, int mode,
+                void* workspace, size_t workspace_bytes, void* stream) {
+    return entry(true, false, q, k, v, g, beta, conv_w, conv_ring, state_in, state_out, z,
+                 norm_w, out, o_core, B, T, H, D, K, scale, rms_eps, dtype, mode, workspace,
+                 workspace_bytes, stream);
+}
+
+int kda_decode(const void* q, const void* k, const void* v, const void* g, const void* beta,
+               const float* conv_w, float* conv_ring, const float* state_in, float* state_out,
+               const void* z, const float* norm_w, void* out, float* o_core, int B, int T,
+               int H, int D, int K, float scale, float rms_eps, int dtype, void* stream) {
+    return entry(false, true, q, k, v, g, beta, conv_w, conv_ring, state_in, state_out, z,
+                 norm_w, out, o_core, B, T, H, D, K, scale, rms_eps, dtype,
+                 KDA_MODE_SEQUENTIAL, nullptr, 0, stream);
+}
+
+int gdn_decode(const void* q, const void* k, const void* v, const void* g, const void* beta,
+               const float* conv_w, float* conv_ring, const float* state_in, float* state_out,
+               const void* z, const float* norm_w, void* out, float* o_core, int B, int T,
+               int H, int D, int K, float scale, float rms_eps, int dtype, void* stream) {
+    return entry(true, true, q, k, v, g, beta, conv_w, conv_ring, state_in, state_out, z,
+                 norm_w, out, o_core, B, T, H, D, K, scale, rms_eps, dtype,
+                 KDA_MODE_SEQUENTIAL, nullptr, 0, stream);
+}
+
+size_t kda_prefill_workspace_bytes(int B, int T, int H, int D, int dtype, int mode) {
+    return ws_query(false, B, T, H, D, dtype, mode);
+}
+size_t gdn_prefill_workspace_bytes(int B, int T, int H, int D, int dtype, int mode) {
+    return ws_query(true, B, T, H, D, dtype, mode);
+}
+int kda_prefill_arm(int B, int T, int H, int D, int dtype, int mode) {
+    return arm_query(B, T, H, D, dtype, mode);
+}
+int gdn_prefill_arm(int B, int T, int H, int D, int dtype, int mode) {
+    return arm_query(B, T, H, D, dtype, mode);
+}
+
+const char* kda_status_string(int rc) {
+    switch (rc) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_NULL: return "a required pointer is NULL";
+        case KDA_ERR_HEAD_DIM: return "unsupported head dim: D must be 16 or 128";
+        case KDA_ERR_CONV_KERNEL: return "conv kernel size K must be in 2..8";
+        case KDA_ERR_SHAPE: return "B, T and H must be >= 1 and sizes must fit the launch limits";
+        case KDA_ERR_DECODE_T: return "decode entry points take exactly one token (T == 1)";
+        case KDA_ERR_WORKSPACE: return "workspace missing or smaller than the query returned";
+        case KDA_ERR_ALIGN: return "every pointer must be 16-byte aligned";
+        case KDA_ERR_DTYPE_MODE: return "unknown dtype or mode, or mode not valid for this shape";
+        case KDA_ERR_ALIAS: return "buffers overlap (only state_in == state_out may alias)";
+        default: break;
+    }
+    if (rc >= KDA_ERR_RUNTIME_BASE && rc < 20000) return "HIP runtime error during launch";
+    return "unknown status code";
+}
+
+}  // extern "C"

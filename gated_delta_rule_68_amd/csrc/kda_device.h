@@ -1,0 +1,264 @@
+// Device helpers shared by every arm of the mixer. Each stage of the path is
+// written once here and called by all kernels with the same lane mapping, so the
+// fused decode kernel, the split prefill pipeline and the chunked prefill see
+// bit-identical conv, l2 and norm results (the decode == verify identity of
+// memra-engine kda.rs, ConvArm notes, and its scan-chain identity in stage 5).
+//
+// Build with -ffp-contract=off: every fused multiply-add below is explicit, so no
+// arm can differ from another by a contraction the compiler chose on its own.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "kda_internal.h"
+
+namespace kda {
+
+// Widest conv kernel. The conv window lives in KMAX-1 registers per channel.
+// (memra-engine kda.rs, KDA_MAX_CONV_KERNEL.)
+constexpr int KMAX = 8;
+// l2 epsilon, added to the sum of squares inside the square root (kda.rs,
+// KDA_L2_EPS; aprender-serve gdn_ops.rs, gdn_per_head_l2_norm_into).
+constexpr float L2_EPS = 1e-6f;
+constexpr float LOG2E = 1.4426950408889634f;
+
+using bf16_t = unsigned short;
+
+__device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float((unsigned)b << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ bf16_t f2bf(float f) {
+    unsigned u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (bf16_t)(u >> 16);
+}
+
+template <bool BF>
+__device__ __forceinline__ float ld_act(const void* p, size_t i) {
+    if constexpr (BF)
+        return bf2f(static_cast<const bf16_t*>(p)[i]);
+    else
+        return static_cast<const float*>(p)[i];
+}
+
+template <bool BF>
+__device__ __forceinline__ void st_act(void* p, size_t i, float x) {
+    if constexpr (BF)
+        static_cast<bf16_t*>(p)[i] = f2bf(x);
+    else
+        static_cast<float*>(p)[i] = x;
+}
+
+// e^x through the hardware base-2 exponential.
+__device__ __forceinline__ float exp_f(float x) { return __builtin_amdgcn_exp2f(x * LOG2E); }
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + exp_f(-x)); }
+__device__ __forceinline__ float silu_f(float x) { return x * sigmoid_f(x); }
+
+// Butterfly sums. Every lane of the group ends with the same bits (each step adds
+// the same two operands, only in swapped order).
+__device__ __forceinline__ float sum_lanes8(float v) {
+    v += __shfl_xor(v, 1, 64);
+    v += __shfl_xor(v, 2, 64);
+    v += __shfl_xor(v, 4, 64);
+    return v;
+}
+
+__device__ __forceinline__ float sum_lanes64(float v) {
+    v += __shfl_xor(v, 1, 64);
+    v += __shfl_xor(v, 2, 64);
+    v += __shfl_xor(v, 4, 64);
+    v += __shfl_xor(v, 8, 64);
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Causal depthwise conv, one channel per thread (memra-engine kda.rs, CONV FUSION
+// notes and ConvArm; aprender-serve gdn_ops.rs, gdn_causal_conv1d_silu_into).
+// win[KMAX-2] is the newest previous raw input, win[KMAX-1-d] the input d steps
+// back; tap[d] = w[K-1-d] multiplies the input d steps back (tap[0] the current
+// one); taps beyond K are zero, so the sum runs over the window in ascending time
+// order (oldest first) exactly as for a K-wide window.
+// ---------------------------------------------------------------------------
+struct ConvChannel {
+    float win[KMAX - 1];
+    float tap[KMAX];
+};
+
+__device__ __forceinline__ void conv_load_taps(ConvChannel& c, const float* w_row, int K) {
+#pragma unroll
+    for (int d = 0; d < KMAX; ++d) c.tap[d] = (d < K) ? w_row[K - 1 - d] : 0.0f;
+}
+
+// Push the raw input x, return the pre-activation conv output for it.
+__device__ __forceinline__ float conv_push(ConvChannel& c, float x) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int d = KMAX - 1; d >= 1; --d) acc = fmaf(c.tap[d], c.win[KMAX - 1 - d], acc);
+    acc = fmaf(c.tap[0], x, acc);
+#pragma unroll
+    for (int e = 0; e < KMAX - 2; ++e) c.win[e] = c.win[e + 1];
+    c.win[KMAX - 2] = x;
+    return acc;
+}
+
+// Ring row of one channel: K-1 fp32 slots, slot 0 = oldest raw input.
+__device__ __forceinline__ void conv_window_from_ring(ConvChannel& c, const float* ring_row, int K) {
+#pragma unroll
+    for (int d = 1; d < KMAX; ++d) c.win[KMAX - 1 - d] = (d <= K - 1) ? ring_row[K - 1 - d] : 0.0f;
+}
+
+__device__ __forceinline__ void conv_window_to_ring(const ConvChannel& c, float* ring_row, int K) {
+#pragma unroll
+    for (int d = 1; d < KMAX; ++d)
+        if (d <= K - 1) ring_row[K - 1 - d] = c.win[KMAX - 1 - d];
+}
+
+// ---------------------------------------------------------------------------
+// Per-row reductions, one wavefront per row of D <= 128 values held in LDS:
+// lane l owns elements l and l + 64.
+// ---------------------------------------------------------------------------
+
+// l2-normalise the q and k rows of one (token, head) in place and return k.q of the
+// normalised rows in *kq_out (memra-engine kda.rs, kda_core_gated stage 3).
+template <int D>
+__device__ __forceinline__ void l2_qk_row(float* qrow, float* krow, int lane, float* kq_out) {
+    const bool h0 = lane < D, h1 = lane + 64 < D;
+    float q0 = h0 ? qrow[lane] : 0.0f, q1 = h1 ? qrow[lane + 64] : 0.0f;
+    float k0 = h0 ? krow[lane] : 0.0f, k1 = h1 ? krow[lane + 64] : 0.0f;
+    const float iq = rsqrtf(sum_lanes64(fmaf(q1, q1, q0 * q0)) + L2_EPS);
+    const float ik = rsqrtf(sum_lanes64(fmaf(k1, k1, k0 * k0)) + L2_EPS);
+    q0 *= iq;
+    q1 *= iq;
+    k0 *= ik;
+    k1 *= ik;
+    if (h0) {
+        qrow[lane] = q0;
+        krow[lane] = k0;
+    }
+    if (h1) {
+        qrow[lane + 64] = q1;
+        krow[lane + 64] = k1;
+    }
+    const float kq = sum_lanes64(fmaf(k1, q1, k0 * q0));
+    if (lane == 0) *kq_out = kq;
+}
+
+// Gated RMSNorm of one (token, head) row: o / sqrt(mean o^2 + eps) * w * gate(z),
+// gate = sigmoid (KDA) or SiLU (GDN) (memra-engine kda.rs, kda_core_gated stage 6
+// and kda_gated_rmsnorm; aprender-serve gdn_ops.rs, gdn_gated_rmsnorm_into).
+// `off` is the element offset of the row in z / out; o_copy (may be null) receives
+// the un-normalised row.
+template <int D, bool BF, bool GDN>
+__device__ __forceinline__ void gated_rmsnorm_row(const float* orow, const MixerArgs& a,
+                                                  size_t off, int lane, float* o_copy) {
+    const bool h0 = lane < D, h1 = lane + 64 < D;
+    const float o0 = h0 ? orow[lane] : 0.0f, o1 = h1 ? orow[lane + 64] : 0.0f;
+    const float ss = sum_lanes64(fmaf(o1, o1, o0 * o0));
+    const float inv = rsqrtf(fmaf(ss, 1.0f / D, a.rms_eps));
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        if (!(half ? h1 : h0)) continue;
+        const int j = lane + 64 * half;
+        const float o = half ? o1 : o0;
+        const float zz = ld_act<BF>(a.z, off + j);
+        const float gate = GDN ? silu_f(zz) : sigmoid_f(zz);
+        st_act<BF>(a.out, off + j, ((o * inv) * a.norm_w[j]) * gate);
+        if (o_copy) o_copy[off + j] = o;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The sequential scan on register-resident state (memra-engine kda.rs,
+// kda_core_gated stage 5 and kda_scan; aprender-serve gdn_ops.rs,
+// gdn_delta_rule_into). Value column j of a head's state is owned by 8
+// consecutive lanes; sub-lane s (0..7) holds the D/8 keys
+//   i = m*8*VEC + s*VEC + e   (m < D/(8*VEC), e < VEC, VEC = min(4, D/8)),
+// so each 16-byte load of 8 sub-lanes covers 128 contiguous bytes of the row.
+// ---------------------------------------------------------------------------
+template <int D>
+struct ColLayout {
+    static constexpr int KPL = D / 8;
+    static constexpr int VEC = KPL >= 4 ? 4 : KPL;
+    static constexpr int M = KPL / VEC;
+};
+
+// Gather this sub-lane's keys of a D-long row (LDS or global).
+template <int D>
+__device__ __forceinline__ void load_keys(float (&dst)[D / 8], const float* row, int s) {
+    using L = ColLayout<D>;
+#pragma unroll
+    for (int m = 0; m < L::M; ++m) {
+        const float* p = row + m * 8 * L::VEC + s * L::VEC;
+        if constexpr (L::VEC == 4) {
+            const float4 t = *reinterpret_cast<const float4*>(p);
+            dst[4 * m + 0] = t.x;
+            dst[4 * m + 1] = t.y;
+            dst[4 * m + 2] = t.z;
+            dst[4 * m + 3] = t.w;
+        } else {
+            static_assert(L::VEC == 2, "D must be 16 or a multiple of 32");
+            const float2 t = *reinterpret_cast<const float2*>(p);
+            dst[2 * m + 0] = t.x;
+            dst[2 * m + 1] = t.y;
+        }
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void store_keys(float* row, const float (&src)[D / 8], int s) {
+    using L = ColLayout<D>;
+#pragma unroll
+    for (int m = 0; m < L::M; ++m) {
+        float* p = row + m * 8 * L::VEC + s * L::VEC;
+        if constexpr (L::VEC == 4) {
+            *reinterpret_cast<float4*>(p) =
+                make_float4(src[4 * m], src[4 * m + 1], src[4 * m + 2], src[4 * m + 3]);
+        } else {
+            *reinterpret_cast<float2*>(p) = make_float2(src[2 * m], src[2 * m + 1]);
+        }
+    }
+}
+
+// One token of the recurrence for column j. q, k are the l2-normalised rows, erow
+// holds exp(g) (D values for KDA, one for GDN), kq = k.q. The readout uses the
+// post-update state, expanded as S'^T q + beta u (k.q) where S' is the decayed
+// state, so both reductions run in one pass.
+template <int D, bool GDN>
+__device__ __forceinline__ float scan_step(float (&S)[D / 8], const float* qrow,
+                                           const float* krow, const float* erow, float vj,
+                                           float beta, float kq, float scale, int s) {
+    constexpr int KPL = D / 8;
+    float kv[KPL], qv[KPL];
+    load_keys<D>(kv, krow, s);
+    load_keys<D>(qv, qrow, s);
+    if constexpr (GDN) {
+        const float e = erow[0];
+#pragma unroll
+        for (int x = 0; x < KPL; ++x) S[x] *= e;
+    } else {
+        float ev[KPL];
+        load_keys<D>(ev, erow, s);
+#pragma unroll
+        for (int x = 0; x < KPL; ++x) S[x] *= ev[x];
+    }
+    float a0 = 0.0f, a1 = 0.0f, b0 = 0.0f, b1 = 0.0f;
+#pragma unroll
+    for (int x = 0; x < KPL; x += 2) {
+        a0 = fmaf(S[x], kv[x], a0);
+        a1 = fmaf(S[x + 1], kv[x + 1], a1);
+        b0 = fmaf(S[x], qv[x], b0);
+        b1 = fmaf(S[x + 1], qv[x + 1], b1);
+    }
+    const float sk = sum_lanes8(a0 + a1);
+    const float sq = sum_lanes8(b0 + b1);
+    const float bu = beta * (vj - sk);
+    const float o = scale * fmaf(bu, kq, sq);
+#pragma unroll
+    for (int x = 0; x < KPL; ++x) S[x] = fmaf(kv[x], bu, S[x]);
+    return o;
+}
+
+}  // namespace kda

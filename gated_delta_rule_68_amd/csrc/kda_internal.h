@@ -1,0 +1,56 @@
+// Private interface between the host entry points (kda_api.cpp) and the HIP
+// kernels. Nothing here is part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+// Everything one mixer call needs, already validated by the host entry point.
+struct MixerArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* g;
+    const void* beta;
+    const float* conv_w;
+    float* ring;
+    const float* state_in;
+    float* state_out;
+    const void* z;
+    const float* norm_w;
+    void* out;
+    float* o_core;  // may be null
+    int B, T, H, D, K;
+    float scale, rms_eps;
+    bool bf16;  // activations are bf16 (else fp32)
+    bool gdn;   // scalar gate per (token, head) and SiLU output gate
+    void* ws;
+    size_t ws_bytes;
+    hipStream_t stream;
+};
+
+// Arms (values match the KDA_ARM_* codes of the public header).
+enum Arm { ARM_SEQ_FUSED = 1, ARM_SEQ_SPLIT = 2, ARM_CHUNKED = 3 };
+
+// Workspace carve-up of the split sequential arm: fp32 arrays, each starting on a
+// 256-byte boundary.
+struct SplitWorkspace {
+    size_t qh, kh, vh, eg, kq, o, total;  // byte offsets and total size
+};
+SplitWorkspace split_workspace(int B, int T, int H, int D, bool gdn);
+
+// Whether this build carries the chunked prefill arm.
+extern const bool kChunkedArmBuilt;
+
+// Workspace of the chunked arm.
+size_t chunked_workspace_bytes(int B, int T, int H, int D, bool gdn);
+
+// Launchers: enqueue on a.stream, return the first launch error (hipSuccess if none).
+hipError_t launch_seq_fused(const MixerArgs& a);
+hipError_t launch_seq_split(const MixerArgs& a);
+hipError_t launch_chunked(const MixerArgs& a);
+
+}  // namespace kda

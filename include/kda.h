@@ -1,0 +1,152 @@
+/*
+ * kda.h - C ABI of the MI355X (gfx950) KDA / GDN gated delta-rule mixer library.
+ *
+ * What the library computes (the mixer hot path, without its projections):
+ *   memra-engine 0.125.0 kda.rs, module notes and kda_core_gated stages 2-6:
+ *     2. per-plane causal depthwise conv (kernel K) + SiLU over q, k, v, reading
+ *        the conv ring as the left pad, then the ring rolled to the last K-1 raw
+ *        inputs (ConvArm; "CONV FUSION" notes);
+ *     3. l2 normalisation of q and k over head_dim, eps 1e-6 inside the sqrt
+ *        (KDA_L2_EPS);
+ *     5. the gated delta rule per head: S <- diag(exp g_t) S (key axis),
+ *        u = v_t - S^T k_t, S <- S + beta_t k_t u^T, o_t = scale * S^T q_t;
+ *     6. gated RMSNorm over head_dim: o / sqrt(mean o^2 + rms_eps) * norm_w * gate(z),
+ *        gate = sigmoid (KDA) or SiLU (GDN, aprender-serve gdn_ops.rs,
+ *        gdn_gated_rmsnorm_into).
+ *   The chunked prefill arm computes the same recurrence in chunks of 64 tokens
+ *   (kda.rs module notes on the chunked twin: cumulative log gate per channel,
+ *   UT/WY intra-chunk solve).
+ *   Status codes follow memra-engine 0.124.0 mla_ffi.rs, module header:
+ *   0 ok, 10000 + runtime error, 40000 + contract violation; the stream is
+ *   passed as a void pointer.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers, caller-owned, 16-byte aligned.
+ *    The library never allocates, frees or synchronises; it enqueues kernels on
+ *    `stream` (a hipStream_t, NULL = the legacy default stream) and returns.
+ *  - dtype (KDA_DTYPE_*) applies to q, k, v, g, beta, z and out. conv_w,
+ *    conv_ring, state_in/state_out, norm_w and o_core are always fp32.
+ *  - Shapes (row-major, batch outermost, channel c = h*D + i, token-major):
+ *      q, k, v  [B][T][H*D]  raw (pre-conv) activations
+ *      g        [B][T][H*D]  per-channel log gate (KDA)   | [B][T][H] (GDN)
+ *               precondition g <= 0; the chunked arm also needs g >= -5
+ *      beta     [B][T][H]    in [0, 1]
+ *      conv_w   [3*H*D][K]   planes q, k, v; tap K-1 multiplies the newest input
+ *      conv_ring[B][3*H*D][K-1]  in/out; slot 0 = oldest raw input
+ *      state_in / state_out [B][H][D][D]: element [b][h][j][i] is S[i][j]
+ *               (value column j major, key i fastest); may be the SAME pointer
+ *               (updated in place), otherwise must not overlap
+ *      z        [B][T][H*D]  output gate
+ *      norm_w   [D]          shared by all heads
+ *      out      [B][T][H*D]  gated, normalised output (dtype)
+ *      o_core   [B][T][H*D]  fp32 scan output before the norm; may be NULL
+ *  - D must be 16 or 128, 2 <= K <= 8, B, T, H >= 1.
+ *  - Contract violations are detected on the host BEFORE any launch: nothing is
+ *    written on the device when a 4xxxx code is returned.
+ *  - On 10000 + hipError_t the contents of every output are undefined.
+ *  - The library keeps no state between calls. Calls on different streams with
+ *    disjoint buffers may run concurrently.
+ */
+#ifndef KDA_MI355X_H
+#define KDA_MI355X_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+#define KDA_OK 0
+#define KDA_ERR_RUNTIME_BASE 10000 /* + hipError_t of the failing launch */
+#define KDA_ERR_NULL 40001         /* a required pointer is NULL */
+#define KDA_ERR_HEAD_DIM 40002     /* D not in {16, 128} */
+#define KDA_ERR_CONV_KERNEL 40003  /* K outside 2..8 */
+#define KDA_ERR_SHAPE 40004        /* B, T or H < 1, or sizes overflow */
+#define KDA_ERR_DECODE_T 40005     /* a decode entry point called with T != 1 */
+#define KDA_ERR_WORKSPACE 40006    /* workspace NULL or smaller than required */
+#define KDA_ERR_ALIGN 40007        /* a pointer is not 16-byte aligned */
+#define KDA_ERR_DTYPE_MODE 40008   /* unknown dtype or mode, or mode not valid here */
+#define KDA_ERR_ALIAS 40009        /* two buffers overlap (other than state_in == state_out) */
+
+/* ---- dtype and prefill mode ---- */
+#define KDA_DTYPE_F32 0
+#define KDA_DTYPE_BF16 1
+#define KDA_MODE_AUTO 0       /* library picks sequential or chunked from the shape */
+#define KDA_MODE_SEQUENTIAL 1 /* token-by-token scan (bit-identical to chained decodes) */
+#define KDA_MODE_CHUNKED 2    /* chunk-64 WY form, bf16 MFMA operands, fp32 state (D = 128) */
+
+/* Which kernel arm a prefill with these arguments runs (for reporting). */
+#define KDA_ARM_SEQ_FUSED 1   /* one kernel per (b, h): conv, l2, scan, norm and ring fused */
+#define KDA_ARM_SEQ_SPLIT 2   /* pre-kernel, column-split scan, norm kernel */
+#define KDA_ARM_CHUNKED 3     /* chunked prefill */
+
+/*
+ * kda_prefill - run the mixer over T tokens of B sequences.
+ *   Reads q, k, v, g, beta, z, conv_w, norm_w, conv_ring (old), state_in.
+ *   Writes out, o_core (if not NULL), conv_ring (rolled), state_out.
+ *   scale multiplies the readout (head_dim^-1/2 in the source model);
+ *   rms_eps is the RMSNorm epsilon.
+ *   mode: KDA_MODE_*. The sequential mode gives results bit-identical to T
+ *   successive kda_decode calls. The chunked mode agrees with it to bf16-operand
+ *   accuracy and requires D == 128.
+ *   workspace: device buffer of at least kda_prefill_workspace_bytes(...) bytes
+ *   (may be NULL when that is 0). Its contents on entry are ignored.
+ * Returns KDA_OK or a status code above.
+ */
+int kda_prefill(const void* q, const void* k, const void* v, const void* g,
+                const void* beta, const float* conv_w, float* conv_ring,
+                const float* state_in, float* state_out, const void* z,
+                const float* norm_w, void* out, float* o_core,
+                int B, int T, int H, int D, int K, float scale, float rms_eps,
+                int dtype, int mode, void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/*
+ * kda_decode - one new token per sequence (T must be 1, else KDA_ERR_DECODE_T).
+ *   Same arguments and semantics as kda_prefill with T = 1 and the sequential
+ *   arm; runs one fused kernel and needs no workspace. The ring is rolled and the
+ *   state updated exactly as by kda_prefill(T = 1, KDA_MODE_SEQUENTIAL).
+ */
+int kda_decode(const void* q, const void* k, const void* v, const void* g,
+               const void* beta, const float* conv_w, float* conv_ring,
+               const float* state_in, float* state_out, const void* z,
+               const float* norm_w, void* out, float* o_core,
+               int B, int T, int H, int D, int K, float scale, float rms_eps,
+               int dtype, void* stream);
+
+/* GDN twins: g is [B][T][H] (one scalar log gate per token and head) and the
+ * output gate is SiLU(z) = z * sigmoid(z) (aprender-serve gdn_ops.rs,
+ * gdn_delta_rule_into and gdn_gated_rmsnorm_into). Everything else as above. */
+int gdn_prefill(const void* q, const void* k, const void* v, const void* g,
+                const void* beta, const float* conv_w, float* conv_ring,
+                const float* state_in, float* state_out, const void* z,
+                const float* norm_w, void* out, float* o_core,
+                int B, int T, int H, int D, int K, float scale, float rms_eps,
+                int dtype, int mode, void* workspace, size_t workspace_bytes,
+                void* stream);
+int gdn_decode(const void* q, const void* k, const void* v, const void* g,
+               const void* beta, const float* conv_w, float* conv_ring,
+               const float* state_in, float* state_out, const void* z,
+               const float* norm_w, void* out, float* o_core,
+               int B, int T, int H, int D, int K, float scale, float rms_eps,
+               int dtype, void* stream);
+
+/* Workspace bytes a prefill with these arguments needs (0 if none). Returns
+ * (size_t)-1 for arguments the prefill would reject. */
+size_t kda_prefill_workspace_bytes(int B, int T, int H, int D, int dtype, int mode);
+size_t gdn_prefill_workspace_bytes(int B, int T, int H, int D, int dtype, int mode);
+
+/* The arm (KDA_ARM_*) a prefill with these arguments runs, or -1 if rejected. */
+int kda_prefill_arm(int B, int T, int H, int D, int dtype, int mode);
+int gdn_prefill_arm(int B, int T, int H, int D, int dtype, int mode);
+
+/* Static description of a status code (never NULL). */
+const char* kda_status_string(int rc);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_MI355X_H */

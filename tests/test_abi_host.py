@@ -1,0 +1,138 @@
+"""C-ABI tests that need no GPU: the library loads, exports every function the
+header declares, and rejects every contract violation before any launch.
+
+The rejected calls pass fake (never dereferenced) device addresses. They are
+skipped when a GPU is visible, where test_gpu_contract.py repeats them with real
+buffers."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_68_amd as kda
+from gated_delta_rule_68_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(?:int|size_t|const char\*)\s+(\w+)\s*\(", text)))
+
+
+def test_library_exports_every_header_symbol():
+    lib = kda.lib()
+    names = header_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), f"libkda.so does not export {n}"
+
+
+def test_status_strings():
+    assert kda.status_string(0) == "ok"
+    for rc in range(40001, 40010):
+        s = kda.status_string(rc)
+        assert s and s != "unknown status code", rc
+    assert "HIP" in kda.status_string(10001)
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+BASE = 1 << 40  # fake, 256-byte aligned, far-apart addresses; never dereferenced
+
+
+def fake_args(B=2, T=3, H=2, D=16, K=4, dtype=0, mode=1):
+    names = ["q", "k", "v", "g", "beta", "conv_w", "ring", "state_in", "state_out", "z",
+             "norm_w", "out", "o_core", "ws"]
+    a = {n: BASE + i * (1 << 32) for i, n in enumerate(names)}
+    a.update(B=B, T=T, H=H, D=D, K=K, dtype=dtype, mode=mode, ws_bytes=1 << 31)
+    return a
+
+
+def call_prefill(a, gdn=False):
+    f = kda.lib().gdn_prefill if gdn else kda.lib().kda_prefill
+    return f(a["q"], a["k"], a["v"], a["g"], a["beta"], a["conv_w"], a["ring"], a["state_in"],
+             a["state_out"], a["z"], a["norm_w"], a["out"], a["o_core"], a["B"], a["T"], a["H"],
+             a["D"], a["K"], 0.25, 1e-5, a["dtype"], a["mode"], a["ws"], a["ws_bytes"], None)
+
+
+def call_decode(a, gdn=False):
+    f = kda.lib().gdn_decode if gdn else kda.lib().kda_decode
+    return f(a["q"], a["k"], a["v"], a["g"], a["beta"], a["conv_w"], a["ring"], a["state_in"],
+             a["state_out"], a["z"], a["norm_w"], a["out"], a["o_core"], a["B"], a["T"], a["H"],
+             a["D"], a["K"], 0.25, 1e-5, a["dtype"], None)
+
+
+CASES = [
+    ("null q", dict(q=None), 40001),
+    ("null state_out", dict(state_out=None), 40001),
+    ("null norm_w", dict(norm_w=None), 40001),
+    ("D=64", dict(D=64), 40002),
+    ("D=0", dict(D=0), 40002),
+    ("K=1", dict(K=1), 40003),
+    ("K=9", dict(K=9), 40003),
+    ("B=0", dict(B=0), 40004),
+    ("T=0", dict(T=0), 40004),
+    ("H=0", dict(H=0), 40004),
+    ("huge", dict(B=1 << 20, T=1 << 20), 40004),
+    ("misaligned q", dict(q=BASE + 8), 40007),
+    ("misaligned ring", dict(ring=BASE + 6 * (1 << 32) + 4), 40007),
+    ("dtype 2", dict(dtype=2), 40008),
+    ("mode 7", dict(mode=7), 40008),
+    ("chunked D=16", dict(mode=2, D=16), 40008),
+    ("out overlaps q", dict(out=BASE + 64), 40009),
+    ("state partial overlap", dict(state_out=BASE + 7 * (1 << 32) + 256), 40009),
+    ("ring overlaps conv_w", dict(ring=BASE + 5 * (1 << 32) + 16), 40009),
+    ("o_core overlaps out", dict(o_core=BASE + 11 * (1 << 32) + 32), 40009),
+]
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="fake pointers only where no GPU is visible")
+@pytest.mark.parametrize("gdn", [False, True])
+@pytest.mark.parametrize("what,over,rc", CASES, ids=[c[0] for c in CASES])
+def test_prefill_contract(what, over, rc, gdn):
+    a = fake_args()
+    a.update({k: (0 if v is None else v) for k, v in over.items()})
+    assert call_prefill(a, gdn) == rc
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="fake pointers only where no GPU is visible")
+@pytest.mark.parametrize("gdn", [False, True])
+def test_decode_contract(gdn):
+    a = fake_args(T=2)
+    assert call_decode(a, gdn) == 40005
+    a = fake_args(T=1, D=64)
+    assert call_decode(a, gdn) == 40002
+    a = fake_args(T=1)
+    a["z"] = 0
+    assert call_decode(a, gdn) == 40001
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="fake pointers only where no GPU is visible")
+def test_workspace_too_small():
+    # B*H small and T long: the split sequential arm, which needs a workspace.
+    a = fake_args(B=1, T=100, H=2, D=16, mode=1)
+    need = kda.workspace_bytes(1, 100, 2, 16, 0, 1)
+    assert need > 0
+    a["ws_bytes"] = need - 1
+    assert call_prefill(a) == 40006
+    a["ws"] = 0
+    a["ws_bytes"] = need
+    assert call_prefill(a) == 40006
+
+
+def test_queries():
+    assert kda.workspace_bytes(1, 1, 64, 128, 1, 1) == 0  # T = 1: fused arm
+    assert kda.prefill_arm(64, 1, 64, 128, 1, 1) == 1
+    assert kda.prefill_arm(1, 4626, 64, 128, 1, 1) == 2
+    assert kda.prefill_arm(1, 64, 2, 64, 0, 1) == -1
+    assert kda.workspace_bytes(0, 1, 1, 16, 0, 1) == ctypes.c_size_t(-1).value
