@@ -63,17 +63,43 @@ def chunk_flops(cfg, C=64) -> float:
     return 2.0 * (5 * C * cfg.D + 3 * cfg.D * cfg.D) * cfg.B * cfg.T * cfg.H
 
 
-def traffic_from_profile(kernel_src: str, name: str):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, if it was
-    taken on the current kernel source; else None."""
+def traffic_from_profile(name: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary
+    (profiles/<name>_traffic.json), if it was taken on the current kernel sources;
+    else None."""
     path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = open(os.path.join(ROOT, "gated_delta_rule_68_amd", "csrc", kernel_src), "rb").read()
-    if rec.get("source_sha256") != hashlib.sha256(src).hexdigest():
+    h = hashlib.sha256()
+    for f in rec.get("source_files", []):
+        h.update(open(os.path.join(ROOT, "gated_delta_rule_68_amd", "csrc", f), "rb").read())
+    if rec.get("source_sha256") != h.hexdigest():
         return None
     return rec.get("bytes_per_launch")
+
+
+COPY_BYTES = 1 << 30
+
+
+def measure_copy(reps: int = 20) -> float:
+    """A plain device copy of COPY_BYTES (torch's copy kernel): read + write GB/s.
+    Also the calibration kernel for the HBM byte counters."""
+    import torch
+
+    x = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        y.copy_(x)
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+    return 2 * COPY_BYTES / (ms * 1e-3) / 1e9
 
 
 def cpu_baseline(cfg, inp, budget_s: float = 12.0):
@@ -182,6 +208,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--copy-only", action="store_true",
+                    help="only run the 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -198,6 +226,9 @@ def main():
         import __graft_entry__
         __graft_entry__.build()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_only:
+        print(json.dumps({"copy_bytes": COPY_BYTES, "copy_gbs": measure_copy()}), flush=True)
+        return
 
     cfg = CONFIGS["kda_decode"]
     log(f"decode: {cfg}")
@@ -206,7 +237,7 @@ def main():
     tokens_per_step = cfg.B * cfg.T
     nbytes = decode_bytes(cfg)
     achieved = nbytes / (kern_avg_ms * 1e-3) / 1e9
-    traffic = traffic_from_profile("kda_seq.hip", "seq_fused_decode")
+    traffic = traffic_from_profile("seq_fused_decode")
     line = {
         "metric": METRIC,
         "value": tokens_per_step / (ms_per_step * 1e-3),
@@ -227,7 +258,7 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "seq_fused_kernel<128,bf16,kda>",
                      "kernel_avg_us": kern_avg_ms * 1e3, "kernel_median_us": kern_med_ms * 1e3,
-                     "algorithmic_bytes": nbytes},
+                     "algorithmic_bytes": nbytes, "measured_copy_gbs": measure_copy()},
     }
     if not args.no_prefill:
         import gated_delta_rule_68_amd as kda

@@ -19,16 +19,27 @@ namespace kda {
 
 namespace {
 
-constexpr int TB_FUSED = 16;  // tokens staged in LDS per pass of the fused kernel
+constexpr int TB_FUSED = 4;   // tokens staged in LDS per pass of the fused kernel
 constexpr int TB_PRE = 32;    // tokens per pre-kernel workgroup
 constexpr int TB_SCAN = 32;   // tokens staged in LDS per pass of the split scan
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // ------------------------------------------------------------------ fused arm
+// Value columns per thread of the fused kernel at D = 128. Two columns (512
+// threads, ~117 VGPRs, two workgroups per CU) measured fastest on the decode step:
+// one column (1024 threads) keeps too little state in flight per CU, four or eight
+// columns raise the register count until occupancy drops.
+template <int D>
+constexpr int fused_cpt() { return D >= 128 ? 2 : 1; }
+template <int D>
+constexpr int fused_threads() { return 8 * D / fused_cpt<D>(); }
+
 template <int D, bool BF, bool GDN>
-__global__ __launch_bounds__(8 * D) void seq_fused_kernel(MixerArgs a) {
-    constexpr int NT = 8 * D;
+__global__ __launch_bounds__(fused_threads<D>()) void seq_fused_kernel(MixerArgs a) {
+    constexpr int CPT = fused_cpt<D>();
+    constexpr int NT = fused_threads<D>();
+    constexpr int NG = NT / 8;  // 8-lane column groups; column of (group g, slot c) = g + c*NG
     constexpr int NW = NT / 64;
     constexpr int KPL = D / 8;
     constexpr int EW = GDN ? 1 : D;
@@ -36,39 +47,47 @@ __global__ __launch_bounds__(8 * D) void seq_fused_kernel(MixerArgs a) {
     __shared__ float es[TB_FUSED][EW];     // exp(g)
     __shared__ float os[TB_FUSED][D];      // scan readout
     __shared__ float bs[TB_FUSED], kqs[TB_FUSED];
+    __shared__ float wins[3 * D][KMAX - 1];  // conv windows between token blocks
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
     const int H = a.H, T = a.T, K = a.K;
     const size_t qkv = (size_t)H * D;
     const size_t head_off = (size_t)h * D;
+    const int grp = wave * 8 + (lane >> 3), s = lane & 7;
 
-    // Scan role: column j, sub-lane s. Issue the state loads first so their HBM
-    // latency overlaps the conv / l2 work below.
-    const int j = wave * 8 + (lane >> 3), s = lane & 7;
-    float S[KPL];
-    load_keys<D>(S, a.state_in + ((size_t)bh * D + j) * D, s);
+    // Issue the state loads first so their HBM latency overlaps the conv / l2 work.
+    float S[CPT][KPL];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+        load_keys<D>(S[c], a.state_in + ((size_t)bh * D + grp + c * NG) * D, s);
 
-    // Conv role: one (plane, channel) per thread for the first 3*D threads.
-    const bool conv_thread = tid < 3 * D;
-    const int plane = tid / D, ch = tid % D;
-    const size_t cf = (size_t)plane * qkv + head_off + ch;
-    float* ring_row = a.ring + ((size_t)b * 3 * qkv + cf) * (K - 1);
-    const void* xsrc = plane == 0 ? a.q : (plane == 1 ? a.k : a.v);
-    ConvChannel cc;
-    if (conv_thread) {
-        conv_load_taps(cc, a.conv_w + cf * K, K);
+    // Conv windows of this head's 3*D (plane, channel) rows start as the old ring.
+    for (int r = tid; r < 3 * D; r += NT) {
+        const int plane = r / D, ch = r % D;
+        const float* ring_row = a.ring + ((size_t)b * 3 * qkv + plane * qkv + head_off + ch) * (K - 1);
+        ConvChannel cc;
         conv_window_from_ring(cc, ring_row, K);
+#pragma unroll
+        for (int e = 0; e < KMAX - 1; ++e) wins[r][e] = cc.win[e];
     }
 
     for (int t0 = 0; t0 < T; t0 += TB_FUSED) {
         const int nt = min(TB_FUSED, T - t0);
         const size_t row0 = (size_t)b * T + t0;
-        if (conv_thread) {
+        for (int r = tid; r < 3 * D; r += NT) {
+            const int plane = r / D, ch = r % D;
+            const void* xsrc = plane == 0 ? a.q : (plane == 1 ? a.k : a.v);
+            ConvChannel cc;
+            conv_load_taps(cc, a.conv_w + (plane * qkv + head_off + ch) * K, K);
+#pragma unroll
+            for (int e = 0; e < KMAX - 1; ++e) cc.win[e] = wins[r][e];
             for (int tt = 0; tt < nt; ++tt) {
                 const float x = ld_act<BF>(xsrc, (row0 + tt) * qkv + head_off + ch);
                 pre[plane][tt][ch] = silu_f(conv_push(cc, x));
             }
+#pragma unroll
+            for (int e = 0; e < KMAX - 1; ++e) wins[r][e] = cc.win[e];
         }
         if constexpr (GDN) {
             if (tid < nt) es[tid][0] = exp_f(ld_act<BF>(a.g, (row0 + tid) * H + h));
@@ -83,20 +102,38 @@ __global__ __launch_bounds__(8 * D) void seq_fused_kernel(MixerArgs a) {
         for (int tt = wave; tt < nt; tt += NW) l2_qk_row<D>(pre[0][tt], pre[1][tt], lane, &kqs[tt]);
         __syncthreads();
         for (int tt = 0; tt < nt; ++tt) {
-            const float o = scan_step<D, GDN>(S, pre[0][tt], pre[1][tt], es[tt], pre[2][tt][j],
-                                              bs[tt], kqs[tt], a.scale, s);
-            if (s == 0) os[tt][j] = o;
+            float vj[CPT], o[CPT];
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) vj[c] = pre[2][tt][grp + c * NG];
+            scan_step_cols<D, GDN, CPT>(S, pre[0][tt], pre[1][tt], es[tt], vj, bs[tt], kqs[tt],
+                                        a.scale, s, o);
+            if (s == 0) {
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) os[tt][grp + c * NG] = o[c];
+            }
         }
         __syncthreads();
-        for (int tt = wave; tt < nt; tt += NW)
-            gated_rmsnorm_row<D, BF, GDN>(os[tt], a, (row0 + tt) * qkv + head_off, lane, a.o_core);
+        for (int tt = wave; tt < nt; tt += NW) {
+            const size_t off = (row0 + tt) * qkv + head_off;
+            const GateRow gz = load_gate_row<D, BF>(a, off, lane);
+            gated_rmsnorm_row<D, BF, GDN>(os[tt], gz, a, off, lane, a.o_core);
+        }
         __syncthreads();
     }
 
-    store_keys<D>(a.state_out + ((size_t)bh * D + j) * D, S, s);
-    // The ring row was read only by this thread (window init); the window now holds
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+        store_keys<D>(a.state_out + ((size_t)bh * D + grp + c * NG) * D, S[c], s);
+    // Each ring row was read only by this workgroup (window init); the windows now hold
     // the last K-1 raw inputs of [old ring ++ x].
-    if (conv_thread) conv_window_to_ring(cc, ring_row, K);
+    for (int r = tid; r < 3 * D; r += NT) {
+        const int plane = r / D, ch = r % D;
+        float* ring_row = a.ring + ((size_t)b * 3 * qkv + plane * qkv + head_off + ch) * (K - 1);
+        ConvChannel cc;
+#pragma unroll
+        for (int e = 0; e < KMAX - 1; ++e) cc.win[e] = wins[r][e];
+        conv_window_to_ring(cc, ring_row, K);
+    }
 }
 
 // ------------------------------------------------------------------ split arm
@@ -193,8 +230,8 @@ __global__ __launch_bounds__(8 * split_cols<D>()) void scan_split_kernel(
     const int jl = wave * 8 + (lane >> 3), s = lane & 7;
     const int j = split * COLS + jl;
 
-    float S[KPL];
-    load_keys<D>(S, a.state_in + ((size_t)bh * D + j) * D, s);
+    float S[1][KPL];
+    load_keys<D>(S[0], a.state_in + ((size_t)bh * D + j) * D, s);
 
     for (int t0 = 0; t0 < T; t0 += TB_SCAN) {
         const int nt = min(TB_SCAN, T - t0);
@@ -218,9 +255,10 @@ __global__ __launch_bounds__(8 * split_cols<D>()) void scan_split_kernel(
         }
         __syncthreads();
         for (int tt = 0; tt < nt; ++tt) {
-            const float ov = scan_step<D, GDN>(S, qs[tt], ks[tt], es[tt], vs[tt][jl], bs[tt],
-                                               kqs[tt], a.scale, s);
-            if (s == 0) os[tt][jl] = ov;
+            const float vj[1] = {vs[tt][jl]};
+            float ov[1];
+            scan_step_cols<D, GDN, 1>(S, qs[tt], ks[tt], es[tt], vj, bs[tt], kqs[tt], a.scale, s, ov);
+            if (s == 0) os[tt][jl] = ov[0];
         }
         __syncthreads();
         for (int idx = tid; idx < nt * COLS; idx += NT) {
@@ -228,7 +266,7 @@ __global__ __launch_bounds__(8 * split_cols<D>()) void scan_split_kernel(
             o[(row0 + tt) * qkv + head_off + split * COLS + c] = os[tt][c];
         }
     }
-    store_keys<D>(a.state_out + ((size_t)bh * D + j) * D, S, s);
+    store_keys<D>(a.state_out + ((size_t)bh * D + j) * D, S[0], s);
 }
 
 // One wavefront per (b, t, h) row.
@@ -239,12 +277,14 @@ __global__ __launch_bounds__(256) void norm_kernel(MixerArgs a, const float* o) 
     const size_t row = (size_t)blockIdx.x * 4 + wave;
     if (row >= rows) return;
     const size_t off = (row / a.H) * ((size_t)a.H * D) + (row % a.H) * D;
-    gated_rmsnorm_row<D, BF, GDN>(o + off, a, off, lane, nullptr);
+    const GateRow gz = load_gate_row<D, BF>(a, off, lane);
+    gated_rmsnorm_row<D, BF, GDN>(o + off, gz, a, off, lane, nullptr);
 }
 
 template <int D, bool BF, bool GDN>
 hipError_t fused_launch(const MixerArgs& a) {
-    hipLaunchKernelGGL((seq_fused_kernel<D, BF, GDN>), dim3(a.B * a.H), dim3(8 * D), 0, a.stream, a);
+    hipLaunchKernelGGL((seq_fused_kernel<D, BF, GDN>), dim3(a.B * a.H), dim3(fused_threads<D>()), 0,
+                       a.stream, a);
     return hipGetLastError();
 }
 
