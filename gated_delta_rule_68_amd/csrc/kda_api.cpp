@@ -42,11 +42,12 @@ int check_shape(int B, int T, int H, int D, int K) {
 // Which arm runs. Sequential work needs many (b, h) pairs to fill the chip with one
 // fused workgroup per pair; below that the column-split pipeline is used, except for
 // very short prefills where its extra launches would dominate.
+// The chunked arm (D = 128) computes its contractions with bf16 operands, so AUTO
+// takes it only for bf16 activations and prefills of at least two chunks.
 int pick_arm(int B, int T, int H, int D, bool bf16, int mode) {
-    (void)bf16;
     const bool chunk_ok = kda::kChunkedArmBuilt && D == 128;
     if (mode == KDA_MODE_CHUNKED) return chunk_ok ? kda::ARM_CHUNKED : -1;
-    if (mode == KDA_MODE_AUTO && chunk_ok && T >= 128) return kda::ARM_CHUNKED;
+    if (mode == KDA_MODE_AUTO && chunk_ok && bf16 && T >= 128) return kda::ARM_CHUNKED;
     if (mode != KDA_MODE_AUTO && mode != KDA_MODE_SEQUENTIAL) return -1;
     if (T <= 16 || (long)B * H >= 1024) return kda::ARM_SEQ_FUSED;
     return kda::ARM_SEQ_SPLIT;

@@ -1,12 +1,547 @@
-// Chunked prefill arm (not built yet: the host never selects it).
+// Chunked prefill arm of the KDA / GDN mixer for gfx950 (D = 128, chunks of 64).
+//
+// The recurrence is taken 64 tokens at a time in its WY / UT form (memra-engine
+// kda.rs, module notes on the chunked twin: a per-channel cumulative log gate,
+// k scaled by exp(-Gcum) and q by exp(+Gcum), and a triangular intra-chunk solve;
+// for GDN the cumulative gate is one scalar per (token, head)). Per chunk of n rows
+// with carried state S (key i x value j) and G the inclusive cumulative log gate:
+//   L[s][j] = sum_i k_s[i] k_j[i] e^{G_s[i]-G_j[i]}  (j < s)
+//   P[s][j] = sum_i q_s[i] k_j[i] e^{G_s[i]-G_j[i]}  (j <= s)
+//   T  = (I + diag(beta) L)^-1
+//   W  = T diag(beta) (e^{G} * k),   U = T diag(beta) v
+//   Ub = U - W S,   O = scale ((e^{G} * q) S + P Ub)
+//   S  = diag(e^{G_last}) S + (e^{G_last - G} * k)^T Ub
+// Every factor e^{...} that multiplies an MFMA operand is <= 1 except on the
+// diagonal 16x16 blocks of L and P, where the decay is rebased to the first row of
+// the block (at most 15 steps of g >= -5, so e^{75} at worst, inside fp32/bf16
+// range); this is why the arm needs g >= -5.
+//
+// One workgroup of 4 wavefronts owns one (sequence, head, value-column split) and
+// walks the chunks in order; the state lives in MFMA accumulator registers as S^T
+// tiles. All contractions run on v_mfma_f32_16x16x32_bf16 (bf16 operands, fp32
+// accumulation); the 64x64 unit-triangular inverse is solved in fp32 (16x16 diagonal
+// blocks by forward substitution, off-diagonal blocks with v_mfma_f32_16x16x4f32).
+// conv + SiLU and l2 run in-kernel on the raw inputs, so the only HBM traffic is the
+// raw activations, the gates, the output and the state once in and once out.
+#include "kda_device.h"
 #include "kda_internal.h"
 
 namespace kda {
 
-const bool kChunkedArmBuilt = false;
+const bool kChunkedArmBuilt = true;
 
-size_t chunked_workspace_bytes(int, int, int, int, bool) { return 0; }
+namespace {
 
-hipError_t launch_chunked(const MixerArgs&) { return hipErrorNotSupported; }
+constexpr int CH = 64;         // chunk length
+constexpr int DK = 128;        // head dim of this arm
+constexpr int NTHR = 256;      // 4 wavefronts
+constexpr int LDH = DK + 8;    // bf16 row stride of [*][128] tiles (272 B: 16-byte aligned, skewed banks)
+constexpr int LDC = CH + 8;    // bf16 row stride of [*][64] tiles (144 B)
+constexpr int LDF = CH + 4;    // fp32 row stride of the 64x64 solve matrices
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4v mfma_bf16(bf16x8 a, bf16x8 b, f32x4v c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4v mfma_f32(float a, float b, f32x4v c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 ld8(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ f32x4v zero4() { return f32x4v{0.0f, 0.0f, 0.0f, 0.0f}; }
+
+// MFMA 16x16x32 operand layout (lane l, q4 = l / 16, l16 = l % 16): an A fragment
+// holds A[l16][8*q4 .. 8*q4+7] of a 16x32 tile, a B fragment B[8*q4 .. +7][l16] of a
+// 32x16 tile, and the 16x16 result D[4*q4 + r][l16] for r = 0..3. With both operands
+// stored "row = M or N index, contiguous = K index" one loader serves A and B.
+
+template <bool GDN, int NC>
+struct ChunkLds {
+    alignas(16) float gam[CH][GDN ? 4 : DK];  // inclusive cumulative log gate
+    alignas(16) __bf16 qh[CH][LDH];           // SiLU(conv q), before l2
+    alignas(16) __bf16 kh[CH][LDH];           // SiLU(conv k), before l2
+    alignas(16) __bf16 pb[CH][LDC];           // P (lower incl. diagonal)
+    alignas(16) float iq[CH], ik[CH], beta[CH];
+    alignas(16) float fn[DK];                 // e^{G_last}
+    alignas(16) float xs[4][16][17];          // per-wave 16x16 scratch of the block solve
+    union {
+        struct {
+            float lf[CH][LDF];  // beta_s L[s][j], strictly lower
+            float tf[CH][LDF];  // T in fp32
+        } solve;
+        __bf16 wneg[CH][LDH];  // -W
+        __bf16 ubt[NC][LDC];   // Ub^T [value][row]
+    } c;
+    union {
+        struct {
+            __bf16 vbt[NC][LDC];  // (beta v)^T [value][row]
+            __bf16 tb[CH][LDC];   // T in bf16
+        } pre;
+        __bf16 sb[NC][LDH];  // S^T in bf16 [value][key]
+    } e;
+};
+
+template <bool GDN>
+__device__ __forceinline__ float gam_at(const float (*gam)[GDN ? 4 : DK], int r, int i) {
+    if constexpr (GDN)
+        return gam[r][0];
+    else
+        return gam[r][i];
+}
+
+// Split index / (b, h) of a block: the column splits of one (b, h) share blockIdx % 8,
+// so they run on the same XCD and share its L2 for the raw q / k / g rows they all read.
+__device__ __forceinline__ void block_coords(int ncol, int nbh, int* bh, int* split) {
+    const int x = blockIdx.x;
+    const int group = x / (8 * ncol), within = x % (8 * ncol);
+    *split = within / 8;
+    *bh = group * 8 + within % 8;
+    if (*bh >= nbh) *bh = -1;
+}
+
+template <bool BF, bool GDN, int NC>
+__global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) {
+    constexpr int NCOL = DK / NC;
+    constexpr int NJB = NC / 16;  // value-column 16-blocks of this split
+    __shared__ ChunkLds<GDN, NC> sm;
+
+    int bh, split;
+    block_coords(NCOL, a.B * a.H, &bh, &split);
+    if (bh < 0) return;  // whole block exits before any barrier
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int q4 = lane >> 4, l16 = lane & 15;
+    const int b = bh / a.H, h = bh % a.H;
+    const int H = a.H, T = a.T, K = a.K;
+    const size_t qkv = (size_t)H * DK;
+    const size_t head_off = (size_t)h * DK;
+    const int jv0 = split * NC;  // first value column of this split
+
+    // ---- state: S^T tiles (value block jb, key blocks 2*wave and 2*wave+1) ----
+    f32x4v accS[NJB][2];
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int jv = jv0 + jb * 16 + 4 * q4 + r, i = (2 * wave + t) * 16 + l16;
+                accS[jb][t][r] = a.state_in[((size_t)bh * DK + jv) * DK + i];
+            }
+
+    // ---- conv channels: (plane q/k, channel) per thread; v channels of the split ----
+    const int cplane = tid / DK, cch = tid % DK;
+    const float* ring_b = a.ring + (size_t)b * 3 * qkv * (K - 1);
+    ConvChannel ccqk, ccv;
+    conv_load_taps(ccqk, a.conv_w + ((size_t)cplane * qkv + head_off + cch) * K, K);
+    conv_window_from_ring(ccqk, ring_b + ((size_t)cplane * qkv + head_off + cch) * (K - 1), K);
+    const void* xqk = cplane == 0 ? a.q : a.k;
+    const bool vthread = tid < NC;
+    if (vthread) {
+        const size_t row = 2 * qkv + head_off + jv0 + tid;
+        conv_load_taps(ccv, a.conv_w + row * K, K);
+        conv_window_from_ring(ccv, ring_b + row * (K - 1), K);
+    }
+
+    for (int c0 = 0; c0 < T; c0 += CH) {
+        const int n = min(CH, T - c0);
+        const size_t row0 = (size_t)b * T + c0;
+
+        // ---- P0: beta and the cumulative gate ----
+        if (tid < CH) sm.beta[tid] = tid < n ? ld_act<BF>(a.beta, (row0 + tid) * H + h) : 0.0f;
+        if constexpr (GDN) {
+            if (tid == 0) {
+                float acc = 0.0f;
+                for (int r = 0; r < CH; ++r) {
+                    if (r < n) acc += ld_act<BF>(a.g, (row0 + r) * H + h);
+                    sm.gam[r][0] = acc;
+                }
+                sm.fn[0] = exp_f(acc);
+            }
+        } else {
+            if (tid < DK) {
+                float acc = 0.0f;
+                for (int r = 0; r < CH; ++r) {
+                    if (r < n) acc += ld_act<BF>(a.g, (row0 + r) * qkv + head_off + tid);
+                    sm.gam[r][tid] = acc;
+                }
+                sm.fn[tid] = exp_f(acc);
+            }
+        }
+        __syncthreads();
+
+        // ---- P1: conv + SiLU of q, k (all channels) and beta * v (split channels) ----
+        {
+            __bf16* dst = cplane == 0 ? &sm.qh[0][0] : &sm.kh[0][0];
+            for (int r = 0; r < CH; ++r) {
+                float y = 0.0f;
+                if (r < n) y = silu_f(conv_push(ccqk, ld_act<BF>(xqk, (row0 + r) * qkv + head_off + cch)));
+                dst[r * LDH + cch] = (__bf16)y;
+            }
+            if (vthread) {
+                for (int r = 0; r < CH; ++r) {
+                    float y = 0.0f;
+                    if (r < n)
+                        y = silu_f(conv_push(ccv, ld_act<BF>(a.v, (row0 + r) * qkv + head_off + jv0 + tid)));
+                    sm.e.pre.vbt[tid][r] = (__bf16)(sm.beta[r] * y);
+                }
+            }
+        }
+        __syncthreads();
+        if (tid < 2 * CH) {  // l2 norms of the rows
+            const int r = tid & (CH - 1);
+            const __bf16* row = (tid < CH) ? &sm.qh[r][0] : &sm.kh[r][0];
+            float ss = 0.0f;
+            for (int i = 0; i < DK; i += 8) {
+                const bf16x8 v8 = ld8(row + i);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss = fmaf((float)v8[e], (float)v8[e], ss);
+            }
+            const float inv = rsqrtf(ss + L2_EPS);
+            if (tid < CH) sm.iq[r] = inv; else sm.ik[r] = inv;
+        }
+        __syncthreads();
+
+        // ---- P2: L and P, block-row a = wave; decay rebased to row 16a ----
+        {
+            const int ab = wave, ra = 16 * ab, s = ra + l16;
+            f32x4v accL[4], accP[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) accL[t] = accP[t] = zero4();
+            const float iks = sm.ik[s], iqs = sm.iq[s];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int i0 = 32 * kk + 8 * q4;
+                float gr[8];
+                bf16x8 ak, aq;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    gr[e] = gam_at<GDN>(sm.gam, ra, i0 + e);
+                    const float ea = exp_f(gam_at<GDN>(sm.gam, s, i0 + e) - gr[e]);
+                    ak[e] = (__bf16)((float)sm.kh[s][i0 + e] * iks * ea);
+                    aq[e] = (__bf16)((float)sm.qh[s][i0 + e] * iqs * ea);
+                }
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) {
+                    if (bb > ab) break;
+                    const int j = 16 * bb + l16;
+                    const float ikj = sm.ik[j];
+                    bf16x8 bk;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float eb = exp_f(gr[e] - gam_at<GDN>(sm.gam, j, i0 + e));
+                        bk[e] = (__bf16)((float)sm.kh[j][i0 + e] * ikj * eb);
+                    }
+                    accL[bb] = mfma_bf16(ak, bk, accL[bb]);
+                    accP[bb] = mfma_bf16(aq, bk, accP[bb]);
+                }
+            }
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int sr = ra + 4 * q4 + r, j = 16 * bb + l16;
+                    const bool lo = bb <= ab;
+                    sm.c.solve.lf[sr][j] = (lo && j < sr) ? sm.beta[sr] * accL[bb][r] : 0.0f;
+                    sm.pb[sr][j] = (__bf16)((lo && j <= sr) ? accP[bb][r] : 0.0f);
+                }
+        }
+        __syncthreads();
+
+        // ---- P3: T = (I + A)^-1, A = diag(beta) L, 16x16 blocks ----
+        {
+            float (*lf)[LDF] = sm.c.solve.lf;
+            float (*tf)[LDF] = sm.c.solve.tf;
+            const int ab = wave;
+            if (q4 == 0) {  // diagonal block ab, column l16, forward substitution
+                float x[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float acc = (r == l16) ? 1.0f : 0.0f;
+#pragma unroll
+                    for (int jj = 0; jj < r; ++jj) acc = fmaf(-lf[16 * ab + r][16 * ab + jj], x[jj], acc);
+                    x[r] = acc;
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) tf[16 * ab + r][16 * ab + l16] = x[r];
+            }
+            for (int idx = lane; idx < 16 * CH; idx += 64) {  // zero the strictly-upper blocks of row block ab
+                const int r = idx / CH, j = idx % CH;
+                if (j >= 16 * (ab + 1)) tf[16 * ab + r][j] = 0.0f;
+            }
+            __syncthreads();
+            // Off-diagonal blocks by distance: T_ab = -T_aa * sum_{c=b}^{a-1} A_ac T_cb.
+            for (int d = 1; d < 4; ++d) {
+                const int bb = ab - d;
+                if (bb >= 0) {
+                    f32x4v xacc = zero4();
+                    for (int cc = bb; cc < ab; ++cc)
+#pragma unroll
+                        for (int kk = 0; kk < 4; ++kk)
+                            xacc = mfma_f32(lf[16 * ab + l16][16 * cc + 4 * kk + q4],
+                                            tf[16 * cc + 4 * kk + q4][16 * bb + l16], xacc);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sm.xs[wave][4 * q4 + r][l16] = xacc[r];
+                }
+                __syncthreads();
+                if (bb >= 0) {
+                    f32x4v tacc = zero4();
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk)
+                        tacc = mfma_f32(tf[16 * ab + l16][16 * ab + 4 * kk + q4],
+                                        sm.xs[wave][4 * kk + q4][l16], tacc);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) tf[16 * ab + 4 * q4 + r][16 * bb + l16] = -tacc[r];
+                }
+                __syncthreads();
+            }
+            for (int idx = tid; idx < CH * CH; idx += NTHR) {
+                const int r = idx / CH, j = idx % CH;
+                sm.e.pre.tb[r][j] = (__bf16)tf[r][j];
+            }
+        }
+        __syncthreads();
+
+        // ---- P4: W = T (beta e^{G} k) -> -W in LDS;  U = T (beta v) in registers ----
+        f32x4v accU[NJB];
+        {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int ib = 2 * wave + t, i = 16 * ib + l16;
+                f32x4v accW[4];
+#pragma unroll
+                for (int sb = 0; sb < 4; ++sb) accW[sb] = zero4();
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    bf16x8 bw;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int j = 32 * kk + 8 * q4 + e;
+                        bw[e] = (__bf16)(sm.beta[j] * (float)sm.kh[j][i] * sm.ik[j] *
+                                         exp_f(gam_at<GDN>(sm.gam, j, i)));
+                    }
+#pragma unroll
+                    for (int sb = 0; sb < 4; ++sb)
+                        accW[sb] = mfma_bf16(ld8(&sm.e.pre.tb[16 * sb + l16][32 * kk + 8 * q4]), bw, accW[sb]);
+                }
+#pragma unroll
+                for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sm.c.wneg[16 * sb + 4 * q4 + r][i] = (__bf16)(-accW[sb][r]);
+            }
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb) accU[jb] = zero4();
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const bf16x8 at = ld8(&sm.e.pre.tb[16 * wave + l16][32 * kk + 8 * q4]);
+#pragma unroll
+                for (int jb = 0; jb < NJB; ++jb)
+                    accU[jb] = mfma_bf16(at, ld8(&sm.e.pre.vbt[16 * jb + l16][32 * kk + 8 * q4]), accU[jb]);
+            }
+        }
+        __syncthreads();
+
+        // ---- P5: S^T to LDS in bf16, then Ub = U - W S ----
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sm.e.sb[16 * jb + 4 * q4 + r][(2 * wave + t) * 16 + l16] = (__bf16)accS[jb][t][r];
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const bf16x8 aw = ld8(&sm.c.wneg[16 * wave + l16][32 * kk + 8 * q4]);
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb)
+                accU[jb] = mfma_bf16(aw, ld8(&sm.e.sb[16 * jb + l16][32 * kk + 8 * q4]), accU[jb]);
+        }
+        __syncthreads();  // every read of -W is done before Ub^T overwrites it
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sm.c.ubt[16 * jb + l16][16 * wave + 4 * q4 + r] = (__bf16)accU[jb][r];
+        __syncthreads();
+
+        // ---- P6: O = scale (Q+ S + P Ub), rows of block `wave`, then the norm ----
+        {
+            const int s = 16 * wave + l16;
+            const float iqs = sm.iq[s];
+            f32x4v accO[NJB];
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb) accO[jb] = zero4();
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int i0 = 32 * kk + 8 * q4;
+                bf16x8 aq;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    aq[e] = (__bf16)((float)sm.qh[s][i0 + e] * iqs * exp_f(gam_at<GDN>(sm.gam, s, i0 + e)));
+#pragma unroll
+                for (int jb = 0; jb < NJB; ++jb)
+                    accO[jb] = mfma_bf16(aq, ld8(&sm.e.sb[16 * jb + l16][i0]), accO[jb]);
+            }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                if (32 * kk > 16 * wave + 15) break;  // P is lower triangular
+                const bf16x8 ap = ld8(&sm.pb[s][32 * kk + 8 * q4]);
+#pragma unroll
+                for (int jb = 0; jb < NJB; ++jb)
+                    accO[jb] = mfma_bf16(ap, ld8(&sm.c.ubt[16 * jb + l16][32 * kk + 8 * q4]), accO[jb]);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int sr = 16 * wave + 4 * q4 + r;
+                const size_t off = (row0 + sr) * qkv + head_off + jv0;
+                float o[NJB];
+#pragma unroll
+                for (int jb = 0; jb < NJB; ++jb) o[jb] = a.scale * accO[jb][r];
+                if constexpr (NCOL == 1) {
+                    float ss = 0.0f;
+#pragma unroll
+                    for (int jb = 0; jb < NJB; ++jb) ss = fmaf(o[jb], o[jb], ss);
+                    ss += __shfl_xor(ss, 1, 64);
+                    ss += __shfl_xor(ss, 2, 64);
+                    ss += __shfl_xor(ss, 4, 64);
+                    ss += __shfl_xor(ss, 8, 64);
+                    const float inv = rsqrtf(fmaf(ss, 1.0f / DK, a.rms_eps));
+                    if (sr < n) {
+#pragma unroll
+                        for (int jb = 0; jb < NJB; ++jb) {
+                            const int jv = 16 * jb + l16;
+                            const float zz = ld_act<BF>(a.z, off + jv);
+                            const float gate = GDN ? silu_f(zz) : sigmoid_f(zz);
+                            st_act<BF>(a.out, off + jv, ((o[jb] * inv) * a.norm_w[jv]) * gate);
+                            if (o_buf) o_buf[off + jv] = o[jb];
+                        }
+                    }
+                } else {
+                    if (sr < n) {
+#pragma unroll
+                        for (int jb = 0; jb < NJB; ++jb) o_buf[off + 16 * jb + l16] = o[jb];
+                    }
+                }
+            }
+        }
+
+        // ---- P7: S = diag(e^{G_last}) S + K_dec^T Ub ----
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int ib = 2 * wave + t, i = 16 * ib + l16;
+            const float dec = sm.fn[GDN ? 0 : i];
+            const float glast = gam_at<GDN>(sm.gam, CH - 1, i);
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) accS[jb][t][r] *= dec;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                bf16x8 bkd;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int sr = 32 * kk + 8 * q4 + e;
+                    bkd[e] = (__bf16)((float)sm.kh[sr][i] * sm.ik[sr] *
+                                      exp_f(glast - gam_at<GDN>(sm.gam, sr, i)));
+                }
+#pragma unroll
+                for (int jb = 0; jb < NJB; ++jb)
+                    accS[jb][t] = mfma_bf16(ld8(&sm.c.ubt[16 * jb + l16][32 * kk + 8 * q4]), bkd, accS[jb][t]);
+            }
+        }
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int jv = jv0 + jb * 16 + 4 * q4 + r, i = (2 * wave + t) * 16 + l16;
+                a.state_out[((size_t)bh * DK + jv) * DK + i] = accS[jb][t][r];
+            }
+}
+
+// The ring roll of the chunked arm: new slot K-1-d = raw input at token T-d (the old
+// ring for T-d < 0). Launched after the chunk kernel, which read the old ring.
+template <bool BF>
+__global__ __launch_bounds__(256) void ring_roll_kernel(MixerArgs a) {
+    const size_t rows = (size_t)a.B * 3 * a.H * DK;
+    const size_t row = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (row >= rows) return;
+    const size_t qkv = (size_t)a.H * DK;
+    const int b = (int)(row / (3 * qkv));
+    const size_t cf = row % (3 * qkv);
+    const int plane = (int)(cf / qkv);
+    const size_t ch = cf % qkv;
+    const void* x = plane == 0 ? a.q : (plane == 1 ? a.k : a.v);
+    const int K = a.K, T = a.T;
+    float* ring_row = a.ring + row * (K - 1);
+    float nr[KMAX - 1];
+#pragma unroll
+    for (int d = 1; d < KMAX; ++d) {
+        const int pos = T - d;
+        nr[KMAX - 1 - d] = (d <= K - 1) ? (pos >= 0 ? ld_act<BF>(x, ((size_t)b * T + pos) * qkv + ch)
+                                                     : ring_row[pos + K - 1])
+                                        : 0.0f;
+    }
+#pragma unroll
+    for (int d = 1; d < KMAX; ++d)
+        if (d <= K - 1) ring_row[K - 1 - d] = nr[KMAX - 1 - d];
+}
+
+int chunk_ncol(int B, int H) {
+    const long bh = (long)B * H;
+    if (bh >= 256) return 1;
+    if (bh >= 128) return 2;
+    return 4;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+template <bool BF, bool GDN, int NC>
+hipError_t chunk_launch_nc(const MixerArgs& a, float* o_buf) {
+    constexpr int NCOL = DK / NC;
+    const int nbh = a.B * a.H;
+    const int grid = ((nbh + 7) / 8) * 8 * NCOL;
+    hipLaunchKernelGGL((chunk_kernel<BF, GDN, NC>), dim3(grid), dim3(NTHR), 0, a.stream, a, o_buf);
+    return hipGetLastError();
+}
+
+template <bool BF, bool GDN>
+hipError_t chunk_launch(const MixerArgs& a) {
+    const int ncol = chunk_ncol(a.B, a.H);
+    float* o_buf = a.o_core;
+    if (ncol > 1 && !o_buf) o_buf = static_cast<float*>(a.ws);
+    hipError_t e;
+    if (ncol == 1) e = chunk_launch_nc<BF, GDN, 128>(a, o_buf);
+    else if (ncol == 2) e = chunk_launch_nc<BF, GDN, 64>(a, o_buf);
+    else e = chunk_launch_nc<BF, GDN, 32>(a, o_buf);
+    if (e != hipSuccess) return e;
+    if (ncol > 1) {
+        e = launch_norm(a, o_buf);
+        if (e != hipSuccess) return e;
+    }
+    const size_t rows = (size_t)a.B * 3 * a.H * DK;
+    hipLaunchKernelGGL((ring_roll_kernel<BF>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
+                       a.stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t chunked_workspace_bytes(int B, int T, int H, int D, bool gdn) {
+    (void)gdn;
+    if (D != DK || chunk_ncol(B, H) == 1) return 0;
+    return align256((size_t)B * T * H * D * 4);  // fp32 pre-norm output of the column splits
+}
+
+hipError_t launch_chunked(const MixerArgs& a) {
+    if (a.D != DK) return hipErrorInvalidValue;
+    if (a.bf16) return a.gdn ? chunk_launch<true, true>(a) : chunk_launch<true, false>(a);
+    return a.gdn ? chunk_launch<false, true>(a) : chunk_launch<false, false>(a);
+}
 
 }  // namespace kda

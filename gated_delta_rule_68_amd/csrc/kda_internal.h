@@ -52,5 +52,7 @@ size_t chunked_workspace_bytes(int B, int T, int H, int D, bool gdn);
 hipError_t launch_seq_fused(const MixerArgs& a);
 hipError_t launch_seq_split(const MixerArgs& a);
 hipError_t launch_chunked(const MixerArgs& a);
+// Gated RMSNorm of a fp32 pre-norm output o [B][T][H*D] into a.out.
+hipError_t launch_norm(const MixerArgs& a, const float* o);
 
 }  // namespace kda

@@ -353,6 +353,31 @@ SplitWorkspace split_workspace(int B, int T, int H, int D, bool gdn) {
 }
 
 hipError_t launch_seq_fused(const MixerArgs& a) { return dispatch<FusedOp>(a); }
+
+hipError_t launch_norm(const MixerArgs& a, const float* o) {
+    const size_t rows = (size_t)a.B * a.T * a.H;
+    const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+    if (a.D == 128) {
+        if (a.bf16) {
+            if (a.gdn) hipLaunchKernelGGL((norm_kernel<128, true, true>), grid, block, 0, a.stream, a, o);
+            else hipLaunchKernelGGL((norm_kernel<128, true, false>), grid, block, 0, a.stream, a, o);
+        } else {
+            if (a.gdn) hipLaunchKernelGGL((norm_kernel<128, false, true>), grid, block, 0, a.stream, a, o);
+            else hipLaunchKernelGGL((norm_kernel<128, false, false>), grid, block, 0, a.stream, a, o);
+        }
+    } else if (a.D == 16) {
+        if (a.bf16) {
+            if (a.gdn) hipLaunchKernelGGL((norm_kernel<16, true, true>), grid, block, 0, a.stream, a, o);
+            else hipLaunchKernelGGL((norm_kernel<16, true, false>), grid, block, 0, a.stream, a, o);
+        } else {
+            if (a.gdn) hipLaunchKernelGGL((norm_kernel<16, false, true>), grid, block, 0, a.stream, a, o);
+            else hipLaunchKernelGGL((norm_kernel<16, false, false>), grid, block, 0, a.stream, a, o);
+        }
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
 hipError_t launch_seq_split(const MixerArgs& a) { return dispatch<SplitOp>(a); }
 
 }  // namespace kda

@@ -1,0 +1,150 @@
+"""GPU parity of the chunked prefill arm (D = 128, chunks of 64, bf16 MFMA operands)
+against the fp64 oracle and against the sequential arm on identical inputs."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_68_amd as kda
+import oracle
+from gated_delta_rule_68_amd.synth import CONFIGS, make_inputs
+from gated_delta_rule_68_amd.torch_io import to_device, to_f64
+from tests.gpu_util import (DEV, compare_to_oracle, inputs_for, oracle_run, run_gpu)
+
+pytestmark = pytest.mark.gpu
+SEQ, CHK = kda.KDA_MODE_SEQUENTIAL, kda.KDA_MODE_CHUNKED
+TOL = 2e-2  # bf16-operand arm
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+def _rel(a, b):
+    return oracle.rel_linf(to_f64(a), to_f64(b))
+
+
+def _vs_sequential(cfg, dev, got, keys=("out", "o_core", "state", "ring"), tol=TOL):
+    ref = run_gpu(cfg, dev, mode=SEQ)
+    errs = {k: _rel(got[k], ref[k]) for k in keys}
+    _print("chunked vs sequential:", errs)
+    for k, e in errs.items():
+        assert e <= tol, f"{k}: chunked vs sequential {e:.3e} > {tol}"
+    assert errs.get("ring", 0.0) == 0.0
+    return errs
+
+
+@pytest.mark.parametrize("T", [1, 37, 64, 65, 200])
+@pytest.mark.parametrize("gdn", [False, True])
+@pytest.mark.parametrize("B,H", [(2, 3), (1, 200), (2, 160)])
+def test_small_vs_oracle(T, gdn, B, H):
+    """Ragged T (partial chunks, T < K-1), every column-split variant (B*H < 128 -> 4
+    splits, 128..255 -> 2, >= 256 -> 1), random state and ring."""
+    cfg = CONFIGS["kda_decode"].with_(B=B, H=H, T=T, gdn=gdn)
+    _print("case", cfg)
+    inp, dev = inputs_for(cfg)
+    got = run_gpu(cfg, dev, mode=CHK)
+    torch.cuda.synchronize()
+    heads = [0, H // 2, H - 1]
+    ref, ch, rows, bsel, hh = oracle_run(inp, heads=heads, threads=16)
+    errs = compare_to_oracle(cfg, got, ref, ch, rows, bsel, hh, tol=TOL)
+    _print("errs", errs)
+
+
+@pytest.mark.parametrize("gdn", [False, True])
+def test_alternating_gates_vs_oracle(gdn):
+    """Gates pushed to both ends of [-5, 0] on alternate heads (the long-prefill regime)
+    exercise the rebased decay of the intra-chunk blocks."""
+    cfg = CONFIGS["kda_long"].with_(B=2, T=300, H=8, gdn=gdn, random_init=True)
+    inp, dev = inputs_for(cfg)
+    got = run_gpu(cfg, dev, mode=CHK)
+    torch.cuda.synchronize()
+    ref, ch, rows, bsel, hh = oracle_run(inp, threads=16)
+    errs = compare_to_oracle(cfg, got, ref, ch, rows, bsel, hh, tol=TOL)
+    _print("errs", errs)
+
+
+def test_fp32_inputs_chunked():
+    """fp32 activations through the chunked arm: bf16-operand accuracy."""
+    cfg = CONFIGS["kda_decode"].with_(B=2, H=4, T=150, dtype="fp32")
+    inp, dev = inputs_for(cfg)
+    got = run_gpu(cfg, dev, mode=CHK)
+    torch.cuda.synchronize()
+    ref, ch, rows, bsel, hh = oracle_run(inp, threads=16)
+    compare_to_oracle(cfg, got, ref, ch, rows, bsel, hh, tol=TOL)
+
+
+def test_prefill_full_size():
+    """Single-sequence prefill T=4626, H=64 (4 column splits): sampled heads against the
+    oracle, everything against the sequential arm."""
+    cfg = CONFIGS["kda_prefill"]
+    inp, dev = inputs_for(cfg)
+    assert kda.prefill_arm(cfg.B, cfg.T, cfg.H, cfg.D, 1, kda.KDA_MODE_AUTO) == 3
+    got = run_gpu(cfg, dev, mode=kda.KDA_MODE_AUTO)
+    torch.cuda.synchronize()
+    ref, ch, rows, bsel, hh = oracle_run(inp, heads=[0, 33, 63])
+    errs = compare_to_oracle(cfg, got, ref, ch, rows, bsel, hh, tol=TOL)
+    _print("oracle errs", errs)
+    _vs_sequential(cfg, dev, got)
+
+
+def test_gdn_full_size():
+    cfg = CONFIGS["gdn_prefill"]
+    inp, dev = inputs_for(cfg)
+    got = run_gpu(cfg, dev, mode=CHK)
+    torch.cuda.synchronize()
+    ref, ch, rows, bsel, hh = oracle_run(inp, heads=[7], batches=[1, 2])
+    errs = compare_to_oracle(cfg, got, ref, ch, rows, bsel, hh, tol=TOL)
+    _print("oracle errs", errs)
+    _vs_sequential(cfg, dev, got)
+
+
+def _long_device_inputs(cfg, prefix=512, period=1024):
+    """Full-size long-prefill inputs on the device: the first `period` tokens of every
+    sequence come from the seeded host generator and are repeated to length T (the
+    prefix [0, prefix) is exactly the generator's, so the oracle can check it)."""
+    inp = make_inputs(cfg, T=period)
+    small = to_device(inp, DEV)
+    reps = (cfg.T + period - 1) // period
+    dev = {}
+    for n, t in small.items():
+        if n in ("q", "k", "v", "g", "beta", "z"):
+            dev[n] = t.repeat(1, reps, *([1] * (t.dim() - 2)))[:, :cfg.T].contiguous()
+        else:
+            dev[n] = t
+    del small
+    return make_inputs(cfg, T=prefix), dev
+
+
+def test_long_full_size():
+    """B=8, T=16384, H=64 (one column split): outputs of tokens [0, 512) against the
+    oracle, the full run against the sequential arm, and the state after 512 tokens
+    (a separate run) against the oracle."""
+    cfg = CONFIGS["kda_long"]
+    pinp, dev = _long_device_inputs(cfg)
+    got = run_gpu(cfg, dev, mode=CHK, o_core=True)
+    torch.cuda.synchronize()
+    ref, ch, rows, bsel, hh = oracle_run(pinp, heads=[0, 1, 62, 63], threads=16)
+    P = 512
+    out_err = oracle.rel_linf(to_f64(got["out"][:, :P])[bsel][:, :, ch], ref["out"])
+    core_err = oracle.rel_linf(to_f64(got["o_core"][:, :P])[bsel][:, :, ch], ref["o_core"])
+    _print("prefix errs out", out_err, "o_core", core_err)
+    assert out_err <= TOL and core_err <= TOL
+    short = run_gpu(cfg, dev, mode=CHK, T=P)
+    st_err = oracle.rel_linf(to_f64(short["state"])[bsel][:, hh], ref["state"])
+    _print("512-token state err", st_err)
+    assert st_err <= TOL
+    _vs_sequential(cfg, dev, got, keys=("out", "state", "ring"))
+
+
+@pytest.mark.parametrize("split", [64, 100])
+def test_split_prefill_close_to_one(split):
+    cfg = CONFIGS["kda_decode"].with_(B=2, H=4, T=300)
+    inp, dev = inputs_for(cfg)
+    one = run_gpu(cfg, dev, mode=CHK)
+    ring, state = dev["ring"].clone(), dev["state"].clone()
+    a = run_gpu(cfg, dev, mode=CHK, T=split, ring=ring, state=state, inplace=True)
+    b = run_gpu(cfg, dev, mode=CHK, t0=split, T=cfg.T - split, ring=ring, state=state, inplace=True)
+    out = torch.cat([a["out"], b["out"]], 1)
+    assert _rel(out, one["out"]) <= TOL
+    assert _rel(state, one["state"]) <= TOL
+    assert torch.equal(ring, one["ring"])
