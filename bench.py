@@ -166,14 +166,13 @@ def run_decode(cfg, steps, warmup):
     return inp, wall, sum(kern_ms) / len(kern_ms), kern_ms[len(kern_ms) // 2]
 
 
-def run_prefill(cfg, mode, reps=5):
+def run_prefill(cfg, mode, reps=5, d=None):
     import torch
 
     import gated_delta_rule_68_amd as kda
-    from gated_delta_rule_68_amd.synth import make_inputs
-    from gated_delta_rule_68_amd.torch_io import alloc_outputs, to_device
+    from gated_delta_rule_68_amd.torch_io import alloc_outputs, tiled_device_inputs
 
-    d = to_device(make_inputs(cfg), "cuda")
+    d = dict(tiled_device_inputs(cfg) if d is None else d)
     d.update(alloc_outputs(cfg, cfg.T, "cuda", o_core=False))
     code = kda.KDA_DTYPE_BF16 if cfg.dtype == "bf16" else kda.KDA_DTYPE_F32
     nb = kda.workspace_bytes(cfg.B, cfg.T, cfg.H, cfg.D, code, mode, gdn=cfg.gdn)
@@ -199,6 +198,40 @@ def run_prefill(cfg, mode, reps=5):
     ms = sorted(a.elapsed_time(b) for a, b in evs)[reps // 2]
     arm = kda.prefill_arm(cfg.B, cfg.T, cfg.H, cfg.D, code, mode, gdn=cfg.gdn)
     return ms, kda.ARM_NAMES.get(arm, str(arm))
+
+
+def run_prefill_legs() -> dict:
+    """Each prefill workload on the chunked and the sequential arm: time of the whole
+    arm (every kernel it launches), tokens/s, algorithmic HBM GB/s and, for the
+    chunked arm, the dense-tile contraction TFLOP/s as a fraction of the bf16 peak."""
+    import torch
+
+    import gated_delta_rule_68_amd as kda
+    from gated_delta_rule_68_amd.synth import CONFIGS
+    from gated_delta_rule_68_amd.torch_io import tiled_device_inputs
+
+    legs = {}
+    for name in ("kda_prefill", "gdn_prefill", "kda_long"):
+        cfg = CONFIGS[name]
+        d = tiled_device_inputs(cfg)
+        rec = {"workload": f"{'GDN' if cfg.gdn else 'KDA'} prefill B={cfg.B} T={cfg.T} "
+                           f"H={cfg.H} D={cfg.D} {cfg.dtype}",
+               "algorithmic_bytes": prefill_bytes(cfg), "dense_tile_flops": chunk_flops(cfg)}
+        for mode in (kda.KDA_MODE_CHUNKED, kda.KDA_MODE_SEQUENTIAL):
+            if kda.prefill_arm(cfg.B, cfg.T, cfg.H, cfg.D, 1, mode, gdn=cfg.gdn) < 0:
+                continue
+            ms, arm = run_prefill(cfg, mode, reps=3 if cfg.T * cfg.B > 50000 else 5, d=d)
+            r = {"ms": ms, "tokens_per_s": cfg.B * cfg.T / (ms * 1e-3),
+                 "hbm_gbs": prefill_bytes(cfg) / (ms * 1e-3) / 1e9}
+            if arm == "chunked":
+                tf = chunk_flops(cfg) / (ms * 1e-3) / 1e12
+                r.update({"mfma_tflops": tf, "mfma_frac": tf / BF16_PEAK_TFLOPS})
+            rec[arm] = r
+            log(f"prefill {name} {arm}: {r}")
+        legs[name] = rec
+        del d
+        torch.cuda.empty_cache()
+    return legs
 
 
 def main():
@@ -261,21 +294,7 @@ def main():
                      "algorithmic_bytes": nbytes, "measured_copy_gbs": measure_copy()},
     }
     if not args.no_prefill:
-        import gated_delta_rule_68_amd as kda
-        pcfg = CONFIGS["kda_prefill"]
-        extra = {}
-        for mode in (kda.KDA_MODE_SEQUENTIAL, kda.KDA_MODE_CHUNKED):
-            if kda.prefill_arm(pcfg.B, pcfg.T, pcfg.H, pcfg.D, 1, mode) < 0:
-                continue
-            ms, arm = run_prefill(pcfg, mode)
-            rec = {"arm": arm, "ms": ms, "tokens_per_s": pcfg.B * pcfg.T / (ms * 1e-3),
-                   "hbm_gbs": prefill_bytes(pcfg) / (ms * 1e-3) / 1e9}
-            if arm == "chunked":
-                tf = chunk_flops(pcfg) / (ms * 1e-3) / 1e12
-                rec.update({"mfma_tflops": tf, "mfma_frac": tf / BF16_PEAK_TFLOPS})
-            extra[arm] = rec
-            log(f"prefill {arm}: {rec}")
-        line["prefill"] = {"workload": "KDA prefill B=1 T=4626 H=64 D=128 bf16", **extra}
+        line["prefill"] = run_prefill_legs()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, inp)
     print(json.dumps(line), flush=True)

@@ -24,6 +24,23 @@ def to_device(inp: Inputs, device="cuda") -> dict:
     return d
 
 
+def tiled_device_inputs(cfg, period: int = 1024, device="cuda") -> dict:
+    """Device inputs of a long workload: the seeded generator draws the first `period`
+    tokens of every sequence and they are repeated up to cfg.T (values keep the
+    workload's distributions; tokens [0, period) are exactly the generator's)."""
+    from .synth import make_inputs
+
+    small = to_device(make_inputs(cfg, T=min(period, cfg.T)), device)
+    reps = (cfg.T + period - 1) // period
+    out = {}
+    for n, t in small.items():
+        if n in ACTS:
+            out[n] = t.repeat(1, reps, *([1] * (t.dim() - 2)))[:, :cfg.T].contiguous()
+        else:
+            out[n] = t
+    return out
+
+
 def act_dtype(cfg) -> torch.dtype:
     return torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
 

@@ -7,7 +7,7 @@ import torch
 import gated_delta_rule_68_amd as kda
 import oracle
 from gated_delta_rule_68_amd.synth import CONFIGS, make_inputs
-from gated_delta_rule_68_amd.torch_io import to_device, to_f64
+from gated_delta_rule_68_amd.torch_io import tiled_device_inputs, to_f64
 from tests.gpu_util import (DEV, compare_to_oracle, inputs_for, oracle_run, run_gpu)
 
 pytestmark = pytest.mark.gpu
@@ -98,29 +98,12 @@ def test_gdn_full_size():
     _vs_sequential(cfg, dev, got)
 
 
-def _long_device_inputs(cfg, prefix=512, period=1024):
-    """Full-size long-prefill inputs on the device: the first `period` tokens of every
-    sequence come from the seeded host generator and are repeated to length T (the
-    prefix [0, prefix) is exactly the generator's, so the oracle can check it)."""
-    inp = make_inputs(cfg, T=period)
-    small = to_device(inp, DEV)
-    reps = (cfg.T + period - 1) // period
-    dev = {}
-    for n, t in small.items():
-        if n in ("q", "k", "v", "g", "beta", "z"):
-            dev[n] = t.repeat(1, reps, *([1] * (t.dim() - 2)))[:, :cfg.T].contiguous()
-        else:
-            dev[n] = t
-    del small
-    return make_inputs(cfg, T=prefix), dev
-
-
 def test_long_full_size():
     """B=8, T=16384, H=64 (one column split): outputs of tokens [0, 512) against the
     oracle, the full run against the sequential arm, and the state after 512 tokens
     (a separate run) against the oracle."""
     cfg = CONFIGS["kda_long"]
-    pinp, dev = _long_device_inputs(cfg)
+    pinp, dev = make_inputs(cfg, T=512), tiled_device_inputs(cfg, period=1024)
     got = run_gpu(cfg, dev, mode=CHK, o_core=True)
     torch.cuda.synchronize()
     ref, ch, rows, bsel, hh = oracle_run(pinp, heads=[0, 1, 62, 63], threads=16)
@@ -148,3 +131,15 @@ def test_split_prefill_close_to_one(split):
     assert _rel(out, one["out"]) <= TOL
     assert _rel(state, one["state"]) <= TOL
     assert torch.equal(ring, one["ring"])
+
+
+@pytest.mark.parametrize("K", [2, 3, 6, 8])
+@pytest.mark.parametrize("mode", [SEQ, CHK])
+def test_conv_kernel_widths(K, mode):
+    """Conv kernels other than 4 (2..8 are allowed) on both arms, with a ragged chunk."""
+    cfg = CONFIGS["kda_decode"].with_(B=2, H=3, T=70, K=K)
+    inp, dev = inputs_for(cfg)
+    got = run_gpu(cfg, dev, mode=mode)
+    torch.cuda.synchronize()
+    ref, ch, rows, bsel, hh = oracle_run(inp, threads=16)
+    compare_to_oracle(cfg, got, ref, ch, rows, bsel, hh, tol=TOL)
