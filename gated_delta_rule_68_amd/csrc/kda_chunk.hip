@@ -343,10 +343,12 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
     // (KDA) the per-channel gate scans run on threads 128..255 meanwhile.
     // The taps are re-read every chunk (a few L2-resident bytes) rather than held in
     // registers across the whole chunk loop.
-    // q / k item: (plane, 8-row group, 4-channel group); the 32 lanes of one row
-    // group and plane are consecutive, so the row norm is a 32-lane reduction.
-    const int cplane = tid / 256, crg = (tid / 32) % 8, ccg = tid % 32;
-    constexpr int NVI = 8 * (NC / 4);
+    // Conv items are 4 rows x 4 channels: thread tid convolves q rows (tid / 32) * 4..
+    // and k rows of the same group, channels (tid % 32) * 4.., and, if tid < NVI, one v
+    // item; the 32 lanes of one row group are consecutive, so the l2 norm of a row is a
+    // 32-lane reduction.
+    const int crg = (tid / 32) % 16, ccg = tid % 32;
+    constexpr int NVI = 16 * (NC / 4);
     const bool vthread = tid < NVI;
     const int vrg = tid / (NC / 4), vcg = tid % (NC / 4);
 
@@ -362,22 +364,40 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
         KDA_LAUNDER_LANE();
         // ---- P0: conv taps (the chunk's raw rows are already in LDS: the previous
         // iteration, or the prologue, staged them) ----
-        float wqk[4][KT], wv[4][KT];
-        load_taps4<KT>(wqk, a.conv_w, (size_t)cplane * qkv + head_off + ccg * 4, K);
+        float wq[4][KT], wk[4][KT], wv[4][KT];
+        load_taps4<KT>(wq, a.conv_w, head_off + ccg * 4, K);
+        load_taps4<KT>(wk, a.conv_w, qkv + head_off + ccg * 4, K);
         if (vthread) load_taps4<KT>(wv, a.conv_w, 2 * qkv + head_off + jv0 + vcg * 4, K);
 
         KDA_LAUNDER_LANE();
-        // ---- P1: conv + SiLU (+ l2 for q, k) of 8 rows x 4 channels per item ----
-        {
-            const __bf16* rawp = (cplane == 0 ? &sm.c.raw.rq[0][0] : &sm.c.raw.rk[0][0]) + ccg * 4;
-            __bf16* dst = (cplane == 0 ? &sm.qh[0][0] : &sm.kh[0][0]) + ccg * 4;
+        // ---- P1: cumulative gate (4 threads per channel), then conv + SiLU (+ l2 for
+        // q, k) of 4-row x 4-channel items ----
+        if constexpr (!GDN) {
+            const int c = tid >> 2, qq = tid & 3;  // rows 16 qq .. 16 qq + 15 of channel c
+            float g16[16], acc = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                acc += sm.gam[16 * qq + r][c];
+                g16[r] = acc;
+            }
+            // exclusive prefix of the quarter totals over the 4 lanes of the channel
+            const float t1 = __shfl_up(acc, 1, 4), t2 = __shfl_up(acc, 2, 4), t3 = __shfl_up(acc, 3, 4);
+            const float base = (qq >= 1 ? t1 : 0.0f) + (qq >= 2 ? t2 : 0.0f) + (qq >= 3 ? t3 : 0.0f);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sm.gam[16 * qq + r][c] = base + g16[r];
+            if (qq == 3) sm.fn[c] = exp_f(base + acc);
+        }
+#pragma unroll
+        for (int plane = 0; plane < 2; ++plane) {
+            const __bf16* rawp = (plane == 0 ? &sm.c.raw.rq[0][0] : &sm.c.raw.rk[0][0]) + ccg * 4;
+            __bf16* dst = (plane == 0 ? &sm.qh[0][0] : &sm.kh[0][0]) + ccg * 4;
             ConvWin4<KT> cw;
-            cw.init(rawp, LDH, &sm.hist[0][cplane * DK + ccg * 4], HLD, crg * 8);
-#pragma unroll 2
-            for (int rr = 0; rr < 8; ++rr) {
-                const int r = crg * 8 + rr;
+            cw.init(rawp, LDH, &sm.hist[0][plane * DK + ccg * 4], HLD, crg * 4);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int r = crg * 4 + rr;
                 float y[4];
-                cw.step(ld4(rawp + r * LDH), wqk, r < n, y);
+                cw.step(ld4(rawp + r * LDH), plane == 0 ? wq : wk, r < n, y);
                 float ss = 0.0f;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) ss = fmaf(y[e], y[e], ss);
@@ -396,27 +416,15 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
         if (vthread) {
             const __bf16* rawp = &sm.e.pre.u.rv[0][vcg * 4];
             ConvWin4<KT> cw;
-            cw.init(rawp, NC + 8, &sm.hist[0][2 * DK + vcg * 4], HLD, vrg * 8);
-#pragma unroll 2
-            for (int rr = 0; rr < 8; ++rr) {
-                const int r = vrg * 8 + rr;
+            cw.init(rawp, NC + 8, &sm.hist[0][2 * DK + vcg * 4], HLD, vrg * 4);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int r = vrg * 4 + rr;
                 float y[4];
                 cw.step(ld4(rawp + r * (NC + 8)), wv, r < n, y);
                 const float bt = sm.beta[r];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) sm.e.pre.vbt[vcg * 4 + e][r] = (__bf16)(bt * y[e]);
-            }
-        }
-        if constexpr (!GDN) {
-            if (tid >= NTHR - DK) {  // inclusive scan of the log gate over the rows, per channel
-                const int c = tid - (NTHR - DK);
-                float acc = 0.0f;
-#pragma unroll 8
-                for (int r = 0; r < CH; ++r) {
-                    acc += sm.gam[r][c];
-                    sm.gam[r][c] = acc;
-                }
-                sm.fn[c] = exp_f(acc);
             }
         }
         lds_barrier();
@@ -485,7 +493,17 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
         lds_barrier();
 
         // The next chunk's raw rows are requested here and stored at the end of this
-        // iteration, so their HBM latency overlaps P3..P7.
+        // iteration, and this chunk's output gates z for the norm in P6, so both HBM
+        // latencies overlap P3..P6.
+        constexpr int NZ = NCOL == 1 ? CH * (DK / 8) / NTHR : 1;
+        bf16x8 zpre[NZ];
+        if constexpr (NCOL == 1) {
+#pragma unroll
+            for (int it = 0; it < NZ; ++it) {
+                const int r = (tid + NTHR * it) / (DK / 8), c8 = (tid % (DK / 8)) * 8;
+                zpre[it] = ld_act8<BF>(a.z, (row0 + min(r, n - 1)) * qkv + head_off + c8);
+            }
+        }
         if (c0 + CH < T) load_raw<BF, GDN, NC>(raw, a, b, h, c0 + CH, jv0, tid);
         KDA_LAUNDER_LANE();
         // ---- P3: T = (I + A)^-1, A = diag(beta) L, 16x16 blocks ----
@@ -658,13 +676,8 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
             const float* of = reinterpret_cast<const float*>(&sm.e.sb[0][0]);
             const int c8 = (tid % (NC / 8)) * 8;  // the same columns for every item of a thread
             if constexpr (NCOL == 1) {
-                bf16x8 zz[NE];
-#pragma unroll
-                for (int it = 0; it < NE; ++it) {
-                    const int r = (tid + NTHR * it) / (NC / 8);
-                    const bool ok = tid + NTHR * it < NITEMS && r < n;
-                    zz[it] = sel8(ok, ld_act8<BF>(a.z, (row0 + min(r, n - 1)) * qkv + head_off + c8));
-                }
+                static_assert(NE == NZ, "z prefetch covers the epilogue items");
+                const bf16x8* zz = zpre;
                 float w8[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) w8[e] = a.norm_w[c8 + e];
