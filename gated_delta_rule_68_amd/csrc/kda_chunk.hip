@@ -11,19 +11,31 @@
 //   W  = T diag(beta) (e^{G} * k),   U = T diag(beta) v
 //   Ub = U - W S,   O = scale ((e^{G} * q) S + P Ub)
 //   S  = diag(e^{G_last}) S + (e^{G_last - G} * k)^T Ub
-// Every factor e^{...} that multiplies an MFMA operand is <= 1 except on the
-// diagonal 16x16 blocks of L and P, where the decay is rebased to the first row of
-// the block (at most 15 steps of g >= -5, so e^{75} at worst, inside fp32/bf16
-// range); this is why the arm needs g >= -5.
+//
+// Decay factorisation. The 64 rows form four 16-row blocks; with B_a = G at the
+// first row of block a and gamma_s = G_s - B_{a(s)} (a sum of at most 15 gates), the
+// conv stage writes three decayed operand tiles once per chunk,
+//   qa = q e^{gamma},  ka = k e^{gamma},  kb = k e^{-gamma},
+// and a table of per-block, per-channel factors e^{B_a}, e^{G_last - B_a},
+// e^{B_a - B_b} (a > b) and e^{G_last}. Every decayed operand of the chunk is then one
+// of these tiles times one table entry:
+//   L, P block (a, b):  ka_s (or qa_s) . (e^{B_a - B_b} kb_j)     (the factor is 1 on the diagonal)
+//   W row j:            beta_j e^{B_{a(j)}} ka_j
+//   O row s:            e^{B_{a(s)}} qa_s
+//   S update row j:     e^{G_last - B_{a(j)}} kb_j
+// so the exponentials are taken once per (row, channel) instead of once per use.
+// Every factor is <= 1 except e^{-gamma} <= e^{75} (15 gates >= -5), inside the
+// fp32 / bf16 range; this is why the arm needs g >= -5.
 //
 // One workgroup of 8 wavefronts owns one (sequence, head, value-column split) and
-// walks the chunks in order; the state lives in MFMA accumulator registers as S^T
-// tiles (wavefront w holds key block w). All contractions run on v_mfma_f32_16x16x32_bf16 (bf16 operands, fp32
-// accumulation); the 64x64 unit-triangular inverse is solved in fp32 (16x16 diagonal
-// blocks by forward substitution, off-diagonal blocks with v_mfma_f32_16x16x4f32).
-// conv + SiLU and l2 run in-kernel on the raw inputs, so the only HBM traffic is the
-// raw activations, the gates, the output and the state once in and once out. For
-// bf16 inputs the raw rows of chunk c+1 are requested while chunk c computes.
+// walks the chunks in order; the state lives in MFMA accumulator registers as S
+// tiles (wavefront w holds key block w). All contractions run on
+// v_mfma_f32_16x16x32_bf16 (bf16 operands, fp32 accumulation); the 64x64
+// unit-triangular inverse is solved in fp32 (16x16 diagonal blocks by forward
+// substitution, off-diagonal blocks with v_mfma_f32_16x16x4f32). conv + SiLU and l2
+// run in-kernel on the raw inputs, so the only HBM traffic is the raw activations,
+// the gates, the output and the state once in and once out. For bf16 inputs the raw
+// rows of chunk c+1 are requested while chunk c computes.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -41,6 +53,8 @@ constexpr int LDC = CH + 8;    // bf16 row stride of [*][64] tiles (144 B)
 constexpr int LDF = CH + 4;    // fp32 row stride of the 64x64 solve matrices
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4v mfma_bf16(bf16x8 a, bf16x8 b, f32x4v c) {
@@ -51,13 +65,18 @@ __device__ __forceinline__ f32x4v mfma_f32(float a, float b, f32x4v c) {
 }
 __device__ __forceinline__ bf16x8 ld8(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 __device__ __forceinline__ void st8(__bf16* p, bf16x8 v) { *reinterpret_cast<bf16x8*>(p) = v; }
+__device__ __forceinline__ bf16x2 ld2(const __bf16* p) { return *reinterpret_cast<const bf16x2*>(p); }
+__device__ __forceinline__ void st2(__bf16* p, bf16x2 v) { *reinterpret_cast<bf16x2*>(p) = v; }
 __device__ __forceinline__ f32x4v zero4() { return f32x4v{0.0f, 0.0f, 0.0f, 0.0f}; }
+__device__ __forceinline__ f32x4v ld4f(const float* p) { return *reinterpret_cast<const f32x4v*>(p); }
 
 // Workgroup barrier that orders LDS only: it waits for this wave's LDS operations and
 // not for its outstanding global loads, so the next chunk's prefetched rows stay in
 // flight across the phases of the current chunk. (Every value crossing phases inside
 // the chunk loop goes through LDS or registers; global stores are never read back.)
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// Orders this wave's own LDS writes before its later LDS reads (no other wave involved).
+__device__ __forceinline__ void lds_wave_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ bf16x8 zero8() {
     const __bf16 z = (__bf16)0.0f;
     return bf16x8{z, z, z, z, z, z, z, z};
@@ -76,32 +95,98 @@ __device__ __forceinline__ bf16x8 ld_act8(const void* p, size_t off) {
     }
 }
 
+// ---- cross-lane sums on the DPP / permlane paths (no LDS traffic) ----
+// DPP controls: quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E, row_ror:8 = 0x128,
+// row_mirror = 0x140, row_half_mirror = 0x141.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(x), CTRL, 0xf, 0xf, false));
+}
+// Sum over the 16 lanes of a DPP row (every lane of the row gets the sum).
+__device__ __forceinline__ float sum_row16(float x) {
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    x += dpp<0x141>(x);  // lanes l and 7 - l: the two quads of each half row
+    x += dpp<0x140>(x);  // lanes l and 15 - l: the two halves
+    return x;
+}
+// Sixteen sums over the 64 lanes at once: lane l returns sum over all lanes of
+// p[l >> 2]. Each step halves the values a lane keeps (it keeps the half selected by
+// one lane bit and adds its partner's copy of that half): v_permlane32_swap pairs lane
+// bit 5, v_permlane16_swap bit 4, DPP row_ror:8 bit 3, row_half_mirror bit 2, and the
+// quad permutations finish the sum over bits 0 and 1.
+__device__ __forceinline__ float sum16x64(float (&p)[16], int lane) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[i]), __float_as_uint(p[i + 8]), false, false);
+        p[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);  // row i + 8 * bit5
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(p[i]), __float_as_uint(p[i + 4]), false, false);
+        p[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);  // row i + 4 * bit4 + 8 * bit5
+    }
+    const bool b3 = lane & 8, b2 = lane & 4;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const float lo = p[i] + dpp<0x128>(p[i]), hi = p[i + 2] + dpp<0x128>(p[i + 2]);
+        p[i] = b3 ? hi : lo;
+    }
+    const float lo = p[0] + dpp<0x141>(p[0]), hi = p[1] + dpp<0x141>(p[1]);
+    float x = b2 ? hi : lo;
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    return x;
+}
+
 // MFMA 16x16x32 operand layout (lane l, q4 = l / 16, l16 = l % 16): an A fragment
 // holds A[l16][8*q4 .. 8*q4+7] of a 16x32 tile, a B fragment B[8*q4 .. +7][l16] of a
 // 32x16 tile, and the 16x16 result D[4*q4 + r][l16] for r = 0..3. With both operands
 // stored "row = M or N index, contiguous = K index" one loader serves A and B.
+// Swapping the two fragments yields the transposed tile: mfma(B-frag, A-frag) leaves
+// (AB)[l16][4*q4 + r] in lane l, four consecutive columns of one row, which this file
+// uses wherever a result is stored row-major so that the store is one vector write.
 
-template <bool GDN, int NC>
+// Rows of the per-block factor table (one float per channel; GDN uses column 0).
+enum : int {
+    F_EBR = 0,   // [4] e^{B_a}
+    F_ELR = 4,   // [4] e^{G_last - B_a}
+    F_DAB = 8,   // [6] e^{B_a - B_b}, a > b, row F_DAB + a(a-1)/2 + b
+    F_FN = 14,   // e^{G_last}
+    F_TOT = 15,  // [4] sum of the 16 gates of block a
+    F_G0 = 19,   // [4] gate of the first row of block a
+    NFAC = 23
+};
+__device__ __forceinline__ int dab_row(int a, int b) { return F_DAB + a * (a - 1) / 2 + b; }
+
+template <bool GDN, int NC, int KT>
 struct ChunkLds {
-    alignas(16) float gam[CH][GDN ? 4 : DK];  // inclusive cumulative log gate
-    alignas(16) __bf16 qh[CH][LDH];           // l2-normalised SiLU(conv q)
-    alignas(16) __bf16 kh[CH][LDH];           // l2-normalised SiLU(conv k)
-    alignas(16) __bf16 pb[CH][LDC];           // P (lower incl. diagonal)
-    alignas(16) __bf16 hist[KMAX - 1][2 * DK + NC];  // raw rows before the chunk: [d-1] is d rows back
+    alignas(16) __bf16 qa[CH][LDH];  // q^ e^{gamma}
+    alignas(16) __bf16 ka[CH][LDH];  // k^ e^{gamma}
+    alignas(16) __bf16 kb[CH][LDH];  // k^ e^{-gamma}
+    alignas(16) __bf16 hist[KT - 1][2 * DK + NC];  // raw rows before the chunk: [d-1] is d rows back
     alignas(16) float beta[CH];
-    alignas(16) float fn[DK];                 // e^{G_last}
-    alignas(16) float xs[4][16][17];          // 16x16 scratch of the block solve, waves 0..3
+    alignas(16) float fac[NFAC][GDN ? 4 : DK];
+    alignas(16) float nrm[8][16];  // per-wave 1/||row|| of the l2 norm
     union {
         struct {
-            __bf16 rq[CH][LDH];  // raw q rows of the chunk
-            __bf16 rk[CH][LDH];  // raw k rows
+            __bf16 rq[CH][LDH];               // raw q rows of the chunk
+            __bf16 rk[CH][LDH];               // raw k rows
+            __bf16 rg[GDN ? 1 : CH][LDH];     // raw gates (KDA), zero past row n
+            float gs[CH];                     // raw scalar gates (GDN), zero past row n
         } raw;
         struct {
-            float lf[CH][LDF];  // beta_s L[s][j], strictly lower
-            float tf[CH][LDF];  // T in fp32
-        } solve;
-        __bf16 wneg[CH][LDH];  // -W
-        __bf16 ubt[NC][LDC];   // Ub^T [value][row]
+            union {
+                struct {
+                    float lf[CH][LDF];        // beta_s L[s][j], strictly lower
+                    float tf[CH][LDF];        // T in fp32
+                    float xs[4][16][17];      // 16x16 scratch of the block solve, waves 0..3
+                } solve;
+                __bf16 wneg[CH][LDH];         // -W
+                __bf16 ubt[NC][LDC];          // Ub^T [value][row]
+            } w;
+            __bf16 pb[CH][LDC];               // P (lower incl. diagonal)
+        } m;
     } c;
     union {
         struct {
@@ -115,14 +200,6 @@ struct ChunkLds {
     } e;
 };
 
-template <bool GDN>
-__device__ __forceinline__ float gam_at(const float (*gam)[GDN ? 4 : DK], int r, int i) {
-    if constexpr (GDN)
-        return gam[r][0];
-    else
-        return gam[r][i];
-}
-
 // Split index / (b, h) of a block: the column splits of one (b, h) share blockIdx % 8,
 // so they run on the same XCD and share its L2 for the raw q / k / g rows they all read.
 __device__ __forceinline__ void block_coords(int ncol, int nbh, int* bh, int* split) {
@@ -135,8 +212,8 @@ __device__ __forceinline__ void block_coords(int ncol, int nbh, int* bh, int* sp
 
 // Raw rows of one chunk held in registers between their load (issued one chunk ahead
 // for bf16 inputs, so the HBM latency overlaps the previous chunk's compute) and
-// their store into LDS. Item it of thread tid covers row (tid + 256 it) / 16 and the
-// 8 channels ((tid + 256 it) % 16) * 8 of q, k and the gate; v items cover the NC
+// their store into LDS. Item it of thread tid covers row (tid + 512 it) / 16 and the
+// 8 channels ((tid + 512 it) % 16) * 8 of q, k and the gate; v items cover the NC
 // value channels of the split.
 template <bool GDN, int NC>
 struct ChunkRaw {
@@ -148,14 +225,10 @@ struct ChunkRaw {
 };
 
 // Every load is unconditional from a clamped, in-bounds row (rows past T repeat row
-// T-1) and nothing consumes the values until the next chunk's P0: a load inside a
+// T-1) and nothing consumes the values until the next chunk's P1: a load inside a
 // divergent branch, or a select right after it, makes the compiler wait for the load
 // on the spot, which would stall on the prefetch itself. Rows past T are masked
-// where they are consumed (gates and beta in P0, conv outputs in P1).
-__device__ __forceinline__ bf16x8 sel8(bool keep, bf16x8 x) {
-    return keep ? x : zero8();
-}
-
+// where they are stored (gates and beta) or consumed (conv outputs).
 template <bool BF, bool GDN, int NC>
 __device__ __forceinline__ void load_raw(ChunkRaw<GDN, NC>& cr, const MixerArgs& a, int b, int h,
                                          int c0, int jv0, int tid) {
@@ -166,9 +239,7 @@ __device__ __forceinline__ void load_raw(ChunkRaw<GDN, NC>& cr, const MixerArgs&
 #pragma unroll
     for (int it = 0; it < CR::NI; ++it) {
         const int idx = tid + NTHR * it, r = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8;
-        const bool ok = c0 + r < T;
         const size_t off = (rowb + min(c0 + r, T - 1)) * qkv + head_off + c8;
-        (void)ok;
         cr.q[it] = ld_act8<BF>(a.q, off);
         cr.k[it] = ld_act8<BF>(a.k, off);
         if constexpr (!GDN) cr.g[it] = ld_act8<BF>(a.g, off);
@@ -185,94 +256,36 @@ __device__ __forceinline__ void load_raw(ChunkRaw<GDN, NC>& cr, const MixerArgs&
     cr.gs = GDN ? ld_act<BF>(a.g, hr) : 0.0f;
 }
 
-// The raw rows of a chunk (n valid rows) from registers into LDS: q, k to the raw
-// staging tiles, v to its staging tile, the gates (zero past row n, so G stays at
-// G[n-1]) and beta; for GDN the scalar gates are scanned here (wave 0).
+// The raw rows of a chunk (n valid rows) from registers into LDS; the gates and beta
+// are zero past row n, so G stays at G[n-1] and padded rows change nothing.
 template <bool GDN, int NC, typename Lds>
-__device__ __forceinline__ void store_raw(Lds& sm, const ChunkRaw<GDN, NC>& raw, int n, int tid, int lane) {
+__device__ __forceinline__ void store_raw(Lds& sm, const ChunkRaw<GDN, NC>& raw, int n, int tid) {
     using CR = ChunkRaw<GDN, NC>;
 #pragma unroll
     for (int it = 0; it < CR::NI; ++it) {
         const int idx = tid + NTHR * it, r = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8;
-        *reinterpret_cast<bf16x8*>(&sm.c.raw.rq[r][c8]) = raw.q[it];
-        *reinterpret_cast<bf16x8*>(&sm.c.raw.rk[r][c8]) = raw.k[it];
-        if constexpr (!GDN) {
-            float4* gp = reinterpret_cast<float4*>(&sm.gam[r][c8]);
-            const bf16x8 g8 = raw.g[it];
-            const bool ok = r < n;
-            gp[0] = make_float4(ok ? (float)g8[0] : 0.0f, ok ? (float)g8[1] : 0.0f,
-                                ok ? (float)g8[2] : 0.0f, ok ? (float)g8[3] : 0.0f);
-            gp[1] = make_float4(ok ? (float)g8[4] : 0.0f, ok ? (float)g8[5] : 0.0f,
-                                ok ? (float)g8[6] : 0.0f, ok ? (float)g8[7] : 0.0f);
-        }
+        st8(&sm.c.raw.rq[r][c8], raw.q[it]);
+        st8(&sm.c.raw.rk[r][c8], raw.k[it]);
+        if constexpr (!GDN) st8(&sm.c.raw.rg[r][c8], r < n ? raw.g[it] : zero8());
     }
 #pragma unroll
     for (int it = 0; it < CR::NV; ++it) {
         const int idx = tid + NTHR * it, r = idx / (NC / 8), c8 = (idx % (NC / 8)) * 8;
-        if (idx < CR::VITEMS) *reinterpret_cast<bf16x8*>(&sm.e.pre.u.rv[r][c8]) = raw.v[it];
+        if (idx < CR::VITEMS) st8(&sm.e.pre.u.rv[r][c8], raw.v[it]);
     }
-    if (tid < CH) sm.beta[tid] = tid < n ? raw.beta : 0.0f;
-    if constexpr (GDN) {
-        if (tid < CH) {  // wave 0: inclusive scan of the 64 scalar gates
-            float gv = tid < n ? raw.gs : 0.0f;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float up = __shfl_up(gv, off, 64);
-                if (lane >= off) gv += up;
-            }
-            sm.gam[tid][0] = gv;
-            if (tid == CH - 1) sm.fn[0] = exp_f(gv);
-        }
+    if (tid < CH) {
+        sm.beta[tid] = tid < n ? raw.beta : 0.0f;
+        if constexpr (GDN) sm.c.raw.gs[tid] = tid < n ? raw.gs : 0.0f;
     }
 }
 
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ bf16x4 ld4(const __bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
-
-// Sliding conv window over 4 channels: raw rows of the chunk come from `raw` (row
-// stride ld), earlier rows from `hist` (hist + (d-1)*hld is the row d rows before the
-// chunk). step() takes the next raw row and returns SiLU(conv) of its 4 channels; the
-// taps w[e][j] multiply x~[r-(KT-1)+j] (taps beyond K are zero), so the sum runs over
-// the window in ascending time order.
-template <int KT>
-struct ConvWin4 {
-    float win[KT - 1][4];  // win[KT-2] = previous row
-
-    __device__ __forceinline__ void init(const __bf16* raw, int ld, const __bf16* hist, int hld, int r0) {
+// Conv taps of N consecutive channels starting at fused conv row `row`, aligned so
+// that w[e][KT-1] multiplies the current input (zero for the KT-K oldest slots).
+// KT == 4 is the K == 4 kernel; K of 2, 3 and 5..8 run the KT == 8 kernel.
+template <int KT, int N>
+__device__ __forceinline__ void load_taps(float (&w)[N][KT], const float* conv_w, size_t row, int K) {
 #pragma unroll
-        for (int d = 1; d < KT; ++d) {
-            const int r = r0 - d;
-            const bf16x4 x = r >= 0 ? ld4(raw + r * ld) : ld4(hist + (d - r0 - 1) * hld);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) win[KT - 1 - d][e] = (float)x[e];
-        }
-    }
-
-    __device__ __forceinline__ void step(bf16x4 x, const float (&w)[4][KT], bool valid, float (&y)[4]) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float acc = 0.0f;
-#pragma unroll
-            for (int j = 0; j < KT - 1; ++j) acc = fmaf(w[e][j], win[j][e], acc);
-            acc = fmaf(w[e][KT - 1], (float)x[e], acc);
-            y[e] = valid ? silu_f(acc) : 0.0f;
-        }
-#pragma unroll
-        for (int j = 0; j < KT - 2; ++j)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) win[j][e] = win[j + 1][e];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) win[KT - 2][e] = (float)x[e];
-    }
-};
-
-// Taps of 4 channels starting at fused conv row `row`, aligned so that w[e][KT-1]
-// multiplies the current input (zero for the KT-K oldest slots). KT == 4 is the
-// K == 4 kernel; K of 2, 3 and 5..8 run the KT == 8 kernel.
-template <int KT>
-__device__ __forceinline__ void load_taps4(float (&w)[4][KT], const float* conv_w, size_t row, int K) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
+    for (int e = 0; e < N; ++e)
 #pragma unroll
         for (int j = 0; j < KT; ++j) {
             if constexpr (KT == 4) {  // this instantiation runs only for K == 4
@@ -285,12 +298,34 @@ __device__ __forceinline__ void load_taps4(float (&w)[4][KT], const float* conv_
         }
 }
 
+// One causal-conv step over N channels: win holds the KT-1 previous raw inputs (oldest
+// first), x the current one; returns SiLU of the sum (0 for padded rows) and slides
+// the window.
+template <int KT, int N>
+__device__ __forceinline__ void conv_step(float (&win)[KT - 1][N], const float (&x)[N], const float (&w)[N][KT],
+                                          bool valid, float (&y)[N]) {
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int j = 0; j < KT - 1; ++j) acc = fmaf(w[e][j], win[j][e], acc);
+        acc = fmaf(w[e][KT - 1], x[e], acc);
+        y[e] = valid ? silu_f(acc) : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < KT - 2; ++j)
+#pragma unroll
+        for (int e = 0; e < N; ++e) win[j][e] = win[j + 1][e];
+#pragma unroll
+    for (int e = 0; e < N; ++e) win[KT - 2][e] = x[e];
+}
+
 template <bool BF, bool GDN, int NC, int KT>
 __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) {
     constexpr int NCOL = DK / NC;
     constexpr int NJB = NC / 16;  // value-column 16-blocks of this split
     constexpr int HLD = 2 * DK + NC;
-    __shared__ ChunkLds<GDN, NC> sm;
+    __shared__ ChunkLds<GDN, NC, KT> sm;
     using CR = ChunkRaw<GDN, NC>;
 
     int bh, split;
@@ -313,15 +348,14 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
     const size_t head_off = (size_t)h * DK;
     const int jv0 = split * NC;  // first value column of this split
 
-    // ---- state: S^T tiles (value block jb, key block `wave`) ----
+    // ---- state: S tiles (key block `wave`, value block jb): lane holds keys
+    // 16 wave + 4 q4 .. +3 of value column 16 jb + l16 ----
     f32x4v accS[NJB];
 #pragma unroll
-    for (int jb = 0; jb < NJB; ++jb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int jv = jv0 + jb * 16 + 4 * q4 + r, i = wave * 16 + l16;
-            accS[jb][r] = a.state_in[((size_t)bh * DK + jv) * DK + i];
-        }
+    for (int jb = 0; jb < NJB; ++jb) {
+        const int jv = jv0 + jb * 16 + l16;
+        accS[jb] = ld4f(&a.state_in[((size_t)bh * DK + jv) * DK + 16 * wave + 4 * q4]);
+    }
     // Wavefront (sw, hv) = (wave % 4, wave / 4) owns rows 16*sw.. of U / Ub / O and the
     // value blocks [hv*NJB2, (hv+1)*NJB2).
     constexpr int NJB2 = NJB / 2;
@@ -330,7 +364,7 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
     // ---- conv history of the first chunk: the old ring (slot K-1-d is d rows back) ----
     {
         const float* ring_b = a.ring + (size_t)b * 3 * qkv * (K - 1);
-        for (int idx = tid; idx < (KMAX - 1) * HLD; idx += NTHR) {
+        for (int idx = tid; idx < (KT - 1) * HLD; idx += NTHR) {
             const int d = idx / HLD + 1, col = idx % HLD;
             const size_t fr = col < 2 * DK ? (size_t)(col / DK) * qkv + head_off + col % DK
                                            : 2 * qkv + head_off + jv0 + (col - 2 * DK);
@@ -338,23 +372,19 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
         }
     }
 
-    // Conv roles: thread = (plane q/k, 8-row group, 8-channel group) for q and k; the
-    // v channels of the split are 8-row x 8-channel items of threads 0 .. NVI-1, and
-    // (KDA) the per-channel gate scans run on threads 128..255 meanwhile.
-    // The taps are re-read every chunk (a few L2-resident bytes) rather than held in
-    // registers across the whole chunk loop.
-    // Conv items are 4 rows x 4 channels: thread tid convolves q rows (tid / 32) * 4..
-    // and k rows of the same group, channels (tid % 32) * 4.., and, if tid < NVI, one v
-    // item; the 32 lanes of one row group are consecutive, so the l2 norm of a row is a
-    // 32-lane reduction.
-    const int crg = (tid / 32) % 16, ccg = tid % 32;
-    constexpr int NVI = 16 * (NC / 4);
-    const bool vthread = tid < NVI;
-    const int vrg = tid / (NC / 4), vcg = tid % (NC / 4);
+    // Conv roles. q / k: wavefront w < 4 convolves k, w >= 4 convolves q, rows
+    // 16 (w % 4) .. +15 (one 16-row block), channels 2 lane and 2 lane + 1, so the
+    // l2 norm of a row is a sum over the 64 lanes of one wavefront and the block's
+    // gate prefix is a per-thread running sum. v: item (channel, 16-row block), one
+    // per thread from the top thread down (all threads when NC == 128).
+    const bool kplane = wave < 4;
+    constexpr int NVIT = 4 * NC;
+    const int vi = tid - (NTHR - NVIT);
+    const int cv = vi % NC, qv = vi / NC;
 
     CR raw;
     load_raw<BF, GDN, NC>(raw, a, b, h, 0, jv0, tid);
-    store_raw<GDN, NC>(sm, raw, min(CH, T), tid, lane);
+    store_raw<GDN, NC>(sm, raw, min(CH, T), tid);
     __syncthreads();
 
     for (int c0 = 0; c0 < T; c0 += CH) {
@@ -362,76 +392,126 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
         const size_t row0 = (size_t)b * T + c0;
 
         KDA_LAUNDER_LANE();
-        // ---- P0: conv taps (the chunk's raw rows are already in LDS: the previous
-        // iteration, or the prologue, staged them) ----
-        float wq[4][KT], wk[4][KT], wv[4][KT];
-        load_taps4<KT>(wq, a.conv_w, head_off + ccg * 4, K);
-        load_taps4<KT>(wk, a.conv_w, qkv + head_off + ccg * 4, K);
-        if (vthread) load_taps4<KT>(wv, a.conv_w, 2 * qkv + head_off + jv0 + vcg * 4, K);
+        // ---- P0: conv taps (re-read every chunk: a few L2-resident bytes) ----
+        float wqk[2][KT], wv[1][KT];
+        load_taps<KT, 2>(wqk, a.conv_w, (kplane ? qkv : 0) + head_off + 2 * lane, K);
+        if (vi >= 0) load_taps<KT, 1>(wv, a.conv_w, 2 * qkv + head_off + jv0 + cv, K);
 
         KDA_LAUNDER_LANE();
-        // ---- P1: cumulative gate (4 threads per channel), then conv + SiLU (+ l2 for
-        // q, k) of 4-row x 4-channel items ----
-        if constexpr (!GDN) {
-            const int c = tid >> 2, qq = tid & 3;  // rows 16 qq .. 16 qq + 15 of channel c
-            float g16[16], acc = 0.0f;
+        // ---- P1: gate prefix, conv + SiLU + l2, decayed operand tiles ----
+        {
+            const int qq = wave & 3, rb = 16 * qq, c2 = 2 * lane;
+            constexpr int NG = GDN ? 1 : 2;
+            // gamma (gate sum of rows rb+1 .. rb+r), block total and first gate
+            float gm[16][NG], tot[NG], g0[NG];
+#pragma unroll
+            for (int e = 0; e < NG; ++e) gm[0][e] = 0.0f;
+            if constexpr (GDN) {
+                float acc = 0.0f;
+#pragma unroll
+                for (int r = 1; r < 16; ++r) {
+                    acc += sm.c.raw.gs[rb + r];
+                    gm[r][0] = acc;
+                }
+                g0[0] = sm.c.raw.gs[rb];
+                tot[0] = g0[0] + acc;
+            } else {
+                const bf16x2 gf = ld2(&sm.c.raw.rg[rb][c2]);
+                float acc[2] = {0.0f, 0.0f};
+#pragma unroll
+                for (int r = 1; r < 16; ++r) {
+                    const bf16x2 gv = ld2(&sm.c.raw.rg[rb + r][c2]);
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        acc[e] += (float)gv[e];
+                        gm[r][e] = acc[e];
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    g0[e] = (float)gf[e];
+                    tot[e] = g0[e] + acc[e];
+                }
+            }
+            if (kplane) {
+                if constexpr (GDN) {
+                    if (lane == 0) {
+                        sm.fac[F_TOT + qq][0] = tot[0];
+                        sm.fac[F_G0 + qq][0] = g0[0];
+                    }
+                } else {
+                    *reinterpret_cast<float2*>(&sm.fac[F_TOT + qq][c2]) = make_float2(tot[0], tot[1]);
+                    *reinterpret_cast<float2*>(&sm.fac[F_G0 + qq][c2]) = make_float2(g0[0], g0[1]);
+                }
+            }
+
+            // conv + SiLU of 16 rows x 2 channels
+            const __bf16* rawp = (kplane ? &sm.c.raw.rk[0][0] : &sm.c.raw.rq[0][0]) + c2;
+            float win[KT - 1][2];
+#pragma unroll
+            for (int d = 1; d < KT; ++d) {  // rows rb - d: in the chunk, or (block 0) the history
+                const bf16x2 x = qq > 0 ? ld2(rawp + (rb - d) * LDH) : ld2(&sm.hist[d - 1][(kplane ? DK : 0) + c2]);
+#pragma unroll
+                for (int e = 0; e < 2; ++e) win[KT - 1 - d][e] = (float)x[e];
+            }
+            float y[16][2], ps[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                acc += sm.gam[16 * qq + r][c];
-                g16[r] = acc;
+                const bf16x2 xv = ld2(rawp + (rb + r) * LDH);
+                const float x[2] = {(float)xv[0], (float)xv[1]};
+                conv_step<KT, 2>(win, x, wqk, rb + r < n, y[r]);
+                ps[r] = fmaf(y[r][0], y[r][0], y[r][1] * y[r][1]);
             }
-            // exclusive prefix of the quarter totals over the 4 lanes of the channel
-            const float t1 = __shfl_up(acc, 1, 4), t2 = __shfl_up(acc, 2, 4), t3 = __shfl_up(acc, 3, 4);
-            const float base = (qq >= 1 ? t1 : 0.0f) + (qq >= 2 ? t2 : 0.0f) + (qq >= 3 ? t3 : 0.0f);
+            const float ss = sum16x64(ps, lane);  // sum of squares of row rb + lane / 4
+            if ((lane & 3) == 0) sm.nrm[wave][lane >> 2] = rsqrtf(ss + L2_EPS);
+            lds_wave_sync();
+            float nr[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sm.gam[16 * qq + r][c] = base + g16[r];
-            if (qq == 3) sm.fn[c] = exp_f(base + acc);
-        }
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const f32x4v v4 = ld4f(&sm.nrm[wave][4 * r4]);
 #pragma unroll
-        for (int plane = 0; plane < 2; ++plane) {
-            const __bf16* rawp = (plane == 0 ? &sm.c.raw.rq[0][0] : &sm.c.raw.rk[0][0]) + ccg * 4;
-            __bf16* dst = (plane == 0 ? &sm.qh[0][0] : &sm.kh[0][0]) + ccg * 4;
-            ConvWin4<KT> cw;
-            cw.init(rawp, LDH, &sm.hist[0][plane * DK + ccg * 4], HLD, crg * 4);
+                for (int e = 0; e < 4; ++e) nr[4 * r4 + e] = v4[e];
+            }
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int r = crg * 4 + rr;
-                float y[4];
-                cw.step(ld4(rawp + r * LDH), plane == 0 ? wq : wk, r < n, y);
-                float ss = 0.0f;
+            for (int r = 0; r < 16; ++r) {
+                bf16x2 o1, o2;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) ss = fmaf(y[e], y[e], ss);
-                ss += __shfl_xor(ss, 1, 64);  // the 32 channel groups of the row
-                ss += __shfl_xor(ss, 2, 64);
-                ss += __shfl_xor(ss, 4, 64);
-                ss += __shfl_xor(ss, 8, 64);
-                ss += __shfl_xor(ss, 16, 64);
-                const float inv = rsqrtf(ss + L2_EPS);
-                bf16x4 o;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = (__bf16)(y[e] * inv);
-                *reinterpret_cast<bf16x4*>(dst + r * LDH) = o;
+                for (int e = 0; e < 2; ++e) {
+                    const float g = gm[r][GDN ? 0 : e];
+                    const float kh = y[r][e] * nr[r];
+                    o1[e] = (__bf16)(kh * exp_f(g));
+                    if (kplane) o2[e] = (__bf16)(kh * exp_f(-g));
+                }
+                if (kplane) {
+                    st2(&sm.ka[rb + r][c2], o1);
+                    st2(&sm.kb[rb + r][c2], o2);
+                } else {
+                    st2(&sm.qa[rb + r][c2], o1);
+                }
             }
         }
-        if (vthread) {
-            const __bf16* rawp = &sm.e.pre.u.rv[0][vcg * 4];
-            ConvWin4<KT> cw;
-            cw.init(rawp, NC + 8, &sm.hist[0][2 * DK + vcg * 4], HLD, vrg * 4);
+        if (vi >= 0) {  // v: conv + SiLU, times beta, stored transposed
+            const int rbv = 16 * qv;
+            float win[KT - 1][1];
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int r = vrg * 4 + rr;
-                float y[4];
-                cw.step(ld4(rawp + r * (NC + 8)), wv, r < n, y);
-                const float bt = sm.beta[r];
+            for (int d = 1; d < KT; ++d)
+                win[KT - 1 - d][0] = qv > 0 ? (float)sm.e.pre.u.rv[rbv - d][cv] : (float)sm.hist[d - 1][2 * DK + cv];
+            bf16x8 o[2];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) sm.e.pre.vbt[vcg * 4 + e][r] = (__bf16)(bt * y[e]);
+            for (int r = 0; r < 16; ++r) {
+                const float x[1] = {(float)sm.e.pre.u.rv[rbv + r][cv]};
+                float y[1];
+                conv_step<KT, 1>(win, x, wv, rbv + r < n, y);
+                o[r >> 3][r & 7] = (__bf16)(sm.beta[rbv + r] * y[0]);
             }
+            st8(&sm.e.pre.vbt[cv][rbv], o[0]);
+            st8(&sm.e.pre.vbt[cv][rbv + 8], o[1]);
         }
         lds_barrier();
-        // The last KMAX-1 raw rows become the next chunk's history (only a full chunk
-        // has a successor).
+        // The last KT-1 raw rows become the next chunk's history (only a full chunk has
+        // a successor), and the per-block factor table is formed from the block sums.
         if (n == CH) {
-            for (int idx = tid; idx < (KMAX - 1) * (HLD / 8); idx += NTHR) {
+            for (int idx = tid; idx < (KT - 1) * (HLD / 8); idx += NTHR) {
                 const int d = idx / (HLD / 8) + 1, col = (idx % (HLD / 8)) * 8;
                 const __bf16* src = col < DK ? &sm.c.raw.rq[CH - d][col]
                                   : col < 2 * DK ? &sm.c.raw.rk[CH - d][col - DK]
@@ -439,55 +519,81 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
                 st8(&sm.hist[d - 1][col], ld8(src));
             }
         }
+        {
+            const int c = tid & (DK - 1), part = tid >> 7;
+            if (!GDN || c == 0) {
+                float tt[4], bs[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) tt[q] = sm.fac[F_TOT + q][c];
+                float run = 0.0f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    bs[q] = run + sm.fac[F_G0 + q][c];  // B_q = G at row 16 q
+                    run += tt[q];
+                }
+                const float gl = run;  // G_last
+                if (part == 0) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) sm.fac[F_EBR + q][c] = exp_f(bs[q]);
+                } else if (part == 1) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) sm.fac[F_ELR + q][c] = exp_f(gl - bs[q]);
+                } else if (part == 2) {
+                    sm.fac[dab_row(1, 0)][c] = exp_f(bs[1] - bs[0]);
+                    sm.fac[dab_row(2, 0)][c] = exp_f(bs[2] - bs[0]);
+                    sm.fac[dab_row(2, 1)][c] = exp_f(bs[2] - bs[1]);
+                    sm.fac[F_FN][c] = exp_f(gl);
+                } else {
+                    sm.fac[dab_row(3, 0)][c] = exp_f(bs[3] - bs[0]);
+                    sm.fac[dab_row(3, 1)][c] = exp_f(bs[3] - bs[1]);
+                    sm.fac[dab_row(3, 2)][c] = exp_f(bs[3] - bs[2]);
+                }
+            }
+        }
         lds_barrier();
 
         KDA_LAUNDER_LANE();
         // ---- P2: L and P; wavefront (a, p) = (wave / 2, wave % 2) computes block-row a,
-        // column blocks p and p + 2; the decay is rebased to row 16a ----
+        // column blocks p and p + 2 ----
         {
             const int ab = wave >> 1, par = wave & 1, ra = 16 * ab, s = ra + l16;
             f32x4v accL[2], accP[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) accL[t] = accP[t] = zero4();
             if (par <= ab) {
-#pragma unroll 1
+#pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
                     const int i0 = 32 * kk + 8 * q4;
-                    float gr[8];
-                    bf16x8 ak, aq;
-                    const bf16x8 kx = ld8(&sm.kh[s][i0]), qx = ld8(&sm.qh[s][i0]);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        gr[e] = gam_at<GDN>(sm.gam, ra, i0 + e);
-                        const float ea = exp_f(gam_at<GDN>(sm.gam, s, i0 + e) - gr[e]);
-                        ak[e] = (__bf16)((float)kx[e] * ea);
-                        aq[e] = (__bf16)((float)qx[e] * ea);
-                    }
+                    const bf16x8 ak = ld8(&sm.ka[s][i0]), aq = ld8(&sm.qa[s][i0]);
 #pragma unroll
                     for (int t = 0; t < 2; ++t) {
                         const int bb = par + 2 * t;
                         if (bb > ab) break;
-                        const int j = 16 * bb + l16;
-                        const bf16x8 kj = ld8(&sm.kh[j][i0]);
-                        bf16x8 bk;
+                        bf16x8 bk = ld8(&sm.kb[16 * bb + l16][i0]);
+                        if (bb < ab) {  // off-diagonal block: rebase from B_b to B_a
+                            const float* d = &sm.fac[dab_row(ab, bb)][GDN ? 0 : i0];
 #pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            bk[e] = (__bf16)((float)kj[e] * exp_f(gr[e] - gam_at<GDN>(sm.gam, j, i0 + e)));
-                        accL[t] = mfma_bf16(ak, bk, accL[t]);
-                        accP[t] = mfma_bf16(aq, bk, accP[t]);
+                            for (int e = 0; e < 8; ++e) bk[e] = (__bf16)((float)bk[e] * d[GDN ? 0 : e]);
+                        }
+                        accL[t] = mfma_bf16(bk, ak, accL[t]);  // lane: L[ra + l16][16 bb + 4 q4 + r]
+                        accP[t] = mfma_bf16(bk, aq, accP[t]);
                     }
                 }
             }
+            const float bs = sm.beta[s];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const int bb = par + 2 * t;
+                const int bb = par + 2 * t, j0 = 16 * bb + 4 * q4;
+                const bool lo = bb <= ab;
+                f32x4v lv;
+                bf16x4 pv;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int sr = ra + 4 * q4 + r, j = 16 * bb + l16;
-                    const bool lo = bb <= ab;
-                    sm.c.solve.lf[sr][j] = (lo && j < sr) ? sm.beta[sr] * accL[t][r] : 0.0f;
-                    sm.pb[sr][j] = (__bf16)((lo && j <= sr) ? accP[t][r] : 0.0f);
+                    lv[r] = (lo && j0 + r < s) ? bs * accL[t][r] : 0.0f;
+                    pv[r] = (__bf16)((lo && j0 + r <= s) ? accP[t][r] : 0.0f);
                 }
+                *reinterpret_cast<f32x4v*>(&sm.c.m.w.solve.lf[s][j0]) = lv;
+                *reinterpret_cast<bf16x4*>(&sm.c.m.pb[s][j0]) = pv;
             }
         }
         lds_barrier();
@@ -508,8 +614,9 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
         KDA_LAUNDER_LANE();
         // ---- P3: T = (I + A)^-1, A = diag(beta) L, 16x16 blocks ----
         {
-            float (*lf)[LDF] = sm.c.solve.lf;
-            float (*tf)[LDF] = sm.c.solve.tf;
+            float (*lf)[LDF] = sm.c.m.w.solve.lf;
+            float (*tf)[LDF] = sm.c.m.w.solve.tf;
+            float (*xs)[16][17] = sm.c.m.w.solve.xs;
             const int ab = wave;  // waves 0..3: one 16-row block each
             if (wave < 4 && q4 == 0) {  // diagonal block ab, column l16, forward substitution
                 float x[16];
@@ -544,15 +651,14 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
                             xacc = mfma_f32(lf[16 * ab + l16][16 * cc + 4 * kk + q4],
                                             tf[16 * cc + 4 * kk + q4][16 * bb + l16], xacc);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) sm.xs[wave][4 * q4 + r][l16] = xacc[r];
+                    for (int r = 0; r < 4; ++r) xs[wave][4 * q4 + r][l16] = xacc[r];
                 }
                 lds_barrier();
                 if (bb >= 0) {
                     f32x4v tacc = zero4();
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk)
-                        tacc = mfma_f32(tf[16 * ab + l16][16 * ab + 4 * kk + q4],
-                                        sm.xs[wave][4 * kk + q4][l16], tacc);
+                        tacc = mfma_f32(tf[16 * ab + l16][16 * ab + 4 * kk + q4], xs[wave][4 * kk + q4][l16], tacc);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) tf[16 * ab + 4 * q4 + r][16 * bb + l16] = -tacc[r];
                 }
@@ -576,20 +682,22 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
             for (int sb = 0; sb < 4; ++sb) accW[sb] = zero4();
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
+                const int j0 = 32 * kk + 8 * q4;
+                const float eb = sm.fac[F_EBR + (j0 >> 4)][GDN ? 0 : i];  // e^{B} of the rows' block
                 bf16x8 bw;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int j = 32 * kk + 8 * q4 + e;
-                    bw[e] = (__bf16)(sm.beta[j] * (float)sm.kh[j][i] * exp_f(gam_at<GDN>(sm.gam, j, i)));
-                }
+                for (int e = 0; e < 8; ++e) bw[e] = (__bf16)(sm.beta[j0 + e] * eb * (float)sm.ka[j0 + e][i]);
 #pragma unroll
-                for (int sb = 0; sb < 4; ++sb)
-                    accW[sb] = mfma_bf16(ld8(&sm.e.pre.u.tb[16 * sb + l16][32 * kk + 8 * q4]), bw, accW[sb]);
+                for (int sb = 0; sb < 4; ++sb)  // lane: W[16 sb + l16][16 wave + 4 q4 + r]
+                    accW[sb] = mfma_bf16(bw, ld8(&sm.e.pre.u.tb[16 * sb + l16][32 * kk + 8 * q4]), accW[sb]);
             }
 #pragma unroll
-            for (int sb = 0; sb < 4; ++sb)
+            for (int sb = 0; sb < 4; ++sb) {
+                bf16x4 wv4;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sm.c.wneg[16 * sb + 4 * q4 + r][i] = (__bf16)(-accW[sb][r]);
+                for (int r = 0; r < 4; ++r) wv4[r] = (__bf16)(-accW[sb][r]);
+                *reinterpret_cast<bf16x4*>(&sm.c.m.w.wneg[16 * sb + l16][16 * wave + 4 * q4]) = wv4;
+            }
 #pragma unroll
             for (int t = 0; t < NJB2; ++t) accU[t] = zero4();
 #pragma unroll
@@ -607,13 +715,16 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
         KDA_LAUNDER_LANE();
         // ---- P5: S^T to LDS in bf16, then Ub = U - W S ----
 #pragma unroll
-        for (int jb = 0; jb < NJB; ++jb)
+        for (int jb = 0; jb < NJB; ++jb) {
+            bf16x4 s4;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sm.e.sb[16 * jb + 4 * q4 + r][16 * wave + l16] = (__bf16)accS[jb][r];
+            for (int r = 0; r < 4; ++r) s4[r] = (__bf16)accS[jb][r];
+            *reinterpret_cast<bf16x4*>(&sm.e.sb[16 * jb + l16][16 * wave + 4 * q4]) = s4;
+        }
         lds_barrier();
 #pragma unroll 2
         for (int kk = 0; kk < 4; ++kk) {
-            const bf16x8 aw = ld8(&sm.c.wneg[16 * sw + l16][32 * kk + 8 * q4]);
+            const bf16x8 aw = ld8(&sm.c.m.w.wneg[16 * sw + l16][32 * kk + 8 * q4]);
 #pragma unroll
             for (int t = 0; t < NJB2; ++t) {
                 const int jb = hv * NJB2 + t;
@@ -622,10 +733,12 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
         }
         lds_barrier();  // every read of -W is done before Ub^T overwrites it
 #pragma unroll
-        for (int t = 0; t < NJB2; ++t)
+        for (int t = 0; t < NJB2; ++t) {
+            bf16x4 u4;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                sm.c.ubt[16 * (hv * NJB2 + t) + l16][16 * sw + 4 * q4 + r] = (__bf16)accU[t][r];
+            for (int r = 0; r < 4; ++r) u4[r] = (__bf16)accU[t][r];
+            *reinterpret_cast<bf16x4*>(&sm.c.m.w.ubt[16 * (hv * NJB2 + t) + l16][16 * sw + 4 * q4]) = u4;
+        }
         lds_barrier();
 
         KDA_LAUNDER_LANE();
@@ -635,45 +748,45 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
             const int s = 16 * sw + l16;
 #pragma unroll
             for (int t = 0; t < NJB2; ++t) accO[t] = zero4();
-#pragma unroll 1
+#pragma unroll 2
             for (int kk = 0; kk < 4; ++kk) {
                 const int i0 = 32 * kk + 8 * q4;
-                const bf16x8 qx = ld8(&sm.qh[s][i0]);
+                const bf16x8 qx = ld8(&sm.qa[s][i0]);
+                const float* eb = &sm.fac[F_EBR + sw][GDN ? 0 : i0];  // e^{B} of block sw
                 bf16x8 aq;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) aq[e] = (__bf16)((float)qx[e] * exp_f(gam_at<GDN>(sm.gam, s, i0 + e)));
+                for (int e = 0; e < 8; ++e) aq[e] = (__bf16)((float)qx[e] * eb[GDN ? 0 : e]);
 #pragma unroll
-                for (int t = 0; t < NJB2; ++t)
-                    accO[t] = mfma_bf16(aq, ld8(&sm.e.sb[16 * (hv * NJB2 + t) + l16][i0]), accO[t]);
+                for (int t = 0; t < NJB2; ++t)  // lane: O[s][16 jb + 4 q4 + r]
+                    accO[t] = mfma_bf16(ld8(&sm.e.sb[16 * (hv * NJB2 + t) + l16][i0]), aq, accO[t]);
             }
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 if (32 * kk > 16 * sw + 15) break;  // P is lower triangular
-                const bf16x8 ap = ld8(&sm.pb[s][32 * kk + 8 * q4]);
+                const bf16x8 ap = ld8(&sm.c.m.pb[s][32 * kk + 8 * q4]);
 #pragma unroll
                 for (int t = 0; t < NJB2; ++t)
-                    accO[t] = mfma_bf16(ap, ld8(&sm.c.ubt[16 * (hv * NJB2 + t) + l16][32 * kk + 8 * q4]), accO[t]);
+                    accO[t] = mfma_bf16(ld8(&sm.c.m.w.ubt[16 * (hv * NJB2 + t) + l16][32 * kk + 8 * q4]), ap, accO[t]);
             }
         }
         // O goes through LDS (over S^T, no longer needed this chunk) so that every
         // thread then owns 8 consecutive columns of a row: 16-byte z loads and
         // out / o stores.
+        constexpr int LDO = NC + 4;
+        static_assert(sizeof(sm.e) >= sizeof(float) * CH * LDO, "O staging fits over S^T");
         lds_barrier();
         {
-            constexpr int LDO = NC + 4;
-            float* of = reinterpret_cast<float*>(&sm.e.sb[0][0]);
+            float* of = reinterpret_cast<float*>(&sm.e);
 #pragma unroll
             for (int t = 0; t < NJB2; ++t)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    of[(16 * sw + 4 * q4 + r) * LDO + 16 * (hv * NJB2 + t) + l16] = a.scale * accO[t][r];
+                *reinterpret_cast<f32x4v*>(&of[(16 * sw + l16) * LDO + 16 * (hv * NJB2 + t) + 4 * q4]) =
+                    a.scale * accO[t];
         }
         lds_barrier();
         {
-            constexpr int LDO = NC + 4;
             constexpr int NITEMS = CH * (NC / 8);
             constexpr int NE = (NITEMS + NTHR - 1) / NTHR;  // items per thread
-            const float* of = reinterpret_cast<const float*>(&sm.e.sb[0][0]);
+            const float* of = reinterpret_cast<const float*>(&sm.e);
             const int c8 = (tid % (NC / 8)) * 8;  // the same columns for every item of a thread
             if constexpr (NCOL == 1) {
                 static_assert(NE == NZ, "z prefetch covers the epilogue items");
@@ -683,7 +796,7 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
                 for (int e = 0; e < 8; ++e) w8[e] = a.norm_w[c8 + e];
 #pragma unroll
                 for (int it = 0; it < NE; ++it) {
-                    const int r = (tid + NTHR * it) / (NC / 8);
+                    const int r = (tid + NTHR * it) / (NC / 8);  // the 16 lanes of a DPP row share r
                     float o8[8];
                     float ss = 0.0f;
 #pragma unroll
@@ -691,10 +804,7 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
                         o8[e] = of[r * LDO + c8 + e];
                         ss = fmaf(o8[e], o8[e], ss);
                     }
-                    ss += __shfl_xor(ss, 1, 64);  // the 16 lanes of one row
-                    ss += __shfl_xor(ss, 2, 64);
-                    ss += __shfl_xor(ss, 4, 64);
-                    ss += __shfl_xor(ss, 8, 64);
+                    ss = sum_row16(ss);
                     const float inv = rsqrtf(fmaf(ss, 1.0f / DK, a.rms_eps));
                     if (tid + NTHR * it < NITEMS && r < n) {
                         const size_t off = (row0 + r) * qkv + head_off + c8;
@@ -740,39 +850,34 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
         // ---- P7: S = diag(e^{G_last}) S + K_dec^T Ub (key block `wave`) ----
         {
             const int i = 16 * wave + l16;
-            const float dec = sm.fn[GDN ? 0 : i];
-            const float glast = gam_at<GDN>(sm.gam, CH - 1, i);
+            const f32x4v dec = GDN ? f32x4v{sm.fac[F_FN][0], sm.fac[F_FN][0], sm.fac[F_FN][0], sm.fac[F_FN][0]}
+                                   : ld4f(&sm.fac[F_FN][16 * wave + 4 * q4]);
 #pragma unroll
-            for (int jb = 0; jb < NJB; ++jb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) accS[jb][r] *= dec;
+            for (int jb = 0; jb < NJB; ++jb) accS[jb] *= dec;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
+                const int j0 = 32 * kk + 8 * q4;
+                const float el = sm.fac[F_ELR + (j0 >> 4)][GDN ? 0 : i];  // e^{G_last - B} of the rows' block
                 bf16x8 bkd;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int sr = 32 * kk + 8 * q4 + e;
-                    bkd[e] = (__bf16)((float)sm.kh[sr][i] * exp_f(glast - gam_at<GDN>(sm.gam, sr, i)));
-                }
+                for (int e = 0; e < 8; ++e) bkd[e] = (__bf16)((float)sm.kb[j0 + e][i] * el);
 #pragma unroll
                 for (int jb = 0; jb < NJB; ++jb)
-                    accS[jb] = mfma_bf16(ld8(&sm.c.ubt[16 * jb + l16][32 * kk + 8 * q4]), bkd, accS[jb]);
+                    accS[jb] = mfma_bf16(bkd, ld8(&sm.c.m.w.ubt[16 * jb + l16][32 * kk + 8 * q4]), accS[jb]);
             }
         }
         lds_barrier();
         if (c0 + CH < T) {
-            store_raw<GDN, NC>(sm, raw, min(CH, T - c0 - CH), tid, lane);
+            store_raw<GDN, NC>(sm, raw, min(CH, T - c0 - CH), tid);
             lds_barrier();
         }
     }
 
 #pragma unroll
-    for (int jb = 0; jb < NJB; ++jb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int jv = jv0 + jb * 16 + 4 * q4 + r, i = wave * 16 + l16;
-            a.state_out[((size_t)bh * DK + jv) * DK + i] = accS[jb][r];
-        }
+    for (int jb = 0; jb < NJB; ++jb) {
+        const int jv = jv0 + jb * 16 + l16;
+        *reinterpret_cast<f32x4v*>(&a.state_out[((size_t)bh * DK + jv) * DK + 16 * wave + 4 * q4]) = accS[jb];
+    }
 }
 #undef KDA_LAUNDER_LANE
 
@@ -816,6 +921,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 template <bool BF, bool GDN, int NC>
 hipError_t chunk_launch_nc(const MixerArgs& a, float* o_buf) {
     constexpr int NCOL = DK / NC;
+    static_assert(sizeof(ChunkLds<GDN, NC, KMAX>) <= 160 * 1024, "LDS budget of one workgroup");
     const int nbh = a.B * a.H;
     const int grid = ((nbh + 7) / 8) * 8 * NCOL;
     if (a.K == 4)
