@@ -69,6 +69,8 @@ __device__ __forceinline__ bf16x2 ld2(const __bf16* p) { return *reinterpret_cas
 __device__ __forceinline__ void st2(__bf16* p, bf16x2 v) { *reinterpret_cast<bf16x2*>(p) = v; }
 __device__ __forceinline__ f32x4v zero4() { return f32x4v{0.0f, 0.0f, 0.0f, 0.0f}; }
 __device__ __forceinline__ f32x4v ld4f(const float* p) { return *reinterpret_cast<const f32x4v*>(p); }
+// 2^x; the gate sums of this file are kept in log2 units (scaled by log2 e once).
+__device__ __forceinline__ float exp2_f(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Workgroup barrier that orders LDS only: it waits for this wave's LDS operations and
 // not for its outstanding global loads, so the next chunk's prefetched rows stay in
@@ -153,8 +155,8 @@ enum : int {
     F_ELR = 4,   // [4] e^{G_last - B_a}
     F_DAB = 8,   // [6] e^{B_a - B_b}, a > b, row F_DAB + a(a-1)/2 + b
     F_FN = 14,   // e^{G_last}
-    F_TOT = 15,  // [4] sum of the 16 gates of block a
-    F_G0 = 19,   // [4] gate of the first row of block a
+    F_TOT = 15,  // [4] sum of the 16 gates of block a, times log2 e
+    F_G0 = 19,   // [4] gate of the first row of block a, times log2 e
     NFAC = 23
 };
 __device__ __forceinline__ int dab_row(int a, int b) { return F_DAB + a * (a - 1) / 2 + b; }
@@ -178,23 +180,21 @@ struct ChunkLds {
         struct {
             union {
                 struct {
-                    float lf[CH][LDF];        // beta_s L[s][j], strictly lower
-                    float tf[CH][LDF];        // T in fp32
-                    float xs[4][16][17];      // 16x16 scratch of the block solve, waves 0..3
+                    float lf[CH][LDF];             // A = beta_s L[s][j], blocks below the diagonal
+                    float ltd[4][16 * 16 + 4];     // diagonal blocks of A, transposed: [a][c * 16 + r] = A[16a+r][16a+c]
+                    float tdiag[4][16][17];        // diagonal blocks of T in fp32
                 } solve;
                 __bf16 wneg[CH][LDH];         // -W
                 __bf16 ubt[NC][LDC];          // Ub^T [value][row]
             } w;
+            __bf16 tb[CH][LDC];               // T in bf16
             __bf16 pb[CH][LDC];               // P (lower incl. diagonal)
         } m;
     } c;
     union {
         struct {
-            __bf16 vbt[NC][LDC];  // (beta v)^T [value][row]
-            union {
-                __bf16 rv[CH][NC + 8];  // raw v rows of the split
-                __bf16 tb[CH][LDC];     // T in bf16
-            } u;
+            __bf16 vbt[NC][LDC];     // (beta v)^T [value][row]
+            __bf16 rv[CH][NC + 8];   // raw v rows of the split
         } pre;
         __bf16 sb[NC][LDH];  // S^T in bf16 [value][key]
     } e;
@@ -229,35 +229,55 @@ struct ChunkRaw {
 // divergent branch, or a select right after it, makes the compiler wait for the load
 // on the spot, which would stall on the prefetch itself. Rows past T are masked
 // where they are stored (gates and beta) or consumed (conv outputs).
-template <bool BF, bool GDN, int NC>
-__device__ __forceinline__ void load_raw(ChunkRaw<GDN, NC>& cr, const MixerArgs& a, int b, int h,
-                                         int c0, int jv0, int tid) {
+// Parts of one chunk's rows, so that the requests can be spread over the phases of
+// the previous chunk: a burst of all of them stalls every wavefront at the issue.
+enum RawPart { RAW_Q, RAW_K, RAW_G, RAW_V, RAW_BETA };
+template <bool BF, bool GDN, int NC, RawPart PART>
+__device__ __forceinline__ void load_raw_part(ChunkRaw<GDN, NC>& cr, const MixerArgs& a, int b, int h,
+                                              int c0, int jv0, int tid) {
     using CR = ChunkRaw<GDN, NC>;
     const int T = a.T, H = a.H;
     const size_t qkv = (size_t)H * DK, head_off = (size_t)h * DK;
     const size_t rowb = (size_t)b * T;
+    if constexpr (PART == RAW_Q || PART == RAW_K || PART == RAW_G) {
+        if constexpr (PART == RAW_G && GDN) return;
 #pragma unroll
-    for (int it = 0; it < CR::NI; ++it) {
-        const int idx = tid + NTHR * it, r = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8;
-        const size_t off = (rowb + min(c0 + r, T - 1)) * qkv + head_off + c8;
-        cr.q[it] = ld_act8<BF>(a.q, off);
-        cr.k[it] = ld_act8<BF>(a.k, off);
-        if constexpr (!GDN) cr.g[it] = ld_act8<BF>(a.g, off);
-    }
+        for (int it = 0; it < CR::NI; ++it) {
+            const int idx = tid + NTHR * it, r = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8;
+            const size_t off = (rowb + min(c0 + r, T - 1)) * qkv + head_off + c8;
+            if constexpr (PART == RAW_Q) cr.q[it] = ld_act8<BF>(a.q, off);
+            if constexpr (PART == RAW_K) cr.k[it] = ld_act8<BF>(a.k, off);
+            if constexpr (PART == RAW_G && !GDN) cr.g[it] = ld_act8<BF>(a.g, off);
+        }
+    } else if constexpr (PART == RAW_V) {
 #pragma unroll
-    for (int it = 0; it < CR::NV; ++it) {
-        const int idx = min(tid + NTHR * it, CR::VITEMS - 1);
-        const int r = idx / (NC / 8), c8 = (idx % (NC / 8)) * 8;
-        cr.v[it] = ld_act8<BF>(a.v, (rowb + min(c0 + r, T - 1)) * qkv + head_off + jv0 + c8);
+        for (int it = 0; it < CR::NV; ++it) {
+            const int idx = min(tid + NTHR * it, CR::VITEMS - 1);
+            const int r = idx / (NC / 8), c8 = (idx % (NC / 8)) * 8;
+            cr.v[it] = ld_act8<BF>(a.v, (rowb + min(c0 + r, T - 1)) * qkv + head_off + jv0 + c8);
+        }
+    } else {
+        const int rr = tid & (CH - 1);
+        const size_t hr = (rowb + min(c0 + rr, T - 1)) * H + h;
+        cr.beta = ld_act<BF>(a.beta, hr);
+        cr.gs = GDN ? ld_act<BF>(a.g, hr) : 0.0f;
     }
-    const int rr = tid & (CH - 1);
-    const size_t hr = (rowb + min(c0 + rr, T - 1)) * H + h;
-    cr.beta = ld_act<BF>(a.beta, hr);
-    cr.gs = GDN ? ld_act<BF>(a.g, hr) : 0.0f;
+}
+template <bool BF, bool GDN, int NC>
+__device__ __forceinline__ void load_raw(ChunkRaw<GDN, NC>& cr, const MixerArgs& a, int b, int h,
+                                         int c0, int jv0, int tid) {
+    load_raw_part<BF, GDN, NC, RAW_Q>(cr, a, b, h, c0, jv0, tid);
+    load_raw_part<BF, GDN, NC, RAW_K>(cr, a, b, h, c0, jv0, tid);
+    load_raw_part<BF, GDN, NC, RAW_G>(cr, a, b, h, c0, jv0, tid);
+    load_raw_part<BF, GDN, NC, RAW_V>(cr, a, b, h, c0, jv0, tid);
+    load_raw_part<BF, GDN, NC, RAW_BETA>(cr, a, b, h, c0, jv0, tid);
 }
 
 // The raw rows of a chunk (n valid rows) from registers into LDS; the gates and beta
-// are zero past row n, so G stays at G[n-1] and padded rows change nothing.
+// are zero past row n, so G stays at G[n-1] and padded rows change nothing. Every
+// thread stores every item it loaded (threads with the same clamped item store the
+// same value): a store under a branch leaves its load possibly in flight on the
+// other path, and the compiler then waits for all memory traffic at the loop head.
 template <bool GDN, int NC, typename Lds>
 __device__ __forceinline__ void store_raw(Lds& sm, const ChunkRaw<GDN, NC>& raw, int n, int tid) {
     using CR = ChunkRaw<GDN, NC>;
@@ -270,13 +290,12 @@ __device__ __forceinline__ void store_raw(Lds& sm, const ChunkRaw<GDN, NC>& raw,
     }
 #pragma unroll
     for (int it = 0; it < CR::NV; ++it) {
-        const int idx = tid + NTHR * it, r = idx / (NC / 8), c8 = (idx % (NC / 8)) * 8;
-        if (idx < CR::VITEMS) st8(&sm.e.pre.u.rv[r][c8], raw.v[it]);
+        const int idx = min(tid + NTHR * it, CR::VITEMS - 1), r = idx / (NC / 8), c8 = (idx % (NC / 8)) * 8;
+        st8(&sm.e.pre.rv[r][c8], raw.v[it]);
     }
-    if (tid < CH) {
-        sm.beta[tid] = tid < n ? raw.beta : 0.0f;
-        if constexpr (GDN) sm.c.raw.gs[tid] = tid < n ? raw.gs : 0.0f;
-    }
+    const int rr = tid & (CH - 1);
+    sm.beta[rr] = rr < n ? raw.beta : 0.0f;
+    if constexpr (GDN) sm.c.raw.gs[rr] = rr < n ? raw.gs : 0.0f;
 }
 
 // Conv taps of N consecutive channels starting at fused conv row `row`, aligned so
@@ -299,18 +318,20 @@ __device__ __forceinline__ void load_taps(float (&w)[N][KT], const float* conv_w
 }
 
 // One causal-conv step over N channels: win holds the KT-1 previous raw inputs (oldest
-// first), x the current one; returns SiLU of the sum (0 for padded rows) and slides
-// the window.
+// first), x the current one; returns SiLU of the sum and slides the window. Rows past
+// the end of the sequence are not masked here: they hold copies of the last row
+// (finite), and with beta = 0 and zero gates on those rows they drop out of A, W, U,
+// the state update and the stored outputs.
 template <int KT, int N>
 __device__ __forceinline__ void conv_step(float (&win)[KT - 1][N], const float (&x)[N], const float (&w)[N][KT],
-                                          bool valid, float (&y)[N]) {
+                                          float (&y)[N]) {
 #pragma unroll
     for (int e = 0; e < N; ++e) {
         float acc = 0.0f;
 #pragma unroll
         for (int j = 0; j < KT - 1; ++j) acc = fmaf(w[e][j], win[j][e], acc);
         acc = fmaf(w[e][KT - 1], x[e], acc);
-        y[e] = valid ? silu_f(acc) : 0.0f;
+        y[e] = silu_f(acc);
     }
 #pragma unroll
     for (int j = 0; j < KT - 2; ++j)
@@ -318,6 +339,38 @@ __device__ __forceinline__ void conv_step(float (&win)[KT - 1][N], const float (
         for (int e = 0; e < N; ++e) win[j][e] = win[j + 1][e];
 #pragma unroll
     for (int e = 0; e < N; ++e) win[KT - 2][e] = x[e];
+}
+
+// Column block BB of T below the diagonal: T_ab = -T_aa X_ab with
+// X_ab = sum_{c=BB}^{a-1} A_ac T_cb, a = BB+1 .. 3 (v_mfma_f32_16x16x4f32; lane l holds
+// A[l16][k] and B[k][l16] of each 4-wide k slice). X and the T_cb of this column stay in
+// registers in the result layout (lane holds rows 4 q4 .. 4 q4 + 3 of column l16);
+// they enter the next product as its B operand with the k slice permuted to
+// k = 4 q4 + kk, and the A operand is read from LDS with the same permutation.
+template <int BB, typename M>
+__device__ __forceinline__ void merge_column(M& m, int lane) {
+    const int q4 = lane >> 4, l16 = lane & 15;
+    const auto& lf = m.w.solve.lf;
+    const auto& td = m.w.solve.tdiag;
+    f32x4v tcol[3 - BB];  // T_{BB+1,BB} .. T_{3,BB}
+#pragma unroll
+    for (int a = BB + 1; a < 4; ++a) {
+        f32x4v x = zero4();
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)  // c = BB: T_bb from LDS, k = 4 kk + q4
+            x = mfma_f32(lf[16 * a + l16][16 * BB + 4 * kk + q4], td[BB][4 * kk + q4][l16], x);
+#pragma unroll
+        for (int c = BB + 1; c < a; ++c)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)  // k = 4 q4 + kk
+                x = mfma_f32(lf[16 * a + l16][16 * c + 4 * q4 + kk], tcol[c - BB - 1][kk], x);
+        f32x4v y = zero4();
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) y = mfma_f32(td[a][l16][4 * q4 + kk], x[kk], y);
+        tcol[a - BB - 1] = -y;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) m.tb[16 * a + 4 * q4 + r][16 * BB + l16] = (__bf16)(-y[r]);
+    }
 }
 
 template <bool BF, bool GDN, int NC, int KT>
@@ -372,15 +425,17 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
         }
     }
 
-    // Conv roles. q / k: wavefront w < 4 convolves k, w >= 4 convolves q, rows
+    // Conv roles. q / k (P1): wavefront w < 4 convolves k, w >= 4 convolves q, rows
     // 16 (w % 4) .. +15 (one 16-row block), channels 2 lane and 2 lane + 1, so the
     // l2 norm of a row is a sum over the 64 lanes of one wavefront and the block's
-    // gate prefix is a per-thread running sum. v: item (channel, 16-row block), one
-    // per thread from the top thread down (all threads when NC == 128).
+    // gate prefix is a per-thread running sum. v (P3, while wavefronts 0..3 solve for
+    // T): items (channel, 16-row block) on the threads of wavefronts 4..7, NVP per
+    // thread, all of one channel.
     const bool kplane = wave < 4;
-    constexpr int NVIT = 4 * NC;
-    const int vi = tid - (NTHR - NVIT);
-    const int cv = vi % NC, qv = vi / NC;
+    constexpr int NVIT = 4 * NC, NVP = (NVIT + NTHR / 2 - 1) / (NTHR / 2);
+    static_assert((NTHR / 2) % NC == 0, "the v items of a thread share one channel");
+    const int vt = tid - NTHR / 2;  // >= 0 on wavefronts 4..7
+    const int cv = vt % NC;
 
     CR raw;
     load_raw<BF, GDN, NC>(raw, a, b, h, 0, jv0, tid);
@@ -392,17 +447,25 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
         const size_t row0 = (size_t)b * T + c0;
 
         KDA_LAUNDER_LANE();
-        // ---- P0: conv taps (re-read every chunk: a few L2-resident bytes) ----
-        float wqk[2][KT], wv[1][KT];
+        // ---- P0: conv taps and norm weight (re-read every chunk: a few L2-resident
+        // bytes). They are requested here, before any prefetch of the next chunk:
+        // vector-memory counters complete in order, so a small load issued after the
+        // prefetch could only be waited for together with all of it.
+        float wqk[2][KT], wv[1][KT], w8[8];
         load_taps<KT, 2>(wqk, a.conv_w, (kplane ? qkv : 0) + head_off + 2 * lane, K);
-        if (vi >= 0) load_taps<KT, 1>(wv, a.conv_w, 2 * qkv + head_off + jv0 + cv, K);
+        load_taps<KT, 1>(wv, a.conv_w, 2 * qkv + head_off + jv0 + max(cv, 0), K);  // used by wavefronts 4..7
+        if constexpr (NCOL == 1) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) w8[e] = a.norm_w[(tid % (DK / 8)) * 8 + e];
+        }
 
         KDA_LAUNDER_LANE();
         // ---- P1: gate prefix, conv + SiLU + l2, decayed operand tiles ----
         {
             const int qq = wave & 3, rb = 16 * qq, c2 = 2 * lane;
             constexpr int NG = GDN ? 1 : 2;
-            // gamma (gate sum of rows rb+1 .. rb+r), block total and first gate
+            // gamma (gate sum of rows rb+1 .. rb+r), block total and first gate, all
+            // times log2 e
             float gm[16][NG], tot[NG], g0[NG];
 #pragma unroll
             for (int e = 0; e < NG; ++e) gm[0][e] = 0.0f;
@@ -410,10 +473,10 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
                 float acc = 0.0f;
 #pragma unroll
                 for (int r = 1; r < 16; ++r) {
-                    acc += sm.c.raw.gs[rb + r];
+                    acc = fmaf(sm.c.raw.gs[rb + r], LOG2E, acc);
                     gm[r][0] = acc;
                 }
-                g0[0] = sm.c.raw.gs[rb];
+                g0[0] = sm.c.raw.gs[rb] * LOG2E;
                 tot[0] = g0[0] + acc;
             } else {
                 const bf16x2 gf = ld2(&sm.c.raw.rg[rb][c2]);
@@ -423,13 +486,13 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
                     const bf16x2 gv = ld2(&sm.c.raw.rg[rb + r][c2]);
 #pragma unroll
                     for (int e = 0; e < 2; ++e) {
-                        acc[e] += (float)gv[e];
+                        acc[e] = fmaf((float)gv[e], LOG2E, acc[e]);
                         gm[r][e] = acc[e];
                     }
                 }
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
-                    g0[e] = (float)gf[e];
+                    g0[e] = (float)gf[e] * LOG2E;
                     tot[e] = g0[e] + acc[e];
                 }
             }
@@ -459,7 +522,7 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
             for (int r = 0; r < 16; ++r) {
                 const bf16x2 xv = ld2(rawp + (rb + r) * LDH);
                 const float x[2] = {(float)xv[0], (float)xv[1]};
-                conv_step<KT, 2>(win, x, wqk, rb + r < n, y[r]);
+                conv_step<KT, 2>(win, x, wqk, y[r]);
                 ps[r] = fmaf(y[r][0], y[r][0], y[r][1] * y[r][1]);
             }
             const float ss = sum16x64(ps, lane);  // sum of squares of row rb + lane / 4
@@ -479,8 +542,8 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
                 for (int e = 0; e < 2; ++e) {
                     const float g = gm[r][GDN ? 0 : e];
                     const float kh = y[r][e] * nr[r];
-                    o1[e] = (__bf16)(kh * exp_f(g));
-                    if (kplane) o2[e] = (__bf16)(kh * exp_f(-g));
+                    o1[e] = (__bf16)(kh * exp2_f(g));
+                    if (kplane) o2[e] = (__bf16)(kh * exp2_f(-g));
                 }
                 if (kplane) {
                     st2(&sm.ka[rb + r][c2], o1);
@@ -490,32 +553,14 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
                 }
             }
         }
-        if (vi >= 0) {  // v: conv + SiLU, times beta, stored transposed
-            const int rbv = 16 * qv;
-            float win[KT - 1][1];
-#pragma unroll
-            for (int d = 1; d < KT; ++d)
-                win[KT - 1 - d][0] = qv > 0 ? (float)sm.e.pre.u.rv[rbv - d][cv] : (float)sm.hist[d - 1][2 * DK + cv];
-            bf16x8 o[2];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float x[1] = {(float)sm.e.pre.u.rv[rbv + r][cv]};
-                float y[1];
-                conv_step<KT, 1>(win, x, wv, rbv + r < n, y);
-                o[r >> 3][r & 7] = (__bf16)(sm.beta[rbv + r] * y[0]);
-            }
-            st8(&sm.e.pre.vbt[cv][rbv], o[0]);
-            st8(&sm.e.pre.vbt[cv][rbv + 8], o[1]);
-        }
         lds_barrier();
-        // The last KT-1 raw rows become the next chunk's history (only a full chunk has
-        // a successor), and the per-block factor table is formed from the block sums.
+        // The last KT-1 raw q / k rows become the next chunk's history (only a full
+        // chunk has a successor; the v rows follow in P4, after this chunk's v conv),
+        // and the per-block factor table is formed from the block sums.
         if (n == CH) {
-            for (int idx = tid; idx < (KT - 1) * (HLD / 8); idx += NTHR) {
-                const int d = idx / (HLD / 8) + 1, col = (idx % (HLD / 8)) * 8;
-                const __bf16* src = col < DK ? &sm.c.raw.rq[CH - d][col]
-                                  : col < 2 * DK ? &sm.c.raw.rk[CH - d][col - DK]
-                                                 : &sm.e.pre.u.rv[CH - d][col - 2 * DK];
+            for (int idx = tid; idx < (KT - 1) * (2 * DK / 8); idx += NTHR) {
+                const int d = idx / (2 * DK / 8) + 1, col = (idx % (2 * DK / 8)) * 8;
+                const __bf16* src = col < DK ? &sm.c.raw.rq[CH - d][col] : &sm.c.raw.rk[CH - d][col - DK];
                 st8(&sm.hist[d - 1][col], ld8(src));
             }
         }
@@ -528,25 +573,25 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
                 float run = 0.0f;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    bs[q] = run + sm.fac[F_G0 + q][c];  // B_q = G at row 16 q
+                    bs[q] = run + sm.fac[F_G0 + q][c];  // B_q = G at row 16 q (log2 units)
                     run += tt[q];
                 }
                 const float gl = run;  // G_last
                 if (part == 0) {
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) sm.fac[F_EBR + q][c] = exp_f(bs[q]);
+                    for (int q = 0; q < 4; ++q) sm.fac[F_EBR + q][c] = exp2_f(bs[q]);
                 } else if (part == 1) {
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) sm.fac[F_ELR + q][c] = exp_f(gl - bs[q]);
+                    for (int q = 0; q < 4; ++q) sm.fac[F_ELR + q][c] = exp2_f(gl - bs[q]);
                 } else if (part == 2) {
-                    sm.fac[dab_row(1, 0)][c] = exp_f(bs[1] - bs[0]);
-                    sm.fac[dab_row(2, 0)][c] = exp_f(bs[2] - bs[0]);
-                    sm.fac[dab_row(2, 1)][c] = exp_f(bs[2] - bs[1]);
-                    sm.fac[F_FN][c] = exp_f(gl);
+                    sm.fac[dab_row(1, 0)][c] = exp2_f(bs[1] - bs[0]);
+                    sm.fac[dab_row(2, 0)][c] = exp2_f(bs[2] - bs[0]);
+                    sm.fac[dab_row(2, 1)][c] = exp2_f(bs[2] - bs[1]);
+                    sm.fac[F_FN][c] = exp2_f(gl);
                 } else {
-                    sm.fac[dab_row(3, 0)][c] = exp_f(bs[3] - bs[0]);
-                    sm.fac[dab_row(3, 1)][c] = exp_f(bs[3] - bs[1]);
-                    sm.fac[dab_row(3, 2)][c] = exp_f(bs[3] - bs[2]);
+                    sm.fac[dab_row(3, 0)][c] = exp2_f(bs[3] - bs[0]);
+                    sm.fac[dab_row(3, 1)][c] = exp2_f(bs[3] - bs[1]);
+                    sm.fac[dab_row(3, 2)][c] = exp2_f(bs[3] - bs[2]);
                 }
             }
         }
@@ -592,15 +637,20 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
                     lv[r] = (lo && j0 + r < s) ? bs * accL[t][r] : 0.0f;
                     pv[r] = (__bf16)((lo && j0 + r <= s) ? accP[t][r] : 0.0f);
                 }
-                *reinterpret_cast<f32x4v*>(&sm.c.m.w.solve.lf[s][j0]) = lv;
+                if (bb < ab) {
+                    *reinterpret_cast<f32x4v*>(&sm.c.m.w.solve.lf[s][j0]) = lv;
+                } else if (bb == ab) {  // A[s][16 ab + 4 q4 + r] -> ltd[ab][(4 q4 + r) * 16 + l16]
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sm.c.m.w.solve.ltd[ab][(4 * q4 + r) * 16 + l16] = lv[r];
+                }
                 *reinterpret_cast<bf16x4*>(&sm.c.m.pb[s][j0]) = pv;
             }
         }
         lds_barrier();
 
-        // The next chunk's raw rows are requested here and stored at the end of this
-        // iteration, and this chunk's output gates z for the norm in P6, so both HBM
-        // latencies overlap P3..P6.
+        // This chunk's output gates z for the norm in P6 are requested here, and the
+        // next chunk's raw rows part by part from here to P6; they are stored into LDS
+        // at the end of this iteration.
         constexpr int NZ = NCOL == 1 ? CH * (DK / 8) / NTHR : 1;
         bf16x8 zpre[NZ];
         if constexpr (NCOL == 1) {
@@ -610,70 +660,90 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
                 zpre[it] = ld_act8<BF>(a.z, (row0 + min(r, n - 1)) * qkv + head_off + c8);
             }
         }
-        if (c0 + CH < T) load_raw<BF, GDN, NC>(raw, a, b, h, c0 + CH, jv0, tid);
+        // (unconditional, like the store into LDS at the end of the iteration: past the
+        // last chunk the rows clamp to T-1 and are never used, and a branch would make
+        // the compiler wait for every outstanding load and store at its join)
+        load_raw_part<BF, GDN, NC, RAW_Q>(raw, a, b, h, c0 + CH, jv0, tid);
         KDA_LAUNDER_LANE();
-        // ---- P3: T = (I + A)^-1, A = diag(beta) L, 16x16 blocks ----
-        {
-            float (*lf)[LDF] = sm.c.m.w.solve.lf;
-            float (*tf)[LDF] = sm.c.m.w.solve.tf;
-            float (*xs)[16][17] = sm.c.m.w.solve.xs;
-            const int ab = wave;  // waves 0..3: one 16-row block each
-            if (wave < 4 && q4 == 0) {  // diagonal block ab, column l16, forward substitution
+        // ---- P3: T = (I + A)^-1, A = diag(beta) L, in 16x16 blocks; meanwhile the v conv ----
+        if (wave < 4) {
+            if (q4 == 0) {
+                // Diagonal block `wave`, column l16: (I + A_aa) x = e_l16 in column
+                // (axpy) order, so each step's 15 - c updates are independent. Column c
+                // of A_aa is row c of the transposed copy; the next column is read
+                // while this one is applied.
+                const float* at = sm.c.m.w.solve.ltd[wave];
                 float x[16];
 #pragma unroll
+                for (int r = 0; r < 16; ++r) x[r] = (r == l16) ? 1.0f : 0.0f;
+                f32x4v cur[4], nxt[4];
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) nxt[r4] = ld4f(at + 4 * r4);
+#pragma unroll
+                for (int c = 0; c < 15; ++c) {
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) cur[r4] = nxt[r4];
+                    asm volatile("" ::: "memory");  // at most one column in flight
+                    if (c + 1 < 15) {
+#pragma unroll
+                        for (int r4 = 0; r4 < 4; ++r4) nxt[r4] = ld4f(at + (c + 1) * 16 + 4 * r4);
+                    }
+#pragma unroll
+                    for (int r = c + 1; r < 16; ++r) x[r] = fmaf(-cur[r >> 2][r & 3], x[c], x[r]);
+                }
+#pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    // Keep this row's coefficient loads here: hoisting all 120 of them
-                    // would hold 120 registers across the solve.
-                    asm volatile("" ::: "memory");
-                    float acc = (r == l16) ? 1.0f : 0.0f;
-#pragma unroll
-                    for (int jj = 0; jj < r; ++jj) acc = fmaf(-lf[16 * ab + r][16 * ab + jj], x[jj], acc);
-                    x[r] = acc;
-                }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) tf[16 * ab + r][16 * ab + l16] = x[r];
-            }
-            if (wave < 4) {
-                for (int idx = lane; idx < 16 * CH; idx += 64) {  // zero the strictly-upper blocks of row block ab
-                    const int r = idx / CH, j = idx % CH;
-                    if (j >= 16 * (ab + 1)) tf[16 * ab + r][j] = 0.0f;
+                    sm.c.m.w.solve.tdiag[wave][r][l16] = x[r];
+                    sm.c.m.tb[16 * wave + r][16 * wave + l16] = (__bf16)x[r];
                 }
             }
-            lds_barrier();
-            // Off-diagonal blocks by distance: T_ab = -T_aa * sum_{c=b}^{a-1} A_ac T_cb.
-            for (int d = 1; d < 4; ++d) {
-                const int bb = wave < 4 ? ab - d : -1;
-                if (bb >= 0) {
-                    f32x4v xacc = zero4();
-                    for (int cc = bb; cc < ab; ++cc)
-#pragma unroll
-                        for (int kk = 0; kk < 4; ++kk)
-                            xacc = mfma_f32(lf[16 * ab + l16][16 * cc + 4 * kk + q4],
-                                            tf[16 * cc + 4 * kk + q4][16 * bb + l16], xacc);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) xs[wave][4 * q4 + r][l16] = xacc[r];
-                }
-                lds_barrier();
-                if (bb >= 0) {
-                    f32x4v tacc = zero4();
-#pragma unroll
-                    for (int kk = 0; kk < 4; ++kk)
-                        tacc = mfma_f32(tf[16 * ab + l16][16 * ab + 4 * kk + q4], xs[wave][4 * kk + q4][l16], tacc);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) tf[16 * ab + 4 * q4 + r][16 * bb + l16] = -tacc[r];
-                }
-                lds_barrier();
+        } else {
+            // zero T's blocks above the diagonal (row block s / 16, column groups of 8)
+            for (int idx = vt; idx < CH * (CH / 8); idx += NTHR / 2) {
+                const int r = idx / (CH / 8), c8 = (idx % (CH / 8)) * 8;
+                if (c8 >= 16 * ((r >> 4) + 1)) st8(&sm.c.m.tb[r][c8], zero8());
             }
-            for (int idx = tid; idx < CH * CH; idx += NTHR) {
-                const int r = idx / CH, j = idx % CH;
-                sm.e.pre.u.tb[r][j] = (__bf16)tf[r][j];
+            // v: conv + SiLU, times beta, stored transposed
+#pragma unroll
+            for (int m = 0; m < NVP; ++m) {
+                const int item = vt + (NTHR / 2) * m;
+                if (item < NVIT) {
+                    const int qv = item / NC, rbv = 16 * qv;
+                    float win[KT - 1][1];
+#pragma unroll
+                    for (int d = 1; d < KT; ++d)
+                        win[KT - 1 - d][0] = qv > 0 ? (float)sm.e.pre.rv[rbv - d][cv] : (float)sm.hist[d - 1][2 * DK + cv];
+                    bf16x8 o[2];
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float x[1] = {(float)sm.e.pre.rv[rbv + r][cv]};
+                        float y[1];
+                        conv_step<KT, 1>(win, x, wv, y);
+                        o[r >> 3][r & 7] = (__bf16)(sm.beta[rbv + r] * y[0]);
+                    }
+                    st8(&sm.e.pre.vbt[cv][rbv], o[0]);
+                    st8(&sm.e.pre.vbt[cv][rbv + 8], o[1]);
+                }
             }
         }
         lds_barrier();
+        // Blocks below the diagonal, one column block per wavefront:
+        // T_ab = -T_aa sum_{c=b}^{a-1} A_ac T_cb for a = b+1 .. 3.
+        if (wave == 0) merge_column<0>(sm.c.m, lane);
+        else if (wave == 1) merge_column<1>(sm.c.m, lane);
+        else if (wave == 2) merge_column<2>(sm.c.m, lane);
+        lds_barrier();
 
         KDA_LAUNDER_LANE();
+        load_raw_part<BF, GDN, NC, RAW_K>(raw, a, b, h, c0 + CH, jv0, tid);
         // ---- P4: W = T (beta e^{G} k) -> -W in LDS (key block `wave`);
         //      U = T (beta v) in registers (rows 16*sw.., value blocks of half hv) ----
+        if (n == CH) {  // the last KT-1 raw v rows become the next chunk's history
+            for (int idx = tid; idx < (KT - 1) * (NC / 8); idx += NTHR) {
+                const int d = idx / (NC / 8) + 1, col = (idx % (NC / 8)) * 8;
+                st8(&sm.hist[d - 1][2 * DK + col], ld8(&sm.e.pre.rv[CH - d][col]));
+            }
+        }
         f32x4v accU[NJB2];
         {
             const int i = 16 * wave + l16;
@@ -689,7 +759,7 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
                 for (int e = 0; e < 8; ++e) bw[e] = (__bf16)(sm.beta[j0 + e] * eb * (float)sm.ka[j0 + e][i]);
 #pragma unroll
                 for (int sb = 0; sb < 4; ++sb)  // lane: W[16 sb + l16][16 wave + 4 q4 + r]
-                    accW[sb] = mfma_bf16(bw, ld8(&sm.e.pre.u.tb[16 * sb + l16][32 * kk + 8 * q4]), accW[sb]);
+                    accW[sb] = mfma_bf16(bw, ld8(&sm.c.m.tb[16 * sb + l16][32 * kk + 8 * q4]), accW[sb]);
             }
 #pragma unroll
             for (int sb = 0; sb < 4; ++sb) {
@@ -702,7 +772,7 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
             for (int t = 0; t < NJB2; ++t) accU[t] = zero4();
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8 at = ld8(&sm.e.pre.u.tb[16 * sw + l16][32 * kk + 8 * q4]);
+                const bf16x8 at = ld8(&sm.c.m.tb[16 * sw + l16][32 * kk + 8 * q4]);
 #pragma unroll
                 for (int t = 0; t < NJB2; ++t) {
                     const int jb = hv * NJB2 + t;
@@ -713,6 +783,7 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
         lds_barrier();
 
         KDA_LAUNDER_LANE();
+        load_raw_part<BF, GDN, NC, RAW_G>(raw, a, b, h, c0 + CH, jv0, tid);
         // ---- P5: S^T to LDS in bf16, then Ub = U - W S ----
 #pragma unroll
         for (int jb = 0; jb < NJB; ++jb) {
@@ -742,6 +813,8 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
         lds_barrier();
 
         KDA_LAUNDER_LANE();
+        load_raw_part<BF, GDN, NC, RAW_V>(raw, a, b, h, c0 + CH, jv0, tid);
+        load_raw_part<BF, GDN, NC, RAW_BETA>(raw, a, b, h, c0 + CH, jv0, tid);
         // ---- P6: O = scale (Q+ S + P Ub), rows 16*sw.., value blocks of half hv ----
         f32x4v accO[NJB2];
         {
@@ -783,20 +856,21 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
                     a.scale * accO[t];
         }
         lds_barrier();
+        // Items past the last row (or past the item count) store a copy of the last
+        // row's values to the last row: the stores need no branch, and a branch would
+        // make the compiler wait for all memory traffic where it joins.
         {
             constexpr int NITEMS = CH * (NC / 8);
             constexpr int NE = (NITEMS + NTHR - 1) / NTHR;  // items per thread
             const float* of = reinterpret_cast<const float*>(&sm.e);
-            const int c8 = (tid % (NC / 8)) * 8;  // the same columns for every item of a thread
             if constexpr (NCOL == 1) {
-                static_assert(NE == NZ, "z prefetch covers the epilogue items");
+                static_assert(NE == NZ && NITEMS == NE * NTHR, "z prefetch covers the epilogue items");
+                const int c8 = (tid % (NC / 8)) * 8;  // the same columns for every item of a thread
                 const bf16x8* zz = zpre;
-                float w8[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) w8[e] = a.norm_w[c8 + e];
 #pragma unroll
                 for (int it = 0; it < NE; ++it) {
-                    const int r = (tid + NTHR * it) / (NC / 8);  // the 16 lanes of a DPP row share r
+                    // the 16 lanes of a DPP row share r
+                    const int r = min((tid + NTHR * it) / (NC / 8), n - 1);
                     float o8[8];
                     float ss = 0.0f;
 #pragma unroll
@@ -806,7 +880,7 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
                     }
                     ss = sum_row16(ss);
                     const float inv = rsqrtf(fmaf(ss, 1.0f / DK, a.rms_eps));
-                    if (tid + NTHR * it < NITEMS && r < n) {
+                    {
                         const size_t off = (row0 + r) * qkv + head_off + c8;
                         float y[8];
 #pragma unroll
@@ -835,13 +909,12 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
             } else {
 #pragma unroll
                 for (int it = 0; it < NE; ++it) {
-                    const int r = (tid + NTHR * it) / (NC / 8);
-                    if (tid + NTHR * it < NITEMS && r < n) {
-                        const float* src = of + r * LDO + c8;
-                        float4* d = reinterpret_cast<float4*>(o_buf + (row0 + r) * qkv + head_off + jv0 + c8);
-                        d[0] = make_float4(src[0], src[1], src[2], src[3]);
-                        d[1] = make_float4(src[4], src[5], src[6], src[7]);
-                    }
+                    const int idx = min(tid + NTHR * it, NITEMS - 1);
+                    const int r = min(idx / (NC / 8), n - 1), c8 = (idx % (NC / 8)) * 8;
+                    const float* src = of + r * LDO + c8;
+                    float4* d = reinterpret_cast<float4*>(o_buf + (row0 + r) * qkv + head_off + jv0 + c8);
+                    d[0] = make_float4(src[0], src[1], src[2], src[3]);
+                    d[1] = make_float4(src[4], src[5], src[6], src[7]);
                 }
             }
         }
@@ -867,10 +940,8 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
             }
         }
         lds_barrier();
-        if (c0 + CH < T) {
-            store_raw<GDN, NC>(sm, raw, min(CH, T - c0 - CH), tid);
-            lds_barrier();
-        }
+        store_raw<GDN, NC>(sm, raw, max(min(CH, T - c0 - CH), 0), tid);
+        lds_barrier();
     }
 
 #pragma unroll
