@@ -102,6 +102,26 @@ def measure_copy(reps: int = 20) -> float:
     return 2 * COPY_BYTES / (ms * 1e-3) / 1e9
 
 
+def measure_gemm(n: int = 8192, reps: int = 10) -> float:
+    """A large dense bf16 GEMM (torch.mm, contiguous operands): the measured MFMA rate
+    that the chunked arm's contraction fraction is also compared against."""
+    import torch
+
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.mm(a, b)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for x, y in ev:
+        x.record()
+        torch.mm(a, b)
+        y.record()
+    torch.cuda.synchronize()
+    ms = sorted(x.elapsed_time(y) for x, y in ev)[reps // 2]
+    return 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+
+
 def cpu_baseline(cfg, inp, budget_s: float = 12.0):
     """The fp64 oracle on the host cores: whole decode steps of the same workload,
     repeated until the budget is spent."""
@@ -210,7 +230,7 @@ def run_prefill_legs() -> dict:
     from gated_delta_rule_68_amd.synth import CONFIGS
     from gated_delta_rule_68_amd.torch_io import tiled_device_inputs
 
-    legs = {}
+    legs = {"measured_gemm_tflops": measure_gemm()}
     for name in ("kda_prefill", "gdn_prefill", "kda_long"):
         cfg = CONFIGS[name]
         d = tiled_device_inputs(cfg)
@@ -225,7 +245,9 @@ def run_prefill_legs() -> dict:
                  "hbm_gbs": prefill_bytes(cfg) / (ms * 1e-3) / 1e9}
             if arm == "chunked":
                 tf = chunk_flops(cfg) / (ms * 1e-3) / 1e12
-                r.update({"mfma_tflops": tf, "mfma_frac": tf / BF16_PEAK_TFLOPS})
+                r.update({"mfma_tflops": tf, "mfma_frac": tf / BF16_PEAK_TFLOPS,
+                          "mfma_frac_of_measured_gemm": tf / legs["measured_gemm_tflops"],
+                          "hbm_frac": r["hbm_gbs"] / HBM_PEAK_GBS})
             rec[arm] = r
             log(f"prefill {name} {arm}: {r}")
         legs[name] = rec
@@ -243,6 +265,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--copy-only", action="store_true",
                     help="only run the 1 GiB device copy (counter calibration)")
+    ap.add_argument("--prefill-only", metavar="WORKLOAD",
+                    help="only run this prefill workload (kda_prefill, gdn_prefill, kda_long) on "
+                         "the chunked arm, --steps times after one warm-up (for profilers)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -261,6 +286,14 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_only:
         print(json.dumps({"copy_bytes": COPY_BYTES, "copy_gbs": measure_copy()}), flush=True)
+        return
+    if args.prefill_only:
+        import gated_delta_rule_68_amd as kda
+
+        cfg = CONFIGS[args.prefill_only]
+        ms, arm = run_prefill(cfg, kda.KDA_MODE_CHUNKED, reps=max(1, args.steps))
+        print(json.dumps({"workload": args.prefill_only, "arm": arm, "ms": ms,
+                          "tokens_per_s": cfg.B * cfg.T / (ms * 1e-3)}), flush=True)
         return
 
     cfg = CONFIGS["kda_decode"]
@@ -282,9 +315,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 activations, fp32 state and math",
+        "dtype": "f32",
         "data": "synthetic (seeded)",
-        "config": {"workload": "KDA batched decode step", "B": cfg.B, "T": cfg.T, "H": cfg.H,
+        "config": {"workload": "KDA batched decode step", "activations": "bf16",
+                   "B": cfg.B, "T": cfg.T, "H": cfg.H,
                    "D": cfg.D, "conv_kernel": cfg.K, "state": "fp32, in place",
                    "buffers_cycled": NBUF, "arm": "seq_fused"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
