@@ -298,6 +298,18 @@ __device__ __forceinline__ void store_raw(Lds& sm, const ChunkRaw<GDN, NC>& raw,
     if constexpr (GDN) sm.c.raw.gs[rr] = rr < n ? raw.gs : 0.0f;
 }
 
+// N consecutive bf16 channels (N = 1 or 2) as floats.
+template <int N>
+__device__ __forceinline__ void ld_chan(const __bf16* p, float (&x)[N]) {
+    if constexpr (N == 2) {
+        const bf16x2 v = ld2(p);
+        x[0] = (float)v[0];
+        x[1] = (float)v[1];
+    } else {
+        x[0] = (float)*p;
+    }
+}
+
 // Conv taps of N consecutive channels starting at fused conv row `row`, aligned so
 // that w[e][KT-1] multiplies the current input (zero for the KT-K oldest slots).
 // KT == 4 is the K == 4 kernel; K of 2, 3 and 5..8 run the KT == 8 kernel.
@@ -429,13 +441,14 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
     // 16 (w % 4) .. +15 (one 16-row block), channels 2 lane and 2 lane + 1, so the
     // l2 norm of a row is a sum over the 64 lanes of one wavefront and the block's
     // gate prefix is a per-thread running sum. v (P3, while wavefronts 0..3 solve for
-    // T): items (channel, 16-row block) on the threads of wavefronts 4..7, NVP per
-    // thread, all of one channel.
+    // T): items (NVCH channels, 16-row block) on the threads of wavefronts 4..7, NVP
+    // per thread, all of the same channels.
     const bool kplane = wave < 4;
-    constexpr int NVIT = 4 * NC, NVP = (NVIT + NTHR / 2 - 1) / (NTHR / 2);
-    static_assert((NTHR / 2) % NC == 0, "the v items of a thread share one channel");
+    constexpr int NVCH = NC == 128 ? 2 : 1;
+    constexpr int NVIT = 4 * NC / NVCH, NVP = (NVIT + NTHR / 2 - 1) / (NTHR / 2);
+    static_assert((NTHR / 2) % (NC / NVCH) == 0, "the v items of a thread share its channels");
     const int vt = tid - NTHR / 2;  // >= 0 on wavefronts 4..7
-    const int cv = vt % NC;
+    const int cv = (vt % (NC / NVCH)) * NVCH;
 
     CR raw;
     load_raw<BF, GDN, NC>(raw, a, b, h, 0, jv0, tid);
@@ -451,9 +464,9 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
         // bytes). They are requested here, before any prefetch of the next chunk:
         // vector-memory counters complete in order, so a small load issued after the
         // prefetch could only be waited for together with all of it.
-        float wqk[2][KT], wv[1][KT], w8[8];
+        float wqk[2][KT], wv[NVCH][KT], w8[8];
         load_taps<KT, 2>(wqk, a.conv_w, (kplane ? qkv : 0) + head_off + 2 * lane, K);
-        load_taps<KT, 1>(wv, a.conv_w, 2 * qkv + head_off + jv0 + max(cv, 0), K);  // used by wavefronts 4..7
+        load_taps<KT, NVCH>(wv, a.conv_w, 2 * qkv + head_off + jv0 + max(cv, 0), K);  // used by wavefronts 4..7
         if constexpr (NCOL == 1) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) w8[e] = a.norm_w[(tid % (DK / 8)) * 8 + e];
@@ -708,21 +721,36 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
             for (int m = 0; m < NVP; ++m) {
                 const int item = vt + (NTHR / 2) * m;
                 if (item < NVIT) {
-                    const int qv = item / NC, rbv = 16 * qv;
-                    float win[KT - 1][1];
+                    const int qv = item / (NC / NVCH), rbv = 16 * qv;
+                    float win[KT - 1][NVCH];
 #pragma unroll
-                    for (int d = 1; d < KT; ++d)
-                        win[KT - 1 - d][0] = qv > 0 ? (float)sm.e.pre.rv[rbv - d][cv] : (float)sm.hist[d - 1][2 * DK + cv];
-                    bf16x8 o[2];
+                    for (int d = 1; d < KT; ++d) {
+                        float x[NVCH];
+                        ld_chan<NVCH>(qv > 0 ? &sm.e.pre.rv[rbv - d][cv] : &sm.hist[d - 1][2 * DK + cv], x);
+#pragma unroll
+                        for (int e = 0; e < NVCH; ++e) win[KT - 1 - d][e] = x[e];
+                    }
+                    float bt[16];
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        const f32x4v b4 = ld4f(&sm.beta[rbv + 4 * r4]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) bt[4 * r4 + e] = b4[e];
+                    }
+                    bf16x8 o[NVCH][2];
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const float x[1] = {(float)sm.e.pre.rv[rbv + r][cv]};
-                        float y[1];
-                        conv_step<KT, 1>(win, x, wv, y);
-                        o[r >> 3][r & 7] = (__bf16)(sm.beta[rbv + r] * y[0]);
+                        float x[NVCH], y[NVCH];
+                        ld_chan<NVCH>(&sm.e.pre.rv[rbv + r][cv], x);
+                        conv_step<KT, NVCH>(win, x, wv, y);
+#pragma unroll
+                        for (int e = 0; e < NVCH; ++e) o[e][r >> 3][r & 7] = (__bf16)(bt[r] * y[e]);
                     }
-                    st8(&sm.e.pre.vbt[cv][rbv], o[0]);
-                    st8(&sm.e.pre.vbt[cv][rbv + 8], o[1]);
+#pragma unroll
+                    for (int e = 0; e < NVCH; ++e) {
+                        st8(&sm.e.pre.vbt[cv + e][rbv], o[e][0]);
+                        st8(&sm.e.pre.vbt[cv + e][rbv + 8], o[e][1]);
+                    }
                 }
             }
         }
