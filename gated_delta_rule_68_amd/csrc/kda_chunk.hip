@@ -611,22 +611,30 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
         lds_barrier();
 
         KDA_LAUNDER_LANE();
-        // ---- P2: L and P; wavefront (a, p) = (wave / 2, wave % 2) computes block-row a,
-        // column blocks p and p + 2 ----
+        // ---- P2: L and P, 16x16 blocks (a, b). Wavefront w < 4 computes the diagonal
+        // block (w, w) (and solves it in P3 without waiting for the others) plus one
+        // block below it; wavefronts 4..6 take the remaining blocks below the diagonal
+        // before their v conv. Blocks above the diagonal that P6 reads, (0,1) and (2,3),
+        // are written as zeros. ----
         {
-            const int ab = wave >> 1, par = wave & 1, ra = 16 * ab, s = ra + l16;
+            const int w = __builtin_amdgcn_readfirstlane(wave);
+            // (row block, first column block, second column block or -1)
+            const int ab = w < 4 ? w : (w == 4 ? 2 : 3);
+            const int bsel[2] = {w < 4 ? w : (w == 4 ? 1 : (w == 5 ? 0 : (w == 6 ? 2 : -1))),
+                                 w == 0 ? 1 : (w == 1 || w == 2 ? 0 : (w == 3 ? 1 : (w == 4 ? 3 : -1)))};
+            const int ra = 16 * ab, s = ra + l16;
             f32x4v accL[2], accP[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) accL[t] = accP[t] = zero4();
-            if (par <= ab) {
+            if (bsel[0] >= 0) {
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
                     const int i0 = 32 * kk + 8 * q4;
                     const bf16x8 ak = ld8(&sm.ka[s][i0]), aq = ld8(&sm.qa[s][i0]);
 #pragma unroll
                     for (int t = 0; t < 2; ++t) {
-                        const int bb = par + 2 * t;
-                        if (bb > ab) break;
+                        const int bb = bsel[t];
+                        if (bb < 0 || bb > ab) continue;
                         bf16x8 bk = ld8(&sm.kb[16 * bb + l16][i0]);
                         if (bb < ab) {  // off-diagonal block: rebase from B_b to B_a
                             const float* d = &sm.fac[dab_row(ab, bb)][GDN ? 0 : i0];
@@ -641,7 +649,8 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
             const float bs = sm.beta[s];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const int bb = par + 2 * t, j0 = 16 * bb + 4 * q4;
+                const int bb = bsel[t], j0 = 16 * bb + 4 * q4;
+                if (bb < 0) continue;
                 const bool lo = bb <= ab;
                 f32x4v lv;
                 bf16x4 pv;
@@ -659,7 +668,8 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
                 *reinterpret_cast<bf16x4*>(&sm.c.m.pb[s][j0]) = pv;
             }
         }
-        lds_barrier();
+        // No barrier here: P3's first step only reads blocks its own wavefront wrote, and
+        // the barrier inside P3 orders everything else P2 wrote before its readers.
 
         // This chunk's output gates z for the norm in P6 are requested here, and the
         // next chunk's raw rows part by part from here to P6; they are stored into LDS
@@ -680,6 +690,7 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
         KDA_LAUNDER_LANE();
         // ---- P3: T = (I + A)^-1, A = diag(beta) L, in 16x16 blocks; meanwhile the v conv ----
         if (wave < 4) {
+            lds_wave_sync();  // this wavefront's own diagonal block from P2
             if (q4 == 0) {
                 // Diagonal block `wave`, column l16: (I + A_aa) x = e_l16 in column
                 // (axpy) order, so each step's 15 - c updates are independent. Column c
