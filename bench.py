@@ -220,6 +220,62 @@ def run_prefill(cfg, mode, reps=5, d=None):
     return ms, kda.ARM_NAMES.get(arm, str(arm))
 
 
+def run_verify_leg(T_stash: int = 8, keep: int = 4, reps: int = 20) -> dict:
+    """Speculative verify at the decode shape (B=64, H=64, D=128, bf16): one sequential
+    prefill over T_stash draft rows, and the exact rollback of that round to `keep` rows
+    (ring restore + replay from the pre-round state). HIP-event time of each call, and
+    algorithmic HBM bytes (state both ways, ring both ways, rows read / written)."""
+    import torch
+
+    import gated_delta_rule_68_amd as kda
+    from gated_delta_rule_68_amd.synth import CONFIGS
+    from gated_delta_rule_68_amd.torch_io import alloc_outputs, tiled_device_inputs
+
+    cfg = CONFIGS["kda_decode"].with_(T=T_stash)
+    d = dict(tiled_device_inputs(cfg))
+    d.update(alloc_outputs(cfg, T_stash, "cuda", o_core=False))
+    ring_snap, state_snap = d["ring"].clone(), d["state"].clone()
+    ring, state = d["ring"].clone(), d["state"].clone()
+    scale = 1.0 / math.sqrt(cfg.D)
+
+    def verify():
+        kda.kda_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["conv_w"], ring, state, state,
+                        d["z"], d["norm_w"], d["out"], None, scale=scale, rms_eps=RMS_EPS,
+                        mode=kda.KDA_MODE_SEQUENTIAL)
+
+    def rollback():
+        kda.kda_rollback(d["q"], d["k"], d["v"], d["g"], d["beta"], d["conv_w"], ring_snap, state_snap,
+                         ring, state, keep)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+
+    es = 2
+    qkv, B, H = cfg.qkv, cfg.B, cfg.H
+    state_b = 2 * B * H * cfg.D * cfg.D * 4
+    ring_b = 2 * B * 3 * qkv * (cfg.K - 1) * 4
+    row_in = (5 * qkv + H) * es  # q, k, v, g, z + beta
+    ms_v = timed(verify)
+    ms_r = timed(rollback)
+    bytes_v = state_b + ring_b + B * T_stash * (row_in + qkv * es)
+    bytes_r = state_b + 2 * ring_b + B * keep * (row_in - qkv * es)  # ring copy, no z / out
+    rec = {"workload": f"KDA verify B={B} H={H} D={cfg.D} bf16, {T_stash} draft rows, rollback to {keep}",
+           "verify_ms": ms_v, "verify_tokens_per_s": B * T_stash / (ms_v * 1e-3),
+           "verify_hbm_gbs": bytes_v / (ms_v * 1e-3) / 1e9,
+           "rollback_ms": ms_r, "rollback_hbm_gbs": bytes_r / (ms_r * 1e-3) / 1e9}
+    log(f"verify/rollback: {rec}")
+    return rec
+
+
 def run_prefill_legs() -> dict:
     """Each prefill workload on the chunked and the sequential arm: time of the whole
     arm (every kernel it launches), tokens/s, algorithmic HBM GB/s and, for the
@@ -263,6 +319,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-verify", action="store_true")
     ap.add_argument("--copy-only", action="store_true",
                     help="only run the 1 GiB device copy (counter calibration)")
     ap.add_argument("--prefill-only", metavar="WORKLOAD",
@@ -329,6 +386,8 @@ def main():
     }
     if not args.no_prefill:
         line["prefill"] = run_prefill_legs()
+    if not args.no_verify:
+        line["verify_rollback"] = run_verify_leg()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, inp)
     print(json.dumps(line), flush=True)

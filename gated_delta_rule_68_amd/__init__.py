@@ -2,6 +2,6 @@
 (``libkda.so``, declared in include/kda.h) and its thin Python binding."""
 from ._lib import (  # noqa: F401
     ARM_NAMES, EXPORTS, KDA_DTYPE_BF16, KDA_DTYPE_F32, KDA_MODE_AUTO, KDA_MODE_CHUNKED,
-    KDA_MODE_SEQUENTIAL, KdaError, gdn_decode, gdn_prefill, kda_decode, kda_prefill, lib,
-    prefill_arm, status_string, workspace_bytes,
+    KDA_MODE_SEQUENTIAL, KdaError, gdn_decode, gdn_prefill, gdn_rollback, kda_decode, kda_prefill,
+    kda_rollback, lib, prefill_arm, rollback_workspace_bytes, status_string, workspace_bytes,
 )

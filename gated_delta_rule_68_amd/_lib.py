@@ -21,9 +21,11 @@ _lib = None
 _vp, _fp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _PREFILL_ARGS = [_vp] * 5 + [_fp, _fp, _fp, _fp, _vp, _fp, _vp, _fp] + [_i] * 5 + [_f, _f, _i, _i, _vp, _sz, _vp]
 _DECODE_ARGS = [_vp] * 5 + [_fp, _fp, _fp, _fp, _vp, _fp, _vp, _fp] + [_i] * 5 + [_f, _f, _i, _vp]
+_ROLLBACK_ARGS = [_vp] * 5 + [_fp] * 5 + [_i] * 7 + [_vp, _sz, _vp]
 EXPORTS = ("kda_prefill", "kda_decode", "gdn_prefill", "gdn_decode",
            "kda_prefill_workspace_bytes", "gdn_prefill_workspace_bytes",
-           "kda_prefill_arm", "gdn_prefill_arm", "kda_status_string")
+           "kda_prefill_arm", "gdn_prefill_arm", "kda_rollback", "gdn_rollback",
+           "kda_rollback_workspace_bytes", "gdn_rollback_workspace_bytes", "kda_status_string")
 
 
 class KdaError(RuntimeError):
@@ -52,6 +54,12 @@ def lib() -> ctypes.CDLL:
         for n in ("kda_prefill_arm", "gdn_prefill_arm"):
             getattr(l, n).argtypes = [_i] * 6
             getattr(l, n).restype = _i
+        for n in ("kda_rollback", "gdn_rollback"):
+            getattr(l, n).argtypes = _ROLLBACK_ARGS
+            getattr(l, n).restype = _i
+        for n in ("kda_rollback_workspace_bytes", "gdn_rollback_workspace_bytes"):
+            getattr(l, n).argtypes = [_i] * 5
+            getattr(l, n).restype = _sz
         l.kda_status_string.argtypes = [_i]
         l.kda_status_string.restype = ctypes.c_char_p
         _lib = l
@@ -149,3 +157,36 @@ def gdn_decode(q, k, v, g, beta, conv_w, conv_ring, state_in, state_out, z, norm
                o_core=None, *, scale, rms_eps, stream=None, check=True):
     return _decode("gdn_decode", q, k, v, g, beta, conv_w, conv_ring, state_in, state_out, z,
                    norm_w, out, o_core, scale, rms_eps, stream, check)
+
+
+def rollback_workspace_bytes(B, keep, H, D, dtype_code, gdn=False) -> int:
+    fn = lib().gdn_rollback_workspace_bytes if gdn else lib().kda_rollback_workspace_bytes
+    return int(fn(B, keep, H, D, dtype_code))
+
+
+def _rollback(name, q, k, v, g, beta, conv_w, ring_snap, state_snap, conv_ring, state_out, keep,
+              workspace, stream, check):
+    B, T, H, D, K = _geometry(q, state_snap, conv_w)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = getattr(lib(), name)(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(conv_w), _ptr(ring_snap),
+        _ptr(state_snap), _ptr(conv_ring), _ptr(state_out), B, T, int(keep), H, D, K,
+        _dtype_code(q), _ptr(workspace), ws_bytes, _stream_handle(stream))
+    if check and rc != 0:
+        raise KdaError(rc, name)
+    return rc
+
+
+def kda_rollback(q, k, v, g, beta, conv_w, ring_snap, state_snap, conv_ring, state_out, keep, *,
+                 workspace=None, stream=None, check=True):
+    """Rebuild conv_ring / state_out as after the first `keep` rows of a verify round whose
+    raw inputs are q, k, v, g, beta ([B][T_stash][...]) and whose pre-round ring and state
+    were ring_snap and state_snap. Returns the status."""
+    return _rollback("kda_rollback", q, k, v, g, beta, conv_w, ring_snap, state_snap, conv_ring,
+                     state_out, keep, workspace, stream, check)
+
+
+def gdn_rollback(q, k, v, g, beta, conv_w, ring_snap, state_snap, conv_ring, state_out, keep, *,
+                 workspace=None, stream=None, check=True):
+    return _rollback("gdn_rollback", q, k, v, g, beta, conv_w, ring_snap, state_snap, conv_ring,
+                     state_out, keep, workspace, stream, check)

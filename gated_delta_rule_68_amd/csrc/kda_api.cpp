@@ -132,10 +132,74 @@ int entry(bool gdn, bool decode, const void* q, const void* k, const void* v, co
     if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return KDA_ERR_DTYPE_MODE;
     MixerArgs a{q, k, v, g, beta, conv_w, conv_ring, state_in, state_out, z, norm_w, out,
                 o_core, B, T, H, D, K, scale, rms_eps, dtype == KDA_DTYPE_BF16, gdn,
-                workspace, workspace_bytes, (hipStream_t)stream};
+                workspace, workspace_bytes, (hipStream_t)stream, T, true};
     int arm = 0;
     const int rc = validate(a, decode, mode, &arm);
     if (rc) return rc;
+    return run(a, arm);
+}
+
+// Rollback of a verify round: ring <- ring_snap, then the sequential arm replays the
+// first `keep` of the T_stash stored rows of every sequence from state_snap, with no
+// readout. Validated in full before the copy or any launch.
+int rollback(bool gdn, const void* q, const void* k, const void* v, const void* g,
+             const void* beta, const float* conv_w, const float* ring_snap,
+             const float* state_snap, float* conv_ring, float* state_out, int B, int T_stash,
+             int keep, int H, int D, int K, int dtype, void* workspace, size_t workspace_bytes,
+             void* stream) {
+    if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return KDA_ERR_DTYPE_MODE;
+    if (!q || !k || !v || !g || !beta || !conv_w || !ring_snap || !state_snap || !conv_ring ||
+        !state_out)
+        return KDA_ERR_NULL;
+    int rc = check_shape(B, T_stash, H, D, K);
+    if (rc) return rc;
+    if (keep < 1 || keep > T_stash) return KDA_ERR_SHAPE;
+    const bool bf16 = dtype == KDA_DTYPE_BF16;
+    const int arm = pick_arm(B, keep, H, D, bf16, KDA_MODE_SEQUENTIAL);
+    const void* ptrs[] = {q, k, v, g, beta, conv_w, ring_snap, state_snap, conv_ring, state_out, workspace};
+    for (const void* p : ptrs)
+        if (p && ((uintptr_t)p & 15u)) return KDA_ERR_ALIGN;
+    const size_t need_ws = workspace_for(B, keep, H, D, gdn, arm);
+    if (need_ws > 0 && (!workspace || workspace_bytes < need_ws)) return KDA_ERR_WORKSPACE;
+
+    const size_t es = bf16 ? 2 : 4;
+    const size_t qkv = (size_t)H * D;
+    const size_t act = (size_t)B * T_stash * qkv;
+    const size_t ring_bytes = (size_t)B * 3 * qkv * (K - 1) * 4;
+    const size_t state_bytes = (size_t)B * H * D * D * 4;
+    auto Rg = [](const void* p, size_t bytes, bool w, int id) {
+        return Range{(uintptr_t)p, (uintptr_t)p + bytes, w, id};
+    };
+    Range rs[11];
+    int n = 0;
+    rs[n++] = Rg(q, act * es, false, 0);
+    rs[n++] = Rg(k, act * es, false, 1);
+    rs[n++] = Rg(v, act * es, false, 2);
+    rs[n++] = Rg(g, (gdn ? (size_t)B * T_stash * H : act) * es, false, 3);
+    rs[n++] = Rg(beta, (size_t)B * T_stash * H * es, false, 4);
+    rs[n++] = Rg(conv_w, 3 * qkv * K * 4, false, 5);
+    rs[n++] = Rg(ring_snap, ring_bytes, false, 6);
+    rs[n++] = Rg(state_snap, state_bytes, false, 7);
+    rs[n++] = Rg(conv_ring, ring_bytes, true, 8);
+    rs[n++] = Rg(state_out, state_bytes, true, 9);
+    if (need_ws > 0) rs[n++] = Rg(workspace, need_ws, true, 10);
+    for (int i = 0; i < n; ++i)
+        for (int j = i + 1; j < n; ++j) {
+            if (!(rs[i].writable || rs[j].writable) || !overlaps(rs[i], rs[j])) continue;
+            const bool same = rs[i].lo == rs[j].lo;
+            const bool ring_pair = rs[i].id == 6 && rs[j].id == 8 && same;
+            const bool state_pair = rs[i].id == 7 && rs[j].id == 9 && same;
+            if (!ring_pair && !state_pair) return KDA_ERR_ALIAS;
+        }
+
+    if (conv_ring != ring_snap) {
+        const hipError_t e = hipMemcpyAsync(conv_ring, ring_snap, ring_bytes, hipMemcpyDeviceToDevice,
+                                            (hipStream_t)stream);
+        if (e != hipSuccess) return KDA_ERR_RUNTIME_BASE + (int)e;
+    }
+    MixerArgs a{q, k, v, g, beta, conv_w, conv_ring, state_snap, state_out, nullptr, nullptr, nullptr,
+                nullptr, B, keep, H, D, K, 1.0f, 0.0f, bf16, gdn, workspace, workspace_bytes,
+                (hipStream_t)stream, T_stash, false};
     return run(a, arm);
 }
 
@@ -195,6 +259,29 @@ int gdn_decode(const void* q, const void* k, const void* v, const void* g, const
                  KDA_MODE_SEQUENTIAL, nullptr, 0, stream);
 }
 
+int kda_rollback(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                 const float* conv_w, const float* ring_snap, const float* state_snap,
+                 float* conv_ring, float* state_out, int B, int T_stash, int keep, int H, int D,
+                 int K, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    return rollback(false, q, k, v, g, beta, conv_w, ring_snap, state_snap, conv_ring, state_out,
+                    B, T_stash, keep, H, D, K, dtype, workspace, workspace_bytes, stream);
+}
+
+int gdn_rollback(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                 const float* conv_w, const float* ring_snap, const float* state_snap,
+                 float* conv_ring, float* state_out, int B, int T_stash, int keep, int H, int D,
+                 int K, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    return rollback(true, q, k, v, g, beta, conv_w, ring_snap, state_snap, conv_ring, state_out,
+                    B, T_stash, keep, H, D, K, dtype, workspace, workspace_bytes, stream);
+}
+
+size_t kda_rollback_workspace_bytes(int B, int keep, int H, int D, int dtype) {
+    return ws_query(false, B, keep, H, D, dtype, KDA_MODE_SEQUENTIAL);
+}
+size_t gdn_rollback_workspace_bytes(int B, int keep, int H, int D, int dtype) {
+    return ws_query(true, B, keep, H, D, dtype, KDA_MODE_SEQUENTIAL);
+}
+
 size_t kda_prefill_workspace_bytes(int B, int T, int H, int D, int dtype, int mode) {
     return ws_query(false, B, T, H, D, dtype, mode);
 }
@@ -219,7 +306,9 @@ const char* kda_status_string(int rc) {
         case KDA_ERR_WORKSPACE: return "workspace missing or smaller than the query returned";
         case KDA_ERR_ALIGN: return "every pointer must be 16-byte aligned";
         case KDA_ERR_DTYPE_MODE: return "unknown dtype or mode, or mode not valid for this shape";
-        case KDA_ERR_ALIAS: return "buffers overlap (only state_in == state_out may alias)";
+        case KDA_ERR_ALIAS:
+            return "buffers overlap (only state_in == state_out, or a rollback's snapshot and "
+                   "live ring / state, may be the same buffer)";
         default: break;
     }
     if (rc >= KDA_ERR_RUNTIME_BASE && rc < 20000) return "HIP runtime error during launch";

@@ -30,6 +30,12 @@ struct MixerArgs {
     void* ws;
     size_t ws_bytes;
     hipStream_t stream;
+    // Rows of each sequence in memory for the activation inputs (q, k, v, g, beta):
+    // T except for a rollback replay, which walks the first T of tp stored rows.
+    int tp;
+    // Whether the readout (z, norm_w in; out, o_core out) is produced; a rollback
+    // replay only rebuilds the state and the ring (the sequential arms honour it).
+    bool readout;
 };
 
 // Arms (values match the KDA_ARM_* codes of the public header).

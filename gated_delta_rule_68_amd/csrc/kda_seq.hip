@@ -74,7 +74,7 @@ __global__ __launch_bounds__(fused_threads<D>()) void seq_fused_kernel(MixerArgs
 
     for (int t0 = 0; t0 < T; t0 += TB_FUSED) {
         const int nt = min(TB_FUSED, T - t0);
-        const size_t row0 = (size_t)b * T + t0;
+        const size_t row0 = (size_t)b * a.tp + t0;  // tp == T whenever the readout is produced
         for (int r = tid; r < 3 * D; r += NT) {
             const int plane = r / D, ch = r % D;
             const void* xsrc = plane == 0 ? a.q : (plane == 1 ? a.k : a.v);
@@ -113,10 +113,12 @@ __global__ __launch_bounds__(fused_threads<D>()) void seq_fused_kernel(MixerArgs
             }
         }
         __syncthreads();
-        for (int tt = wave; tt < nt; tt += NW) {
-            const size_t off = (row0 + tt) * qkv + head_off;
-            const GateRow gz = load_gate_row<D, BF>(a, off, lane);
-            gated_rmsnorm_row<D, BF, GDN>(os[tt], gz, a, off, lane, a.o_core);
+        if (a.readout) {
+            for (int tt = wave; tt < nt; tt += NW) {
+                const size_t off = (row0 + tt) * qkv + head_off;
+                const GateRow gz = load_gate_row<D, BF>(a, off, lane);
+                gated_rmsnorm_row<D, BF, GDN>(os[tt], gz, a, off, lane, a.o_core);
+            }
         }
         __syncthreads();
     }
@@ -155,7 +157,8 @@ __global__ __launch_bounds__(pre_threads<D>()) void pre_kernel(MixerArgs a, floa
     const int nt = min(TB_PRE, T - t0);
     const size_t qkv = (size_t)H * D;
     const size_t head_off = (size_t)h * D;
-    const size_t row0 = (size_t)b * T + t0;
+    const size_t row0 = (size_t)b * T + t0;      // workspace rows
+    const size_t rin0 = (size_t)b * a.tp + t0;   // input rows
 
     const bool conv_thread = tid < 3 * D;
     const int plane = tid / D, ch = tid % D;
@@ -163,7 +166,7 @@ __global__ __launch_bounds__(pre_threads<D>()) void pre_kernel(MixerArgs a, floa
     float* ring_row = a.ring + ((size_t)b * 3 * qkv + cf) * (K - 1);
     const void* xsrc = plane == 0 ? a.q : (plane == 1 ? a.k : a.v);
     auto raw_at = [&](int pos) -> float {  // x~[K-1+pos]: raw input at token pos (< 0: ring)
-        return pos >= 0 ? ld_act<BF>(xsrc, ((size_t)b * T + pos) * qkv + head_off + ch)
+        return pos >= 0 ? ld_act<BF>(xsrc, ((size_t)b * a.tp + pos) * qkv + head_off + ch)
                         : ring_row[pos + K - 1];
     };
     if (conv_thread) {
@@ -172,7 +175,7 @@ __global__ __launch_bounds__(pre_threads<D>()) void pre_kernel(MixerArgs a, floa
 #pragma unroll
         for (int d = 1; d < KMAX; ++d) cc.win[KMAX - 1 - d] = (d <= K - 1) ? raw_at(t0 - d) : 0.0f;
         for (int tt = 0; tt < nt; ++tt)
-            pre[plane][tt][ch] = silu_f(conv_push(cc, ld_act<BF>(xsrc, (row0 + tt) * qkv + head_off + ch)));
+            pre[plane][tt][ch] = silu_f(conv_push(cc, ld_act<BF>(xsrc, (rin0 + tt) * qkv + head_off + ch)));
         // Only the first token block reads the old ring (TB_PRE >= KMAX - 1), so it
         // alone rolls it, after its own reads: new slot K-1-d = raw input at T-d.
         if (blockIdx.y == 0) {
@@ -185,11 +188,11 @@ __global__ __launch_bounds__(pre_threads<D>()) void pre_kernel(MixerArgs a, floa
         }
     }
     if constexpr (GDN) {
-        if (tid < nt) eg[(row0 + tid) * H + h] = exp_f(ld_act<BF>(a.g, (row0 + tid) * H + h));
+        if (tid < nt) eg[(row0 + tid) * H + h] = exp_f(ld_act<BF>(a.g, (rin0 + tid) * H + h));
     } else {
         for (int idx = tid; idx < nt * D; idx += NT) {
-            const size_t off = (row0 + idx / D) * qkv + head_off + idx % D;
-            eg[off] = exp_f(ld_act<BF>(a.g, off));
+            const size_t col = head_off + idx % D;
+            eg[(row0 + idx / D) * qkv + col] = exp_f(ld_act<BF>(a.g, (rin0 + idx / D) * qkv + col));
         }
     }
     __syncthreads();
@@ -249,7 +252,7 @@ __global__ __launch_bounds__(8 * split_cols<D>()) void scan_split_kernel(
         }
         if (tid < nt) {
             const size_t hr = (row0 + tid) * H + h;
-            bs[tid] = ld_act<BF>(a.beta, hr);
+            bs[tid] = ld_act<BF>(a.beta, ((size_t)b * a.tp + t0 + tid) * H + h);
             kqs[tid] = kqv[hr];
             if constexpr (GDN) es[tid][0] = eg[hr];
         }
@@ -307,7 +310,7 @@ hipError_t split_launch(const MixerArgs& a) {
     hipLaunchKernelGGL((scan_split_kernel<D, BF, GDN>), dim3(a.B * a.H * NS), dim3(8 * split_cols<D>()),
                        0, a.stream, a, qh, kh, vh, eg, kq, o);
     e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || !a.readout) return e;
     const size_t rows = (size_t)a.B * a.T * a.H;
     hipLaunchKernelGGL((norm_kernel<D, BF, GDN>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
                        a.stream, a, o);

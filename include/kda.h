@@ -63,12 +63,12 @@ extern "C" {
 #define KDA_ERR_NULL 40001         /* a required pointer is NULL */
 #define KDA_ERR_HEAD_DIM 40002     /* D not in {16, 128} */
 #define KDA_ERR_CONV_KERNEL 40003  /* K outside 2..8 */
-#define KDA_ERR_SHAPE 40004        /* B, T or H < 1, or sizes overflow */
+#define KDA_ERR_SHAPE 40004        /* B, T or H < 1, keep outside 1..T_stash, or sizes overflow */
 #define KDA_ERR_DECODE_T 40005     /* a decode entry point called with T != 1 */
 #define KDA_ERR_WORKSPACE 40006    /* workspace NULL or smaller than required */
 #define KDA_ERR_ALIGN 40007        /* a pointer is not 16-byte aligned */
 #define KDA_ERR_DTYPE_MODE 40008   /* unknown dtype or mode, or mode not valid here */
-#define KDA_ERR_ALIAS 40009        /* two buffers overlap (other than state_in == state_out) */
+#define KDA_ERR_ALIAS 40009        /* two buffers overlap (other than the allowed in-place pairs) */
 
 /* ---- dtype and prefill mode ---- */
 #define KDA_DTYPE_F32 0
@@ -141,6 +141,45 @@ size_t gdn_prefill_workspace_bytes(int B, int T, int H, int D, int dtype, int mo
 /* The arm (KDA_ARM_*) a prefill with these arguments runs, or -1 if rejected. */
 int kda_prefill_arm(int B, int T, int H, int D, int dtype, int mode);
 int gdn_prefill_arm(int B, int T, int H, int D, int dtype, int mode);
+
+/*
+ * Speculative verify and exact rollback (memra-engine kda.rs: the batched verify-rows
+ * call and the rollback of a verify round, which restores the pre-round conv ring,
+ * re-rolls it over the kept raw rows, and replays the scan from the caller's
+ * pre-round state snapshot).
+ *
+ * A verify round is kda_prefill over T_stash = K+1 draft rows with
+ * mode = KDA_MODE_SEQUENTIAL: every output row, the rolled ring and the final
+ * state are bit-identical to T_stash chained kda_decode calls. The caller keeps
+ * copies of the conv ring and the state taken BEFORE that call (ring_snap,
+ * state_snap) and the call's raw inputs q, k, v, g, beta ([B][T_stash][...]).
+ *
+ * kda_rollback - rebuild the ring and the state as they were after the first
+ * `keep` rows of every sequence (1 <= keep <= T_stash): conv_ring <- ring_snap,
+ * then the sequential arm replays rows 0 .. keep-1 of the stored inputs from
+ * state_snap with no readout. The result is bit-identical to `keep` chained
+ * kda_decode calls from the snapshots (same kernels, same per-step arithmetic).
+ *   Reads q, k, v, g, beta (T_stash rows per sequence, only the first keep used),
+ *   conv_w, ring_snap, state_snap. Writes conv_ring, state_out.
+ *   ring_snap may be the same pointer as conv_ring (already restored: no copy) and
+ *   state_snap the same pointer as state_out (replayed in place); any other overlap
+ *   between a written buffer and another buffer is KDA_ERR_ALIAS.
+ *   keep outside 1 .. T_stash is KDA_ERR_SHAPE. workspace: at least
+ *   kda_rollback_workspace_bytes(B, keep, H, D, dtype) bytes (0 for keep <= 16 or
+ *   B*H >= 1024). Other arguments and codes as for kda_prefill.
+ */
+int kda_rollback(const void* q, const void* k, const void* v, const void* g,
+                 const void* beta, const float* conv_w, const float* ring_snap,
+                 const float* state_snap, float* conv_ring, float* state_out,
+                 int B, int T_stash, int keep, int H, int D, int K, int dtype,
+                 void* workspace, size_t workspace_bytes, void* stream);
+int gdn_rollback(const void* q, const void* k, const void* v, const void* g,
+                 const void* beta, const float* conv_w, const float* ring_snap,
+                 const float* state_snap, float* conv_ring, float* state_out,
+                 int B, int T_stash, int keep, int H, int D, int K, int dtype,
+                 void* workspace, size_t workspace_bytes, void* stream);
+size_t kda_rollback_workspace_bytes(int B, int keep, int H, int D, int dtype);
+size_t gdn_rollback_workspace_bytes(int B, int keep, int H, int D, int dtype);
 
 /* Static description of a status code (never NULL). */
 const char* kda_status_string(int rc);

@@ -52,7 +52,7 @@ BASE = 1 << 40  # fake, 256-byte aligned, far-apart addresses; never dereference
 
 def fake_args(B=2, T=3, H=2, D=16, K=4, dtype=0, mode=1):
     names = ["q", "k", "v", "g", "beta", "conv_w", "ring", "state_in", "state_out", "z",
-             "norm_w", "out", "o_core", "ws"]
+             "norm_w", "out", "o_core", "ws", "ring_snap", "state_snap"]
     a = {n: BASE + i * (1 << 32) for i, n in enumerate(names)}
     a.update(B=B, T=T, H=H, D=D, K=K, dtype=dtype, mode=mode, ws_bytes=1 << 31)
     return a
@@ -136,3 +136,50 @@ def test_queries():
     assert kda.prefill_arm(1, 4626, 64, 128, 1, 1) == 2
     assert kda.prefill_arm(1, 64, 2, 64, 0, 1) == -1
     assert kda.workspace_bytes(0, 1, 1, 16, 0, 1) == ctypes.c_size_t(-1).value
+
+
+def call_rollback(a, gdn=False, T_stash=3, keep=2):
+    f = kda.lib().gdn_rollback if gdn else kda.lib().kda_rollback
+    return f(a["q"], a["k"], a["v"], a["g"], a["beta"], a["conv_w"], a["ring_snap"], a["state_snap"],
+             a["ring"], a["state_out"], a["B"], T_stash, keep, a["H"], a["D"], a["K"], a["dtype"],
+             a["ws"], a["ws_bytes"], None)
+
+
+ROLLBACK_CASES = [
+    ("keep 0", dict(), dict(keep=0), 40004),
+    ("keep past the stash", dict(), dict(keep=4), 40004),
+    ("null ring_snap", dict(ring_snap=None), dict(), 40001),
+    ("null state_out", dict(state_out=None), dict(), 40001),
+    ("misaligned state_snap", dict(state_snap=BASE + 15 * (1 << 32) + 4), dict(), 40007),
+    ("ring_snap partially over ring", dict(ring_snap=BASE + 6 * (1 << 32) + 16), dict(), 40009),
+    ("state_out over q", dict(state_out=BASE + 256), dict(), 40009),
+    ("state_snap over ring", dict(state_snap=BASE + 6 * (1 << 32) + 64), dict(), 40009),
+    ("dtype 2", dict(dtype=2), dict(), 40008),
+    ("D=64", dict(D=64), dict(), 40002),
+    ("K=9", dict(K=9), dict(), 40003),
+]
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="fake pointers only where no GPU is visible")
+@pytest.mark.parametrize("gdn", [False, True])
+@pytest.mark.parametrize("what,over,kw,rc", ROLLBACK_CASES, ids=[c[0] for c in ROLLBACK_CASES])
+def test_rollback_contract(what, over, kw, rc, gdn):
+    a = fake_args()
+    a.update({k: (0 if v is None else v) for k, v in over.items()})
+    assert call_rollback(a, gdn, **kw) == rc
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="fake pointers only where no GPU is visible")
+def test_rollback_workspace_too_small():
+    # few (b, h) pairs and keep > 16: the split arm, which needs a workspace
+    a = fake_args(B=1, H=2, D=16)
+    need = kda.rollback_workspace_bytes(1, 40, 2, 16, 0)
+    assert need > 0
+    a["ws_bytes"] = need - 1
+    assert call_rollback(a, T_stash=50, keep=40) == 40006
+
+
+def test_rollback_queries():
+    assert kda.rollback_workspace_bytes(64, 8, 64, 128, 1) == 0  # short replay: fused arm
+    assert kda.rollback_workspace_bytes(1, 40, 2, 16, 0) == kda.workspace_bytes(1, 40, 2, 16, 0, 1)
+    assert kda.rollback_workspace_bytes(1, 40, 2, 64, 0) == ctypes.c_size_t(-1).value

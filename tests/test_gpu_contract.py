@@ -9,13 +9,13 @@ import pytest
 import torch
 
 import gated_delta_rule_68_amd as kda
-from tests.test_abi_host import CASES, call_decode, call_prefill
+from tests.test_abi_host import CASES, ROLLBACK_CASES, call_decode, call_prefill, call_rollback
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 SLOT = 1 << 20  # bytes per argument slot (the shapes below need a few KB)
 NAMES = ["q", "k", "v", "g", "beta", "conv_w", "ring", "state_in", "state_out", "z",
-         "norm_w", "out", "o_core", "ws"]
+         "norm_w", "out", "o_core", "ws", "ring_snap", "state_snap"]
 OUTPUTS = ("ring", "state_out", "out", "o_core")
 SENTINEL = 0x5A
 
@@ -124,3 +124,12 @@ def test_valid_calls_after_rejections(gdn):
     assert call_decode(a, gdn) == 0
     torch.cuda.synchronize()
     assert float(t1["out"].abs().max()) == 0.0
+
+
+@pytest.mark.parametrize("gdn", [False, True])
+@pytest.mark.parametrize("what,over,kw,rc", ROLLBACK_CASES, ids=[c[0] for c in ROLLBACK_CASES])
+def test_rollback_rejected_before_copy_or_launch(arena, what, over, kw, rc, gdn):
+    a = real_args(arena)
+    a.update(rebase(arena, over))
+    assert call_rollback(a, gdn, **kw) == rc
+    assert outputs_untouched(arena) is None
