@@ -276,6 +276,105 @@ def run_verify_leg(T_stash: int = 8, keep: int = 4, reps: int = 20) -> dict:
     return rec
 
 
+def _timed(fn, reps):
+    """Median HIP-event time (ms) of fn() over reps calls after one untimed call."""
+    import torch
+
+    fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        fn(i)
+        b.record()
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+
+
+def run_gated_leg(reps: int = 50) -> dict:
+    """The fused gate activation (softplus form, g = max(-5, -e^A_log * softplus(x +
+    dt_bias)), beta = sigmoid(b)): the gated decode step at the decode shape and the
+    gated chunked prefill of the single-sequence KDA workload, each beside the same
+    call on precomputed g / beta. Algorithmic bytes are the plain path's plus the gate
+    parameters (A_log-derived factor per head, bias per gate column, fp32)."""
+    import torch
+
+    import gated_delta_rule_68_amd as kda
+    from gated_delta_rule_68_amd.synth import CONFIGS
+    from gated_delta_rule_68_amd.torch_io import alloc_outputs, tiled_device_inputs
+
+    rec = {"form": "softplus, lower bound -5"}
+    cfg = CONFIGS["kda_decode"]
+    base = tiled_device_inputs(cfg)
+    ga = -torch.exp(base["A_log"])
+    sets = []
+    for _ in range(NBUF):
+        d = {n: t.clone() for n, t in base.items()}
+        d.update(alloc_outputs(cfg, 1, "cuda", o_core=False))
+        sets.append(d)
+    del base
+    scale = 1.0 / math.sqrt(cfg.D)
+
+    def dec_gated(i=0):
+        d = sets[i % NBUF]
+        kda.kda_decode_gated(d["q"], d["k"], d["v"], d["gate_x"], d["beta_x"], ga, d["dt_bias"],
+                             d["conv_w"], d["ring"], d["state"], d["state"], d["z"], d["norm_w"],
+                             d["out"], None, gate_form=kda.KDA_GATE_SOFTPLUS, gate_lb=-5.0,
+                             scale=scale, rms_eps=RMS_EPS)
+
+    def dec_plain(i=0):
+        d = sets[i % NBUF]
+        kda.kda_decode(d["q"], d["k"], d["v"], d["g"], d["beta"], d["conv_w"], d["ring"],
+                       d["state"], d["state"], d["z"], d["norm_w"], d["out"], None,
+                       scale=scale, rms_eps=RMS_EPS)
+
+    nb = decode_bytes(cfg) + (cfg.H + cfg.qkv) * 4
+    ms_g, ms_p = _timed(dec_gated, reps), _timed(dec_plain, reps)
+    rec["decode"] = {"workload": f"KDA decode B={cfg.B} H={cfg.H} D={cfg.D} bf16",
+                     "gated_ms": ms_g, "plain_ms": ms_p,
+                     "gated_tokens_per_s": cfg.B / (ms_g * 1e-3),
+                     "gated_hbm_gbs": nb / (ms_g * 1e-3) / 1e9,
+                     "gated_hbm_frac": nb / (ms_g * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    del sets
+    torch.cuda.empty_cache()
+
+    for name in ("kda_prefill", "gdn_prefill"):
+        cfg = CONFIGS[name]
+        d = dict(tiled_device_inputs(cfg))
+        d.update(alloc_outputs(cfg, cfg.T, "cuda", o_core=False))
+        ga = -torch.exp(d["A_log"])
+        mode = kda.KDA_MODE_CHUNKED
+        ws = torch.empty(max(kda.workspace_bytes(cfg.B, cfg.T, cfg.H, cfg.D, kda.KDA_DTYPE_BF16, mode,
+                                                 gdn=cfg.gdn), 1), dtype=torch.uint8, device="cuda")
+        ring0, s_out = d["ring"].clone(), torch.empty_like(d["state"])
+        gated = kda.gdn_prefill_gated if cfg.gdn else kda.kda_prefill_gated
+        plain = kda.gdn_prefill if cfg.gdn else kda.kda_prefill
+
+        def pre_gated(i=0):
+            d["ring"].copy_(ring0)
+            gated(d["q"], d["k"], d["v"], d["gate_x"], d["beta_x"], ga, d["dt_bias"], d["conv_w"],
+                  d["ring"], d["state"], s_out, d["z"], d["norm_w"], d["out"], None,
+                  gate_form=kda.KDA_GATE_SOFTPLUS, gate_lb=-5.0, scale=scale, rms_eps=RMS_EPS,
+                  mode=mode, workspace=ws)
+
+        def pre_plain(i=0):
+            d["ring"].copy_(ring0)
+            plain(d["q"], d["k"], d["v"], d["g"], d["beta"], d["conv_w"], d["ring"], d["state"], s_out,
+                  d["z"], d["norm_w"], d["out"], None, scale=scale, rms_eps=RMS_EPS, mode=mode,
+                  workspace=ws)
+
+        ms_g, ms_p = _timed(pre_gated, 5), _timed(pre_plain, 5)
+        rec[name] = {"workload": f"{'GDN' if cfg.gdn else 'KDA'} chunked prefill B={cfg.B} T={cfg.T} "
+                                 f"H={cfg.H} D={cfg.D} bf16 (incl. a ring reset copy)",
+                     "gated_ms": ms_g, "plain_ms": ms_p,
+                     "gated_tokens_per_s": cfg.B * cfg.T / (ms_g * 1e-3)}
+        del d, ws
+        torch.cuda.empty_cache()
+    log(f"gated: {rec}")
+    return rec
+
+
 def run_prefill_legs() -> dict:
     """Each prefill workload on the chunked and the sequential arm: time of the whole
     arm (every kernel it launches), tokens/s, algorithmic HBM GB/s and, for the
@@ -320,6 +419,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-verify", action="store_true")
+    ap.add_argument("--no-gated", action="store_true")
     ap.add_argument("--copy-only", action="store_true",
                     help="only run the 1 GiB device copy (counter calibration)")
     ap.add_argument("--prefill-only", metavar="WORKLOAD",
@@ -388,6 +488,8 @@ def main():
         line["prefill"] = run_prefill_legs()
     if not args.no_verify:
         line["verify_rollback"] = run_verify_leg()
+    if not args.no_gated:
+        line["gated"] = run_gated_leg()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, inp)
     print(json.dumps(line), flush=True)

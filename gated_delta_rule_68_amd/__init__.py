@@ -1,7 +1,9 @@
 """MI355X (gfx950) KDA / GDN gated delta-rule mixer: a C-ABI HIP library
 (``libkda.so``, declared in include/kda.h) and its thin Python binding."""
 from ._lib import (  # noqa: F401
-    ARM_NAMES, EXPORTS, KDA_DTYPE_BF16, KDA_DTYPE_F32, KDA_MODE_AUTO, KDA_MODE_CHUNKED,
+    ARM_NAMES, EXPORTS, KDA_DTYPE_BF16, KDA_DTYPE_F32, KDA_GATE_SIGMOID, KDA_GATE_SOFTPLUS,
+    KDA_MODE_AUTO, KDA_MODE_CHUNKED, gdn_decode_gated, gdn_prefill_gated, kda_decode_gated,
+    kda_prefill_gated,
     KDA_MODE_SEQUENTIAL, KdaError, gdn_decode, gdn_prefill, gdn_rollback, kda_decode, kda_prefill,
     kda_rollback, lib, prefill_arm, rollback_workspace_bytes, status_string, workspace_bytes,
 )

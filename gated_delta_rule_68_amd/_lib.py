@@ -22,10 +22,15 @@ _vp, _fp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c
 _PREFILL_ARGS = [_vp] * 5 + [_fp, _fp, _fp, _fp, _vp, _fp, _vp, _fp] + [_i] * 5 + [_f, _f, _i, _i, _vp, _sz, _vp]
 _DECODE_ARGS = [_vp] * 5 + [_fp, _fp, _fp, _fp, _vp, _fp, _vp, _fp] + [_i] * 5 + [_f, _f, _i, _vp]
 _ROLLBACK_ARGS = [_vp] * 5 + [_fp] * 5 + [_i] * 7 + [_vp, _sz, _vp]
+_GATE_ARGS = [_fp, _fp, _f, _i]
+_GATED_PREFILL_ARGS = _PREFILL_ARGS[:5] + _GATE_ARGS + _PREFILL_ARGS[5:]
+_GATED_DECODE_ARGS = _DECODE_ARGS[:5] + _GATE_ARGS + _DECODE_ARGS[5:]
+KDA_GATE_SIGMOID, KDA_GATE_SOFTPLUS = 1, 2
 EXPORTS = ("kda_prefill", "kda_decode", "gdn_prefill", "gdn_decode",
            "kda_prefill_workspace_bytes", "gdn_prefill_workspace_bytes",
            "kda_prefill_arm", "gdn_prefill_arm", "kda_rollback", "gdn_rollback",
-           "kda_rollback_workspace_bytes", "gdn_rollback_workspace_bytes", "kda_status_string")
+           "kda_rollback_workspace_bytes", "gdn_rollback_workspace_bytes", "kda_prefill_gated",
+           "gdn_prefill_gated", "kda_decode_gated", "gdn_decode_gated", "kda_status_string")
 
 
 class KdaError(RuntimeError):
@@ -53,6 +58,12 @@ def lib() -> ctypes.CDLL:
             getattr(l, n).restype = _sz
         for n in ("kda_prefill_arm", "gdn_prefill_arm"):
             getattr(l, n).argtypes = [_i] * 6
+            getattr(l, n).restype = _i
+        for n in ("kda_prefill_gated", "gdn_prefill_gated"):
+            getattr(l, n).argtypes = _GATED_PREFILL_ARGS
+            getattr(l, n).restype = _i
+        for n in ("kda_decode_gated", "gdn_decode_gated"):
+            getattr(l, n).argtypes = _GATED_DECODE_ARGS
             getattr(l, n).restype = _i
         for n in ("kda_rollback", "gdn_rollback"):
             getattr(l, n).argtypes = _ROLLBACK_ARGS
@@ -190,3 +201,54 @@ def gdn_rollback(q, k, v, g, beta, conv_w, ring_snap, state_snap, conv_ring, sta
                  workspace=None, stream=None, check=True):
     return _rollback("gdn_rollback", q, k, v, g, beta, conv_w, ring_snap, state_snap, conv_ring,
                      state_out, keep, workspace, stream, check)
+
+
+def _gated(name, decode, q, k, v, gate_x, beta_x, gate_a, gate_bias, conv_w, conv_ring, state_in,
+           state_out, z, norm_w, out, o_core, gate_form, gate_lb, scale, rms_eps, mode, workspace,
+           stream, check):
+    B, T, H, D, K = _geometry(q, state_in, conv_w)
+    head = (_ptr(q), _ptr(k), _ptr(v), _ptr(gate_x), _ptr(beta_x), _ptr(gate_a), _ptr(gate_bias),
+            float(gate_lb), int(gate_form), _ptr(conv_w), _ptr(conv_ring), _ptr(state_in),
+            _ptr(state_out), _ptr(z), _ptr(norm_w), _ptr(out), _ptr(o_core), B, T, H, D, K,
+            float(scale), float(rms_eps), _dtype_code(q))
+    if decode:
+        rc = getattr(lib(), name)(*head, _stream_handle(stream))
+    else:
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        rc = getattr(lib(), name)(*head, int(mode), _ptr(workspace), ws_bytes, _stream_handle(stream))
+    if check and rc != 0:
+        raise KdaError(rc, name)
+    return rc
+
+
+def kda_prefill_gated(q, k, v, gate_x, beta_x, gate_a, gate_bias, conv_w, conv_ring, state_in,
+                      state_out, z, norm_w, out, o_core=None, *, gate_form, gate_lb, scale, rms_eps,
+                      mode=KDA_MODE_AUTO, workspace=None, stream=None, check=True):
+    """kda_prefill with the gate and beta pre-activations (include/kda.h, KDA_GATE_*)."""
+    return _gated("kda_prefill_gated", False, q, k, v, gate_x, beta_x, gate_a, gate_bias, conv_w,
+                  conv_ring, state_in, state_out, z, norm_w, out, o_core, gate_form, gate_lb, scale,
+                  rms_eps, mode, workspace, stream, check)
+
+
+def gdn_prefill_gated(q, k, v, gate_x, beta_x, gate_a, gate_bias, conv_w, conv_ring, state_in,
+                      state_out, z, norm_w, out, o_core=None, *, gate_form, gate_lb, scale, rms_eps,
+                      mode=KDA_MODE_AUTO, workspace=None, stream=None, check=True):
+    return _gated("gdn_prefill_gated", False, q, k, v, gate_x, beta_x, gate_a, gate_bias, conv_w,
+                  conv_ring, state_in, state_out, z, norm_w, out, o_core, gate_form, gate_lb, scale,
+                  rms_eps, mode, workspace, stream, check)
+
+
+def kda_decode_gated(q, k, v, gate_x, beta_x, gate_a, gate_bias, conv_w, conv_ring, state_in,
+                     state_out, z, norm_w, out, o_core=None, *, gate_form, gate_lb, scale, rms_eps,
+                     stream=None, check=True):
+    return _gated("kda_decode_gated", True, q, k, v, gate_x, beta_x, gate_a, gate_bias, conv_w,
+                  conv_ring, state_in, state_out, z, norm_w, out, o_core, gate_form, gate_lb, scale,
+                  rms_eps, None, None, stream, check)
+
+
+def gdn_decode_gated(q, k, v, gate_x, beta_x, gate_a, gate_bias, conv_w, conv_ring, state_in,
+                     state_out, z, norm_w, out, o_core=None, *, gate_form, gate_lb, scale, rms_eps,
+                     stream=None, check=True):
+    return _gated("gdn_decode_gated", True, q, k, v, gate_x, beta_x, gate_a, gate_bias, conv_w,
+                  conv_ring, state_in, state_out, z, norm_w, out, o_core, gate_form, gate_lb, scale,
+                  rms_eps, None, None, stream, check)

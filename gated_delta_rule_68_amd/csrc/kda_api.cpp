@@ -71,8 +71,9 @@ int validate(const MixerArgs& a, bool decode, int mode, int* arm_out) {
     const int arm = decode ? (int)kda::ARM_SEQ_FUSED : pick_arm(a.B, a.T, a.H, a.D, a.bf16, mode);
     if (arm < 0) return KDA_ERR_DTYPE_MODE;
 
+    if (a.gate_form != kda::GATE_GIVEN && (!a.gate_a || !a.gate_bias)) return KDA_ERR_NULL;
     const void* ptrs[] = {a.q, a.k, a.v, a.g, a.beta, a.conv_w, a.ring, a.state_in,
-                          a.state_out, a.z, a.norm_w, a.out, a.o_core, a.ws};
+                          a.state_out, a.z, a.norm_w, a.out, a.o_core, a.ws, a.gate_a, a.gate_bias};
     for (const void* p : ptrs)
         if (p && ((uintptr_t)p & 15u)) return KDA_ERR_ALIGN;
 
@@ -87,7 +88,7 @@ int validate(const MixerArgs& a, bool decode, int mode, int* arm_out) {
     auto R = [](const void* p, size_t bytes, bool w, int id) {
         return Range{(uintptr_t)p, (uintptr_t)p + bytes, w, id};
     };
-    Range rs[14];
+    Range rs[16];
     int n = 0;
     rs[n++] = R(a.q, act * es, false, 0);
     rs[n++] = R(a.k, act * es, false, 1);
@@ -103,6 +104,10 @@ int validate(const MixerArgs& a, bool decode, int mode, int* arm_out) {
     rs[n++] = R(a.out, act * es, true, 11);
     if (a.o_core) rs[n++] = R(a.o_core, act * 4, true, 12);
     if (need_ws > 0) rs[n++] = R(a.ws, need_ws, true, 13);
+    if (a.gate_form != kda::GATE_GIVEN) {
+        rs[n++] = R(a.gate_a, (size_t)a.H * 4, false, 14);
+        rs[n++] = R(a.gate_bias, (a.gdn ? (size_t)a.H : qkv) * 4, false, 15);
+    }
     for (int i = 0; i < n; ++i)
         for (int j = i + 1; j < n; ++j) {
             if (!(rs[i].writable || rs[j].writable) || !overlaps(rs[i], rs[j])) continue;
@@ -124,15 +129,32 @@ int run(const MixerArgs& a, int arm) {
     return e == hipSuccess ? KDA_OK : KDA_ERR_RUNTIME_BASE + (int)e;
 }
 
+struct GateArgs {
+    int form;
+    const float* a;
+    const float* bias;
+    float lb;
+};
+constexpr GateArgs kGiven{kda::GATE_GIVEN, nullptr, nullptr, 0.0f};
+
 int entry(bool gdn, bool decode, const void* q, const void* k, const void* v, const void* g,
           const void* beta, const float* conv_w, float* conv_ring, const float* state_in,
           float* state_out, const void* z, const float* norm_w, void* out, float* o_core,
           int B, int T, int H, int D, int K, float scale, float rms_eps, int dtype, int mode,
-          void* workspace, size_t workspace_bytes, void* stream) {
+          void* workspace, size_t workspace_bytes, void* stream, GateArgs ga = kGiven) {
     if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return KDA_ERR_DTYPE_MODE;
+    if (ga.form != kda::GATE_GIVEN && ga.form != KDA_GATE_SIGMOID && ga.form != KDA_GATE_SOFTPLUS)
+        return KDA_ERR_DTYPE_MODE;
     MixerArgs a{q, k, v, g, beta, conv_w, conv_ring, state_in, state_out, z, norm_w, out,
                 o_core, B, T, H, D, K, scale, rms_eps, dtype == KDA_DTYPE_BF16, gdn,
-                workspace, workspace_bytes, (hipStream_t)stream, T, true};
+                workspace, workspace_bytes, (hipStream_t)stream, T, true,
+                ga.form, ga.a, ga.bias, ga.lb};
+    if (ga.form == kda::GATE_GIVEN) {
+        // Kernels read the gate parameters without a branch; point them at conv_w
+        // (3*H*D*K >= H*D floats, allocated and 16-byte aligned), values unused.
+        a.gate_a = conv_w;
+        a.gate_bias = conv_w;
+    }
     int arm = 0;
     const int rc = validate(a, decode, mode, &arm);
     if (rc) return rc;
@@ -199,7 +221,7 @@ int rollback(bool gdn, const void* q, const void* k, const void* v, const void* 
     }
     MixerArgs a{q, k, v, g, beta, conv_w, conv_ring, state_snap, state_out, nullptr, nullptr, nullptr,
                 nullptr, B, keep, H, D, K, 1.0f, 0.0f, bf16, gdn, workspace, workspace_bytes,
-                (hipStream_t)stream, T_stash, false};
+                (hipStream_t)stream, T_stash, false, kda::GATE_GIVEN, conv_w, conv_w, 0.0f};
     return run(a, arm);
 }
 
@@ -258,6 +280,38 @@ int gdn_decode(const void* q, const void* k, const void* v, const void* g, const
                  norm_w, out, o_core, B, T, H, D, K, scale, rms_eps, dtype,
                  KDA_MODE_SEQUENTIAL, nullptr, 0, stream);
 }
+
+#define KDA_GATED_PREFILL(NAME, GDN)                                                              \
+    int NAME(const void* q, const void* k, const void* v, const void* gate_x, const void* beta_x,  \
+             const float* gate_a, const float* gate_bias, float gate_lb, int gate_form,            \
+             const float* conv_w, float* conv_ring, const float* state_in, float* state_out,       \
+             const void* z, const float* norm_w, void* out, float* o_core, int B, int T, int H,    \
+             int D, int K, float scale, float rms_eps, int dtype, int mode, void* workspace,       \
+             size_t workspace_bytes, void* stream) {                                               \
+        if (gate_form == 0) return KDA_ERR_DTYPE_MODE; /* 0: use the plain entry */               \
+        return entry(GDN, false, q, k, v, gate_x, beta_x, conv_w, conv_ring, state_in, state_out,  \
+                     z, norm_w, out, o_core, B, T, H, D, K, scale, rms_eps, dtype, mode,           \
+                     workspace, workspace_bytes, stream,                                           \
+                     GateArgs{gate_form, gate_a, gate_bias, gate_lb});                             \
+    }
+#define KDA_GATED_DECODE(NAME, GDN)                                                               \
+    int NAME(const void* q, const void* k, const void* v, const void* gate_x, const void* beta_x,  \
+             const float* gate_a, const float* gate_bias, float gate_lb, int gate_form,            \
+             const float* conv_w, float* conv_ring, const float* state_in, float* state_out,       \
+             const void* z, const float* norm_w, void* out, float* o_core, int B, int T, int H,    \
+             int D, int K, float scale, float rms_eps, int dtype, void* stream) {                  \
+        if (gate_form == 0) return KDA_ERR_DTYPE_MODE; /* 0: use the plain entry */               \
+        return entry(GDN, true, q, k, v, gate_x, beta_x, conv_w, conv_ring, state_in, state_out,   \
+                     z, norm_w, out, o_core, B, T, H, D, K, scale, rms_eps, dtype,                 \
+                     KDA_MODE_SEQUENTIAL, nullptr, 0, stream,                                      \
+                     GateArgs{gate_form, gate_a, gate_bias, gate_lb});                             \
+    }
+KDA_GATED_PREFILL(kda_prefill_gated, false)
+KDA_GATED_PREFILL(gdn_prefill_gated, true)
+KDA_GATED_DECODE(kda_decode_gated, false)
+KDA_GATED_DECODE(gdn_decode_gated, true)
+#undef KDA_GATED_PREFILL
+#undef KDA_GATED_DECODE
 
 int kda_rollback(const void* q, const void* k, const void* v, const void* g, const void* beta,
                  const float* conv_w, const float* ring_snap, const float* state_snap,

@@ -279,7 +279,8 @@ __device__ __forceinline__ void load_raw(ChunkRaw<GDN, NC>& cr, const MixerArgs&
 // same value): a store under a branch leaves its load possibly in flight on the
 // other path, and the compiler then waits for all memory traffic at the loop head.
 template <bool GDN, int NC, typename Lds>
-__device__ __forceinline__ void store_raw(Lds& sm, const ChunkRaw<GDN, NC>& raw, int n, int tid) {
+__device__ __forceinline__ void store_raw(Lds& sm, const ChunkRaw<GDN, NC>& raw, int n, int tid,
+                                          const MixerArgs& a, float gm_h, float gb) {
     using CR = ChunkRaw<GDN, NC>;
 #pragma unroll
     for (int it = 0; it < CR::NI; ++it) {
@@ -293,9 +294,14 @@ __device__ __forceinline__ void store_raw(Lds& sm, const ChunkRaw<GDN, NC>& raw,
         const int idx = min(tid + NTHR * it, CR::VITEMS - 1), r = idx / (NC / 8), c8 = (idx % (NC / 8)) * 8;
         st8(&sm.e.pre.rv[r][c8], raw.v[it]);
     }
+    // beta and (GDN) the scalar gates are activated here in fp32 (KDA gates in P1, from
+    // their exact bf16 pre-activations, so no activated gate is rounded to bf16)
     const int rr = tid & (CH - 1);
-    sm.beta[rr] = rr < n ? raw.beta : 0.0f;
-    if constexpr (GDN) sm.c.raw.gs[rr] = rr < n ? raw.gs : 0.0f;
+    sm.beta[rr] = rr < n ? beta_in(a, raw.beta) : 0.0f;
+    if constexpr (GDN)
+        sm.c.raw.gs[rr] = rr < n ? (a.gate_form != GATE_GIVEN ? gate_act_core(a.gate_form, a.gate_lb, gm_h, gb, raw.gs)
+                                                               : raw.gs)
+                                 : 0.0f;
 }
 
 // N consecutive bf16 channels (N = 1 or 2) as floats.
@@ -450,9 +456,16 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
     const int vt = tid - NTHR / 2;  // >= 0 on wavefronts 4..7
     const int cv = (vt % (NC / NVCH)) * NVCH;
 
+    // Gate activation parameters of this head and the thread's two P1 channels (unused
+    // for given gates), read once: a global load inside the chunk loop would be waited
+    // for together with the prefetch.
+    const float gm_h = gate_head_factor(a, h);
+    const float gb0 = a.gate_bias[GDN ? h : head_off + 2 * lane];
+    const float gb1 = a.gate_bias[GDN ? h : head_off + 2 * lane + 1];
+
     CR raw;
     load_raw<BF, GDN, NC>(raw, a, b, h, 0, jv0, tid);
-    store_raw<GDN, NC>(sm, raw, min(CH, T), tid);
+    store_raw<GDN, NC>(sm, raw, min(CH, T), tid, a, gm_h, gb0);
     __syncthreads();
 
     for (int c0 = 0; c0 < T; c0 += CH) {
@@ -492,6 +505,14 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
                 g0[0] = sm.c.raw.gs[rb] * LOG2E;
                 tot[0] = g0[0] + acc;
             } else {
+                // the log gate of row rb + r, channel c2 + e: read as given, or activated
+                // here from its pre-activation (rows past n stay 0)
+                const bool act = a.gate_form != GATE_GIVEN;
+                auto gate_of = [&](bf16x2 x, int r, int e) {
+                    const float gb = e ? gb1 : gb0;
+                    return act ? (rb + r < n ? gate_act_core(a.gate_form, a.gate_lb, gm_h, gb, (float)x[e]) : 0.0f)
+                               : (float)x[e];
+                };
                 const bf16x2 gf = ld2(&sm.c.raw.rg[rb][c2]);
                 float acc[2] = {0.0f, 0.0f};
 #pragma unroll
@@ -499,13 +520,13 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
                     const bf16x2 gv = ld2(&sm.c.raw.rg[rb + r][c2]);
 #pragma unroll
                     for (int e = 0; e < 2; ++e) {
-                        acc[e] = fmaf((float)gv[e], LOG2E, acc[e]);
+                        acc[e] = fmaf(gate_of(gv, r, e), LOG2E, acc[e]);
                         gm[r][e] = acc[e];
                     }
                 }
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
-                    g0[e] = (float)gf[e] * LOG2E;
+                    g0[e] = gate_of(gf, 0, e) * LOG2E;
                     tot[e] = g0[e] + acc[e];
                 }
             }
@@ -979,7 +1000,7 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
             }
         }
         lds_barrier();
-        store_raw<GDN, NC>(sm, raw, max(min(CH, T - c0 - CH), 0), tid);
+        store_raw<GDN, NC>(sm, raw, max(min(CH, T - c0 - CH), 0), tid, a, gm_h, gb0);
         lds_barrier();
     }
 

@@ -21,6 +21,7 @@ constexpr int KMAX = 8;
 // KDA_L2_EPS; aprender-serve gdn_ops.rs, gdn_per_head_l2_norm_into).
 constexpr float L2_EPS = 1e-6f;
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
 
 using bf16_t = unsigned short;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -57,6 +58,35 @@ __device__ __forceinline__ float exp_f(float x) { return __builtin_amdgcn_exp2f(
 // sequence costs several times more instructions on the conv's hot loop).
 __device__ __forceinline__ float sigmoid_f(float x) { return __builtin_amdgcn_rcpf(1.0f + exp_f(-x)); }
 __device__ __forceinline__ float silu_f(float x) { return x * sigmoid_f(x); }
+// ln(1 + e^x) through the hardware base-2 exponential and logarithm; x itself from 20
+// on, where the two differ by less than e^-20.
+__device__ __forceinline__ float softplus_f(float x) {
+    return x > 20.0f ? x : __builtin_amdgcn_logf(1.0f + exp_f(x)) * LN2;
+}
+
+// Gate activations (memra-engine kda.rs, stage 4 and its per-channel gate kernel:
+// g = lb * sigmoid(exp(A_log[h]) * (f + dt_bias[c])), beta = sigmoid(b_raw);
+// aprender-serve gdn_ops.rs, the per-head gates: g = a[h] * softplus(alpha + dt_bias[h]),
+// here also bounded below by lb). x is the pre-activation, c indexes the bias.
+// m is the per-head factor of gate_head_factor.
+__device__ __forceinline__ float gate_act_core(int form, float lb, float m, float bias, float x) {
+    const float t = x + bias;
+    return form == GATE_SIGMOID ? lb * sigmoid_f(m * t) : fmaxf(lb, m * softplus_f(t));
+}
+// exp(A_log[h]) for the sigmoid form, a[h] for the softplus form.
+__device__ __forceinline__ float gate_head_factor(const MixerArgs& a, int h) {
+    return a.gate_form == GATE_SIGMOID ? exp_f(a.gate_a[h]) : a.gate_a[h];
+}
+__device__ __forceinline__ float gate_act(const MixerArgs& a, float x, int h, size_t c) {
+    return gate_act_core(a.gate_form, a.gate_lb, gate_head_factor(a, h), a.gate_bias[c], x);
+}
+// The log gate / beta a kernel uses for what it read from g / beta.
+__device__ __forceinline__ float gate_in(const MixerArgs& a, float x, int h, size_t c) {
+    return a.gate_form != GATE_GIVEN ? gate_act(a, x, h, c) : x;
+}
+__device__ __forceinline__ float beta_in(const MixerArgs& a, float x) {
+    return a.gate_form != GATE_GIVEN ? sigmoid_f(x) : x;
+}
 
 // Butterfly sums. Every lane of the group ends with the same bits (each step adds
 // the same two operands, only in swapped order).

@@ -36,7 +36,17 @@ struct MixerArgs {
     // Whether the readout (z, norm_w in; out, o_core out) is produced; a rollback
     // replay only rebuilds the state and the ring (the sequential arms honour it).
     bool readout;
+    // Gate activation (GATE_*): GATE_GIVEN means g and beta hold the log gate and beta;
+    // otherwise they hold their pre-activations and every arm applies the activation
+    // in fp32 as it reads them.
+    int gate_form;
+    const float* gate_a;     // [H]: A_log (GATE_SIGMOID) or the multiplier a (GATE_SOFTPLUS)
+    const float* gate_bias;  // [H*D] (KDA) or [H] (GDN)
+    float gate_lb;           // lower bound of the log gate
 };
+
+// Values of the KDA_GATE_* codes of the public header.
+enum GateForm { GATE_GIVEN = 0, GATE_SIGMOID = 1, GATE_SOFTPLUS = 2 };
 
 // Arms (values match the KDA_ARM_* codes of the public header).
 enum Arm { ARM_SEQ_FUSED = 1, ARM_SEQ_SPLIT = 2, ARM_CHUNKED = 3 };

@@ -90,14 +90,14 @@ __global__ __launch_bounds__(fused_threads<D>()) void seq_fused_kernel(MixerArgs
             for (int e = 0; e < KMAX - 1; ++e) wins[r][e] = cc.win[e];
         }
         if constexpr (GDN) {
-            if (tid < nt) es[tid][0] = exp_f(ld_act<BF>(a.g, (row0 + tid) * H + h));
+            if (tid < nt) es[tid][0] = exp_f(gate_in(a, ld_act<BF>(a.g, (row0 + tid) * H + h), h, h));
         } else {
             for (int idx = tid; idx < nt * D; idx += NT) {
                 const int tt = idx / D, i = idx % D;
-                es[tt][i] = exp_f(ld_act<BF>(a.g, (row0 + tt) * qkv + head_off + i));
+                es[tt][i] = exp_f(gate_in(a, ld_act<BF>(a.g, (row0 + tt) * qkv + head_off + i), h, head_off + i));
             }
         }
-        if (tid < nt) bs[tid] = ld_act<BF>(a.beta, (row0 + tid) * H + h);
+        if (tid < nt) bs[tid] = beta_in(a, ld_act<BF>(a.beta, (row0 + tid) * H + h));
         __syncthreads();
         for (int tt = wave; tt < nt; tt += NW) l2_qk_row<D>(pre[0][tt], pre[1][tt], lane, &kqs[tt]);
         __syncthreads();
@@ -188,11 +188,12 @@ __global__ __launch_bounds__(pre_threads<D>()) void pre_kernel(MixerArgs a, floa
         }
     }
     if constexpr (GDN) {
-        if (tid < nt) eg[(row0 + tid) * H + h] = exp_f(ld_act<BF>(a.g, (rin0 + tid) * H + h));
+        if (tid < nt) eg[(row0 + tid) * H + h] = exp_f(gate_in(a, ld_act<BF>(a.g, (rin0 + tid) * H + h), h, h));
     } else {
         for (int idx = tid; idx < nt * D; idx += NT) {
             const size_t col = head_off + idx % D;
-            eg[(row0 + idx / D) * qkv + col] = exp_f(ld_act<BF>(a.g, (rin0 + idx / D) * qkv + col));
+            eg[(row0 + idx / D) * qkv + col] =
+                exp_f(gate_in(a, ld_act<BF>(a.g, (rin0 + idx / D) * qkv + col), h, col));
         }
     }
     __syncthreads();
@@ -252,7 +253,7 @@ __global__ __launch_bounds__(8 * split_cols<D>()) void scan_split_kernel(
         }
         if (tid < nt) {
             const size_t hr = (row0 + tid) * H + h;
-            bs[tid] = ld_act<BF>(a.beta, ((size_t)b * a.tp + t0 + tid) * H + h);
+            bs[tid] = beta_in(a, ld_act<BF>(a.beta, ((size_t)b * a.tp + t0 + tid) * H + h));
             kqs[tid] = kqv[hr];
             if constexpr (GDN) es[tid][0] = eg[hr];
         }

@@ -107,6 +107,13 @@ class Inputs:
     ring: np.ndarray
     state: np.ndarray
     bits: dict
+    # The draws the gate and beta come from (the pre-activations as the kernel sees
+    # them, like the activations above, and the per-head / per-channel parameters):
+    # g = max(-5, -exp(A_log[h]) * softplus(gate_x + dt_bias)), beta = sigmoid(beta_x).
+    gate_x: np.ndarray = None
+    beta_x: np.ndarray = None
+    A_log: np.ndarray = None
+    dt_bias: np.ndarray = None
 
     def f64(self, name: str) -> np.ndarray:
         return getattr(self, name).astype(np.float64)
@@ -145,11 +152,13 @@ def make_inputs(cfg: Config, seed: int = 0, T: int | None = None) -> Inputs:
     else:
         ring = np.zeros((B, 3 * qkv, K - 1), np.float32)
         state = np.zeros((B, H, D, D), np.float32)
+    gate_x, beta_x32 = gx.astype(np.float32), beta_x.astype(np.float32)
     bits = {}
     if cfg.dtype == "bf16":
-        acts = {"q": q, "k": k, "v": v, "g": g, "beta": beta, "z": z}
+        acts = {"q": q, "k": k, "v": v, "g": g, "beta": beta, "z": z, "gate_x": gate_x, "beta_x": beta_x32}
         bits = {n: bf16_bits(a) for n, a in acts.items()}
-        q, k, v, g, beta, z = (bf16_to_f32(bits[n]) for n in acts)
+        q, k, v, g, beta, z, gate_x, beta_x32 = (bf16_to_f32(bits[n]) for n in acts)
     elif cfg.dtype != "fp32":
         raise ValueError(f"unknown dtype {cfg.dtype}")
-    return Inputs(cfg, q, k, v, g, beta, z, conv_w, norm_w, ring, state, bits)
+    return Inputs(cfg, q, k, v, g, beta, z, conv_w, norm_w, ring, state, bits, gate_x, beta_x32,
+                  A_log.astype(np.float32), dt_bias.astype(np.float32))

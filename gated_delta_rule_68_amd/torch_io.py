@@ -7,7 +7,7 @@ import torch
 
 from .synth import Inputs
 
-ACTS = ("q", "k", "v", "g", "beta", "z")
+ACTS = ("q", "k", "v", "g", "beta", "z", "gate_x", "beta_x")
 
 
 def _act_tensor(inp: Inputs, name: str, device) -> torch.Tensor:
@@ -19,7 +19,7 @@ def _act_tensor(inp: Inputs, name: str, device) -> torch.Tensor:
 
 def to_device(inp: Inputs, device="cuda") -> dict:
     d = {n: _act_tensor(inp, n, device) for n in ACTS}
-    for n in ("conv_w", "norm_w", "ring", "state"):
+    for n in ("conv_w", "norm_w", "ring", "state", "A_log", "dt_bias"):
         d[n] = torch.from_numpy(np.ascontiguousarray(getattr(inp, n), np.float32)).to(device)
     return d
 

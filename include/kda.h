@@ -77,6 +77,19 @@ extern "C" {
 #define KDA_MODE_SEQUENTIAL 1 /* token-by-token scan (bit-identical to chained decodes) */
 #define KDA_MODE_CHUNKED 2    /* chunk-64 WY form, bf16 MFMA operands, fp32 state (D = 128) */
 
+/* Gate activation of the *_gated entry points (the plain entry points take g and
+ * beta already activated). x is the gate pre-activation read from `g`, b the beta
+ * pre-activation read from `beta`; c = h*D + i (KDA) or h (GDN) indexes gate_bias:
+ *   KDA_GATE_SIGMOID:  g = gate_lb * sigmoid(exp(gate_a[h]) * (x + gate_bias[c]))
+ *                      (memra-engine kda.rs, stage 4: gate_a = A_log, gate_lb = the
+ *                      forget-gate lower bound, e.g. -5)
+ *   KDA_GATE_SOFTPLUS: g = max(gate_lb, gate_a[h] * softplus(x + gate_bias[c]))
+ *                      (aprender-serve gdn_ops.rs, the per-head gates: gate_a = a,
+ *                      usually -exp(A_log); gate_lb = -INFINITY for no bound)
+ *   and in both forms beta = sigmoid(b). */
+#define KDA_GATE_SIGMOID 1
+#define KDA_GATE_SOFTPLUS 2
+
 /* Which kernel arm a prefill with these arguments runs (for reporting). */
 #define KDA_ARM_SEQ_FUSED 1   /* one kernel per (b, h): conv, l2, scan, norm and ring fused */
 #define KDA_ARM_SEQ_SPLIT 2   /* pre-kernel, column-split scan, norm kernel */
@@ -141,6 +154,46 @@ size_t gdn_prefill_workspace_bytes(int B, int T, int H, int D, int dtype, int mo
 /* The arm (KDA_ARM_*) a prefill with these arguments runs, or -1 if rejected. */
 int kda_prefill_arm(int B, int T, int H, int D, int dtype, int mode);
 int gdn_prefill_arm(int B, int T, int H, int D, int dtype, int mode);
+
+/*
+ * Fused gate activation: the four mixer entry points with the gate and beta
+ * pre-activations in place of g and beta (same shapes and dtype), activated inside
+ * the kernels as they are read (see KDA_GATE_*). gate_a is [H] fp32, gate_bias is
+ * [H*D] (KDA) or [H] (GDN) fp32, both 16-byte aligned. gate_form must be
+ * KDA_GATE_SIGMOID or KDA_GATE_SOFTPLUS (else KDA_ERR_DTYPE_MODE). Everything else is
+ * as for the plain entry points; the chunked arm's precondition g >= -5 applies to the
+ * activated gate.
+ */
+int kda_prefill_gated(const void* q, const void* k, const void* v, const void* gate_x,
+                      const void* beta_x, const float* gate_a, const float* gate_bias,
+                      float gate_lb, int gate_form, const float* conv_w, float* conv_ring,
+                      const float* state_in, float* state_out, const void* z,
+                      const float* norm_w, void* out, float* o_core,
+                      int B, int T, int H, int D, int K, float scale, float rms_eps,
+                      int dtype, int mode, void* workspace, size_t workspace_bytes,
+                      void* stream);
+int gdn_prefill_gated(const void* q, const void* k, const void* v, const void* gate_x,
+                      const void* beta_x, const float* gate_a, const float* gate_bias,
+                      float gate_lb, int gate_form, const float* conv_w, float* conv_ring,
+                      const float* state_in, float* state_out, const void* z,
+                      const float* norm_w, void* out, float* o_core,
+                      int B, int T, int H, int D, int K, float scale, float rms_eps,
+                      int dtype, int mode, void* workspace, size_t workspace_bytes,
+                      void* stream);
+int kda_decode_gated(const void* q, const void* k, const void* v, const void* gate_x,
+                     const void* beta_x, const float* gate_a, const float* gate_bias,
+                     float gate_lb, int gate_form, const float* conv_w, float* conv_ring,
+                     const float* state_in, float* state_out, const void* z,
+                     const float* norm_w, void* out, float* o_core,
+                     int B, int T, int H, int D, int K, float scale, float rms_eps,
+                     int dtype, void* stream);
+int gdn_decode_gated(const void* q, const void* k, const void* v, const void* gate_x,
+                     const void* beta_x, const float* gate_a, const float* gate_bias,
+                     float gate_lb, int gate_form, const float* conv_w, float* conv_ring,
+                     const float* state_in, float* state_out, const void* z,
+                     const float* norm_w, void* out, float* o_core,
+                     int B, int T, int H, int D, int K, float scale, float rms_eps,
+                     int dtype, void* stream);
 
 /*
  * Speculative verify and exact rollback (memra-engine kda.rs: the batched verify-rows

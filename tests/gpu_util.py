@@ -29,7 +29,10 @@ def run_gpu(cfg: Config, dev: dict, mode=kda.KDA_MODE_SEQUENTIAL, decode=False,
     Returns dict(out, o_core, ring, state) as device tensors."""
     T = cfg.T if T is None else T
     sl = slice(t0, t0 + T)
-    acts = {n: dev[n][:, sl].contiguous() for n in ("q", "k", "v", "g", "beta", "z")}
+    # fresh copies: a contiguous row slice at B == 1 would be a view at an offset that
+    # need not meet the entry points' 16-byte alignment
+    acts = {n: dev[n][:, sl].clone(memory_format=torch.contiguous_format)
+            for n in ("q", "k", "v", "g", "beta", "z")}
     ring = dev["ring"].clone() if ring is None else ring
     s_in = dev["state"].clone() if state is None else state
     s_out = s_in if inplace else torch.empty_like(s_in)

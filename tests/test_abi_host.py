@@ -52,7 +52,7 @@ BASE = 1 << 40  # fake, 256-byte aligned, far-apart addresses; never dereference
 
 def fake_args(B=2, T=3, H=2, D=16, K=4, dtype=0, mode=1):
     names = ["q", "k", "v", "g", "beta", "conv_w", "ring", "state_in", "state_out", "z",
-             "norm_w", "out", "o_core", "ws", "ring_snap", "state_snap"]
+             "norm_w", "out", "o_core", "ws", "ring_snap", "state_snap", "gate_a", "gate_bias"]
     a = {n: BASE + i * (1 << 32) for i, n in enumerate(names)}
     a.update(B=B, T=T, H=H, D=D, K=K, dtype=dtype, mode=mode, ws_bytes=1 << 31)
     return a
@@ -183,3 +183,34 @@ def test_rollback_queries():
     assert kda.rollback_workspace_bytes(64, 8, 64, 128, 1) == 0  # short replay: fused arm
     assert kda.rollback_workspace_bytes(1, 40, 2, 16, 0) == kda.workspace_bytes(1, 40, 2, 16, 0, 1)
     assert kda.rollback_workspace_bytes(1, 40, 2, 64, 0) == ctypes.c_size_t(-1).value
+
+
+def call_gated(a, gdn=False, decode=False, form=1, lb=-5.0):
+    L = kda.lib()
+    head = (a["q"], a["k"], a["v"], a["g"], a["beta"], a["gate_a"], a["gate_bias"], lb, form, a["conv_w"],
+            a["ring"], a["state_in"], a["state_out"], a["z"], a["norm_w"], a["out"], a["o_core"], a["B"],
+            a["T"], a["H"], a["D"], a["K"], 0.25, 1e-5, a["dtype"])
+    if decode:
+        return (L.gdn_decode_gated if gdn else L.kda_decode_gated)(*head, None)
+    return (L.gdn_prefill_gated if gdn else L.kda_prefill_gated)(*head, a["mode"], a["ws"], a["ws_bytes"], None)
+
+
+GATED_CASES = [
+    ("form 0 (use the plain entry)", dict(), dict(form=0), 40008),
+    ("form 3", dict(), dict(form=3), 40008),
+    ("null gate_a", dict(gate_a=None), dict(), 40001),
+    ("null gate_bias", dict(gate_bias=None), dict(), 40001),
+    ("misaligned gate_bias", dict(gate_bias=BASE + 17 * (1 << 32) + 4), dict(), 40007),
+    ("out over gate_bias", dict(out=BASE + 17 * (1 << 32)), dict(), 40009),
+    ("state_out over gate_a", dict(state_out=BASE + 16 * (1 << 32)), dict(), 40009),
+]
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="fake pointers only where no GPU is visible")
+@pytest.mark.parametrize("decode", [False, True])
+@pytest.mark.parametrize("gdn", [False, True])
+@pytest.mark.parametrize("what,over,kw,rc", GATED_CASES, ids=[c[0] for c in GATED_CASES])
+def test_gated_contract(what, over, kw, rc, gdn, decode):
+    a = fake_args(T=1 if decode else 3)
+    a.update({k: (0 if v is None else v) for k, v in over.items()})
+    assert call_gated(a, gdn, decode, **kw) == rc

@@ -9,13 +9,14 @@ import pytest
 import torch
 
 import gated_delta_rule_68_amd as kda
-from tests.test_abi_host import CASES, ROLLBACK_CASES, call_decode, call_prefill, call_rollback
+from tests.test_abi_host import (CASES, GATED_CASES, ROLLBACK_CASES, call_decode, call_gated, call_prefill,
+                                 call_rollback)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 SLOT = 1 << 20  # bytes per argument slot (the shapes below need a few KB)
 NAMES = ["q", "k", "v", "g", "beta", "conv_w", "ring", "state_in", "state_out", "z",
-         "norm_w", "out", "o_core", "ws", "ring_snap", "state_snap"]
+         "norm_w", "out", "o_core", "ws", "ring_snap", "state_snap", "gate_a", "gate_bias"]
 OUTPUTS = ("ring", "state_out", "out", "o_core")
 SENTINEL = 0x5A
 
@@ -132,4 +133,14 @@ def test_rollback_rejected_before_copy_or_launch(arena, what, over, kw, rc, gdn)
     a = real_args(arena)
     a.update(rebase(arena, over))
     assert call_rollback(a, gdn, **kw) == rc
+    assert outputs_untouched(arena) is None
+
+
+@pytest.mark.parametrize("decode", [False, True])
+@pytest.mark.parametrize("gdn", [False, True])
+@pytest.mark.parametrize("what,over,kw,rc", GATED_CASES, ids=[c[0] for c in GATED_CASES])
+def test_gated_rejected_before_launch(arena, what, over, kw, rc, gdn, decode):
+    a = real_args(arena, T=1 if decode else 3)
+    a.update(rebase(arena, over))
+    assert call_gated(a, gdn, decode, **kw) == rc
     assert outputs_untouched(arena) is None

@@ -129,7 +129,9 @@ def test_batch_permutation_equivariance():
     inp, dev = inputs_for(cfg)
     a = run_gpu(cfg, dev, mode=SEQ)
     perm = torch.tensor([3, 0, 4, 1, 2], device=DEV)
-    pdev = {n: (t[perm].contiguous() if n not in ("conv_w", "norm_w") else t) for n, t in dev.items()}
+    # only the batch-major tensors are permuted; weights and per-head parameters are shared
+    batch_major = ("q", "k", "v", "g", "beta", "z", "gate_x", "beta_x", "ring", "state")
+    pdev = {n: (t[perm].contiguous() if n in batch_major else t) for n, t in dev.items()}
     b = run_gpu(cfg, pdev, mode=SEQ)
     assert_bitwise({k: v[perm] for k, v in a.items()}, b)
 
