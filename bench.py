@@ -276,20 +276,23 @@ def run_verify_leg(T_stash: int = 8, keep: int = 4, reps: int = 20) -> dict:
     return rec
 
 
-def _timed(fn, reps):
-    """Median HIP-event time (ms) of fn() over reps calls after one untimed call."""
+def _timed_pair(fa, fb, reps):
+    """Median HIP-event times (ms) of fa(i) and fb(i), interleaved call by call (so that
+    clock or cache drift affects both alike), after one untimed call of each."""
     import torch
 
-    fn()
+    fa(0)
+    fb(0)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(reps)]
-    for i, (a, b) in enumerate(ev):
-        a.record()
-        fn(i)
-        b.record()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)] for _ in range(2)]
+    for i in range(reps):
+        for k, f in enumerate((fa, fb)):
+            ev[k][i][0].record()
+            f(i)
+            ev[k][i][1].record()
     torch.cuda.synchronize()
-    return sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+    return tuple(sorted(a.elapsed_time(b) for a, b in e)[reps // 2] for e in ev)
 
 
 def run_gated_leg(reps: int = 50) -> dict:
@@ -316,21 +319,23 @@ def run_gated_leg(reps: int = 50) -> dict:
     del base
     scale = 1.0 / math.sqrt(cfg.D)
 
+    # interleaved below: the gated call takes the even buffer sets, the plain one the
+    # odd ones, so that no call finds its state left in the last-level cache
     def dec_gated(i=0):
-        d = sets[i % NBUF]
+        d = sets[(2 * i) % NBUF]
         kda.kda_decode_gated(d["q"], d["k"], d["v"], d["gate_x"], d["beta_x"], ga, d["dt_bias"],
                              d["conv_w"], d["ring"], d["state"], d["state"], d["z"], d["norm_w"],
                              d["out"], None, gate_form=kda.KDA_GATE_SOFTPLUS, gate_lb=-5.0,
                              scale=scale, rms_eps=RMS_EPS)
 
     def dec_plain(i=0):
-        d = sets[i % NBUF]
+        d = sets[(2 * i + 1) % NBUF]
         kda.kda_decode(d["q"], d["k"], d["v"], d["g"], d["beta"], d["conv_w"], d["ring"],
                        d["state"], d["state"], d["z"], d["norm_w"], d["out"], None,
                        scale=scale, rms_eps=RMS_EPS)
 
     nb = decode_bytes(cfg) + (cfg.H + cfg.qkv) * 4
-    ms_g, ms_p = _timed(dec_gated, reps), _timed(dec_plain, reps)
+    ms_g, ms_p = _timed_pair(dec_gated, dec_plain, reps)
     rec["decode"] = {"workload": f"KDA decode B={cfg.B} H={cfg.H} D={cfg.D} bf16",
                      "gated_ms": ms_g, "plain_ms": ms_p,
                      "gated_tokens_per_s": cfg.B / (ms_g * 1e-3),
@@ -364,7 +369,7 @@ def run_gated_leg(reps: int = 50) -> dict:
                   d["z"], d["norm_w"], d["out"], None, scale=scale, rms_eps=RMS_EPS, mode=mode,
                   workspace=ws)
 
-        ms_g, ms_p = _timed(pre_gated, 5), _timed(pre_plain, 5)
+        ms_g, ms_p = _timed_pair(pre_gated, pre_plain, 7)
         rec[name] = {"workload": f"{'GDN' if cfg.gdn else 'KDA'} chunked prefill B={cfg.B} T={cfg.T} "
                                  f"H={cfg.H} D={cfg.D} bf16 (incl. a ring reset copy)",
                      "gated_ms": ms_g, "plain_ms": ms_p,

@@ -193,7 +193,10 @@ struct ChunkLds {
     } c;
     union {
         struct {
-            __bf16 vbt[NC][LDC];     // (beta v)^T [value][row]
+            union {
+                __bf16 vbt[NC][LDC];    // (beta v)^T [value][row]
+                uint16_t glo[CH][LDH];  // activated KDA gates: low 16 bits (raw store to P1)
+            } vb;
             __bf16 rv[CH][NC + 8];   // raw v rows of the split
         } pre;
         __bf16 sb[NC][LDH];  // S^T in bf16 [value][key]
@@ -278,30 +281,126 @@ __device__ __forceinline__ void load_raw(ChunkRaw<GDN, NC>& cr, const MixerArgs&
 // thread stores every item it loaded (threads with the same clamped item store the
 // same value): a store under a branch leaves its load possibly in flight on the
 // other path, and the compiler then waits for all memory traffic at the loop head.
-template <bool GDN, int NC, typename Lds>
+// Gate-activation constants of a thread. GDN: the head factor and bias of its head,
+// applied at the raw store with the launch's form. KDA with activated gates: the
+// folded constants (gate_log2_consts) of the 8 channels the thread stores.
+struct ChunkGate {
+    float m, gb;    // GDN
+    float k1, lb2;  // KDA
+    float k0[8];
+};
+
+// KDA gates activated once per element as the raw rows are stored, in log2 units and
+// fp32, kept as their high (rg) and low (glo) 16 bits; rows at or past n are 0 (masked
+// on the packed words, so that no branch is formed around the activation).
+template <int FORM, bool GDN, int NC, typename Lds>
+__device__ __forceinline__ void store_gates(Lds& sm, const ChunkRaw<GDN, NC>& raw, int n, int tid,
+                                            const ChunkGate& cg) {
+    using CR = ChunkRaw<GDN, NC>;
+#pragma unroll
+    for (int it = 0; it < CR::NI; ++it) {
+        const int idx = tid + NTHR * it, r = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8;
+        const uint32_t keep = r < n ? 0xffffffffu : 0u;
+        uint4 hi, lo;
+        uint32_t* h = &hi.x;
+        uint32_t* l = &lo.x;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t u0 = __float_as_uint(gate_act_log2<FORM>(cg.lb2, cg.m, cg.k1, cg.k0[2 * p],
+                                                                    (float)raw.g[it][2 * p]));
+            const uint32_t u1 = __float_as_uint(gate_act_log2<FORM>(cg.lb2, cg.m, cg.k1, cg.k0[2 * p + 1],
+                                                                    (float)raw.g[it][2 * p + 1]));
+            h[p] = (u0 >> 16) | (u1 & 0xffff0000u);
+            l[p] = (u0 & 0xffffu) | (u1 << 16);
+        }
+        if (n < CH) {  // uniform: only the last chunk has rows to clear
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                h[p] &= keep;
+                l[p] &= keep;
+            }
+        }
+        *reinterpret_cast<uint4*>(&sm.c.raw.rg[r][c8]) = hi;
+        *reinterpret_cast<uint4*>(&sm.e.pre.vb.glo[r][c8]) = lo;
+    }
+}
+
+template <bool GDN, int NC, bool ACT, typename Lds>
 __device__ __forceinline__ void store_raw(Lds& sm, const ChunkRaw<GDN, NC>& raw, int n, int tid,
-                                          const MixerArgs& a, float gm_h, float gb) {
+                                          const MixerArgs& a, const ChunkGate& cg) {
     using CR = ChunkRaw<GDN, NC>;
 #pragma unroll
     for (int it = 0; it < CR::NI; ++it) {
         const int idx = tid + NTHR * it, r = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8;
         st8(&sm.c.raw.rq[r][c8], raw.q[it]);
         st8(&sm.c.raw.rk[r][c8], raw.k[it]);
-        if constexpr (!GDN) st8(&sm.c.raw.rg[r][c8], r < n ? raw.g[it] : zero8());
+        if constexpr (!GDN && !ACT) st8(&sm.c.raw.rg[r][c8], r < n ? raw.g[it] : zero8());
+    }
+    if constexpr (!GDN && ACT) {
+        if (a.gate_form == GATE_SIGMOID)
+            store_gates<GATE_SIGMOID>(sm, raw, n, tid, cg);
+        else
+            store_gates<GATE_SOFTPLUS>(sm, raw, n, tid, cg);
     }
 #pragma unroll
     for (int it = 0; it < CR::NV; ++it) {
         const int idx = min(tid + NTHR * it, CR::VITEMS - 1), r = idx / (NC / 8), c8 = (idx % (NC / 8)) * 8;
         st8(&sm.e.pre.rv[r][c8], raw.v[it]);
     }
-    // beta and (GDN) the scalar gates are activated here in fp32 (KDA gates in P1, from
-    // their exact bf16 pre-activations, so no activated gate is rounded to bf16)
+    // beta and (GDN) the scalar gates are activated here in fp32
     const int rr = tid & (CH - 1);
-    sm.beta[rr] = rr < n ? beta_in(a, raw.beta) : 0.0f;
+    sm.beta[rr] = rr < n ? (GDN ? beta_in(a, raw.beta) : (ACT ? sigmoid_f(raw.beta) : raw.beta)) : 0.0f;
     if constexpr (GDN)
-        sm.c.raw.gs[rr] = rr < n ? (a.gate_form != GATE_GIVEN ? gate_act_core(a.gate_form, a.gate_lb, gm_h, gb, raw.gs)
+        sm.c.raw.gs[rr] = rr < n ? (a.gate_form != GATE_GIVEN ? gate_act_core(a.gate_form, a.gate_lb, cg.m, cg.gb, raw.gs)
                                                                : raw.gs)
                                  : 0.0f;
+}
+
+// Gate prefix of one 16-row block over two channels (KDA), in log2 units: gm[r][e] is
+// the gate sum of rows 1..r, g0 the gate of row 0, tot the block's sum. rg points at
+// row 0, channel pair e = 0, 1 of the raw gate rows (pitch LDH).
+__device__ __forceinline__ void gate_prefix_given(const __bf16* rg, float (&gm)[16][2], float (&g0)[2],
+                                                  float (&tot)[2]) {
+    const bf16x2 gf = ld2(rg);
+    float acc[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int r = 1; r < 16; ++r) {
+        const bf16x2 gv = ld2(rg + r * LDH);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            acc[e] = fmaf((float)gv[e], LOG2E, acc[e]);
+            gm[r][e] = acc[e];
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        g0[e] = (float)gf[e] * LOG2E;
+        tot[e] = g0[e] + acc[e];
+    }
+}
+// The same from gates already activated and in log2 units, stored as the high (rg)
+// and low (glo, same pitch) 16 bits of their fp32 values: exact, no bf16 rounding.
+__device__ __forceinline__ void gate_prefix_split(const __bf16* rg, const uint16_t* glo, float (&gm)[16][2],
+                                                  float (&g0)[2], float (&tot)[2]) {
+    float acc[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const uint32_t hi = *reinterpret_cast<const uint32_t*>(rg + r * LDH);
+        const uint32_t lo = *reinterpret_cast<const uint32_t*>(glo + r * LDH);
+        const float g[2] = {__uint_as_float((hi << 16) | (lo & 0xffffu)),
+                            __uint_as_float((hi & 0xffff0000u) | (lo >> 16))};
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            if (r == 0) {
+                g0[e] = g[e];
+            } else {
+                acc[e] += g[e];
+                gm[r][e] = acc[e];
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) tot[e] = g0[e] + acc[e];
 }
 
 // N consecutive bf16 channels (N = 1 or 2) as floats.
@@ -391,8 +490,11 @@ __device__ __forceinline__ void merge_column(M& m, int lane) {
     }
 }
 
-template <bool BF, bool GDN, int NC, int KT>
+// ACT (KDA only): the gates arrive as pre-activations and are activated in P1; the
+// given-gate kernel carries none of that code.
+template <bool BF, bool GDN, int NC, int KT, bool ACT>
 __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) {
+    static_assert(!(GDN && ACT), "GDN gates are activated where they are stored");
     constexpr int NCOL = DK / NC;
     constexpr int NJB = NC / 16;  // value-column 16-blocks of this split
     constexpr int HLD = 2 * DK + NC;
@@ -456,16 +558,31 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
     const int vt = tid - NTHR / 2;  // >= 0 on wavefronts 4..7
     const int cv = (vt % (NC / NVCH)) * NVCH;
 
-    // Gate activation parameters of this head and the thread's two P1 channels (unused
-    // for given gates), read once: a global load inside the chunk loop would be waited
-    // for together with the prefetch.
-    const float gm_h = gate_head_factor(a, h);
-    const float gb0 = a.gate_bias[GDN ? h : head_off + 2 * lane];
-    const float gb1 = a.gate_bias[GDN ? h : head_off + 2 * lane + 1];
+    // Gate-activation constants (unused for given gates), read once: a global load
+    // inside the chunk loop would be waited for together with the prefetch.
+    ChunkGate cg{};
+    if constexpr (GDN) {
+        cg.m = gate_head_factor(a, h);
+        cg.gb = a.gate_bias[h];
+    }
+    if constexpr (ACT) {
+        const float* bp = a.gate_bias + head_off + (tid % (DK / 8)) * 8;  // the store channels
+        const f32x4v b0 = ld4f(bp), b1 = ld4f(bp + 4);
+        const float bias[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+        cg.m = gate_head_factor(a, h);
+        cg.lb2 = a.gate_lb * LOG2E;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if (a.gate_form == GATE_SIGMOID)
+                gate_log2_consts<GATE_SIGMOID>(cg.m, bias[e], &cg.k1, &cg.k0[e]);
+            else
+                gate_log2_consts<GATE_SOFTPLUS>(cg.m, bias[e], &cg.k1, &cg.k0[e]);
+        }
+    }
 
     CR raw;
     load_raw<BF, GDN, NC>(raw, a, b, h, 0, jv0, tid);
-    store_raw<GDN, NC>(sm, raw, min(CH, T), tid, a, gm_h, gb0);
+    store_raw<GDN, NC, ACT>(sm, raw, min(CH, T), tid, a, cg);
     __syncthreads();
 
     for (int c0 = 0; c0 < T; c0 += CH) {
@@ -505,30 +622,11 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
                 g0[0] = sm.c.raw.gs[rb] * LOG2E;
                 tot[0] = g0[0] + acc;
             } else {
-                // the log gate of row rb + r, channel c2 + e: read as given, or activated
-                // here from its pre-activation (rows past n stay 0)
-                const bool act = a.gate_form != GATE_GIVEN;
-                auto gate_of = [&](bf16x2 x, int r, int e) {
-                    const float gb = e ? gb1 : gb0;
-                    return act ? (rb + r < n ? gate_act_core(a.gate_form, a.gate_lb, gm_h, gb, (float)x[e]) : 0.0f)
-                               : (float)x[e];
-                };
-                const bf16x2 gf = ld2(&sm.c.raw.rg[rb][c2]);
-                float acc[2] = {0.0f, 0.0f};
-#pragma unroll
-                for (int r = 1; r < 16; ++r) {
-                    const bf16x2 gv = ld2(&sm.c.raw.rg[rb + r][c2]);
-#pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        acc[e] = fmaf(gate_of(gv, r, e), LOG2E, acc[e]);
-                        gm[r][e] = acc[e];
-                    }
-                }
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    g0[e] = gate_of(gf, 0, e) * LOG2E;
-                    tot[e] = g0[e] + acc[e];
-                }
+                const __bf16* rg = &sm.c.raw.rg[rb][c2];
+                if constexpr (!ACT)
+                    gate_prefix_given(rg, gm, g0, tot);
+                else
+                    gate_prefix_split(rg, &sm.e.pre.vb.glo[rb][c2], gm, g0, tot);
             }
             if (kplane) {
                 if constexpr (GDN) {
@@ -780,8 +878,8 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
                     }
 #pragma unroll
                     for (int e = 0; e < NVCH; ++e) {
-                        st8(&sm.e.pre.vbt[cv + e][rbv], o[e][0]);
-                        st8(&sm.e.pre.vbt[cv + e][rbv + 8], o[e][1]);
+                        st8(&sm.e.pre.vb.vbt[cv + e][rbv], o[e][0]);
+                        st8(&sm.e.pre.vb.vbt[cv + e][rbv + 8], o[e][1]);
                     }
                 }
             }
@@ -836,7 +934,7 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
 #pragma unroll
                 for (int t = 0; t < NJB2; ++t) {
                     const int jb = hv * NJB2 + t;
-                    accU[t] = mfma_bf16(at, ld8(&sm.e.pre.vbt[16 * jb + l16][32 * kk + 8 * q4]), accU[t]);
+                    accU[t] = mfma_bf16(at, ld8(&sm.e.pre.vb.vbt[16 * jb + l16][32 * kk + 8 * q4]), accU[t]);
                 }
             }
         }
@@ -1000,7 +1098,7 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
             }
         }
         lds_barrier();
-        store_raw<GDN, NC>(sm, raw, max(min(CH, T - c0 - CH), 0), tid, a, gm_h, gb0);
+        store_raw<GDN, NC, ACT>(sm, raw, max(min(CH, T - c0 - CH), 0), tid, a, cg);
         lds_barrier();
     }
 
@@ -1055,10 +1153,15 @@ hipError_t chunk_launch_nc(const MixerArgs& a, float* o_buf) {
     static_assert(sizeof(ChunkLds<GDN, NC, KMAX>) <= 160 * 1024, "LDS budget of one workgroup");
     const int nbh = a.B * a.H;
     const int grid = ((nbh + 7) / 8) * 8 * NCOL;
-    if (a.K == 4)
-        hipLaunchKernelGGL((chunk_kernel<BF, GDN, NC, 4>), dim3(grid), dim3(NTHR), 0, a.stream, a, o_buf);
-    else
-        hipLaunchKernelGGL((chunk_kernel<BF, GDN, NC, KMAX>), dim3(grid), dim3(NTHR), 0, a.stream, a, o_buf);
+    const bool act = !GDN && a.gate_form != GATE_GIVEN;
+    const dim3 g(grid), blk(NTHR);
+    if (a.K == 4) {
+        if (act) hipLaunchKernelGGL((chunk_kernel<BF, GDN, NC, 4, !GDN>), g, blk, 0, a.stream, a, o_buf);
+        else hipLaunchKernelGGL((chunk_kernel<BF, GDN, NC, 4, false>), g, blk, 0, a.stream, a, o_buf);
+    } else {
+        if (act) hipLaunchKernelGGL((chunk_kernel<BF, GDN, NC, KMAX, !GDN>), g, blk, 0, a.stream, a, o_buf);
+        else hipLaunchKernelGGL((chunk_kernel<BF, GDN, NC, KMAX, false>), g, blk, 0, a.stream, a, o_buf);
+    }
     return hipGetLastError();
 }
 

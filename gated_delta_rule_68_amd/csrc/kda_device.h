@@ -73,19 +73,50 @@ __device__ __forceinline__ float gate_act_core(int form, float lb, float m, floa
     const float t = x + bias;
     return form == GATE_SIGMOID ? lb * sigmoid_f(m * t) : fmaxf(lb, m * softplus_f(t));
 }
+// The activated log gate times log2(e), for a form fixed at compile time, from the
+// pre-activation x with per-column constants folded in (gate_log2_consts): sigmoid,
+// lb2 / (1 + 2^{k1 x + k0}) with k1 = -m log2 e, k0 = k1 * bias; softplus,
+// max(lb2, m * log2(1 + 2^u)) with u = x log2 e + k0, k0 = bias * log2 e, and u itself
+// from x + bias = 20 on (as softplus_f). lb2 = lb * log2 e.
+template <int FORM>
+__device__ __forceinline__ float gate_act_log2(float lb2, float m, float k1, float k0, float x) {
+    static_assert(FORM == GATE_SIGMOID || FORM == GATE_SOFTPLUS, "an activated form");
+    const float u = fmaf(x, k1, k0);
+    if constexpr (FORM == GATE_SIGMOID) return lb2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(u));
+    else return fmaxf(lb2, m * (u > 20.0f * LOG2E ? u : __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(u))));
+}
+template <int FORM>
+__device__ __forceinline__ void gate_log2_consts(float m, float bias, float* k1, float* k0) {
+    *k1 = FORM == GATE_SIGMOID ? -m * LOG2E : LOG2E;
+    *k0 = *k1 * bias;
+}
 // exp(A_log[h]) for the sigmoid form, a[h] for the softplus form.
 __device__ __forceinline__ float gate_head_factor(const MixerArgs& a, int h) {
     return a.gate_form == GATE_SIGMOID ? exp_f(a.gate_a[h]) : a.gate_a[h];
 }
-__device__ __forceinline__ float gate_act(const MixerArgs& a, float x, int h, size_t c) {
-    return gate_act_core(a.gate_form, a.gate_lb, gate_head_factor(a, h), a.gate_bias[c], x);
-}
-// The log gate / beta a kernel uses for what it read from g / beta.
-__device__ __forceinline__ float gate_in(const MixerArgs& a, float x, int h, size_t c) {
-    return a.gate_form != GATE_GIVEN ? gate_act(a, x, h, c) : x;
-}
+// The beta a kernel uses for what it read from beta.
 __device__ __forceinline__ float beta_in(const MixerArgs& a, float x) {
     return a.gate_form != GATE_GIVEN ? sigmoid_f(x) : x;
+}
+// Raw activation parameters of one gate column (head h, bias column c), for kernels
+// whose threads keep one column: read before any large load is issued, so that using
+// them waits for nothing else (vector-memory counters complete in order).
+struct GateCol {
+    float a, bias;
+};
+__device__ __forceinline__ GateCol gate_col(const MixerArgs& a, int h, size_t c) {
+    GateCol p{0.0f, 0.0f};
+    if (a.gate_form != GATE_GIVEN) {
+        p.a = a.gate_a[h];
+        p.bias = a.gate_bias[c];
+    }
+    return p;
+}
+// The log gate a kernel uses for what it read from g.
+__device__ __forceinline__ float gate_in(const MixerArgs& a, const GateCol& p, float x) {
+    if (a.gate_form == GATE_GIVEN) return x;
+    const float m = a.gate_form == GATE_SIGMOID ? exp_f(p.a) : p.a;
+    return gate_act_core(a.gate_form, a.gate_lb, m, p.bias, x);
 }
 
 // Butterfly sums. Every lane of the group ends with the same bits (each step adds

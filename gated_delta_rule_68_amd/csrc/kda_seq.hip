@@ -62,6 +62,12 @@ __global__ __launch_bounds__(fused_threads<D>()) void seq_fused_kernel(MixerArgs
     for (int c = 0; c < CPT; ++c)
         load_keys<D>(S[c], a.state_in + ((size_t)bh * D + grp + c * NG) * D, s);
 
+    // The gate column of this thread is fixed (NT is a multiple of D); its activation
+    // parameters arrive with the ring rows, which are waited for right below (read
+    // before the state, their pointers' scalar load would hold the state loads back).
+    static_assert(NT % D == 0, "one gate column per thread");
+    const GateCol gp = gate_col(a, h, GDN ? h : head_off + tid % D);
+
     // Conv windows of this head's 3*D (plane, channel) rows start as the old ring.
     for (int r = tid; r < 3 * D; r += NT) {
         const int plane = r / D, ch = r % D;
@@ -90,11 +96,11 @@ __global__ __launch_bounds__(fused_threads<D>()) void seq_fused_kernel(MixerArgs
             for (int e = 0; e < KMAX - 1; ++e) wins[r][e] = cc.win[e];
         }
         if constexpr (GDN) {
-            if (tid < nt) es[tid][0] = exp_f(gate_in(a, ld_act<BF>(a.g, (row0 + tid) * H + h), h, h));
+            if (tid < nt) es[tid][0] = exp_f(gate_in(a, gp, ld_act<BF>(a.g, (row0 + tid) * H + h)));
         } else {
             for (int idx = tid; idx < nt * D; idx += NT) {
                 const int tt = idx / D, i = idx % D;
-                es[tt][i] = exp_f(gate_in(a, ld_act<BF>(a.g, (row0 + tt) * qkv + head_off + i), h, head_off + i));
+                es[tt][i] = exp_f(gate_in(a, gp, ld_act<BF>(a.g, (row0 + tt) * qkv + head_off + i)));
             }
         }
         if (tid < nt) bs[tid] = beta_in(a, ld_act<BF>(a.beta, (row0 + tid) * H + h));
@@ -160,6 +166,8 @@ __global__ __launch_bounds__(pre_threads<D>()) void pre_kernel(MixerArgs a, floa
     const size_t row0 = (size_t)b * T + t0;      // workspace rows
     const size_t rin0 = (size_t)b * a.tp + t0;   // input rows
 
+    static_assert(NT % D == 0, "one gate column per thread");
+    const GateCol gp = gate_col(a, h, GDN ? h : head_off + tid % D);
     const bool conv_thread = tid < 3 * D;
     const int plane = tid / D, ch = tid % D;
     const size_t cf = (size_t)plane * qkv + head_off + ch;
@@ -188,12 +196,11 @@ __global__ __launch_bounds__(pre_threads<D>()) void pre_kernel(MixerArgs a, floa
         }
     }
     if constexpr (GDN) {
-        if (tid < nt) eg[(row0 + tid) * H + h] = exp_f(gate_in(a, ld_act<BF>(a.g, (rin0 + tid) * H + h), h, h));
+        if (tid < nt) eg[(row0 + tid) * H + h] = exp_f(gate_in(a, gp, ld_act<BF>(a.g, (rin0 + tid) * H + h)));
     } else {
         for (int idx = tid; idx < nt * D; idx += NT) {
             const size_t col = head_off + idx % D;
-            eg[(row0 + idx / D) * qkv + col] =
-                exp_f(gate_in(a, ld_act<BF>(a.g, (rin0 + idx / D) * qkv + col), h, col));
+            eg[(row0 + idx / D) * qkv + col] = exp_f(gate_in(a, gp, ld_act<BF>(a.g, (rin0 + idx / D) * qkv + col)));
         }
     }
     __syncthreads();

@@ -97,6 +97,25 @@ def test_gated_prefill_vs_oracle(form, gdn, mode, T):
 
 @pytest.mark.parametrize("form", FORMS, ids=["sigmoid", "softplus"])
 @pytest.mark.parametrize("gdn", [False, True])
+@pytest.mark.parametrize("B", [2, 4], ids=["two_splits", "full_width"])
+def test_gated_chunked_wide_vs_oracle(form, gdn, B):
+    """H = 64 heads at B = 2 (each head split over two column blocks) and B = 4 (one
+    workgroup per head): the other chunked launch widths, on sampled heads."""
+    cfg = CONFIGS["kda_decode"].with_(B=B, H=64, T=130, gdn=gdn)
+    inp, dev = inputs_for(cfg)
+    ncol = 2 if B == 2 else 1
+    assert kda.ARM_NAMES[kda.prefill_arm(cfg.B, cfg.T, cfg.H, cfg.D, kda.KDA_DTYPE_BF16, CHK, gdn=gdn)] == "chunked"
+    _print("case", cfg, "column splits", ncol)
+    ga, gb, g, beta = gate_params(inp, dev, form)
+    got = run_gated(cfg, dev, ga, gb, form, mode=CHK)
+    torch.cuda.synchronize()
+    heads, batches = [0, 37, 63], [0, B - 1]
+    ref, ch, rows, bsel = oracle_gated(inp, g, beta, heads=heads, batches=batches)
+    compare(cfg, got, ref, ch, rows, bsel, heads, TOL["bf16"])
+
+
+@pytest.mark.parametrize("form", FORMS, ids=["sigmoid", "softplus"])
+@pytest.mark.parametrize("gdn", [False, True])
 def test_gated_fp32_sequential_vs_oracle(form, gdn):
     cfg = CONFIGS["tiny_kda"].with_(gdn=gdn, T=40, random_init=True)
     inp, dev = inputs_for(cfg)
