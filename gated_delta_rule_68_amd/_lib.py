@@ -25,12 +25,14 @@ _ROLLBACK_ARGS = [_vp] * 5 + [_fp] * 5 + [_i] * 7 + [_vp, _sz, _vp]
 _GATE_ARGS = [_fp, _fp, _f, _i]
 _GATED_PREFILL_ARGS = _PREFILL_ARGS[:5] + _GATE_ARGS + _PREFILL_ARGS[5:]
 _GATED_DECODE_ARGS = _DECODE_ARGS[:5] + _GATE_ARGS + _DECODE_ARGS[5:]
+_GATED_ROLLBACK_ARGS = _ROLLBACK_ARGS[:5] + _GATE_ARGS + _ROLLBACK_ARGS[5:]
 KDA_GATE_SIGMOID, KDA_GATE_SOFTPLUS = 1, 2
 EXPORTS = ("kda_prefill", "kda_decode", "gdn_prefill", "gdn_decode",
            "kda_prefill_workspace_bytes", "gdn_prefill_workspace_bytes",
            "kda_prefill_arm", "gdn_prefill_arm", "kda_rollback", "gdn_rollback",
            "kda_rollback_workspace_bytes", "gdn_rollback_workspace_bytes", "kda_prefill_gated",
-           "gdn_prefill_gated", "kda_decode_gated", "gdn_decode_gated", "kda_status_string")
+           "gdn_prefill_gated", "kda_decode_gated", "gdn_decode_gated", "kda_rollback_gated",
+           "gdn_rollback_gated", "kda_status_string")
 
 
 class KdaError(RuntimeError):
@@ -67,6 +69,9 @@ def lib() -> ctypes.CDLL:
             getattr(l, n).restype = _i
         for n in ("kda_rollback", "gdn_rollback"):
             getattr(l, n).argtypes = _ROLLBACK_ARGS
+            getattr(l, n).restype = _i
+        for n in ("kda_rollback_gated", "gdn_rollback_gated"):
+            getattr(l, n).argtypes = _GATED_ROLLBACK_ARGS
             getattr(l, n).restype = _i
         for n in ("kda_rollback_workspace_bytes", "gdn_rollback_workspace_bytes"):
             getattr(l, n).argtypes = [_i] * 5
@@ -176,11 +181,11 @@ def rollback_workspace_bytes(B, keep, H, D, dtype_code, gdn=False) -> int:
 
 
 def _rollback(name, q, k, v, g, beta, conv_w, ring_snap, state_snap, conv_ring, state_out, keep,
-              workspace, stream, check):
+              workspace, stream, check, gate=()):
     B, T, H, D, K = _geometry(q, state_snap, conv_w)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = getattr(lib(), name)(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(conv_w), _ptr(ring_snap),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), *gate, _ptr(conv_w), _ptr(ring_snap),
         _ptr(state_snap), _ptr(conv_ring), _ptr(state_out), B, T, int(keep), H, D, K,
         _dtype_code(q), _ptr(workspace), ws_bytes, _stream_handle(stream))
     if check and rc != 0:
@@ -201,6 +206,23 @@ def gdn_rollback(q, k, v, g, beta, conv_w, ring_snap, state_snap, conv_ring, sta
                  workspace=None, stream=None, check=True):
     return _rollback("gdn_rollback", q, k, v, g, beta, conv_w, ring_snap, state_snap, conv_ring,
                      state_out, keep, workspace, stream, check)
+
+
+def kda_rollback_gated(q, k, v, gate_x, beta_x, gate_a, gate_bias, conv_w, ring_snap, state_snap,
+                       conv_ring, state_out, keep, *, gate_form, gate_lb, workspace=None, stream=None,
+                       check=True):
+    """kda_rollback of a round verified with kda_prefill_gated (include/kda.h)."""
+    return _rollback("kda_rollback_gated", q, k, v, gate_x, beta_x, conv_w, ring_snap, state_snap,
+                     conv_ring, state_out, keep, workspace, stream, check,
+                     (_ptr(gate_a), _ptr(gate_bias), float(gate_lb), int(gate_form)))
+
+
+def gdn_rollback_gated(q, k, v, gate_x, beta_x, gate_a, gate_bias, conv_w, ring_snap, state_snap,
+                       conv_ring, state_out, keep, *, gate_form, gate_lb, workspace=None, stream=None,
+                       check=True):
+    return _rollback("gdn_rollback_gated", q, k, v, gate_x, beta_x, conv_w, ring_snap, state_snap,
+                     conv_ring, state_out, keep, workspace, stream, check,
+                     (_ptr(gate_a), _ptr(gate_bias), float(gate_lb), int(gate_form)))
 
 
 def _gated(name, decode, q, k, v, gate_x, beta_x, gate_a, gate_bias, conv_w, conv_ring, state_in,

@@ -168,17 +168,21 @@ int rollback(bool gdn, const void* q, const void* k, const void* v, const void* 
              const void* beta, const float* conv_w, const float* ring_snap,
              const float* state_snap, float* conv_ring, float* state_out, int B, int T_stash,
              int keep, int H, int D, int K, int dtype, void* workspace, size_t workspace_bytes,
-             void* stream) {
+             void* stream, GateArgs ga = kGiven) {
     if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return KDA_ERR_DTYPE_MODE;
+    if (ga.form != kda::GATE_GIVEN && ga.form != KDA_GATE_SIGMOID && ga.form != KDA_GATE_SOFTPLUS)
+        return KDA_ERR_DTYPE_MODE;
     if (!q || !k || !v || !g || !beta || !conv_w || !ring_snap || !state_snap || !conv_ring ||
         !state_out)
         return KDA_ERR_NULL;
+    if (ga.form != kda::GATE_GIVEN && (!ga.a || !ga.bias)) return KDA_ERR_NULL;
     int rc = check_shape(B, T_stash, H, D, K);
     if (rc) return rc;
     if (keep < 1 || keep > T_stash) return KDA_ERR_SHAPE;
     const bool bf16 = dtype == KDA_DTYPE_BF16;
     const int arm = pick_arm(B, keep, H, D, bf16, KDA_MODE_SEQUENTIAL);
-    const void* ptrs[] = {q, k, v, g, beta, conv_w, ring_snap, state_snap, conv_ring, state_out, workspace};
+    const void* ptrs[] = {q, k, v, g, beta, conv_w, ring_snap, state_snap, conv_ring, state_out, workspace,
+                          ga.a, ga.bias};
     for (const void* p : ptrs)
         if (p && ((uintptr_t)p & 15u)) return KDA_ERR_ALIGN;
     const size_t need_ws = workspace_for(B, keep, H, D, gdn, arm);
@@ -192,7 +196,7 @@ int rollback(bool gdn, const void* q, const void* k, const void* v, const void* 
     auto Rg = [](const void* p, size_t bytes, bool w, int id) {
         return Range{(uintptr_t)p, (uintptr_t)p + bytes, w, id};
     };
-    Range rs[11];
+    Range rs[13];
     int n = 0;
     rs[n++] = Rg(q, act * es, false, 0);
     rs[n++] = Rg(k, act * es, false, 1);
@@ -205,6 +209,10 @@ int rollback(bool gdn, const void* q, const void* k, const void* v, const void* 
     rs[n++] = Rg(conv_ring, ring_bytes, true, 8);
     rs[n++] = Rg(state_out, state_bytes, true, 9);
     if (need_ws > 0) rs[n++] = Rg(workspace, need_ws, true, 10);
+    if (ga.form != kda::GATE_GIVEN) {
+        rs[n++] = Rg(ga.a, (size_t)H * 4, false, 11);
+        rs[n++] = Rg(ga.bias, (gdn ? (size_t)H : qkv) * 4, false, 12);
+    }
     for (int i = 0; i < n; ++i)
         for (int j = i + 1; j < n; ++j) {
             if (!(rs[i].writable || rs[j].writable) || !overlaps(rs[i], rs[j])) continue;
@@ -221,7 +229,11 @@ int rollback(bool gdn, const void* q, const void* k, const void* v, const void* 
     }
     MixerArgs a{q, k, v, g, beta, conv_w, conv_ring, state_snap, state_out, nullptr, nullptr, nullptr,
                 nullptr, B, keep, H, D, K, 1.0f, 0.0f, bf16, gdn, workspace, workspace_bytes,
-                (hipStream_t)stream, T_stash, false, kda::GATE_GIVEN, conv_w, conv_w, 0.0f};
+                (hipStream_t)stream, T_stash, false, ga.form, conv_w, conv_w, ga.lb};
+    if (ga.form != kda::GATE_GIVEN) {
+        a.gate_a = ga.a;
+        a.gate_bias = ga.bias;
+    }
     return run(a, arm);
 }
 
@@ -328,6 +340,21 @@ int gdn_rollback(const void* q, const void* k, const void* v, const void* g, con
     return rollback(true, q, k, v, g, beta, conv_w, ring_snap, state_snap, conv_ring, state_out,
                     B, T_stash, keep, H, D, K, dtype, workspace, workspace_bytes, stream);
 }
+
+#define KDA_GATED_ROLLBACK(NAME, GDN)                                                             \
+    int NAME(const void* q, const void* k, const void* v, const void* gate_x, const void* beta_x,  \
+             const float* gate_a, const float* gate_bias, float gate_lb, int gate_form,            \
+             const float* conv_w, const float* ring_snap, const float* state_snap,                 \
+             float* conv_ring, float* state_out, int B, int T_stash, int keep, int H, int D,       \
+             int K, int dtype, void* workspace, size_t workspace_bytes, void* stream) {            \
+        if (gate_form == 0) return KDA_ERR_DTYPE_MODE; /* 0: use the plain entry */               \
+        return rollback(GDN, q, k, v, gate_x, beta_x, conv_w, ring_snap, state_snap, conv_ring,    \
+                        state_out, B, T_stash, keep, H, D, K, dtype, workspace, workspace_bytes,   \
+                        stream, GateArgs{gate_form, gate_a, gate_bias, gate_lb});                  \
+    }
+KDA_GATED_ROLLBACK(kda_rollback_gated, false)
+KDA_GATED_ROLLBACK(gdn_rollback_gated, true)
+#undef KDA_GATED_ROLLBACK
 
 size_t kda_rollback_workspace_bytes(int B, int keep, int H, int D, int dtype) {
     return ws_query(false, B, keep, H, D, dtype, KDA_MODE_SEQUENTIAL);

@@ -234,6 +234,26 @@ int gdn_rollback(const void* q, const void* k, const void* v, const void* g,
 size_t kda_rollback_workspace_bytes(int B, int keep, int H, int D, int dtype);
 size_t gdn_rollback_workspace_bytes(int B, int keep, int H, int D, int dtype);
 
+/* Rollback of a round verified with kda_prefill_gated / gdn_prefill_gated
+ * (mode = KDA_MODE_SEQUENTIAL): the same replay from the stored gate and beta
+ * pre-activations, activated as the gated entry points activate them, so the result
+ * is bit-identical to `keep` chained kda_decode_gated calls. gate_x, beta_x, gate_a,
+ * gate_bias, gate_lb, gate_form as for kda_prefill_gated (gate_form 0 is
+ * KDA_ERR_DTYPE_MODE, null gate_a / gate_bias KDA_ERR_NULL); everything else as for
+ * kda_rollback, with the same workspace query. */
+int kda_rollback_gated(const void* q, const void* k, const void* v, const void* gate_x,
+                       const void* beta_x, const float* gate_a, const float* gate_bias,
+                       float gate_lb, int gate_form, const float* conv_w,
+                       const float* ring_snap, const float* state_snap, float* conv_ring,
+                       float* state_out, int B, int T_stash, int keep, int H, int D, int K,
+                       int dtype, void* workspace, size_t workspace_bytes, void* stream);
+int gdn_rollback_gated(const void* q, const void* k, const void* v, const void* gate_x,
+                       const void* beta_x, const float* gate_a, const float* gate_bias,
+                       float gate_lb, int gate_form, const float* conv_w,
+                       const float* ring_snap, const float* state_snap, float* conv_ring,
+                       float* state_out, int B, int T_stash, int keep, int H, int D, int K,
+                       int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* kda_status_string(int rc);
 

@@ -214,3 +214,32 @@ def test_gated_contract(what, over, kw, rc, gdn, decode):
     a = fake_args(T=1 if decode else 3)
     a.update({k: (0 if v is None else v) for k, v in over.items()})
     assert call_gated(a, gdn, decode, **kw) == rc
+
+
+def call_rollback_gated(a, gdn=False, T_stash=3, keep=2, form=2, lb=-5.0):
+    L = kda.lib()
+    f = L.gdn_rollback_gated if gdn else L.kda_rollback_gated
+    return f(a["q"], a["k"], a["v"], a["g"], a["beta"], a["gate_a"], a["gate_bias"], lb, form, a["conv_w"],
+             a["ring_snap"], a["state_snap"], a["ring"], a["state_out"], a["B"], T_stash, keep, a["H"], a["D"],
+             a["K"], a["dtype"], a["ws"], a["ws_bytes"], None)
+
+
+GATED_ROLLBACK_CASES = [
+    ("form 0 (use the plain entry)", dict(), dict(form=0), 40008),
+    ("form 3", dict(), dict(form=3), 40008),
+    ("null gate_a", dict(gate_a=None), dict(), 40001),
+    ("null gate_bias", dict(gate_bias=None), dict(), 40001),
+    ("misaligned gate_a", dict(gate_a=BASE + 16 * (1 << 32) + 8), dict(), 40007),
+    ("state_out over gate_bias", dict(state_out=BASE + 17 * (1 << 32)), dict(), 40009),
+    ("ring over gate_a", dict(ring=BASE + 16 * (1 << 32)), dict(), 40009),
+    ("keep past the stash", dict(), dict(keep=4), 40004),
+]
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="fake pointers only where no GPU is visible")
+@pytest.mark.parametrize("gdn", [False, True])
+@pytest.mark.parametrize("what,over,kw,rc", GATED_ROLLBACK_CASES, ids=[c[0] for c in GATED_ROLLBACK_CASES])
+def test_gated_rollback_contract(what, over, kw, rc, gdn):
+    a = fake_args()
+    a.update({k: (0 if v is None else v) for k, v in over.items()})
+    assert call_rollback_gated(a, gdn, **kw) == rc

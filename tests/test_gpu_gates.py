@@ -162,3 +162,52 @@ def test_softplus_form_reproduces_the_given_gates():
         e = oracle.rel_linf(to_f64(got[k]), to_f64(ref[k]))
         _print(k, e)
         assert e <= TOL["bf16"]
+
+
+def _rollback_gated(cfg, dev, ga, gb, form, ring_snap, state_snap, ring, state, keep):
+    code = kda.KDA_DTYPE_BF16 if cfg.dtype == "bf16" else kda.KDA_DTYPE_F32
+    nb = kda.rollback_workspace_bytes(cfg.B, keep, cfg.H, cfg.D, code, gdn=cfg.gdn)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV) if nb else None
+    fn = kda.gdn_rollback_gated if cfg.gdn else kda.kda_rollback_gated
+    fn(dev["q"], dev["k"], dev["v"], dev["gate_x"], dev["beta_x"], ga, gb, dev["conv_w"], ring_snap,
+       state_snap, ring, state, keep, gate_form=form, gate_lb=LB, workspace=ws)
+
+
+@pytest.mark.parametrize("form", FORMS, ids=["sigmoid", "softplus"])
+@pytest.mark.parametrize("gdn", [False, True])
+def test_gated_verify_then_rollback_is_bitwise_the_gated_decode_chain(form, gdn):
+    """A round verified with the gated sequential prefill, rolled back with the gated
+    rollback to keep rows, equals keep chained gated decodes bit for bit."""
+    cfg = CONFIGS["kda_decode"].with_(B=2, H=3, T=8, gdn=gdn)
+    inp, dev = inputs_for(cfg)
+    ga, gb, _, _ = gate_params(inp, dev, form)
+    ring, state = dev["ring"].clone(), dev["state"].clone()
+    steps = []
+    for t in range(cfg.T):
+        run_gated(cfg, dev, ga, gb, form, decode=True, t0=t, T=1, ring=ring, state=state)
+        steps.append({"ring": ring.clone(), "state": state.clone()})
+    verify = run_gated(cfg, dev, ga, gb, form, mode=SEQ)
+    torch.cuda.synchronize()
+    assert_bitwise(verify, steps[-1], keys=("ring", "state"))
+    for keep in (1, 3, cfg.T):
+        ring = torch.full_like(dev["ring"], float("nan"))
+        state = torch.full_like(dev["state"], float("nan"))
+        _rollback_gated(cfg, dev, ga, gb, form, dev["ring"], dev["state"], ring, state, keep)
+        torch.cuda.synchronize()
+        assert_bitwise({"ring": ring, "state": state}, steps[keep - 1], keys=("ring", "state"))
+        _print("keep", keep, "bitwise ok")
+
+
+def test_gated_rollback_split_arm_matches_gated_prefill():
+    """keep > 16 rows with few (b, h) pairs: the split arm (with a workspace) equals a
+    gated sequential prefill over the same first keep rows."""
+    cfg = CONFIGS["kda_decode"].with_(B=1, H=2, T=40, D=16, dtype="fp32")
+    inp, dev = inputs_for(cfg)
+    form, keep = kda.KDA_GATE_SIGMOID, 30
+    ga, gb, _, _ = gate_params(inp, dev, form)
+    assert kda.prefill_arm(cfg.B, keep, cfg.H, cfg.D, kda.KDA_DTYPE_F32, SEQ) == 2
+    ref = run_gated(cfg, dev, ga, gb, form, mode=SEQ, T=keep)
+    ring, state = torch.empty_like(dev["ring"]), torch.empty_like(dev["state"])
+    _rollback_gated(cfg, dev, ga, gb, form, dev["ring"], dev["state"], ring, state, keep)
+    torch.cuda.synchronize()
+    assert_bitwise({"ring": ring, "state": state}, ref, keys=("ring", "state"))
