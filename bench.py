@@ -380,6 +380,72 @@ def run_gated_leg(reps: int = 50) -> dict:
     return rec
 
 
+def run_gqa_leg(reps: int = 50) -> dict:
+    """GDN with grouped heads: 32 value heads over 16 query / key heads, D=128, bf16.
+    The batched decode step (B=64, state in place, buffer sets cycled) and the chunked
+    prefill of the GDN workload (B=4, T=8192): HIP-event time of each call (the decode
+    includes the q / k ring roll launch that shared key heads need) and algorithmic
+    HBM bytes (q / k rows are Hk*D wide)."""
+    import torch
+
+    import gated_delta_rule_68_amd as kda
+    from gated_delta_rule_68_amd.synth import CONFIGS
+    from gated_delta_rule_68_amd.torch_io import alloc_outputs, tiled_device_inputs
+
+    rec = {}
+    cfg = CONFIGS["kda_decode"].with_(gdn=True, H=32, Hk=16)
+    base = tiled_device_inputs(cfg)
+    sets = []
+    for _ in range(NBUF):
+        d = {n: t.clone() for n, t in base.items()}
+        d.update(alloc_outputs(cfg, 1, "cuda", o_core=False))
+        sets.append(d)
+    del base
+    scale = 1.0 / math.sqrt(cfg.D)
+
+    def dec(i=0):
+        d = sets[i % NBUF]
+        kda.gdn_decode_gqa(d["q"], d["k"], d["v"], d["g"], d["beta"], d["conv_w"], d["ring"], d["state"],
+                           d["state"], d["z"], d["norm_w"], d["out"], None, scale=scale, rms_eps=RMS_EPS)
+
+    B, H, D, K, kw, vw = cfg.B, cfg.H, cfg.D, cfg.K, cfg.kw, cfg.qkv
+    nb = (2 * B * H * D * D * 4 + 2 * B * cfg.conv_rows * (K - 1) * 4
+          + (2 * B * kw + 3 * B * vw + 2 * B * H) * 2 + cfg.conv_rows * K * 4 + D * 4)
+    ms, _ = _timed_pair(dec, lambda i=0: None, reps)
+    rec["decode"] = {"workload": f"GDN decode B={B} H={H} Hk={cfg.hk} D={D} bf16", "ms": ms,
+                     "tokens_per_s": B / (ms * 1e-3), "hbm_gbs": nb / (ms * 1e-3) / 1e9,
+                     "hbm_frac": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": nb}
+    del sets
+    torch.cuda.empty_cache()
+
+    cfg = CONFIGS["gdn_prefill"].with_(Hk=16)
+    d = dict(tiled_device_inputs(cfg))
+    d.update(alloc_outputs(cfg, cfg.T, "cuda", o_core=False))
+    mode = kda.KDA_MODE_CHUNKED
+    ws = torch.empty(max(kda.gqa_workspace_bytes(cfg.B, cfg.T, cfg.H, cfg.hk, cfg.D, kda.KDA_DTYPE_BF16, mode),
+                         1), dtype=torch.uint8, device="cuda")
+    ring0, s_out = d["ring"].clone(), torch.empty_like(d["state"])
+
+    def pre(i=0):
+        d["ring"].copy_(ring0)
+        kda.gdn_prefill_gqa(d["q"], d["k"], d["v"], d["g"], d["beta"], d["conv_w"], d["ring"], d["state"], s_out,
+                            d["z"], d["norm_w"], d["out"], None, scale=scale, rms_eps=RMS_EPS, mode=mode,
+                            workspace=ws)
+
+    ms, _ = _timed_pair(pre, lambda i=0: None, 5)
+    B, T, H, kw, vw = cfg.B, cfg.T, cfg.H, cfg.kw, cfg.qkv
+    nb = ((2 * kw + 3 * vw + 2 * H) * B * T * 2 + 2 * B * H * D * D * 4 + 2 * B * cfg.conv_rows * (K - 1) * 4
+          + cfg.conv_rows * K * 4 + D * 4)
+    tf = chunk_flops(cfg) / (ms * 1e-3) / 1e12
+    rec["prefill"] = {"workload": f"GDN chunked prefill B={B} T={T} H={H} Hk={cfg.hk} D={D} bf16 "
+                                  "(incl. a ring reset copy)", "ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
+                      "hbm_gbs": nb / (ms * 1e-3) / 1e9, "mfma_tflops": tf, "mfma_frac": tf / BF16_PEAK_TFLOPS}
+    del d, ws
+    torch.cuda.empty_cache()
+    log(f"gqa: {rec}")
+    return rec
+
+
 def run_prefill_legs() -> dict:
     """Each prefill workload on the chunked and the sequential arm: time of the whole
     arm (every kernel it launches), tokens/s, algorithmic HBM GB/s and, for the
@@ -425,6 +491,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-verify", action="store_true")
     ap.add_argument("--no-gated", action="store_true")
+    ap.add_argument("--no-gqa", action="store_true")
     ap.add_argument("--copy-only", action="store_true",
                     help="only run the 1 GiB device copy (counter calibration)")
     ap.add_argument("--prefill-only", metavar="WORKLOAD",
@@ -495,6 +562,8 @@ def main():
         line["verify_rollback"] = run_verify_leg()
     if not args.no_gated:
         line["gated"] = run_gated_leg()
+    if not args.no_gqa:
+        line["gqa"] = run_gqa_leg()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, inp)
     print(json.dumps(line), flush=True)

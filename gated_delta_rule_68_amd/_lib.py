@@ -26,13 +26,19 @@ _GATE_ARGS = [_fp, _fp, _f, _i]
 _GATED_PREFILL_ARGS = _PREFILL_ARGS[:5] + _GATE_ARGS + _PREFILL_ARGS[5:]
 _GATED_DECODE_ARGS = _DECODE_ARGS[:5] + _GATE_ARGS + _DECODE_ARGS[5:]
 _GATED_ROLLBACK_ARGS = _ROLLBACK_ARGS[:5] + _GATE_ARGS + _ROLLBACK_ARGS[5:]
+# grouped heads: Hk follows H
+_GQA_PREFILL_ARGS = _GATED_PREFILL_ARGS[:20] + [_i] + _GATED_PREFILL_ARGS[20:]
+_GQA_DECODE_ARGS = _GATED_DECODE_ARGS[:20] + [_i] + _GATED_DECODE_ARGS[20:]
+_GQA_ROLLBACK_ARGS = _GATED_ROLLBACK_ARGS[:18] + [_i] + _GATED_ROLLBACK_ARGS[18:]
+KDA_GATE_GIVEN = 0
 KDA_GATE_SIGMOID, KDA_GATE_SOFTPLUS = 1, 2
 EXPORTS = ("kda_prefill", "kda_decode", "gdn_prefill", "gdn_decode",
            "kda_prefill_workspace_bytes", "gdn_prefill_workspace_bytes",
            "kda_prefill_arm", "gdn_prefill_arm", "kda_rollback", "gdn_rollback",
            "kda_rollback_workspace_bytes", "gdn_rollback_workspace_bytes", "kda_prefill_gated",
            "gdn_prefill_gated", "kda_decode_gated", "gdn_decode_gated", "kda_rollback_gated",
-           "gdn_rollback_gated", "kda_status_string")
+           "gdn_rollback_gated", "gdn_prefill_gqa", "gdn_decode_gqa", "gdn_rollback_gqa",
+           "gdn_gqa_workspace_bytes", "kda_status_string")
 
 
 class KdaError(RuntimeError):
@@ -73,6 +79,10 @@ def lib() -> ctypes.CDLL:
         for n in ("kda_rollback_gated", "gdn_rollback_gated"):
             getattr(l, n).argtypes = _GATED_ROLLBACK_ARGS
             getattr(l, n).restype = _i
+        l.gdn_prefill_gqa.argtypes, l.gdn_prefill_gqa.restype = _GQA_PREFILL_ARGS, _i
+        l.gdn_decode_gqa.argtypes, l.gdn_decode_gqa.restype = _GQA_DECODE_ARGS, _i
+        l.gdn_rollback_gqa.argtypes, l.gdn_rollback_gqa.restype = _GQA_ROLLBACK_ARGS, _i
+        l.gdn_gqa_workspace_bytes.argtypes, l.gdn_gqa_workspace_bytes.restype = [_i] * 7, _sz
         for n in ("kda_rollback_workspace_bytes", "gdn_rollback_workspace_bytes"):
             getattr(l, n).argtypes = [_i] * 5
             getattr(l, n).restype = _sz
@@ -274,3 +284,62 @@ def gdn_decode_gated(q, k, v, gate_x, beta_x, gate_a, gate_bias, conv_w, conv_ri
     return _gated("gdn_decode_gated", True, q, k, v, gate_x, beta_x, gate_a, gate_bias, conv_w,
                   conv_ring, state_in, state_out, z, norm_w, out, o_core, gate_form, gate_lb, scale,
                   rms_eps, None, None, stream, check)
+
+
+# ---------------------------------------------------------------- grouped heads (GDN)
+def gqa_workspace_bytes(B, T, H, Hk, D, dtype_code, mode=KDA_MODE_AUTO) -> int:
+    return int(lib().gdn_gqa_workspace_bytes(B, T, H, Hk, D, dtype_code, mode))
+
+
+def _gqa_head(q, k, v, g, beta, gate_a, gate_bias, gate_lb, gate_form, conv_w):
+    return (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(gate_a), _ptr(gate_bias), float(gate_lb),
+            int(gate_form), _ptr(conv_w))
+
+
+def _gqa_dims(q, v, state, conv_w):
+    """(B, T, H, Hk, D, K): H value heads from the state, Hk key heads from q's width."""
+    B, T, H, D, K = _geometry(v, state, conv_w)
+    return B, T, H, q.shape[2] // D, D, K
+
+
+def gdn_prefill_gqa(q, k, v, g, beta, conv_w, conv_ring, state_in, state_out, z, norm_w, out, o_core=None,
+                    *, scale, rms_eps, mode=KDA_MODE_AUTO, workspace=None, gate_a=None, gate_bias=None,
+                    gate_form=KDA_GATE_GIVEN, gate_lb=0.0, stream=None, check=True):
+    """gdn_prefill with Hk = q.shape[2] // D query / key heads (include/kda.h)."""
+    B, T, H, Hk, D, K = _gqa_dims(q, v, state_in, conv_w)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().gdn_prefill_gqa(
+        *_gqa_head(q, k, v, g, beta, gate_a, gate_bias, gate_lb, gate_form, conv_w), _ptr(conv_ring),
+        _ptr(state_in), _ptr(state_out), _ptr(z), _ptr(norm_w), _ptr(out), _ptr(o_core), B, T, H, Hk, D, K,
+        float(scale), float(rms_eps), _dtype_code(v), int(mode), _ptr(workspace), ws_bytes,
+        _stream_handle(stream))
+    if check and rc != 0:
+        raise KdaError(rc, "gdn_prefill_gqa")
+    return rc
+
+
+def gdn_decode_gqa(q, k, v, g, beta, conv_w, conv_ring, state_in, state_out, z, norm_w, out, o_core=None,
+                   *, scale, rms_eps, gate_a=None, gate_bias=None, gate_form=KDA_GATE_GIVEN, gate_lb=0.0,
+                   stream=None, check=True):
+    B, T, H, Hk, D, K = _gqa_dims(q, v, state_in, conv_w)
+    rc = lib().gdn_decode_gqa(
+        *_gqa_head(q, k, v, g, beta, gate_a, gate_bias, gate_lb, gate_form, conv_w), _ptr(conv_ring),
+        _ptr(state_in), _ptr(state_out), _ptr(z), _ptr(norm_w), _ptr(out), _ptr(o_core), B, T, H, Hk, D, K,
+        float(scale), float(rms_eps), _dtype_code(v), _stream_handle(stream))
+    if check and rc != 0:
+        raise KdaError(rc, "gdn_decode_gqa")
+    return rc
+
+
+def gdn_rollback_gqa(q, k, v, g, beta, conv_w, ring_snap, state_snap, conv_ring, state_out, keep, *,
+                     workspace=None, gate_a=None, gate_bias=None, gate_form=KDA_GATE_GIVEN, gate_lb=0.0,
+                     stream=None, check=True):
+    B, T, H, Hk, D, K = _gqa_dims(q, v, state_snap, conv_w)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().gdn_rollback_gqa(
+        *_gqa_head(q, k, v, g, beta, gate_a, gate_bias, gate_lb, gate_form, conv_w), _ptr(ring_snap),
+        _ptr(state_snap), _ptr(conv_ring), _ptr(state_out), B, T, int(keep), H, Hk, D, K, _dtype_code(v),
+        _ptr(workspace), ws_bytes, _stream_handle(stream))
+    if check and rc != 0:
+        raise KdaError(rc, "gdn_rollback_gqa")
+    return rc

@@ -53,9 +53,12 @@ int pick_arm(int B, int T, int H, int D, bool bf16, int mode) {
     return kda::ARM_SEQ_SPLIT;
 }
 
-size_t workspace_for(int B, int T, int H, int D, bool gdn, int arm) {
+// Query / key heads: a divisor of the value heads H (grouped heads, GDN only).
+int check_heads(int H, int Hk) { return Hk >= 1 && Hk <= H && H % Hk == 0 ? KDA_OK : KDA_ERR_SHAPE; }
+
+size_t workspace_for(int B, int T, int H, int Hk, int D, bool gdn, int arm) {
     switch (arm) {
-        case kda::ARM_SEQ_SPLIT: return kda::split_workspace(B, T, H, D, gdn).total;
+        case kda::ARM_SEQ_SPLIT: return kda::split_workspace(B, T, H, Hk, D, gdn).total;
         case kda::ARM_CHUNKED: return kda::chunked_workspace_bytes(B, T, H, D, gdn);
         default: return 0;
     }
@@ -80,9 +83,11 @@ int validate(const MixerArgs& a, bool decode, int mode, int* arm_out) {
     const size_t es = a.bf16 ? 2 : 4;
     const size_t qkv = (size_t)a.H * a.D;
     const size_t act = (size_t)a.B * a.T * qkv;
+    const size_t kact = (size_t)a.B * a.T * a.Hk * a.D;  // q, k
+    const size_t rrows = kda::ring_rows(a);
     const size_t gate_n = a.gdn ? (size_t)a.B * a.T * a.H : act;
     const size_t state_n = (size_t)a.B * a.H * a.D * a.D;
-    const size_t need_ws = workspace_for(a.B, a.T, a.H, a.D, a.gdn, arm);
+    const size_t need_ws = workspace_for(a.B, a.T, a.H, a.Hk, a.D, a.gdn, arm);
     if (need_ws > 0 && (!a.ws || a.ws_bytes < need_ws)) return KDA_ERR_WORKSPACE;
 
     auto R = [](const void* p, size_t bytes, bool w, int id) {
@@ -90,13 +95,13 @@ int validate(const MixerArgs& a, bool decode, int mode, int* arm_out) {
     };
     Range rs[16];
     int n = 0;
-    rs[n++] = R(a.q, act * es, false, 0);
-    rs[n++] = R(a.k, act * es, false, 1);
+    rs[n++] = R(a.q, kact * es, false, 0);
+    rs[n++] = R(a.k, kact * es, false, 1);
     rs[n++] = R(a.v, act * es, false, 2);
     rs[n++] = R(a.g, gate_n * es, false, 3);
     rs[n++] = R(a.beta, (size_t)a.B * a.T * a.H * es, false, 4);
-    rs[n++] = R(a.conv_w, 3 * qkv * a.K * 4, false, 5);
-    rs[n++] = R(a.ring, (size_t)a.B * 3 * qkv * (a.K - 1) * 4, true, 6);
+    rs[n++] = R(a.conv_w, rrows * a.K * 4, false, 5);
+    rs[n++] = R(a.ring, (size_t)a.B * rrows * (a.K - 1) * 4, true, 6);
     rs[n++] = R(a.state_in, state_n * 4, false, 7);
     rs[n++] = R(a.state_out, state_n * 4, true, 8);
     rs[n++] = R(a.z, act * es, false, 9);
@@ -141,14 +146,16 @@ int entry(bool gdn, bool decode, const void* q, const void* k, const void* v, co
           const void* beta, const float* conv_w, float* conv_ring, const float* state_in,
           float* state_out, const void* z, const float* norm_w, void* out, float* o_core,
           int B, int T, int H, int D, int K, float scale, float rms_eps, int dtype, int mode,
-          void* workspace, size_t workspace_bytes, void* stream, GateArgs ga = kGiven) {
+          void* workspace, size_t workspace_bytes, void* stream, GateArgs ga = kGiven, int Hk = 0) {
     if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return KDA_ERR_DTYPE_MODE;
     if (ga.form != kda::GATE_GIVEN && ga.form != KDA_GATE_SIGMOID && ga.form != KDA_GATE_SOFTPLUS)
         return KDA_ERR_DTYPE_MODE;
+    if (Hk == 0) Hk = H;
+    if (check_heads(H, Hk) || (!gdn && Hk != H)) return KDA_ERR_SHAPE;
     MixerArgs a{q, k, v, g, beta, conv_w, conv_ring, state_in, state_out, z, norm_w, out,
                 o_core, B, T, H, D, K, scale, rms_eps, dtype == KDA_DTYPE_BF16, gdn,
                 workspace, workspace_bytes, (hipStream_t)stream, T, true,
-                ga.form, ga.a, ga.bias, ga.lb};
+                ga.form, ga.a, ga.bias, ga.lb, Hk};
     if (ga.form == kda::GATE_GIVEN) {
         // Kernels read the gate parameters without a branch; point them at conv_w
         // (3*H*D*K >= H*D floats, allocated and 16-byte aligned), values unused.
@@ -168,7 +175,7 @@ int rollback(bool gdn, const void* q, const void* k, const void* v, const void* 
              const void* beta, const float* conv_w, const float* ring_snap,
              const float* state_snap, float* conv_ring, float* state_out, int B, int T_stash,
              int keep, int H, int D, int K, int dtype, void* workspace, size_t workspace_bytes,
-             void* stream, GateArgs ga = kGiven) {
+             void* stream, GateArgs ga = kGiven, int Hk = 0) {
     if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return KDA_ERR_DTYPE_MODE;
     if (ga.form != kda::GATE_GIVEN && ga.form != KDA_GATE_SIGMOID && ga.form != KDA_GATE_SOFTPLUS)
         return KDA_ERR_DTYPE_MODE;
@@ -179,31 +186,35 @@ int rollback(bool gdn, const void* q, const void* k, const void* v, const void* 
     int rc = check_shape(B, T_stash, H, D, K);
     if (rc) return rc;
     if (keep < 1 || keep > T_stash) return KDA_ERR_SHAPE;
+    if (Hk == 0) Hk = H;
+    if (check_heads(H, Hk) || (!gdn && Hk != H)) return KDA_ERR_SHAPE;
     const bool bf16 = dtype == KDA_DTYPE_BF16;
     const int arm = pick_arm(B, keep, H, D, bf16, KDA_MODE_SEQUENTIAL);
     const void* ptrs[] = {q, k, v, g, beta, conv_w, ring_snap, state_snap, conv_ring, state_out, workspace,
                           ga.a, ga.bias};
     for (const void* p : ptrs)
         if (p && ((uintptr_t)p & 15u)) return KDA_ERR_ALIGN;
-    const size_t need_ws = workspace_for(B, keep, H, D, gdn, arm);
+    const size_t need_ws = workspace_for(B, keep, H, Hk, D, gdn, arm);
     if (need_ws > 0 && (!workspace || workspace_bytes < need_ws)) return KDA_ERR_WORKSPACE;
 
     const size_t es = bf16 ? 2 : 4;
     const size_t qkv = (size_t)H * D;
     const size_t act = (size_t)B * T_stash * qkv;
-    const size_t ring_bytes = (size_t)B * 3 * qkv * (K - 1) * 4;
+    const size_t kact = (size_t)B * T_stash * Hk * D;
+    const size_t rrows = (size_t)(2 * Hk + H) * D;
+    const size_t ring_bytes = (size_t)B * rrows * (K - 1) * 4;
     const size_t state_bytes = (size_t)B * H * D * D * 4;
     auto Rg = [](const void* p, size_t bytes, bool w, int id) {
         return Range{(uintptr_t)p, (uintptr_t)p + bytes, w, id};
     };
     Range rs[13];
     int n = 0;
-    rs[n++] = Rg(q, act * es, false, 0);
-    rs[n++] = Rg(k, act * es, false, 1);
+    rs[n++] = Rg(q, kact * es, false, 0);
+    rs[n++] = Rg(k, kact * es, false, 1);
     rs[n++] = Rg(v, act * es, false, 2);
     rs[n++] = Rg(g, (gdn ? (size_t)B * T_stash * H : act) * es, false, 3);
     rs[n++] = Rg(beta, (size_t)B * T_stash * H * es, false, 4);
-    rs[n++] = Rg(conv_w, 3 * qkv * K * 4, false, 5);
+    rs[n++] = Rg(conv_w, rrows * K * 4, false, 5);
     rs[n++] = Rg(ring_snap, ring_bytes, false, 6);
     rs[n++] = Rg(state_snap, state_bytes, false, 7);
     rs[n++] = Rg(conv_ring, ring_bytes, true, 8);
@@ -229,7 +240,7 @@ int rollback(bool gdn, const void* q, const void* k, const void* v, const void* 
     }
     MixerArgs a{q, k, v, g, beta, conv_w, conv_ring, state_snap, state_out, nullptr, nullptr, nullptr,
                 nullptr, B, keep, H, D, K, 1.0f, 0.0f, bf16, gdn, workspace, workspace_bytes,
-                (hipStream_t)stream, T_stash, false, ga.form, conv_w, conv_w, ga.lb};
+                (hipStream_t)stream, T_stash, false, ga.form, conv_w, conv_w, ga.lb, Hk};
     if (ga.form != kda::GATE_GIVEN) {
         a.gate_a = ga.a;
         a.gate_bias = ga.bias;
@@ -237,12 +248,14 @@ int rollback(bool gdn, const void* q, const void* k, const void* v, const void* 
     return run(a, arm);
 }
 
-size_t ws_query(bool gdn, int B, int T, int H, int D, int dtype, int mode) {
+size_t ws_query(bool gdn, int B, int T, int H, int D, int dtype, int mode, int Hk = 0) {
     if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return (size_t)-1;
     if (check_shape(B, T, H, D, 4)) return (size_t)-1;
+    if (Hk == 0) Hk = H;
+    if (check_heads(H, Hk)) return (size_t)-1;
     const int arm = pick_arm(B, T, H, D, dtype == KDA_DTYPE_BF16, mode);
     if (arm < 0) return (size_t)-1;
-    return workspace_for(B, T, H, D, gdn, arm);
+    return workspace_for(B, T, H, Hk, D, gdn, arm);
 }
 
 int arm_query(int B, int T, int H, int D, int dtype, int mode) {
@@ -355,6 +368,45 @@ int gdn_rollback(const void* q, const void* k, const void* v, const void* g, con
 KDA_GATED_ROLLBACK(kda_rollback_gated, false)
 KDA_GATED_ROLLBACK(gdn_rollback_gated, true)
 #undef KDA_GATED_ROLLBACK
+
+int gdn_prefill_gqa(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                    const float* gate_a, const float* gate_bias, float gate_lb, int gate_form,
+                    const float* conv_w, float* conv_ring, const float* state_in, float* state_out,
+                    const void* z, const float* norm_w, void* out, float* o_core, int B, int T, int H,
+                    int Hk, int D, int K, float scale, float rms_eps, int dtype, int mode,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+    if (Hk < 1) return KDA_ERR_SHAPE;  // (0 is not a default here)
+    return entry(true, false, q, k, v, g, beta, conv_w, conv_ring, state_in, state_out, z, norm_w,
+                 out, o_core, B, T, H, D, K, scale, rms_eps, dtype, mode, workspace, workspace_bytes,
+                 stream, GateArgs{gate_form, gate_a, gate_bias, gate_lb}, Hk);
+}
+
+int gdn_decode_gqa(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                   const float* gate_a, const float* gate_bias, float gate_lb, int gate_form,
+                   const float* conv_w, float* conv_ring, const float* state_in, float* state_out,
+                   const void* z, const float* norm_w, void* out, float* o_core, int B, int T, int H,
+                   int Hk, int D, int K, float scale, float rms_eps, int dtype, void* stream) {
+    if (Hk < 1) return KDA_ERR_SHAPE;  // (0 is not a default here)
+    return entry(true, true, q, k, v, g, beta, conv_w, conv_ring, state_in, state_out, z, norm_w,
+                 out, o_core, B, T, H, D, K, scale, rms_eps, dtype, KDA_MODE_SEQUENTIAL, nullptr, 0,
+                 stream, GateArgs{gate_form, gate_a, gate_bias, gate_lb}, Hk);
+}
+
+int gdn_rollback_gqa(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                     const float* gate_a, const float* gate_bias, float gate_lb, int gate_form,
+                     const float* conv_w, const float* ring_snap, const float* state_snap,
+                     float* conv_ring, float* state_out, int B, int T_stash, int keep, int H, int Hk,
+                     int D, int K, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    if (Hk < 1) return KDA_ERR_SHAPE;
+    return rollback(true, q, k, v, g, beta, conv_w, ring_snap, state_snap, conv_ring, state_out, B,
+                    T_stash, keep, H, D, K, dtype, workspace, workspace_bytes, stream,
+                    GateArgs{gate_form, gate_a, gate_bias, gate_lb}, Hk);
+}
+
+size_t gdn_gqa_workspace_bytes(int B, int T, int H, int Hk, int D, int dtype, int mode) {
+    if (Hk < 1) return (size_t)-1;
+    return ws_query(true, B, T, H, D, dtype, mode, Hk);
+}
 
 size_t kda_rollback_workspace_bytes(int B, int keep, int H, int D, int dtype) {
     return ws_query(false, B, keep, H, D, dtype, KDA_MODE_SEQUENTIAL);

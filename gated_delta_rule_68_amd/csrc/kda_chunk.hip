@@ -241,16 +241,17 @@ __device__ __forceinline__ void load_raw_part(ChunkRaw<GDN, NC>& cr, const Mixer
     using CR = ChunkRaw<GDN, NC>;
     const int T = a.T, H = a.H;
     const size_t qkv = (size_t)H * DK, head_off = (size_t)h * DK;
+    const size_t kw = (size_t)a.Hk * DK, khead = (size_t)(h % a.Hk) * DK;  // q / k: key head
     const size_t rowb = (size_t)b * T;
     if constexpr (PART == RAW_Q || PART == RAW_K || PART == RAW_G) {
         if constexpr (PART == RAW_G && GDN) return;
 #pragma unroll
         for (int it = 0; it < CR::NI; ++it) {
             const int idx = tid + NTHR * it, r = idx / (DK / 8), c8 = (idx % (DK / 8)) * 8;
-            const size_t off = (rowb + min(c0 + r, T - 1)) * qkv + head_off + c8;
-            if constexpr (PART == RAW_Q) cr.q[it] = ld_act8<BF>(a.q, off);
-            if constexpr (PART == RAW_K) cr.k[it] = ld_act8<BF>(a.k, off);
-            if constexpr (PART == RAW_G && !GDN) cr.g[it] = ld_act8<BF>(a.g, off);
+            const size_t row = rowb + min(c0 + r, T - 1);
+            if constexpr (PART == RAW_Q) cr.q[it] = ld_act8<BF>(a.q, row * kw + khead + c8);
+            if constexpr (PART == RAW_K) cr.k[it] = ld_act8<BF>(a.k, row * kw + khead + c8);
+            if constexpr (PART == RAW_G && !GDN) cr.g[it] = ld_act8<BF>(a.g, row * qkv + head_off + c8);
         }
     } else if constexpr (PART == RAW_V) {
 #pragma unroll
@@ -519,6 +520,7 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
     } while (0)
     const size_t qkv = (size_t)a.H * DK;
     const size_t head_off = (size_t)h * DK;
+    const size_t kw = (size_t)a.Hk * DK, khead = (size_t)(h % a.Hk) * DK;  // q / k: key head h % Hk
     const int jv0 = split * NC;  // first value column of this split
 
     // ---- state: S tiles (key block `wave`, value block jb): lane holds keys
@@ -536,11 +538,11 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
 
     // ---- conv history of the first chunk: the old ring (slot K-1-d is d rows back) ----
     {
-        const float* ring_b = a.ring + (size_t)b * 3 * qkv * (K - 1);
+        const float* ring_b = a.ring + (size_t)b * ring_rows(a) * (K - 1);
         for (int idx = tid; idx < (KT - 1) * HLD; idx += NTHR) {
             const int d = idx / HLD + 1, col = idx % HLD;
-            const size_t fr = col < 2 * DK ? (size_t)(col / DK) * qkv + head_off + col % DK
-                                           : 2 * qkv + head_off + jv0 + (col - 2 * DK);
+            const size_t fr = col < 2 * DK ? (size_t)(col / DK) * kw + khead + col % DK
+                                           : 2 * kw + head_off + jv0 + (col - 2 * DK);
             sm.hist[d - 1][col] = (__bf16)(d <= K - 1 ? ring_b[fr * (K - 1) + K - 1 - d] : 0.0f);
         }
     }
@@ -595,8 +597,8 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
         // vector-memory counters complete in order, so a small load issued after the
         // prefetch could only be waited for together with all of it.
         float wqk[2][KT], wv[NVCH][KT], w8[8];
-        load_taps<KT, 2>(wqk, a.conv_w, (kplane ? qkv : 0) + head_off + 2 * lane, K);
-        load_taps<KT, NVCH>(wv, a.conv_w, 2 * qkv + head_off + jv0 + max(cv, 0), K);  // used by wavefronts 4..7
+        load_taps<KT, 2>(wqk, a.conv_w, (kplane ? kw : 0) + khead + 2 * lane, K);
+        load_taps<KT, NVCH>(wv, a.conv_w, 2 * kw + head_off + jv0 + max(cv, 0), K);  // used by wavefronts 4..7
         if constexpr (NCOL == 1) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) w8[e] = a.norm_w[(tid % (DK / 8)) * 8 + e];
@@ -1112,32 +1114,6 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
 
 // The ring roll of the chunked arm: new slot K-1-d = raw input at token T-d (the old
 // ring for T-d < 0). Launched after the chunk kernel, which read the old ring.
-template <bool BF>
-__global__ __launch_bounds__(256) void ring_roll_kernel(MixerArgs a) {
-    const size_t rows = (size_t)a.B * 3 * a.H * DK;
-    const size_t row = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (row >= rows) return;
-    const size_t qkv = (size_t)a.H * DK;
-    const int b = (int)(row / (3 * qkv));
-    const size_t cf = row % (3 * qkv);
-    const int plane = (int)(cf / qkv);
-    const size_t ch = cf % qkv;
-    const void* x = plane == 0 ? a.q : (plane == 1 ? a.k : a.v);
-    const int K = a.K, T = a.T;
-    float* ring_row = a.ring + row * (K - 1);
-    float nr[KMAX - 1];
-#pragma unroll
-    for (int d = 1; d < KMAX; ++d) {
-        const int pos = T - d;
-        nr[KMAX - 1 - d] = (d <= K - 1) ? (pos >= 0 ? ld_act<BF>(x, ((size_t)b * T + pos) * qkv + ch)
-                                                     : ring_row[pos + K - 1])
-                                        : 0.0f;
-    }
-#pragma unroll
-    for (int d = 1; d < KMAX; ++d)
-        if (d <= K - 1) ring_row[K - 1 - d] = nr[KMAX - 1 - d];
-}
-
 int chunk_ncol(int B, int H) {
     const long bh = (long)B * H;
     if (bh >= 256) return 1;
@@ -1179,10 +1155,7 @@ hipError_t chunk_launch(const MixerArgs& a) {
         e = launch_norm(a, o_buf);
         if (e != hipSuccess) return e;
     }
-    const size_t rows = (size_t)a.B * 3 * a.H * DK;
-    hipLaunchKernelGGL((ring_roll_kernel<BF>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
-                       a.stream, a);
-    return hipGetLastError();
+    return launch_ring_roll(a, false);
 }
 
 }  // namespace

@@ -43,7 +43,20 @@ struct MixerArgs {
     const float* gate_a;     // [H]: A_log (GATE_SIGMOID) or the multiplier a (GATE_SOFTPLUS)
     const float* gate_bias;  // [H*D] (KDA) or [H] (GDN)
     float gate_lb;           // lower bound of the log gate
+    // Query / key heads (GDN grouped heads; H for KDA and plain GDN). H is the number
+    // of value heads, a multiple of Hk, and value head h reads query / key head
+    // h % Hk. q and k rows are Hk*D wide; v, z, out, o_core rows H*D; the conv
+    // weight and ring planes are q (Hk*D rows), k (Hk*D), v (H*D), in that order.
+    int Hk;
 };
+
+// Conv-weight / ring row of channel ch of plane (0 q, 1 k, 2 v) for value head h.
+__host__ __device__ inline size_t plane_row(const MixerArgs& a, int plane, int h, int ch) {
+    const size_t kw = (size_t)a.Hk * a.D;
+    return plane < 2 ? plane * kw + (size_t)(h % a.Hk) * a.D + ch : 2 * kw + (size_t)h * a.D + ch;
+}
+// Ring rows (= conv-weight rows) of one sequence.
+__host__ __device__ inline size_t ring_rows(const MixerArgs& a) { return (size_t)(2 * a.Hk + a.H) * a.D; }
 
 // Values of the KDA_GATE_* codes of the public header.
 enum GateForm { GATE_GIVEN = 0, GATE_SIGMOID = 1, GATE_SOFTPLUS = 2 };
@@ -56,7 +69,7 @@ enum Arm { ARM_SEQ_FUSED = 1, ARM_SEQ_SPLIT = 2, ARM_CHUNKED = 3 };
 struct SplitWorkspace {
     size_t qh, kh, vh, eg, kq, o, total;  // byte offsets and total size
 };
-SplitWorkspace split_workspace(int B, int T, int H, int D, bool gdn);
+SplitWorkspace split_workspace(int B, int T, int H, int Hk, int D, bool gdn);
 
 // Whether this build carries the chunked prefill arm.
 extern const bool kChunkedArmBuilt;
@@ -70,5 +83,8 @@ hipError_t launch_seq_split(const MixerArgs& a);
 hipError_t launch_chunked(const MixerArgs& a);
 // Gated RMSNorm of a fp32 pre-norm output o [B][T][H*D] into a.out.
 hipError_t launch_norm(const MixerArgs& a, const float* o);
+// Roll every sequence's ring to the last K-1 raw rows of its T input rows (q, k and
+// v planes, or with qk_only the q and k planes alone).
+hipError_t launch_ring_roll(const MixerArgs& a, bool qk_only);
 
 }  // namespace kda

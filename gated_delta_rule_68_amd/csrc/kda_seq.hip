@@ -55,6 +55,12 @@ __global__ __launch_bounds__(fused_threads<D>()) void seq_fused_kernel(MixerArgs
     const size_t qkv = (size_t)H * D;
     const size_t head_off = (size_t)h * D;
     const int grp = wave * 8 + (lane >> 3), s = lane & 7;
+    // q / k rows are Hk*D wide and this value head reads key head h % Hk
+    const size_t kw = (size_t)a.Hk * D, khead = (size_t)(h % a.Hk) * D;
+    const size_t rrow = ring_rows(a);
+    auto prow = [&](int plane, int ch) -> size_t {  // conv-weight / ring row
+        return plane < 2 ? plane * kw + khead + ch : 2 * kw + head_off + ch;
+    };
 
     // Issue the state loads first so their HBM latency overlaps the conv / l2 work.
     float S[CPT][KPL];
@@ -71,7 +77,7 @@ __global__ __launch_bounds__(fused_threads<D>()) void seq_fused_kernel(MixerArgs
     // Conv windows of this head's 3*D (plane, channel) rows start as the old ring.
     for (int r = tid; r < 3 * D; r += NT) {
         const int plane = r / D, ch = r % D;
-        const float* ring_row = a.ring + ((size_t)b * 3 * qkv + plane * qkv + head_off + ch) * (K - 1);
+        const float* ring_row = a.ring + ((size_t)b * rrow + prow(plane, ch)) * (K - 1);
         ConvChannel cc;
         conv_window_from_ring(cc, ring_row, K);
 #pragma unroll
@@ -85,11 +91,12 @@ __global__ __launch_bounds__(fused_threads<D>()) void seq_fused_kernel(MixerArgs
             const int plane = r / D, ch = r % D;
             const void* xsrc = plane == 0 ? a.q : (plane == 1 ? a.k : a.v);
             ConvChannel cc;
-            conv_load_taps(cc, a.conv_w + (plane * qkv + head_off + ch) * K, K);
+            conv_load_taps(cc, a.conv_w + prow(plane, ch) * K, K);
 #pragma unroll
             for (int e = 0; e < KMAX - 1; ++e) cc.win[e] = wins[r][e];
+            const size_t xw = plane < 2 ? kw : qkv, xc = (plane < 2 ? khead : head_off) + ch;
             for (int tt = 0; tt < nt; ++tt) {
-                const float x = ld_act<BF>(xsrc, (row0 + tt) * qkv + head_off + ch);
+                const float x = ld_act<BF>(xsrc, (row0 + tt) * xw + xc);
                 pre[plane][tt][ch] = silu_f(conv_push(cc, x));
             }
 #pragma unroll
@@ -132,11 +139,14 @@ __global__ __launch_bounds__(fused_threads<D>()) void seq_fused_kernel(MixerArgs
 #pragma unroll
     for (int c = 0; c < CPT; ++c)
         store_keys<D>(a.state_out + ((size_t)bh * D + grp + c * NG) * D, S[c], s);
-    // Each ring row was read only by this workgroup (window init); the windows now hold
-    // the last K-1 raw inputs of [old ring ++ x].
+    // The windows now hold the last K-1 raw inputs of [old ring ++ x]. Each v row was
+    // read only by this workgroup (window init); so were the q / k rows unless key
+    // heads are shared (Hk < H), in which case they are rolled by a kernel of their
+    // own after this one (another workgroup may still be reading them).
     for (int r = tid; r < 3 * D; r += NT) {
         const int plane = r / D, ch = r % D;
-        float* ring_row = a.ring + ((size_t)b * 3 * qkv + plane * qkv + head_off + ch) * (K - 1);
+        if (plane < 2 && a.Hk != a.H) continue;
+        float* ring_row = a.ring + ((size_t)b * rrow + prow(plane, ch)) * (K - 1);
         ConvChannel cc;
 #pragma unroll
         for (int e = 0; e < KMAX - 1; ++e) cc.win[e] = wins[r][e];
@@ -168,13 +178,19 @@ __global__ __launch_bounds__(pre_threads<D>()) void pre_kernel(MixerArgs a, floa
 
     static_assert(NT % D == 0, "one gate column per thread");
     const GateCol gp = gate_col(a, h, GDN ? h : head_off + tid % D);
-    const bool conv_thread = tid < 3 * D;
+    // Key heads shared by several value heads (Hk < H): the workgroups of value heads
+    // h < Hk (key head h) alone convolve, normalise and store q / k and roll their ring
+    // rows; every workgroup does its own v.
+    const bool qk_owner = h < a.Hk;
+    const size_t kw = (size_t)a.Hk * D;
     const int plane = tid / D, ch = tid % D;
-    const size_t cf = (size_t)plane * qkv + head_off + ch;
-    float* ring_row = a.ring + ((size_t)b * 3 * qkv + cf) * (K - 1);
+    const bool conv_thread = tid < 3 * D && (plane == 2 || qk_owner);
+    const size_t cf = plane < 2 ? plane * kw + head_off + ch : 2 * kw + head_off + ch;
+    float* ring_row = a.ring + ((size_t)b * ring_rows(a) + cf) * (K - 1);
     const void* xsrc = plane == 0 ? a.q : (plane == 1 ? a.k : a.v);
+    const size_t xw = plane < 2 ? kw : qkv;
     auto raw_at = [&](int pos) -> float {  // x~[K-1+pos]: raw input at token pos (< 0: ring)
-        return pos >= 0 ? ld_act<BF>(xsrc, ((size_t)b * a.tp + pos) * qkv + head_off + ch)
+        return pos >= 0 ? ld_act<BF>(xsrc, ((size_t)b * a.tp + pos) * xw + head_off + ch)
                         : ring_row[pos + K - 1];
     };
     if (conv_thread) {
@@ -183,7 +199,7 @@ __global__ __launch_bounds__(pre_threads<D>()) void pre_kernel(MixerArgs a, floa
 #pragma unroll
         for (int d = 1; d < KMAX; ++d) cc.win[KMAX - 1 - d] = (d <= K - 1) ? raw_at(t0 - d) : 0.0f;
         for (int tt = 0; tt < nt; ++tt)
-            pre[plane][tt][ch] = silu_f(conv_push(cc, ld_act<BF>(xsrc, (rin0 + tt) * qkv + head_off + ch)));
+            pre[plane][tt][ch] = silu_f(conv_push(cc, ld_act<BF>(xsrc, (rin0 + tt) * xw + head_off + ch)));
         // Only the first token block reads the old ring (TB_PRE >= KMAX - 1), so it
         // alone rolls it, after its own reads: new slot K-1-d = raw input at T-d.
         if (blockIdx.y == 0) {
@@ -204,16 +220,19 @@ __global__ __launch_bounds__(pre_threads<D>()) void pre_kernel(MixerArgs a, floa
         }
     }
     __syncthreads();
-    for (int tt = wave; tt < nt; tt += NW) l2_qk_row<D>(pre[0][tt], pre[1][tt], lane, &kqs[tt]);
+    if (qk_owner)
+        for (int tt = wave; tt < nt; tt += NW) l2_qk_row<D>(pre[0][tt], pre[1][tt], lane, &kqs[tt]);
     __syncthreads();
     for (int idx = tid; idx < nt * D; idx += NT) {
         const int tt = idx / D, i = idx % D;
-        const size_t off = (row0 + tt) * qkv + head_off + i;
-        qh[off] = pre[0][tt][i];
-        kh[off] = pre[1][tt][i];
-        vh[off] = pre[2][tt][i];
+        if (qk_owner) {
+            const size_t koff = (row0 + tt) * kw + head_off + i;  // key head h
+            qh[koff] = pre[0][tt][i];
+            kh[koff] = pre[1][tt][i];
+        }
+        vh[(row0 + tt) * qkv + head_off + i] = pre[2][tt][i];
     }
-    if (tid < nt) kqv[(row0 + tid) * H + h] = kqs[tid];
+    if (qk_owner && tid < nt) kqv[(row0 + tid) * a.Hk + h] = kqs[tid];
 }
 
 template <int D>
@@ -240,6 +259,8 @@ __global__ __launch_bounds__(8 * split_cols<D>()) void scan_split_kernel(
     const size_t head_off = (size_t)h * D;
     const int jl = wave * 8 + (lane >> 3), s = lane & 7;
     const int j = split * COLS + jl;
+    const int hk = h % a.Hk;  // key head of this value head
+    const size_t kw = (size_t)a.Hk * D, khead = (size_t)hk * D;
 
     float S[1][KPL];
     load_keys<D>(S[0], a.state_in + ((size_t)bh * D + j) * D, s);
@@ -249,10 +270,10 @@ __global__ __launch_bounds__(8 * split_cols<D>()) void scan_split_kernel(
         const size_t row0 = (size_t)b * T + t0;
         for (int idx = tid; idx < nt * D; idx += NT) {
             const int tt = idx / D, i = idx % D;
-            const size_t off = (row0 + tt) * qkv + head_off + i;
-            qs[tt][i] = qh[off];
-            ks[tt][i] = kh[off];
-            if constexpr (!GDN) es[tt][i] = eg[off];
+            const size_t koff = (row0 + tt) * kw + khead + i;
+            qs[tt][i] = qh[koff];
+            ks[tt][i] = kh[koff];
+            if constexpr (!GDN) es[tt][i] = eg[(row0 + tt) * qkv + head_off + i];
         }
         for (int idx = tid; idx < nt * COLS; idx += NT) {
             const int tt = idx / COLS, c = idx % COLS;
@@ -261,7 +282,7 @@ __global__ __launch_bounds__(8 * split_cols<D>()) void scan_split_kernel(
         if (tid < nt) {
             const size_t hr = (row0 + tid) * H + h;
             bs[tid] = beta_in(a, ld_act<BF>(a.beta, ((size_t)b * a.tp + t0 + tid) * H + h));
-            kqs[tid] = kqv[hr];
+            kqs[tid] = kqv[(row0 + tid) * a.Hk + hk];
             if constexpr (GDN) es[tid][0] = eg[hr];
         }
         __syncthreads();
@@ -296,12 +317,14 @@ template <int D, bool BF, bool GDN>
 hipError_t fused_launch(const MixerArgs& a) {
     hipLaunchKernelGGL((seq_fused_kernel<D, BF, GDN>), dim3(a.B * a.H), dim3(fused_threads<D>()), 0,
                        a.stream, a);
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.Hk == a.H) return e;
+    return launch_ring_roll(a, true);  // shared q / k rows, after every reader
 }
 
 template <int D, bool BF, bool GDN>
 hipError_t split_launch(const MixerArgs& a) {
-    const SplitWorkspace w = split_workspace(a.B, a.T, a.H, a.D, a.gdn);
+    const SplitWorkspace w = split_workspace(a.B, a.T, a.H, a.Hk, a.D, a.gdn);
     char* base = static_cast<char*>(a.ws);
     float* qh = reinterpret_cast<float*>(base + w.qh);
     float* kh = reinterpret_cast<float*>(base + w.kh);
@@ -349,18 +372,62 @@ hipError_t dispatch(const MixerArgs& a) {
 
 }  // namespace
 
-SplitWorkspace split_workspace(int B, int T, int H, int D, bool gdn) {
+SplitWorkspace split_workspace(int B, int T, int H, int Hk, int D, bool gdn) {
     const size_t act = align256((size_t)B * T * H * D * 4);
+    const size_t kact = align256((size_t)B * T * Hk * D * 4);
     const size_t per_head = align256((size_t)B * T * H * 4);
+    const size_t per_khead = align256((size_t)B * T * Hk * 4);
     SplitWorkspace w;
     w.qh = 0;
-    w.kh = w.qh + act;
-    w.vh = w.kh + act;
+    w.kh = w.qh + kact;
+    w.vh = w.kh + kact;
     w.eg = w.vh + act;
     w.kq = w.eg + (gdn ? per_head : act);
-    w.o = w.kq + per_head;
+    w.o = w.kq + per_khead;
     w.total = w.o + act;
     return w;
+}
+
+namespace {
+
+// One thread per ring row: the K-1 newest raw inputs of [old ring ++ x] (the row's
+// old slots are read into registers before any store). Rows of a sequence are
+// numbered as the ring: q plane, k plane (Hk*D each), v plane (H*D).
+template <bool BF>
+__global__ __launch_bounds__(256) void ring_roll_kernel(MixerArgs a, int rows_per_seq) {
+    const size_t row = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (row >= (size_t)a.B * rows_per_seq) return;
+    const size_t kw = (size_t)a.Hk * a.D, vw = (size_t)a.H * a.D;
+    const int b = (int)(row / rows_per_seq);
+    const size_t cf = row % rows_per_seq;
+    const int plane = cf < kw ? 0 : (cf < 2 * kw ? 1 : 2);
+    const size_t ch = plane < 2 ? cf - plane * kw : cf - 2 * kw;
+    const size_t xw = plane < 2 ? kw : vw;
+    const void* x = plane == 0 ? a.q : (plane == 1 ? a.k : a.v);
+    const int K = a.K, T = a.T;
+    float* ring_row = a.ring + ((size_t)b * ring_rows(a) + cf) * (K - 1);
+    float nr[KMAX - 1];
+#pragma unroll
+    for (int d = 1; d < KMAX; ++d) {
+        const int pos = T - d;
+        nr[KMAX - 1 - d] = (d <= K - 1) ? (pos >= 0 ? ld_act<BF>(x, ((size_t)b * a.tp + pos) * xw + ch)
+                                                     : ring_row[pos + K - 1])
+                                        : 0.0f;
+    }
+#pragma unroll
+    for (int d = 1; d < KMAX; ++d)
+        if (d <= K - 1) ring_row[K - 1 - d] = nr[KMAX - 1 - d];
+}
+
+}  // namespace
+
+hipError_t launch_ring_roll(const MixerArgs& a, bool qk_only) {
+    const int rows_per_seq = (int)(qk_only ? (size_t)2 * a.Hk * a.D : ring_rows(a));
+    const size_t rows = (size_t)a.B * rows_per_seq;
+    const dim3 grid((unsigned)((rows + 255) / 256)), block(256);
+    if (a.bf16) hipLaunchKernelGGL((ring_roll_kernel<true>), grid, block, 0, a.stream, a, rows_per_seq);
+    else hipLaunchKernelGGL((ring_roll_kernel<false>), grid, block, 0, a.stream, a, rows_per_seq);
+    return hipGetLastError();
 }
 
 hipError_t launch_seq_fused(const MixerArgs& a) { return dispatch<FusedOp>(a); }

@@ -14,6 +14,8 @@ Recipe (one independent numpy PCG64 stream per (tensor, sequence)):
   activations (q, k, v, g, beta, z) are then rounded to bf16 (round to nearest
   even). State, conv ring, conv weight and norm weight always stay fp32;
 * q, k, v raw ~ N(0, 1); conv weight ~ N(0, 0.5) (0.5 is the standard deviation);
+  with grouped heads (Hk < H, GDN) q and k have Hk heads and the conv weight and
+  ring have 2*Hk*D + H*D rows (planes q, k, v);
   beta = sigmoid(N(0, 1)) per (token, head);
   log gate g = max(-5, -exp(A_log[h]) * softplus(x + dt_bias)), x ~ N(0, 1),
   A_log ~ U(0, ln 16) per head, dt_bias ~ N(0, 0.1) per channel (KDA) or per head
@@ -50,10 +52,26 @@ class Config:
     gate_regime: str = "normal"  # "normal" or "alternating" (+2 / -2 shift by head parity)
     random_init: bool = False    # random state and ring (decode) instead of zeros (prefill)
     chunk: int = 64
+    Hk: int = 0                  # query / key heads (GDN grouped heads); 0 means H
 
     @property
     def qkv(self) -> int:
+        """Width of the value-head rows (v, z, out): H * D."""
         return self.H * self.D
+
+    @property
+    def hk(self) -> int:
+        return self.Hk or self.H
+
+    @property
+    def kw(self) -> int:
+        """Width of the query / key rows: Hk * D."""
+        return self.hk * self.D
+
+    @property
+    def conv_rows(self) -> int:
+        """Conv-weight and ring rows: planes q, k (Hk * D each), v (H * D)."""
+        return 2 * self.kw + self.qkv
 
     def with_(self, **kw) -> "Config":
         return replace(self, **kw)
@@ -130,10 +148,10 @@ def make_inputs(cfg: Config, seed: int = 0, T: int | None = None) -> Inputs:
     """Draw the inputs of ``cfg`` (optionally only the first ``T`` tokens)."""
     T = cfg.T if T is None else T
     B, H, D, K, qkv = cfg.B, cfg.H, cfg.D, cfg.K, cfg.qkv
-    q = _per_seq(seed, "q", B, (T, qkv))
-    k = _per_seq(seed, "k", B, (T, qkv))
+    q = _per_seq(seed, "q", B, (T, cfg.kw))
+    k = _per_seq(seed, "k", B, (T, cfg.kw))
     v = _per_seq(seed, "v", B, (T, qkv))
-    conv_w = (0.5 * _rng(seed, "conv_w").standard_normal((3 * qkv, K))).astype(np.float32)
+    conv_w = (0.5 * _rng(seed, "conv_w").standard_normal((cfg.conv_rows, K))).astype(np.float32)
     beta_x = _per_seq(seed, "beta_x", B, (T, H)).astype(np.float64)
     beta = (1.0 / (1.0 + np.exp(-beta_x))).astype(np.float32)
     A_log = _rng(seed, "A_log").uniform(0.0, np.log(16.0), H)
@@ -147,10 +165,10 @@ def make_inputs(cfg: Config, seed: int = 0, T: int | None = None) -> Inputs:
     z = _per_seq(seed, "z", B, (T, qkv))
     norm_w = (1.0 + 0.1 * _rng(seed, "norm_w").standard_normal(D)).astype(np.float32)
     if cfg.random_init:
-        ring = _per_seq(seed, "ring", B, (3 * qkv, K - 1))
+        ring = _per_seq(seed, "ring", B, (cfg.conv_rows, K - 1))
         state = _per_seq(seed, "state", B, (H, D, D), scale=0.02)
     else:
-        ring = np.zeros((B, 3 * qkv, K - 1), np.float32)
+        ring = np.zeros((B, cfg.conv_rows, K - 1), np.float32)
         state = np.zeros((B, H, D, D), np.float32)
     gate_x, beta_x32 = gx.astype(np.float32), beta_x.astype(np.float32)
     bits = {}

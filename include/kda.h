@@ -87,6 +87,7 @@ extern "C" {
  *                      (aprender-serve gdn_ops.rs, the per-head gates: gate_a = a,
  *                      usually -exp(A_log); gate_lb = -INFINITY for no bound)
  *   and in both forms beta = sigmoid(b). */
+#define KDA_GATE_GIVEN 0 /* (grouped-head entries) g and beta already activated */
 #define KDA_GATE_SIGMOID 1
 #define KDA_GATE_SOFTPLUS 2
 
@@ -253,6 +254,51 @@ int gdn_rollback_gated(const void* q, const void* k, const void* v, const void* 
                        const float* ring_snap, const float* state_snap, float* conv_ring,
                        float* state_out, int B, int T_stash, int keep, int H, int D, int K,
                        int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Grouped query / key heads for GDN (aprender-serve gdn_ops.rs, the delta-rule
+ * recurrence wrapper: q and k have num_k_heads heads, v, beta and the gate
+ * num_v_heads, and value head h reads query / key head h % num_k_heads, the tiled
+ * order).
+ *
+ * gdn_prefill_gqa / gdn_decode_gqa / gdn_rollback_gqa - gdn_prefill, gdn_decode and
+ * gdn_rollback with Hk query / key heads and H value heads (Hk >= 1 divides H, else
+ * KDA_ERR_SHAPE; Hk == H is the plain layout). Shapes:
+ *   q, k       [B][T][Hk*D]          (dtype)
+ *   v, z, out  [B][T][H*D]           (dtype); o_core [B][T][H*D] fp32
+ *   g, beta    [B][T][H]             (per value head)
+ *   conv_w     [(2*Hk + H)*D][K]     planes q (Hk*D rows), k (Hk*D), v (H*D)
+ *   conv_ring  [B][(2*Hk + H)*D][K-1] same plane order
+ *   state      [B][H][D][D]          (per value head)
+ * The conv, the ring roll and the l2 norm of q / k run once per key head channel; the
+ * scan, the gated norm and the state are per value head.
+ * gate_form 0 (KDA_GATE_GIVEN): g and beta hold the log gate and beta, gate_a and
+ * gate_bias are unused and may be NULL; KDA_GATE_SIGMOID / KDA_GATE_SOFTPLUS: g and
+ * beta hold pre-activations, gate_a [H] and gate_bias [H], as for gdn_prefill_gated.
+ * workspace: at least gdn_gqa_workspace_bytes(B, T, H, Hk, D, dtype, mode) bytes
+ * (rollback: T = keep, mode = KDA_MODE_SEQUENTIAL). Everything else, including the
+ * arm choice (by B*H value heads) and the status codes, as for the plain entries.
+ */
+int gdn_prefill_gqa(const void* q, const void* k, const void* v, const void* g,
+                    const void* beta, const float* gate_a, const float* gate_bias,
+                    float gate_lb, int gate_form, const float* conv_w, float* conv_ring,
+                    const float* state_in, float* state_out, const void* z,
+                    const float* norm_w, void* out, float* o_core, int B, int T, int H,
+                    int Hk, int D, int K, float scale, float rms_eps, int dtype, int mode,
+                    void* workspace, size_t workspace_bytes, void* stream);
+int gdn_decode_gqa(const void* q, const void* k, const void* v, const void* g,
+                   const void* beta, const float* gate_a, const float* gate_bias,
+                   float gate_lb, int gate_form, const float* conv_w, float* conv_ring,
+                   const float* state_in, float* state_out, const void* z,
+                   const float* norm_w, void* out, float* o_core, int B, int T, int H, int Hk,
+                   int D, int K, float scale, float rms_eps, int dtype, void* stream);
+int gdn_rollback_gqa(const void* q, const void* k, const void* v, const void* g,
+                     const void* beta, const float* gate_a, const float* gate_bias,
+                     float gate_lb, int gate_form, const float* conv_w,
+                     const float* ring_snap, const float* state_snap, float* conv_ring,
+                     float* state_out, int B, int T_stash, int keep, int H, int Hk, int D,
+                     int K, int dtype, void* workspace, size_t workspace_bytes, void* stream);
+size_t gdn_gqa_workspace_bytes(int B, int T, int H, int Hk, int D, int dtype, int mode);
 
 /* Static description of a status code (never NULL). */
 const char* kda_status_string(int rc);

@@ -255,30 +255,36 @@ def pin_rmsnorm_closed_forms(lib):
 def brute_mixer(inp_q, inp_k, inp_v, g, beta, conv_w, ring, state, z, norm_w, scale, eps, gdn):
     """Independent restatement of the whole path from numpy/scipy primitives:
     numpy.convolve for the conv, numpy.linalg.norm for l2, the transition-matrix
-    form of the recurrence, expit for the gates."""
-    B, T, qkv = inp_q.shape
+    form of the recurrence, expit for the gates. q and k may have fewer heads than v
+    (grouped heads, GDN): value head h then reads query / key head h % Hk, and the
+    conv weight and ring planes are q, k (Hk*D rows each), v (H*D)."""
+    B, T, kw = inp_q.shape
     H, D = state.shape[1], state.shape[2]
+    Hk = kw // D
     K = conv_w.shape[1]
     convd = []
-    for plane, x in enumerate((inp_q, inp_k, inp_v)):
+    base = 0
+    for x in (inp_q, inp_k, inp_v):
         y = np.empty_like(x)
         for b in range(B):
-            for c in range(qkv):
-                cf = plane * qkv + c
+            for c in range(x.shape[2]):
+                cf = base + c
                 xt = np.concatenate([ring[b, cf], x[b, :, c]])
                 pre = np.convolve(xt, conv_w[cf][::-1], mode="valid")
                 y[b, :, c] = pre * expit(pre)
         convd.append(y)
+        base += x.shape[2]
     qc, kc, vc = convd
-    out = np.empty_like(inp_q)
+    out = np.empty_like(inp_v)
     s_out = np.empty_like(state)
     for b in range(B):
         for h in range(H):
             cs = slice(h * D, (h + 1) * D)
+            ks = slice((h % Hk) * D, (h % Hk + 1) * D)
             S = state[b, h].T.copy()
             for t in range(T):
-                qt = qc[b, t, cs] / np.sqrt(np.linalg.norm(qc[b, t, cs]) ** 2 + 1e-6)
-                kt = kc[b, t, cs] / np.sqrt(np.linalg.norm(kc[b, t, cs]) ** 2 + 1e-6)
+                qt = qc[b, t, ks] / np.sqrt(np.linalg.norm(qc[b, t, ks]) ** 2 + 1e-6)
+                kt = kc[b, t, ks] / np.sqrt(np.linalg.norm(kc[b, t, ks]) ** 2 + 1e-6)
                 gt = np.full(D, g[b, t, h]) if gdn else g[b, t, cs]
                 bt = beta[b, t, h]
                 S = (np.eye(D) - bt * np.outer(kt, kt)) @ np.diag(np.exp(gt)) @ S \

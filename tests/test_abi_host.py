@@ -243,3 +243,45 @@ def test_gated_rollback_contract(what, over, kw, rc, gdn):
     a = fake_args()
     a.update({k: (0 if v is None else v) for k, v in over.items()})
     assert call_rollback_gated(a, gdn, **kw) == rc
+
+
+def call_gqa(a, Hk, decode=False, form=0, lb=0.0):
+    L = kda.lib()
+    head = (a["q"], a["k"], a["v"], a["g"], a["beta"], a["gate_a"], a["gate_bias"], lb, form, a["conv_w"],
+            a["ring"], a["state_in"], a["state_out"], a["z"], a["norm_w"], a["out"], a["o_core"], a["B"],
+            a["T"], a["H"], Hk, a["D"], a["K"], 0.25, 1e-5, a["dtype"])
+    if decode:
+        return L.gdn_decode_gqa(*head, None)
+    return L.gdn_prefill_gqa(*head, a["mode"], a["ws"], a["ws_bytes"], None)
+
+
+GQA_CASES = [
+    ("Hk does not divide H", dict(H=4), 3, 40004),
+    ("Hk above H", dict(H=2), 4, 40004),
+    ("Hk 0", dict(H=4), 0, 40004),
+    ("Hk negative", dict(H=4), -2, 40004),
+    ("null q", dict(H=4, q=None), 2, 40001),
+    ("gate form 5", dict(H=4), 2, 40008),
+    ("misaligned k", dict(H=4, k=BASE + 1 * (1 << 32) + 2), 2, 40007),
+    # q is [B][T][Hk*D] (here 2 x T x 32 floats): out 128 bytes after it overlaps it
+    ("out over q", dict(H=4, out=BASE + 128), 2, 40009),
+]
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="fake pointers only where no GPU is visible")
+@pytest.mark.parametrize("decode", [False, True])
+@pytest.mark.parametrize("what,over,Hk,rc", GQA_CASES, ids=[c[0] for c in GQA_CASES])
+def test_gqa_contract(what, over, Hk, rc, decode):
+    a = fake_args(T=1 if decode else 3, H=over.get("H", 2))
+    a.update({k: (0 if v is None else v) for k, v in over.items() if k != "H"})
+    form = 5 if what == "gate form 5" else 0
+    assert call_gqa(a, Hk, decode, form=form) == rc
+
+
+def test_gqa_queries():
+    # grouped heads need less split-arm workspace (q / k staged once per key head)
+    full = kda.workspace_bytes(1, 100, 4, 16, 0, 1, gdn=True)
+    assert kda.gqa_workspace_bytes(1, 100, 4, 4, 16, 0, 1) == full
+    assert 0 < kda.gqa_workspace_bytes(1, 100, 4, 2, 16, 0, 1) < full
+    assert kda.gqa_workspace_bytes(1, 100, 4, 3, 16, 0, 1) == ctypes.c_size_t(-1).value
+    assert kda.gqa_workspace_bytes(1, 100, 4, 0, 16, 0, 1) == ctypes.c_size_t(-1).value
