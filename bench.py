@@ -446,6 +446,77 @@ def run_gqa_leg(reps: int = 50) -> dict:
     return rec
 
 
+def run_varlen_leg() -> dict:
+    """Packed variable-length KDA prefill (H=64, D=128, bf16, chunked arm): 16 prompt
+    lengths drawn log-uniformly from 64..4096 (numpy seed 7). One packed call, against
+    the same work as a batch padded to the longest prompt and as one call per prompt;
+    tokens/s counts the prompts' own tokens only."""
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_68_amd as kda
+    from gated_delta_rule_68_amd.synth import CONFIGS
+    from gated_delta_rule_68_amd.torch_io import ACTS, alloc_outputs, tiled_device_inputs
+
+    lens = (2.0 ** np.random.default_rng(7).uniform(6, 12, 16)).astype(int)
+    N, Tm = len(lens), int(lens.max())
+    cfg = CONFIGS["kda_prefill"].with_(B=N, T=Tm)
+    d = tiled_device_inputs(cfg)
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).to("cuda")
+    T_total = int(lens.sum())
+    p = {n: torch.cat([d[n][b, :L] for b, L in enumerate(lens)], 0).contiguous() for n in ACTS}
+    mode, code = kda.KDA_MODE_CHUNKED, kda.KDA_DTYPE_BF16
+    scale = 1.0 / math.sqrt(cfg.D)
+    ring0 = d["ring"].clone()
+    s_out = torch.empty_like(d["state"])
+    out_p = torch.empty(T_total, cfg.qkv, dtype=torch.bfloat16, device="cuda")
+    ws_p = torch.empty(max(kda.varlen_workspace_bytes(N, T_total, cfg.H, cfg.D, code, mode), 1),
+                       dtype=torch.uint8, device="cuda")
+
+    def packed(i=0):
+        d["ring"].copy_(ring0)
+        kda.prefill_varlen(p["q"], p["k"], p["v"], p["g"], p["beta"], d["conv_w"], d["ring"], d["state"], s_out,
+                           p["z"], d["norm_w"], out_p, cu, None, scale=scale, rms_eps=RMS_EPS, mode=mode,
+                           workspace=ws_p)
+
+    out_b = alloc_outputs(cfg, Tm, "cuda", o_core=False)["out"]
+    ws_b = torch.empty(max(kda.workspace_bytes(N, Tm, cfg.H, cfg.D, code, mode), 1), dtype=torch.uint8,
+                       device="cuda")
+
+    def padded(i=0):
+        d["ring"].copy_(ring0)
+        kda.kda_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["conv_w"], d["ring"], d["state"], s_out,
+                        d["z"], d["norm_w"], out_b, None, scale=scale, rms_eps=RMS_EPS, mode=mode, workspace=ws_b)
+
+    singles = []
+    for b, L in enumerate(lens):
+        one = {n: d[n][b:b + 1, :L].contiguous() for n in ("q", "k", "v", "g", "beta", "z")}
+        one["ring"], one["state"] = d["ring"][b:b + 1].clone(), d["state"][b:b + 1]
+        one["s_out"] = torch.empty_like(one["state"])
+        one["out"] = torch.empty(1, int(L), cfg.qkv, dtype=torch.bfloat16, device="cuda")
+        one["ws"] = torch.empty(max(kda.workspace_bytes(1, int(L), cfg.H, cfg.D, code, mode), 1),
+                                dtype=torch.uint8, device="cuda")
+        singles.append(one)
+
+    def per_prompt(i=0):
+        for o in singles:
+            kda.kda_prefill(o["q"], o["k"], o["v"], o["g"], o["beta"], d["conv_w"], o["ring"], o["state"],
+                            o["s_out"], o["z"], d["norm_w"], o["out"], None, scale=scale, rms_eps=RMS_EPS,
+                            mode=mode, workspace=o["ws"])
+
+    ms_p, ms_b = _timed_pair(packed, padded, 5)
+    ms_s, _ = _timed_pair(per_prompt, lambda i=0: None, 5)
+    rec = {"workload": f"KDA chunked prefill H={cfg.H} D={cfg.D} bf16, {N} prompts of {int(lens.min())}.."
+                       f"{Tm} tokens ({T_total} in all)", "lengths": [int(x) for x in lens],
+           "packed_ms": ms_p, "packed_tokens_per_s": T_total / (ms_p * 1e-3),
+           "padded_ms": ms_b, "padded_tokens_per_s": T_total / (ms_b * 1e-3),
+           "per_prompt_ms": ms_s, "per_prompt_tokens_per_s": T_total / (ms_s * 1e-3)}
+    del d, p, singles, ws_p, ws_b
+    torch.cuda.empty_cache()
+    log(f"varlen: {rec}")
+    return rec
+
+
 def run_prefill_legs() -> dict:
     """Each prefill workload on the chunked and the sequential arm: time of the whole
     arm (every kernel it launches), tokens/s, algorithmic HBM GB/s and, for the
@@ -492,6 +563,7 @@ def main():
     ap.add_argument("--no-verify", action="store_true")
     ap.add_argument("--no-gated", action="store_true")
     ap.add_argument("--no-gqa", action="store_true")
+    ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--copy-only", action="store_true",
                     help="only run the 1 GiB device copy (counter calibration)")
     ap.add_argument("--prefill-only", metavar="WORKLOAD",
@@ -564,6 +636,8 @@ def main():
         line["gated"] = run_gated_leg()
     if not args.no_gqa:
         line["gqa"] = run_gqa_leg()
+    if not args.no_varlen:
+        line["varlen"] = run_varlen_leg()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, inp)
     print(json.dumps(line), flush=True)

@@ -31,6 +31,9 @@ _GQA_PREFILL_ARGS = _GATED_PREFILL_ARGS[:20] + [_i] + _GATED_PREFILL_ARGS[20:]
 _GQA_DECODE_ARGS = _GATED_DECODE_ARGS[:20] + [_i] + _GATED_DECODE_ARGS[20:]
 _GQA_ROLLBACK_ARGS = _GATED_ROLLBACK_ARGS[:18] + [_i] + _GATED_ROLLBACK_ARGS[18:]
 KDA_GATE_GIVEN = 0
+# packed batches: cu_seqlens, N, T_total in place of B, T
+_VARLEN_KDA_ARGS = _GATED_PREFILL_ARGS[:17] + [_vp, _i, _i] + _GATED_PREFILL_ARGS[19:]
+_VARLEN_GDN_ARGS = _GQA_PREFILL_ARGS[:17] + [_vp, _i, _i] + _GQA_PREFILL_ARGS[19:]
 KDA_GATE_SIGMOID, KDA_GATE_SOFTPLUS = 1, 2
 EXPORTS = ("kda_prefill", "kda_decode", "gdn_prefill", "gdn_decode",
            "kda_prefill_workspace_bytes", "gdn_prefill_workspace_bytes",
@@ -38,7 +41,8 @@ EXPORTS = ("kda_prefill", "kda_decode", "gdn_prefill", "gdn_decode",
            "kda_rollback_workspace_bytes", "gdn_rollback_workspace_bytes", "kda_prefill_gated",
            "gdn_prefill_gated", "kda_decode_gated", "gdn_decode_gated", "kda_rollback_gated",
            "gdn_rollback_gated", "gdn_prefill_gqa", "gdn_decode_gqa", "gdn_rollback_gqa",
-           "gdn_gqa_workspace_bytes", "kda_status_string")
+           "gdn_gqa_workspace_bytes", "kda_prefill_varlen", "gdn_prefill_varlen",
+           "kda_prefill_varlen_workspace_bytes", "gdn_prefill_varlen_workspace_bytes", "kda_status_string")
 
 
 class KdaError(RuntimeError):
@@ -83,6 +87,12 @@ def lib() -> ctypes.CDLL:
         l.gdn_decode_gqa.argtypes, l.gdn_decode_gqa.restype = _GQA_DECODE_ARGS, _i
         l.gdn_rollback_gqa.argtypes, l.gdn_rollback_gqa.restype = _GQA_ROLLBACK_ARGS, _i
         l.gdn_gqa_workspace_bytes.argtypes, l.gdn_gqa_workspace_bytes.restype = [_i] * 7, _sz
+        l.kda_prefill_varlen.argtypes, l.kda_prefill_varlen.restype = _VARLEN_KDA_ARGS, _i
+        l.gdn_prefill_varlen.argtypes, l.gdn_prefill_varlen.restype = _VARLEN_GDN_ARGS, _i
+        l.kda_prefill_varlen_workspace_bytes.argtypes = [_i] * 6
+        l.kda_prefill_varlen_workspace_bytes.restype = _sz
+        l.gdn_prefill_varlen_workspace_bytes.argtypes = [_i] * 7
+        l.gdn_prefill_varlen_workspace_bytes.restype = _sz
         for n in ("kda_rollback_workspace_bytes", "gdn_rollback_workspace_bytes"):
             getattr(l, n).argtypes = [_i] * 5
             getattr(l, n).restype = _sz
@@ -343,3 +353,39 @@ def gdn_rollback_gqa(q, k, v, g, beta, conv_w, ring_snap, state_snap, conv_ring,
     if check and rc != 0:
         raise KdaError(rc, "gdn_rollback_gqa")
     return rc
+
+
+# ---------------------------------------------------------------- packed batches
+def varlen_workspace_bytes(N, T_total, H, D, dtype_code, mode=KDA_MODE_AUTO, gdn=False, Hk=None) -> int:
+    if gdn:
+        return int(lib().gdn_prefill_varlen_workspace_bytes(N, T_total, H, Hk or H, D, dtype_code, mode))
+    return int(lib().kda_prefill_varlen_workspace_bytes(N, T_total, H, D, dtype_code, mode))
+
+
+def prefill_varlen(q, k, v, g, beta, conv_w, conv_ring, state_in, state_out, z, norm_w, out, cu_seqlens,
+                   o_core=None, *, gdn=False, scale, rms_eps, mode=KDA_MODE_AUTO, workspace=None, gate_a=None,
+                   gate_bias=None, gate_form=KDA_GATE_GIVEN, gate_lb=0.0, stream=None, check=True):
+    """Packed variable-length prefill (include/kda.h): activations [T_total][...], the
+    int32 device tensor cu_seqlens [N+1], ring / state [N][...]. Hk (GDN) is read off
+    q's width."""
+    N, H, D = state_in.shape[0], state_in.shape[1], state_in.shape[2]
+    T_total, K = v.shape[-2], conv_w.shape[1]
+    assert cu_seqlens.dtype == torch_int32() and cu_seqlens.numel() == N + 1, "cu_seqlens: int32 [N+1]"
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    head = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(gate_a), _ptr(gate_bias), float(gate_lb),
+            int(gate_form), _ptr(conv_w), _ptr(conv_ring), _ptr(state_in), _ptr(state_out), _ptr(z),
+            _ptr(norm_w), _ptr(out), _ptr(o_core), _ptr(cu_seqlens), N, T_total, H)
+    tail = (D, K, float(scale), float(rms_eps), _dtype_code(v), int(mode), _ptr(workspace), ws_bytes,
+            _stream_handle(stream))
+    if gdn:
+        rc = lib().gdn_prefill_varlen(*head, q.shape[-1] // D, *tail)
+    else:
+        rc = lib().kda_prefill_varlen(*head, *tail)
+    if check and rc != 0:
+        raise KdaError(rc, "gdn_prefill_varlen" if gdn else "kda_prefill_varlen")
+    return rc
+
+
+def torch_int32():
+    import torch
+    return torch.int32

@@ -56,10 +56,23 @@ int pick_arm(int B, int T, int H, int D, bool bf16, int mode) {
 // Query / key heads: a divisor of the value heads H (grouped heads, GDN only).
 int check_heads(int H, int Hk) { return Hk >= 1 && Hk <= H && H % Hk == 0 ? KDA_OK : KDA_ERR_SHAPE; }
 
-size_t workspace_for(int B, int T, int H, int Hk, int D, bool gdn, int arm) {
+// Arm of a packed variable-length batch: the fused sequential arm (one workgroup per
+// (sequence, head), whatever the lengths) or the chunked arm; AUTO takes the chunked
+// arm for bf16 activations at D = 128.
+int pick_arm_varlen(int D, bool bf16, int mode) {
+    const bool chunk_ok = kda::kChunkedArmBuilt && D == 128;
+    if (mode == KDA_MODE_CHUNKED) return chunk_ok ? kda::ARM_CHUNKED : -1;
+    if (mode == KDA_MODE_AUTO && chunk_ok && bf16) return kda::ARM_CHUNKED;
+    if (mode != KDA_MODE_AUTO && mode != KDA_MODE_SEQUENTIAL) return -1;
+    return kda::ARM_SEQ_FUSED;
+}
+
+// rows: activation rows of all sequences (B*T, or T for a packed batch).
+size_t workspace_for(int B, int T, int H, int Hk, int D, bool gdn, int arm, size_t rows = 0) {
+    if (rows == 0) rows = (size_t)B * T;
     switch (arm) {
         case kda::ARM_SEQ_SPLIT: return kda::split_workspace(B, T, H, Hk, D, gdn).total;
-        case kda::ARM_CHUNKED: return kda::chunked_workspace_bytes(B, T, H, D, gdn);
+        case kda::ARM_CHUNKED: return kda::chunked_workspace_bytes(B, rows, H, D);
         default: return 0;
     }
 }
@@ -68,10 +81,14 @@ int validate(const MixerArgs& a, bool decode, int mode, int* arm_out) {
     if (!a.q || !a.k || !a.v || !a.g || !a.beta || !a.conv_w || !a.ring || !a.state_in ||
         !a.state_out || !a.z || !a.norm_w || !a.out)
         return KDA_ERR_NULL;
-    int rc = check_shape(a.B, a.T, a.H, a.D, a.K);
+    const bool packed = a.cu_seqlens != nullptr;
+    // a packed batch: B sequences (the state / ring / grid dimension), T rows in all
+    int rc = packed ? check_shape(1, a.T, a.H, a.D, a.K) : check_shape(a.B, a.T, a.H, a.D, a.K);
+    if (!rc && packed) rc = check_shape(a.B, 1, a.H, a.D, a.K);
     if (rc) return rc;
     if (decode && a.T != 1) return KDA_ERR_DECODE_T;
-    const int arm = decode ? (int)kda::ARM_SEQ_FUSED : pick_arm(a.B, a.T, a.H, a.D, a.bf16, mode);
+    const int arm = decode ? (int)kda::ARM_SEQ_FUSED
+                           : (packed ? pick_arm_varlen(a.D, a.bf16, mode) : pick_arm(a.B, a.T, a.H, a.D, a.bf16, mode));
     if (arm < 0) return KDA_ERR_DTYPE_MODE;
 
     if (a.gate_form != kda::GATE_GIVEN && (!a.gate_a || !a.gate_bias)) return KDA_ERR_NULL;
@@ -79,27 +96,29 @@ int validate(const MixerArgs& a, bool decode, int mode, int* arm_out) {
                           a.state_out, a.z, a.norm_w, a.out, a.o_core, a.ws, a.gate_a, a.gate_bias};
     for (const void* p : ptrs)
         if (p && ((uintptr_t)p & 15u)) return KDA_ERR_ALIGN;
+    if (packed && ((uintptr_t)a.cu_seqlens & 3u)) return KDA_ERR_ALIGN;
 
     const size_t es = a.bf16 ? 2 : 4;
     const size_t qkv = (size_t)a.H * a.D;
-    const size_t act = (size_t)a.B * a.T * qkv;
-    const size_t kact = (size_t)a.B * a.T * a.Hk * a.D;  // q, k
+    const size_t rows = kda::total_rows(a);
+    const size_t act = rows * qkv;
+    const size_t kact = rows * a.Hk * a.D;  // q, k
     const size_t rrows = kda::ring_rows(a);
-    const size_t gate_n = a.gdn ? (size_t)a.B * a.T * a.H : act;
+    const size_t gate_n = a.gdn ? rows * a.H : act;
     const size_t state_n = (size_t)a.B * a.H * a.D * a.D;
-    const size_t need_ws = workspace_for(a.B, a.T, a.H, a.Hk, a.D, a.gdn, arm);
+    const size_t need_ws = workspace_for(a.B, a.T, a.H, a.Hk, a.D, a.gdn, arm, rows);
     if (need_ws > 0 && (!a.ws || a.ws_bytes < need_ws)) return KDA_ERR_WORKSPACE;
 
     auto R = [](const void* p, size_t bytes, bool w, int id) {
         return Range{(uintptr_t)p, (uintptr_t)p + bytes, w, id};
     };
-    Range rs[16];
+    Range rs[17];
     int n = 0;
     rs[n++] = R(a.q, kact * es, false, 0);
     rs[n++] = R(a.k, kact * es, false, 1);
     rs[n++] = R(a.v, act * es, false, 2);
     rs[n++] = R(a.g, gate_n * es, false, 3);
-    rs[n++] = R(a.beta, (size_t)a.B * a.T * a.H * es, false, 4);
+    rs[n++] = R(a.beta, rows * a.H * es, false, 4);
     rs[n++] = R(a.conv_w, rrows * a.K * 4, false, 5);
     rs[n++] = R(a.ring, (size_t)a.B * rrows * (a.K - 1) * 4, true, 6);
     rs[n++] = R(a.state_in, state_n * 4, false, 7);
@@ -113,6 +132,7 @@ int validate(const MixerArgs& a, bool decode, int mode, int* arm_out) {
         rs[n++] = R(a.gate_a, (size_t)a.H * 4, false, 14);
         rs[n++] = R(a.gate_bias, (a.gdn ? (size_t)a.H : qkv) * 4, false, 15);
     }
+    if (packed) rs[n++] = R(a.cu_seqlens, ((size_t)a.B + 1) * 4, false, 16);
     for (int i = 0; i < n; ++i)
         for (int j = i + 1; j < n; ++j) {
             if (!(rs[i].writable || rs[j].writable) || !overlaps(rs[i], rs[j])) continue;
@@ -146,7 +166,8 @@ int entry(bool gdn, bool decode, const void* q, const void* k, const void* v, co
           const void* beta, const float* conv_w, float* conv_ring, const float* state_in,
           float* state_out, const void* z, const float* norm_w, void* out, float* o_core,
           int B, int T, int H, int D, int K, float scale, float rms_eps, int dtype, int mode,
-          void* workspace, size_t workspace_bytes, void* stream, GateArgs ga = kGiven, int Hk = 0) {
+          void* workspace, size_t workspace_bytes, void* stream, GateArgs ga = kGiven, int Hk = 0,
+          const int* cu_seqlens = nullptr) {
     if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return KDA_ERR_DTYPE_MODE;
     if (ga.form != kda::GATE_GIVEN && ga.form != KDA_GATE_SIGMOID && ga.form != KDA_GATE_SOFTPLUS)
         return KDA_ERR_DTYPE_MODE;
@@ -155,7 +176,7 @@ int entry(bool gdn, bool decode, const void* q, const void* k, const void* v, co
     MixerArgs a{q, k, v, g, beta, conv_w, conv_ring, state_in, state_out, z, norm_w, out,
                 o_core, B, T, H, D, K, scale, rms_eps, dtype == KDA_DTYPE_BF16, gdn,
                 workspace, workspace_bytes, (hipStream_t)stream, T, true,
-                ga.form, ga.a, ga.bias, ga.lb, Hk};
+                ga.form, ga.a, ga.bias, ga.lb, Hk, cu_seqlens};
     if (ga.form == kda::GATE_GIVEN) {
         // Kernels read the gate parameters without a branch; point them at conv_w
         // (3*H*D*K >= H*D floats, allocated and 16-byte aligned), values unused.
@@ -240,7 +261,7 @@ int rollback(bool gdn, const void* q, const void* k, const void* v, const void* 
     }
     MixerArgs a{q, k, v, g, beta, conv_w, conv_ring, state_snap, state_out, nullptr, nullptr, nullptr,
                 nullptr, B, keep, H, D, K, 1.0f, 0.0f, bf16, gdn, workspace, workspace_bytes,
-                (hipStream_t)stream, T_stash, false, ga.form, conv_w, conv_w, ga.lb, Hk};
+                (hipStream_t)stream, T_stash, false, ga.form, conv_w, conv_w, ga.lb, Hk, nullptr};
     if (ga.form != kda::GATE_GIVEN) {
         a.gate_a = ga.a;
         a.gate_bias = ga.bias;
@@ -401,6 +422,44 @@ int gdn_rollback_gqa(const void* q, const void* k, const void* v, const void* g,
     return rollback(true, q, k, v, g, beta, conv_w, ring_snap, state_snap, conv_ring, state_out, B,
                     T_stash, keep, H, D, K, dtype, workspace, workspace_bytes, stream,
                     GateArgs{gate_form, gate_a, gate_bias, gate_lb}, Hk);
+}
+
+int kda_prefill_varlen(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                       const float* gate_a, const float* gate_bias, float gate_lb, int gate_form,
+                       const float* conv_w, float* conv_ring, const float* state_in, float* state_out,
+                       const void* z, const float* norm_w, void* out, float* o_core, const int* cu_seqlens,
+                       int N, int T_total, int H, int D, int K, float scale, float rms_eps, int dtype,
+                       int mode, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!cu_seqlens) return KDA_ERR_NULL;
+    return entry(false, false, q, k, v, g, beta, conv_w, conv_ring, state_in, state_out, z, norm_w, out,
+                 o_core, N, T_total, H, D, K, scale, rms_eps, dtype, mode, workspace, workspace_bytes, stream,
+                 GateArgs{gate_form, gate_a, gate_bias, gate_lb}, H, cu_seqlens);
+}
+
+int gdn_prefill_varlen(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                       const float* gate_a, const float* gate_bias, float gate_lb, int gate_form,
+                       const float* conv_w, float* conv_ring, const float* state_in, float* state_out,
+                       const void* z, const float* norm_w, void* out, float* o_core, const int* cu_seqlens,
+                       int N, int T_total, int H, int Hk, int D, int K, float scale, float rms_eps,
+                       int dtype, int mode, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!cu_seqlens) return KDA_ERR_NULL;
+    if (Hk < 1) return KDA_ERR_SHAPE;
+    return entry(true, false, q, k, v, g, beta, conv_w, conv_ring, state_in, state_out, z, norm_w, out,
+                 o_core, N, T_total, H, D, K, scale, rms_eps, dtype, mode, workspace, workspace_bytes, stream,
+                 GateArgs{gate_form, gate_a, gate_bias, gate_lb}, Hk, cu_seqlens);
+}
+
+size_t kda_prefill_varlen_workspace_bytes(int N, int T_total, int H, int D, int dtype, int mode) {
+    if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return (size_t)-1;
+    if (check_shape(1, T_total, H, D, 4) || check_shape(N, 1, H, D, 4)) return (size_t)-1;
+    const int arm = pick_arm_varlen(D, dtype == KDA_DTYPE_BF16, mode);
+    if (arm < 0) return (size_t)-1;
+    return workspace_for(N, T_total, H, H, D, false, arm, (size_t)T_total);
+}
+
+size_t gdn_prefill_varlen_workspace_bytes(int N, int T_total, int H, int Hk, int D, int dtype, int mode) {
+    if (check_heads(H, Hk)) return (size_t)-1;
+    return kda_prefill_varlen_workspace_bytes(N, T_total, H, D, dtype, mode);  // q / k not staged
 }
 
 size_t gdn_gqa_workspace_bytes(int B, int T, int H, int Hk, int D, int dtype, int mode) {

@@ -235,14 +235,14 @@ struct ChunkRaw {
 // Parts of one chunk's rows, so that the requests can be spread over the phases of
 // the previous chunk: a burst of all of them stalls every wavefront at the issue.
 enum RawPart { RAW_Q, RAW_K, RAW_G, RAW_V, RAW_BETA };
+// rowb, T: first activation row and row count (>= 1) of the sequence.
 template <bool BF, bool GDN, int NC, RawPart PART>
-__device__ __forceinline__ void load_raw_part(ChunkRaw<GDN, NC>& cr, const MixerArgs& a, int b, int h,
-                                              int c0, int jv0, int tid) {
+__device__ __forceinline__ void load_raw_part(ChunkRaw<GDN, NC>& cr, const MixerArgs& a, size_t rowb, int T,
+                                              int h, int c0, int jv0, int tid) {
     using CR = ChunkRaw<GDN, NC>;
-    const int T = a.T, H = a.H;
+    const int H = a.H;
     const size_t qkv = (size_t)H * DK, head_off = (size_t)h * DK;
     const size_t kw = (size_t)a.Hk * DK, khead = (size_t)(h % a.Hk) * DK;  // q / k: key head
-    const size_t rowb = (size_t)b * T;
     if constexpr (PART == RAW_Q || PART == RAW_K || PART == RAW_G) {
         if constexpr (PART == RAW_G && GDN) return;
 #pragma unroll
@@ -268,13 +268,13 @@ __device__ __forceinline__ void load_raw_part(ChunkRaw<GDN, NC>& cr, const Mixer
     }
 }
 template <bool BF, bool GDN, int NC>
-__device__ __forceinline__ void load_raw(ChunkRaw<GDN, NC>& cr, const MixerArgs& a, int b, int h,
-                                         int c0, int jv0, int tid) {
-    load_raw_part<BF, GDN, NC, RAW_Q>(cr, a, b, h, c0, jv0, tid);
-    load_raw_part<BF, GDN, NC, RAW_K>(cr, a, b, h, c0, jv0, tid);
-    load_raw_part<BF, GDN, NC, RAW_G>(cr, a, b, h, c0, jv0, tid);
-    load_raw_part<BF, GDN, NC, RAW_V>(cr, a, b, h, c0, jv0, tid);
-    load_raw_part<BF, GDN, NC, RAW_BETA>(cr, a, b, h, c0, jv0, tid);
+__device__ __forceinline__ void load_raw(ChunkRaw<GDN, NC>& cr, const MixerArgs& a, size_t rowb, int T,
+                                         int h, int c0, int jv0, int tid) {
+    load_raw_part<BF, GDN, NC, RAW_Q>(cr, a, rowb, T, h, c0, jv0, tid);
+    load_raw_part<BF, GDN, NC, RAW_K>(cr, a, rowb, T, h, c0, jv0, tid);
+    load_raw_part<BF, GDN, NC, RAW_G>(cr, a, rowb, T, h, c0, jv0, tid);
+    load_raw_part<BF, GDN, NC, RAW_V>(cr, a, rowb, T, h, c0, jv0, tid);
+    load_raw_part<BF, GDN, NC, RAW_BETA>(cr, a, rowb, T, h, c0, jv0, tid);
 }
 
 // The raw rows of a chunk (n valid rows) from registers into LDS; the gates and beta
@@ -510,7 +510,10 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
     const int wave = tid >> 6;
     int q4 = lane >> 4, l16 = lane & 15;
     const int b = bh / a.H, h = bh % a.H;
-    const int T = a.T, K = a.K;
+    const int K = a.K;
+    size_t rowb;  // first activation row of this sequence
+    int T;        // its row count
+    seq_span(a, b, &rowb, &T);
     // Re-materialise the lane indices at every phase: otherwise the compiler hoists
     // each phase's lane-dependent LDS addresses out of the chunk loop and keeps them
     // all alive at once, which overflows the register file.
@@ -582,14 +585,23 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
         }
     }
 
+    if (T == 0) {  // an empty sequence of a packed batch: the state passes through
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb) {
+            const int jv = jv0 + jb * 16 + l16;
+            *reinterpret_cast<f32x4v*>(&a.state_out[((size_t)bh * DK + jv) * DK + 16 * wave + 4 * q4]) = accS[jb];
+        }
+        return;  // uniform over the workgroup, before any barrier
+    }
+
     CR raw;
-    load_raw<BF, GDN, NC>(raw, a, b, h, 0, jv0, tid);
+    load_raw<BF, GDN, NC>(raw, a, rowb, T, h, 0, jv0, tid);
     store_raw<GDN, NC, ACT>(sm, raw, min(CH, T), tid, a, cg);
     __syncthreads();
 
     for (int c0 = 0; c0 < T; c0 += CH) {
         const int n = min(CH, T - c0);
-        const size_t row0 = (size_t)b * T + c0;
+        const size_t row0 = rowb + c0;
 
         KDA_LAUNDER_LANE();
         // ---- P0: conv taps and norm weight (re-read every chunk: a few L2-resident
@@ -807,7 +819,7 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
         // (unconditional, like the store into LDS at the end of the iteration: past the
         // last chunk the rows clamp to T-1 and are never used, and a branch would make
         // the compiler wait for every outstanding load and store at its join)
-        load_raw_part<BF, GDN, NC, RAW_Q>(raw, a, b, h, c0 + CH, jv0, tid);
+        load_raw_part<BF, GDN, NC, RAW_Q>(raw, a, rowb, T, h, c0 + CH, jv0, tid);
         KDA_LAUNDER_LANE();
         // ---- P3: T = (I + A)^-1, A = diag(beta) L, in 16x16 blocks; meanwhile the v conv ----
         if (wave < 4) {
@@ -895,7 +907,7 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
         lds_barrier();
 
         KDA_LAUNDER_LANE();
-        load_raw_part<BF, GDN, NC, RAW_K>(raw, a, b, h, c0 + CH, jv0, tid);
+        load_raw_part<BF, GDN, NC, RAW_K>(raw, a, rowb, T, h, c0 + CH, jv0, tid);
         // ---- P4: W = T (beta e^{G} k) -> -W in LDS (key block `wave`);
         //      U = T (beta v) in registers (rows 16*sw.., value blocks of half hv) ----
         if (n == CH) {  // the last KT-1 raw v rows become the next chunk's history
@@ -943,7 +955,7 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
         lds_barrier();
 
         KDA_LAUNDER_LANE();
-        load_raw_part<BF, GDN, NC, RAW_G>(raw, a, b, h, c0 + CH, jv0, tid);
+        load_raw_part<BF, GDN, NC, RAW_G>(raw, a, rowb, T, h, c0 + CH, jv0, tid);
         // ---- P5: S^T to LDS in bf16, then Ub = U - W S ----
 #pragma unroll
         for (int jb = 0; jb < NJB; ++jb) {
@@ -973,8 +985,8 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
         lds_barrier();
 
         KDA_LAUNDER_LANE();
-        load_raw_part<BF, GDN, NC, RAW_V>(raw, a, b, h, c0 + CH, jv0, tid);
-        load_raw_part<BF, GDN, NC, RAW_BETA>(raw, a, b, h, c0 + CH, jv0, tid);
+        load_raw_part<BF, GDN, NC, RAW_V>(raw, a, rowb, T, h, c0 + CH, jv0, tid);
+        load_raw_part<BF, GDN, NC, RAW_BETA>(raw, a, rowb, T, h, c0 + CH, jv0, tid);
         // ---- P6: O = scale (Q+ S + P Ub), rows 16*sw.., value blocks of half hv ----
         f32x4v accO[NJB2];
         {
@@ -1160,10 +1172,9 @@ hipError_t chunk_launch(const MixerArgs& a) {
 
 }  // namespace
 
-size_t chunked_workspace_bytes(int B, int T, int H, int D, bool gdn) {
-    (void)gdn;
-    if (D != DK || chunk_ncol(B, H) == 1) return 0;
-    return align256((size_t)B * T * H * D * 4);  // fp32 pre-norm output of the column splits
+size_t chunked_workspace_bytes(int nseq, size_t rows, int H, int D) {
+    if (D != DK || chunk_ncol(nseq, H) == 1) return 0;
+    return align256(rows * H * D * 4);  // fp32 pre-norm output of the column splits
 }
 
 hipError_t launch_chunked(const MixerArgs& a) {

@@ -48,7 +48,30 @@ struct MixerArgs {
     // h % Hk. q and k rows are Hk*D wide; v, z, out, o_core rows H*D; the conv
     // weight and ring planes are q (Hk*D rows), k (Hk*D), v (H*D), in that order.
     int Hk;
+    // Packed variable-length batch (null: B sequences of T rows each). Sequence b holds
+    // rows cu_seqlens[b] .. cu_seqlens[b+1]-1 of the [T][...] activations, T being the
+    // total row count; its ring and state slots are b as usual.
+    const int* cu_seqlens;
 };
+
+// Activation rows of all sequences of a call.
+__host__ __device__ inline size_t total_rows(const MixerArgs& a) {
+    return a.cu_seqlens ? (size_t)a.T : (size_t)a.B * a.T;
+}
+// First row and row count of sequence b. Offsets of a packed batch are clamped into
+// [0, T] and made non-decreasing, so a malformed table cannot send a kernel outside
+// the activations (its results are then meaningless, but every access stays in bounds).
+__device__ inline void seq_span(const MixerArgs& a, int b, size_t* start, int* len) {
+    if (a.cu_seqlens) {
+        const int s0 = min(max(a.cu_seqlens[b], 0), a.T);
+        const int s1 = min(max(a.cu_seqlens[b + 1], s0), a.T);
+        *start = (size_t)s0;
+        *len = s1 - s0;
+    } else {
+        *start = (size_t)b * a.tp;
+        *len = a.T;
+    }
+}
 
 // Conv-weight / ring row of channel ch of plane (0 q, 1 k, 2 v) for value head h.
 __host__ __device__ inline size_t plane_row(const MixerArgs& a, int plane, int h, int ch) {
@@ -74,8 +97,8 @@ SplitWorkspace split_workspace(int B, int T, int H, int Hk, int D, bool gdn);
 // Whether this build carries the chunked prefill arm.
 extern const bool kChunkedArmBuilt;
 
-// Workspace of the chunked arm.
-size_t chunked_workspace_bytes(int B, int T, int H, int D, bool gdn);
+// Workspace of the chunked arm: nseq sequences of H heads, rows activation rows in all.
+size_t chunked_workspace_bytes(int nseq, size_t rows, int H, int D);
 
 // Launchers: enqueue on a.stream, return the first launch error (hipSuccess if none).
 hipError_t launch_seq_fused(const MixerArgs& a);

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(fused_threads<D>()) void seq_fused_kernel(MixerArgs
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
-    const int H = a.H, T = a.T, K = a.K;
+    const int H = a.H, K = a.K;
     const size_t qkv = (size_t)H * D;
     const size_t head_off = (size_t)h * D;
     const int grp = wave * 8 + (lane >> 3), s = lane & 7;
@@ -74,6 +74,10 @@ __global__ __launch_bounds__(fused_threads<D>()) void seq_fused_kernel(MixerArgs
     static_assert(NT % D == 0, "one gate column per thread");
     const GateCol gp = gate_col(a, h, GDN ? h : head_off + tid % D);
 
+    size_t rstart;  // first activation row of this sequence
+    int T;          // its row count
+    seq_span(a, b, &rstart, &T);
+
     // Conv windows of this head's 3*D (plane, channel) rows start as the old ring.
     for (int r = tid; r < 3 * D; r += NT) {
         const int plane = r / D, ch = r % D;
@@ -86,7 +90,7 @@ __global__ __launch_bounds__(fused_threads<D>()) void seq_fused_kernel(MixerArgs
 
     for (int t0 = 0; t0 < T; t0 += TB_FUSED) {
         const int nt = min(TB_FUSED, T - t0);
-        const size_t row0 = (size_t)b * a.tp + t0;  // tp == T whenever the readout is produced
+        const size_t row0 = rstart + t0;
         for (int r = tid; r < 3 * D; r += NT) {
             const int plane = r / D, ch = r % D;
             const void* xsrc = plane == 0 ? a.q : (plane == 1 ? a.k : a.v);
@@ -305,7 +309,7 @@ __global__ __launch_bounds__(8 * split_cols<D>()) void scan_split_kernel(
 template <int D, bool BF, bool GDN>
 __global__ __launch_bounds__(256) void norm_kernel(MixerArgs a, const float* o) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const size_t rows = (size_t)a.B * a.T * a.H;
+    const size_t rows = total_rows(a) * a.H;
     const size_t row = (size_t)blockIdx.x * 4 + wave;
     if (row >= rows) return;
     const size_t off = (row / a.H) * ((size_t)a.H * D) + (row % a.H) * D;
@@ -324,6 +328,7 @@ hipError_t fused_launch(const MixerArgs& a) {
 
 template <int D, bool BF, bool GDN>
 hipError_t split_launch(const MixerArgs& a) {
+    if (a.cu_seqlens) return hipErrorInvalidValue;  // packed batches take the fused arm
     const SplitWorkspace w = split_workspace(a.B, a.T, a.H, a.Hk, a.D, a.gdn);
     char* base = static_cast<char*>(a.ws);
     float* qh = reinterpret_cast<float*>(base + w.qh);
@@ -404,13 +409,16 @@ __global__ __launch_bounds__(256) void ring_roll_kernel(MixerArgs a, int rows_pe
     const size_t ch = plane < 2 ? cf - plane * kw : cf - 2 * kw;
     const size_t xw = plane < 2 ? kw : vw;
     const void* x = plane == 0 ? a.q : (plane == 1 ? a.k : a.v);
-    const int K = a.K, T = a.T;
+    const int K = a.K;
+    size_t rstart;
+    int T;
+    seq_span(a, b, &rstart, &T);
     float* ring_row = a.ring + ((size_t)b * ring_rows(a) + cf) * (K - 1);
     float nr[KMAX - 1];
 #pragma unroll
     for (int d = 1; d < KMAX; ++d) {
         const int pos = T - d;
-        nr[KMAX - 1 - d] = (d <= K - 1) ? (pos >= 0 ? ld_act<BF>(x, ((size_t)b * a.tp + pos) * xw + ch)
+        nr[KMAX - 1 - d] = (d <= K - 1) ? (pos >= 0 ? ld_act<BF>(x, (rstart + pos) * xw + ch)
                                                      : ring_row[pos + K - 1])
                                         : 0.0f;
     }
@@ -433,7 +441,7 @@ hipError_t launch_ring_roll(const MixerArgs& a, bool qk_only) {
 hipError_t launch_seq_fused(const MixerArgs& a) { return dispatch<FusedOp>(a); }
 
 hipError_t launch_norm(const MixerArgs& a, const float* o) {
-    const size_t rows = (size_t)a.B * a.T * a.H;
+    const size_t rows = total_rows(a) * a.H;
     const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
     if (a.D == 128) {
         if (a.bf16) {

@@ -300,6 +300,49 @@ int gdn_rollback_gqa(const void* q, const void* k, const void* v, const void* g,
                      int K, int dtype, void* workspace, size_t workspace_bytes, void* stream);
 size_t gdn_gqa_workspace_bytes(int B, int T, int H, int Hk, int D, int dtype, int mode);
 
+/*
+ * Packed variable-length prefill: N sequences of different lengths in one call, their
+ * rows packed back to back (no padding). Sequence n holds activation rows
+ * cu_seqlens[n] .. cu_seqlens[n+1]-1; its conv ring and state are slot n.
+ *   cu_seqlens [N+1] int32 DEVICE array, non-decreasing from 0 to T_total (4-byte
+ *              aligned; a sequence may be empty: its ring and state pass through).
+ *              The kernels clamp every offset into [0, T_total], so a malformed table
+ *              cannot make them read or write outside the buffers, but the results
+ *              are then meaningless; the table is not checked on the host.
+ *   q, k       [T_total][Hk*D]; v, z, out [T_total][H*D]; o_core [T_total][H*D] fp32
+ *   g          [T_total][H*D] (KDA) or [T_total][H] (GDN); beta [T_total][H]
+ *   conv_ring  [N][(2*Hk + H)*D][K-1]; state_in / state_out [N][H][D][D]
+ * Hk: query / key heads (gdn_prefill_varlen; Hk divides H, Hk = H is the plain
+ * layout; kda_prefill_varlen has Hk = H). gate_form / gate_a / gate_bias / gate_lb
+ * as for gdn_prefill_gqa (0: g and beta given).
+ * Arms: KDA_MODE_SEQUENTIAL runs the fused sequential arm (one workgroup per
+ * (sequence, head)); KDA_MODE_CHUNKED the chunked arm (D = 128); KDA_MODE_AUTO the
+ * chunked arm for bf16 activations at D = 128, else the fused arm. Each sequence is
+ * processed exactly as a call on that sequence alone would process it on the same arm
+ * (the fused arm bit for bit). workspace: at least *_prefill_varlen_workspace_bytes
+ * bytes (the chunked arm with N*H < 256 needs one). null cu_seqlens is KDA_ERR_NULL;
+ * everything else as for kda_prefill.
+ */
+int kda_prefill_varlen(const void* q, const void* k, const void* v, const void* g,
+                       const void* beta, const float* gate_a, const float* gate_bias,
+                       float gate_lb, int gate_form, const float* conv_w, float* conv_ring,
+                       const float* state_in, float* state_out, const void* z,
+                       const float* norm_w, void* out, float* o_core, const int* cu_seqlens,
+                       int N, int T_total, int H, int D, int K, float scale, float rms_eps,
+                       int dtype, int mode, void* workspace, size_t workspace_bytes,
+                       void* stream);
+int gdn_prefill_varlen(const void* q, const void* k, const void* v, const void* g,
+                       const void* beta, const float* gate_a, const float* gate_bias,
+                       float gate_lb, int gate_form, const float* conv_w, float* conv_ring,
+                       const float* state_in, float* state_out, const void* z,
+                       const float* norm_w, void* out, float* o_core, const int* cu_seqlens,
+                       int N, int T_total, int H, int Hk, int D, int K, float scale,
+                       float rms_eps, int dtype, int mode, void* workspace,
+                       size_t workspace_bytes, void* stream);
+size_t kda_prefill_varlen_workspace_bytes(int N, int T_total, int H, int D, int dtype, int mode);
+size_t gdn_prefill_varlen_workspace_bytes(int N, int T_total, int H, int Hk, int D, int dtype,
+                                          int mode);
+
 /* Static description of a status code (never NULL). */
 const char* kda_status_string(int rc);
 

@@ -285,3 +285,51 @@ def test_gqa_queries():
     assert 0 < kda.gqa_workspace_bytes(1, 100, 4, 2, 16, 0, 1) < full
     assert kda.gqa_workspace_bytes(1, 100, 4, 3, 16, 0, 1) == ctypes.c_size_t(-1).value
     assert kda.gqa_workspace_bytes(1, 100, 4, 0, 16, 0, 1) == ctypes.c_size_t(-1).value
+
+
+def call_varlen(a, gdn=False, N=2, T_total=5, cu=None, mode=1, Hk=None):
+    L = kda.lib()
+    head = (a["q"], a["k"], a["v"], a["g"], a["beta"], a["gate_a"], a["gate_bias"], 0.0, 0, a["conv_w"],
+            a["ring"], a["state_in"], a["state_out"], a["z"], a["norm_w"], a["out"], a["o_core"],
+            a["ws"] if cu is None else cu, N, T_total, a["H"])
+    tail = (a["D"], a["K"], 0.25, 1e-5, a["dtype"], mode, a["ws"], a["ws_bytes"], None)
+    if gdn:
+        return L.gdn_prefill_varlen(*head, a["H"] if Hk is None else Hk, *tail)
+    return L.kda_prefill_varlen(*head, *tail)
+
+
+# the offsets table sits in the slot named "ws" unless a case places it (cu=...)
+VARLEN_CASES = [
+    ("null cu_seqlens", dict(), dict(cu=0), 40001),
+    ("misaligned cu_seqlens", dict(), dict(cu=BASE + 13 * (1 << 32) + 2), 40007),
+    ("out over cu_seqlens", dict(out=BASE + 13 * (1 << 32)), dict(), 40009),
+    ("T_total 0", dict(), dict(T_total=0), 40004),
+    ("N 0", dict(), dict(N=0), 40004),
+    ("chunked at D=16", dict(), dict(mode=2), 40008),
+    ("mode 7", dict(), dict(mode=7), 40008),
+]
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="fake pointers only where no GPU is visible")
+@pytest.mark.parametrize("gdn", [False, True])
+@pytest.mark.parametrize("what,over,kw,rc", VARLEN_CASES, ids=[c[0] for c in VARLEN_CASES])
+def test_varlen_contract(what, over, kw, rc, gdn):
+    a = fake_args()
+    a.update(over)
+    assert call_varlen(a, gdn, **kw) == rc
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="fake pointers only where no GPU is visible")
+def test_varlen_gqa_heads_checked():
+    a = fake_args(H=4)
+    assert call_varlen(a, True, Hk=3) == 40004
+    assert call_varlen(a, True, Hk=0) == 40004
+
+
+def test_varlen_queries():
+    # fused arm: no workspace; chunked arm with N*H < 256: fp32 pre-norm rows of all tokens
+    assert kda.varlen_workspace_bytes(3, 500, 4, 16, 0, 1) == 0
+    assert kda.varlen_workspace_bytes(3, 500, 4, 128, 1, 2) == 500 * 4 * 128 * 4
+    assert kda.varlen_workspace_bytes(64, 500, 4, 128, 1, 2) == 0  # N*H = 256: one split
+    assert kda.varlen_workspace_bytes(3, 500, 4, 16, 0, 2) == ctypes.c_size_t(-1).value
+    assert kda.varlen_workspace_bytes(3, 500, 4, 128, 1, 2, gdn=True, Hk=3) == ctypes.c_size_t(-1).value
