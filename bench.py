@@ -276,6 +276,21 @@ def run_verify_leg(T_stash: int = 8, keep: int = 4, reps: int = 20) -> dict:
     return rec
 
 
+def _timed(fn, reps):
+    """Median HIP-event time (ms) of fn(i) over reps calls after one untimed call."""
+    import torch
+
+    fn(0)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        fn(i)
+        b.record()
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+
+
 def _timed_pair(fa, fb, reps):
     """Median HIP-event times (ms) of fa(i) and fb(i), interleaved call by call (so that
     clock or cache drift affects both alike), after one untimed call of each."""
@@ -411,7 +426,7 @@ def run_gqa_leg(reps: int = 50) -> dict:
     B, H, D, K, kw, vw = cfg.B, cfg.H, cfg.D, cfg.K, cfg.kw, cfg.qkv
     nb = (2 * B * H * D * D * 4 + 2 * B * cfg.conv_rows * (K - 1) * 4
           + (2 * B * kw + 3 * B * vw + 2 * B * H) * 2 + cfg.conv_rows * K * 4 + D * 4)
-    ms, _ = _timed_pair(dec, lambda i=0: None, reps)
+    ms = _timed(dec, reps)
     rec["decode"] = {"workload": f"GDN decode B={B} H={H} Hk={cfg.hk} D={D} bf16", "ms": ms,
                      "tokens_per_s": B / (ms * 1e-3), "hbm_gbs": nb / (ms * 1e-3) / 1e9,
                      "hbm_frac": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": nb}
@@ -432,7 +447,7 @@ def run_gqa_leg(reps: int = 50) -> dict:
                             d["z"], d["norm_w"], d["out"], None, scale=scale, rms_eps=RMS_EPS, mode=mode,
                             workspace=ws)
 
-    ms, _ = _timed_pair(pre, lambda i=0: None, 5)
+    ms = _timed(pre, 5)
     B, T, H, kw, vw = cfg.B, cfg.T, cfg.H, cfg.kw, cfg.qkv
     nb = ((2 * kw + 3 * vw + 2 * H) * B * T * 2 + 2 * B * H * D * D * 4 + 2 * B * cfg.conv_rows * (K - 1) * 4
           + cfg.conv_rows * K * 4 + D * 4)
@@ -505,7 +520,7 @@ def run_varlen_leg() -> dict:
                             mode=mode, workspace=o["ws"])
 
     ms_p, ms_b = _timed_pair(packed, padded, 5)
-    ms_s, _ = _timed_pair(per_prompt, lambda i=0: None, 5)
+    ms_s = _timed(per_prompt, 5)
     rec = {"workload": f"KDA chunked prefill H={cfg.H} D={cfg.D} bf16, {N} prompts of {int(lens.min())}.."
                        f"{Tm} tokens ({T_total} in all)", "lengths": [int(x) for x in lens],
            "packed_ms": ms_p, "packed_tokens_per_s": T_total / (ms_p * 1e-3),

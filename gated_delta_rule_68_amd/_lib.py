@@ -368,9 +368,12 @@ def prefill_varlen(q, k, v, g, beta, conv_w, conv_ring, state_in, state_out, z, 
     """Packed variable-length prefill (include/kda.h): activations [T_total][...], the
     int32 device tensor cu_seqlens [N+1], ring / state [N][...]. Hk (GDN) is read off
     q's width."""
+    import torch
+
     N, H, D = state_in.shape[0], state_in.shape[1], state_in.shape[2]
     T_total, K = v.shape[-2], conv_w.shape[1]
-    assert cu_seqlens.dtype == torch_int32() and cu_seqlens.numel() == N + 1, "cu_seqlens: int32 [N+1]"
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.numel() != N + 1 or not cu_seqlens.is_contiguous():
+        raise ValueError(f"cu_seqlens must be a contiguous int32 tensor of N + 1 = {N + 1} offsets")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     head = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(gate_a), _ptr(gate_bias), float(gate_lb),
             int(gate_form), _ptr(conv_w), _ptr(conv_ring), _ptr(state_in), _ptr(state_out), _ptr(z),
@@ -385,7 +388,3 @@ def prefill_varlen(q, k, v, g, beta, conv_w, conv_ring, state_in, state_out, z, 
         raise KdaError(rc, "gdn_prefill_varlen" if gdn else "kda_prefill_varlen")
     return rc
 
-
-def torch_int32():
-    import torch
-    return torch.int32
