@@ -176,3 +176,17 @@ def test_gqa_decode_full_size_sampled():
     heads = [0, 15, 16, 31]
     ref, vc, rows, bsel = oracle_heads(inp, heads, [0, 37, 63])
     compare(got, ref, vc, rows, bsel, heads, TOL["bf16"])
+
+
+@pytest.mark.parametrize("T", [1, 3, 9])
+def test_gqa_wide_conv_short_rows_vs_oracle(T):
+    """K = 8 with T < K - 1 rows: the separate q / k ring roll keeps old ring slots."""
+    cfg = CONFIGS["gdn_prefill"].with_(B=2, T=T, H=8, Hk=2, K=8, D=16, dtype="fp32", random_init=True)
+    inp, dev = inputs_for(cfg)
+    got = run_gqa(cfg, dev, mode=SEQ)
+    torch.cuda.synchronize()
+    r = gqa.mixer_gqa(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.conv_w, inp.ring, inp.state, inp.z,
+                      inp.norm_w, scale_of(cfg), RMS_EPS)
+    errs = {n: oracle.rel_linf(to_f64(got[n]), r[n]) for n in ("out", "state", "ring")}
+    _print("errs", errs)
+    assert max(errs.values()) <= TOL["fp32"] and errs["ring"] == 0.0

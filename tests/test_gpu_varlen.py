@@ -172,3 +172,14 @@ def test_chunked_varlen_long_mixed_lengths_sampled():
                 "ring": oracle.rel_linf(to_f64(got["ring"][b])[rows_r], ref["ring"][0])}
         _print("seq", b, "len", L, errs)
         assert max(errs.values()) <= TOL["bf16"] and errs["ring"] == 0.0
+
+
+@pytest.mark.parametrize("mode", [SEQ, CHK], ids=["fused", "chunked"])
+def test_varlen_wide_conv_short_sequences_vs_oracle(mode):
+    """K = 8: sequences shorter than K - 1 rows roll rings that keep old slots."""
+    lens = [1, 3, 0, 6, 8, 70]
+    cfg = CONFIGS["kda_decode"].with_(B=len(lens), T=max(lens), H=3, K=8)
+    inp, dev = inputs_for(cfg)
+    got, cu = run_varlen(cfg, dev, lens, mode)
+    torch.cuda.synchronize()
+    _compare_seqs(inp, got, cu, lens, TOL["bf16"])
