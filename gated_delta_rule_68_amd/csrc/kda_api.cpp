@@ -53,6 +53,10 @@ int pick_arm(int B, int T, int H, int D, bool bf16, int mode) {
     return kda::ARM_SEQ_SPLIT;
 }
 
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+// Head of a packed batch's workspace: the longest-first order of its B sequences.
+size_t order_bytes(int B) { return align256((size_t)B * 4); }
+
 // Query / key heads: a divisor of the value heads H (grouped heads, GDN only).
 int check_heads(int H, int Hk) { return Hk >= 1 && Hk <= H && H % Hk == 0 ? KDA_OK : KDA_ERR_SHAPE; }
 
@@ -106,7 +110,7 @@ int validate(const MixerArgs& a, bool decode, int mode, int* arm_out) {
     const size_t rrows = kda::ring_rows(a);
     const size_t gate_n = a.gdn ? rows * a.H : act;
     const size_t state_n = (size_t)a.B * a.H * a.D * a.D;
-    const size_t need_ws = workspace_for(a.B, a.T, a.H, a.Hk, a.D, a.gdn, arm, rows);
+    const size_t need_ws = workspace_for(a.B, a.T, a.H, a.Hk, a.D, a.gdn, arm, rows) + (packed ? order_bytes(a.B) : 0);
     if (need_ws > 0 && (!a.ws || a.ws_bytes < need_ws)) return KDA_ERR_WORKSPACE;
 
     auto R = [](const void* p, size_t bytes, bool w, int id) {
@@ -176,7 +180,7 @@ int entry(bool gdn, bool decode, const void* q, const void* k, const void* v, co
     MixerArgs a{q, k, v, g, beta, conv_w, conv_ring, state_in, state_out, z, norm_w, out,
                 o_core, B, T, H, D, K, scale, rms_eps, dtype == KDA_DTYPE_BF16, gdn,
                 workspace, workspace_bytes, (hipStream_t)stream, T, true,
-                ga.form, ga.a, ga.bias, ga.lb, Hk, cu_seqlens};
+                ga.form, ga.a, ga.bias, ga.lb, Hk, cu_seqlens, nullptr};
     if (ga.form == kda::GATE_GIVEN) {
         // Kernels read the gate parameters without a branch; point them at conv_w
         // (3*H*D*K >= H*D floats, allocated and 16-byte aligned), values unused.
@@ -186,6 +190,14 @@ int entry(bool gdn, bool decode, const void* q, const void* k, const void* v, co
     int arm = 0;
     const int rc = validate(a, decode, mode, &arm);
     if (rc) return rc;
+    if (a.cu_seqlens) {  // rank the sequences first; the arm's own workspace follows
+        int* order = static_cast<int*>(a.ws);
+        a.ws = static_cast<char*>(a.ws) + order_bytes(a.B);
+        a.ws_bytes -= order_bytes(a.B);
+        a.seq_order = order;
+        const hipError_t e = kda::launch_seq_order(a, order);
+        if (e != hipSuccess) return KDA_ERR_RUNTIME_BASE + (int)e;
+    }
     return run(a, arm);
 }
 
@@ -261,7 +273,7 @@ int rollback(bool gdn, const void* q, const void* k, const void* v, const void* 
     }
     MixerArgs a{q, k, v, g, beta, conv_w, conv_ring, state_snap, state_out, nullptr, nullptr, nullptr,
                 nullptr, B, keep, H, D, K, 1.0f, 0.0f, bf16, gdn, workspace, workspace_bytes,
-                (hipStream_t)stream, T_stash, false, ga.form, conv_w, conv_w, ga.lb, Hk, nullptr};
+                (hipStream_t)stream, T_stash, false, ga.form, conv_w, conv_w, ga.lb, Hk, nullptr, nullptr};
     if (ga.form != kda::GATE_GIVEN) {
         a.gate_a = ga.a;
         a.gate_bias = ga.bias;
@@ -454,7 +466,7 @@ size_t kda_prefill_varlen_workspace_bytes(int N, int T_total, int H, int D, int 
     if (check_shape(1, T_total, H, D, 4) || check_shape(N, 1, H, D, 4)) return (size_t)-1;
     const int arm = pick_arm_varlen(D, dtype == KDA_DTYPE_BF16, mode);
     if (arm < 0) return (size_t)-1;
-    return workspace_for(N, T_total, H, H, D, false, arm, (size_t)T_total);
+    return order_bytes(N) + workspace_for(N, T_total, H, H, D, false, arm, (size_t)T_total);
 }
 
 size_t gdn_prefill_varlen_workspace_bytes(int N, int T_total, int H, int Hk, int D, int dtype, int mode) {

@@ -505,6 +505,7 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
     int bh, split;
     block_coords(NCOL, a.B * a.H, &bh, &split);
     if (bh < 0) return;  // whole block exits before any barrier
+    bh = seq_of(a, bh / a.H) * a.H + bh % a.H;  // packed batches: longest sequences first
 
     int tid = threadIdx.x, lane = tid & 63;
     const int wave = tid >> 6;

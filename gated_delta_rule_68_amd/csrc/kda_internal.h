@@ -52,7 +52,14 @@ struct MixerArgs {
     // rows cu_seqlens[b] .. cu_seqlens[b+1]-1 of the [T][...] activations, T being the
     // total row count; its ring and state slots are b as usual.
     const int* cu_seqlens;
+    // Packed batches: the sequences longest first (a permutation of 0..B-1 written by
+    // launch_seq_order), so that the first workgroups dispatched take the longest work;
+    // null: in index order.
+    const int* seq_order;
 };
+
+// Sequence processed by the workgroups of dispatch rank r.
+__device__ inline int seq_of(const MixerArgs& a, int r) { return a.seq_order ? a.seq_order[r] : r; }
 
 // Activation rows of all sequences of a call.
 __host__ __device__ inline size_t total_rows(const MixerArgs& a) {
@@ -106,6 +113,9 @@ hipError_t launch_seq_split(const MixerArgs& a);
 hipError_t launch_chunked(const MixerArgs& a);
 // Gated RMSNorm of a fp32 pre-norm output o [B][T][H*D] into a.out.
 hipError_t launch_norm(const MixerArgs& a, const float* o);
+// Rank the B sequences of a packed batch by length, longest first (ties by index),
+// into order[0..B-1].
+hipError_t launch_seq_order(const MixerArgs& a, int* order);
 // Roll every sequence's ring to the last K-1 raw rows of its T input rows (q, k and
 // v planes, or with qk_only the q and k planes alone).
 hipError_t launch_ring_roll(const MixerArgs& a, bool qk_only);

@@ -50,7 +50,7 @@ __global__ __launch_bounds__(fused_threads<D>()) void seq_fused_kernel(MixerArgs
     __shared__ float wins[3 * D][KMAX - 1];  // conv windows between token blocks
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
+    const int h = blockIdx.x % a.H, b = seq_of(a, blockIdx.x / a.H), bh = b * a.H + h;
     const int H = a.H, K = a.K;
     const size_t qkv = (size_t)H * D;
     const size_t head_off = (size_t)h * D;
@@ -395,6 +395,31 @@ SplitWorkspace split_workspace(int B, int T, int H, int Hk, int D, bool gdn) {
 
 namespace {
 
+// Thread n ranks sequence n: the number of longer sequences plus the number of equally
+// long ones before it. Lengths are the clamped spans the mixer kernels use.
+__global__ __launch_bounds__(256) void seq_order_kernel(MixerArgs a, int* order) {
+    __shared__ int lens[256];
+    const int n = blockIdx.x * 256 + threadIdx.x;
+    size_t st;
+    int len = -1;
+    if (n < a.B) seq_span(a, n, &st, &len);
+    int rank = 0;
+    for (int m0 = 0; m0 < a.B; m0 += 256) {
+        const int m = m0 + threadIdx.x;
+        int lm = -1;
+        if (m < a.B) seq_span(a, m, &st, &lm);
+        __syncthreads();
+        lens[threadIdx.x] = lm;
+        __syncthreads();
+        const int cnt = min(256, a.B - m0);
+        for (int j = 0; j < cnt; ++j) {
+            const int l = lens[j];
+            rank += (l > len) || (l == len && m0 + j < n);
+        }
+    }
+    if (n < a.B) order[rank] = n;
+}
+
 // One thread per ring row: the K-1 newest raw inputs of [old ring ++ x] (the row's
 // old slots are read into registers before any store). Rows of a sequence are
 // numbered as the ring: q plane, k plane (Hk*D each), v plane (H*D).
@@ -428,6 +453,11 @@ __global__ __launch_bounds__(256) void ring_roll_kernel(MixerArgs a, int rows_pe
 }
 
 }  // namespace
+
+hipError_t launch_seq_order(const MixerArgs& a, int* order) {
+    hipLaunchKernelGGL(seq_order_kernel, dim3((unsigned)((a.B + 255) / 256)), dim3(256), 0, a.stream, a, order);
+    return hipGetLastError();
+}
 
 hipError_t launch_ring_roll(const MixerArgs& a, bool qk_only) {
     const int rows_per_seq = (int)(qk_only ? (size_t)2 * a.Hk * a.D : ring_rows(a));

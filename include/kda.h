@@ -320,8 +320,9 @@ size_t gdn_gqa_workspace_bytes(int B, int T, int H, int Hk, int D, int dtype, in
  * chunked arm for bf16 activations at D = 128, else the fused arm. Each sequence is
  * processed exactly as a call on that sequence alone would process it on the same arm
  * (the fused arm bit for bit). workspace: at least *_prefill_varlen_workspace_bytes
- * bytes (the chunked arm with N*H < 256 needs one). null cu_seqlens is KDA_ERR_NULL;
- * everything else as for kda_prefill.
+ * bytes, never 0: it holds the longest-first order in which the sequences are
+ * dispatched (ranked on the device), and, for the chunked arm with N*H < 256, the
+ * pre-norm rows. null cu_seqlens is KDA_ERR_NULL; everything else as for kda_prefill.
  */
 int kda_prefill_varlen(const void* q, const void* k, const void* v, const void* g,
                        const void* beta, const float* gate_a, const float* gate_bias,

@@ -291,18 +291,19 @@ def call_varlen(a, gdn=False, N=2, T_total=5, cu=None, mode=1, Hk=None):
     L = kda.lib()
     head = (a["q"], a["k"], a["v"], a["g"], a["beta"], a["gate_a"], a["gate_bias"], 0.0, 0, a["conv_w"],
             a["ring"], a["state_in"], a["state_out"], a["z"], a["norm_w"], a["out"], a["o_core"],
-            a["ws"] if cu is None else cu, N, T_total, a["H"])
+            BASE + 18 * (1 << 32) if cu is None else cu, N, T_total, a["H"])
     tail = (a["D"], a["K"], 0.25, 1e-5, a["dtype"], mode, a["ws"], a["ws_bytes"], None)
     if gdn:
         return L.gdn_prefill_varlen(*head, a["H"] if Hk is None else Hk, *tail)
     return L.kda_prefill_varlen(*head, *tail)
 
 
-# the offsets table sits in the slot named "ws" unless a case places it (cu=...)
+# the offsets table sits in a slot of its own (18) unless a case places it (cu=...)
 VARLEN_CASES = [
     ("null cu_seqlens", dict(), dict(cu=0), 40001),
     ("misaligned cu_seqlens", dict(), dict(cu=BASE + 13 * (1 << 32) + 2), 40007),
-    ("out over cu_seqlens", dict(out=BASE + 13 * (1 << 32)), dict(), 40009),
+    ("out over cu_seqlens", dict(out=BASE + 18 * (1 << 32)), dict(), 40009),
+    ("workspace too small", dict(ws_bytes=255), dict(), 40006),
     ("T_total 0", dict(), dict(T_total=0), 40004),
     ("N 0", dict(), dict(N=0), 40004),
     ("chunked at D=16", dict(), dict(mode=2), 40008),
@@ -327,9 +328,12 @@ def test_varlen_gqa_heads_checked():
 
 
 def test_varlen_queries():
-    # fused arm: no workspace; chunked arm with N*H < 256: fp32 pre-norm rows of all tokens
-    assert kda.varlen_workspace_bytes(3, 500, 4, 16, 0, 1) == 0
-    assert kda.varlen_workspace_bytes(3, 500, 4, 128, 1, 2) == 500 * 4 * 128 * 4
-    assert kda.varlen_workspace_bytes(64, 500, 4, 128, 1, 2) == 0  # N*H = 256: one split
+    # the longest-first order of the N sequences (256-byte aligned) heads the workspace;
+    # the fused arm needs nothing more, the chunked arm with N*H < 256 the fp32 pre-norm
+    # rows of all tokens
+    assert kda.varlen_workspace_bytes(3, 500, 4, 16, 0, 1) == 256
+    assert kda.varlen_workspace_bytes(3, 500, 4, 128, 1, 2) == 256 + 500 * 4 * 128 * 4
+    assert kda.varlen_workspace_bytes(64, 500, 4, 128, 1, 2) == 256  # N*H = 256: one split
+    assert kda.varlen_workspace_bytes(65, 500, 4, 128, 1, 2) == 512
     assert kda.varlen_workspace_bytes(3, 500, 4, 16, 0, 2) == ctypes.c_size_t(-1).value
     assert kda.varlen_workspace_bytes(3, 500, 4, 128, 1, 2, gdn=True, Hk=3) == ctypes.c_size_t(-1).value
