@@ -2,7 +2,8 @@
 
 Every device translation unit is compiled with -ffp-contract=off (all fused
 multiply-adds are explicit, which keeps the kernel arms bit-identical to each
-other) and with packed-fp32 instruction selection disabled.
+other) and with packed-fp32 instruction selection disabled. Symbols are hidden
+by default; include/kda.h exports the C ABI.
 """
 from __future__ import annotations
 
@@ -20,7 +21,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC]
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-I", INCLUDE, "-I", CSRC]
 DEVICE = ["-x", "hip", f"--offload-arch={ARCH}", "-ffp-contract=off",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 SOURCES = ["kda_api.cpp", "kda_seq.hip", "kda_chunk.hip"]

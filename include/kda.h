@@ -56,6 +56,10 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+/* The library is built with hidden visibility: only what this header declares is exported. */
+#if defined(__GNUC__) || defined(__clang__)
+#pragma GCC visibility push(default)
+#endif
 
 /* ---- status codes ---- */
 #define KDA_OK 0
@@ -347,6 +351,9 @@ size_t gdn_prefill_varlen_workspace_bytes(int N, int T_total, int H, int Hk, int
 /* Static description of a status code (never NULL). */
 const char* kda_status_string(int rc);
 
+#if defined(__GNUC__) || defined(__clang__)
+#pragma GCC visibility pop
+#endif
 #ifdef __cplusplus
 }
 #endif
