@@ -36,6 +36,12 @@
 // run in-kernel on the raw inputs, so the only HBM traffic is the raw activations,
 // the gates, the output and the state once in and once out. For bf16 inputs the raw
 // rows of chunk c+1 are requested while chunk c computes.
+//
+// Variants carried by the same kernel: gates given as pre-activations (template flag
+// ACT for KDA: activated once per element at the raw-row store, kept as split fp32
+// halves; GDN: activated at that store at run time); query / key rows read from key
+// head h % Hk (grouped heads); packed batches, whose sequences take their rows from an
+// offsets table and are dispatched longest first.
 #include "kda_device.h"
 #include "kda_internal.h"
 

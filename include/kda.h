@@ -41,6 +41,8 @@
  *      norm_w   [D]          shared by all heads
  *      out      [B][T][H*D]  gated, normalised output (dtype)
  *      o_core   [B][T][H*D]  fp32 scan output before the norm; may be NULL
+ *    (The grouped-head entry points give q, k and the conv planes Hk heads, and the
+ *    packed-batch entry points pack the rows of N sequences; see their sections.)
  *  - D must be 16 or 128, 2 <= K <= 8, B, T, H >= 1.
  *  - Contract violations are detected on the host BEFORE any launch: nothing is
  *    written on the device when a 4xxxx code is returned.
