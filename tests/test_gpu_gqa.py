@@ -190,3 +190,20 @@ def test_gqa_wide_conv_short_rows_vs_oracle(T):
     errs = {n: oracle.rel_linf(to_f64(got[n]), r[n]) for n in ("out", "state", "ring")}
     _print("errs", errs)
     assert max(errs.values()) <= TOL["fp32"] and errs["ring"] == 0.0
+
+
+def test_gqa_rollback_split_arm_matches_prefill():
+    """keep = 30 rows with 8 value heads over 2 key heads (B = 1): the split arm
+    replays from the workspace; it equals a grouped sequential prefill of those rows."""
+    cfg = CONFIGS["gdn_prefill"].with_(B=1, T=40, H=8, Hk=2, D=16, dtype="fp32", random_init=True)
+    inp, dev = inputs_for(cfg)
+    keep = 30
+    assert kda.prefill_arm(cfg.B, keep, cfg.H, cfg.D, kda.KDA_DTYPE_F32, SEQ, gdn=True) == 2
+    ref = run_gqa(cfg, dev, mode=SEQ, T=keep)
+    ring, state = torch.empty_like(dev["ring"]), torch.empty_like(dev["state"])
+    nb = kda.gqa_workspace_bytes(cfg.B, keep, cfg.H, cfg.hk, cfg.D, kda.KDA_DTYPE_F32, SEQ)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    kda.gdn_rollback_gqa(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], dev["conv_w"], dev["ring"],
+                         dev["state"], ring, state, keep, workspace=ws)
+    torch.cuda.synchronize()
+    assert_bitwise({"ring": ring, "state": state}, ref, keys=("ring", "state"))
