@@ -972,14 +972,36 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
             *reinterpret_cast<bf16x4*>(&sm.e.sb[16 * jb + l16][16 * wave + 4 * q4]) = s4;
         }
         lds_barrier();
+        // Ub = U - W S. The state part of P6's output, O = Q+ S (rows 16*sw.., value
+        // blocks of half hv), also reads S^T only: from two value blocks per wavefront
+        // on (NC >= 64) it is issued here with Ub, whose independent MFMA chain it
+        // overlaps (measured 4% off the chunk time there); with one block (NC = 32) it
+        // stays in P6.
+        constexpr bool O_EARLY = NJB2 >= 2;
+        f32x4v accO[NJB2];
+#pragma unroll
+        for (int t = 0; t < NJB2; ++t) accO[t] = zero4();
+        auto o_state_part = [&](int kk, int i0, const bf16x8* sbt) {  // accO += Q+ S, k slice kk
+            const bf16x8 qx = ld8(&sm.qa[16 * sw + l16][i0]);
+            const float* eb = &sm.fac[F_EBR + sw][GDN ? 0 : i0];  // e^{B} of block sw
+            bf16x8 aq;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) aq[e] = (__bf16)((float)qx[e] * eb[GDN ? 0 : e]);
+#pragma unroll
+            for (int t = 0; t < NJB2; ++t)  // lane: O[s][16 jb + 4 q4 + r]
+                accO[t] = mfma_bf16(sbt[t], aq, accO[t]);
+        };
 #pragma unroll 2
         for (int kk = 0; kk < 4; ++kk) {
-            const bf16x8 aw = ld8(&sm.c.m.w.wneg[16 * sw + l16][32 * kk + 8 * q4]);
+            const int i0 = 32 * kk + 8 * q4;
+            const bf16x8 aw = ld8(&sm.c.m.w.wneg[16 * sw + l16][i0]);
+            bf16x8 sbt[NJB2];
 #pragma unroll
             for (int t = 0; t < NJB2; ++t) {
-                const int jb = hv * NJB2 + t;
-                accU[t] = mfma_bf16(aw, ld8(&sm.e.sb[16 * jb + l16][32 * kk + 8 * q4]), accU[t]);
+                sbt[t] = ld8(&sm.e.sb[16 * (hv * NJB2 + t) + l16][i0]);
+                accU[t] = mfma_bf16(aw, sbt[t], accU[t]);
             }
+            if constexpr (O_EARLY) o_state_part(kk, i0, sbt);
         }
         lds_barrier();  // every read of -W is done before Ub^T overwrites it
 #pragma unroll
@@ -995,22 +1017,17 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
         load_raw_part<BF, GDN, NC, RAW_V>(raw, a, rowb, T, h, c0 + CH, jv0, tid);
         load_raw_part<BF, GDN, NC, RAW_BETA>(raw, a, rowb, T, h, c0 + CH, jv0, tid);
         // ---- P6: O = scale (Q+ S + P Ub), rows 16*sw.., value blocks of half hv ----
-        f32x4v accO[NJB2];
         {
             const int s = 16 * sw + l16;
-#pragma unroll
-            for (int t = 0; t < NJB2; ++t) accO[t] = zero4();
+            if constexpr (!O_EARLY) {
 #pragma unroll 2
-            for (int kk = 0; kk < 4; ++kk) {
-                const int i0 = 32 * kk + 8 * q4;
-                const bf16x8 qx = ld8(&sm.qa[s][i0]);
-                const float* eb = &sm.fac[F_EBR + sw][GDN ? 0 : i0];  // e^{B} of block sw
-                bf16x8 aq;
+                for (int kk = 0; kk < 4; ++kk) {
+                    const int i0 = 32 * kk + 8 * q4;
+                    bf16x8 sbt[NJB2];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) aq[e] = (__bf16)((float)qx[e] * eb[GDN ? 0 : e]);
-#pragma unroll
-                for (int t = 0; t < NJB2; ++t)  // lane: O[s][16 jb + 4 q4 + r]
-                    accO[t] = mfma_bf16(ld8(&sm.e.sb[16 * (hv * NJB2 + t) + l16][i0]), aq, accO[t]);
+                    for (int t = 0; t < NJB2; ++t) sbt[t] = ld8(&sm.e.sb[16 * (hv * NJB2 + t) + l16][i0]);
+                    o_state_part(kk, i0, sbt);
+                }
             }
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
