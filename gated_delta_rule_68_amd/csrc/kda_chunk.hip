@@ -1052,6 +1052,28 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
                     a.scale * accO[t];
         }
         lds_barrier();
+        KDA_LAUNDER_LANE();
+        // ---- P7: S = diag(e^{G_last}) S + K_dec^T Ub (key block `wave`). Issued ahead of
+        // the output epilogue, whose VALU work then runs while the MFMA chain drains
+        // (nothing here is read or written by the epilogue). ----
+        {
+            const int i = 16 * wave + l16;
+            const f32x4v dec = GDN ? f32x4v{sm.fac[F_FN][0], sm.fac[F_FN][0], sm.fac[F_FN][0], sm.fac[F_FN][0]}
+                                   : ld4f(&sm.fac[F_FN][16 * wave + 4 * q4]);
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb) accS[jb] *= dec;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const int j0 = 32 * kk + 8 * q4;
+                const float el = sm.fac[F_ELR + (j0 >> 4)][GDN ? 0 : i];  // e^{G_last - B} of the rows' block
+                bf16x8 bkd;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) bkd[e] = (__bf16)((float)sm.kb[j0 + e][i] * el);
+#pragma unroll
+                for (int jb = 0; jb < NJB; ++jb)
+                    accS[jb] = mfma_bf16(bkd, ld8(&sm.c.m.w.ubt[16 * jb + l16][32 * kk + 8 * q4]), accS[jb]);
+            }
+        }
         // Items past the last row (or past the item count) store a copy of the last
         // row's values to the last row: the stores need no branch, and a branch would
         // make the compiler wait for all memory traffic where it joins.
@@ -1115,26 +1137,6 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
             }
         }
 
-        KDA_LAUNDER_LANE();
-        // ---- P7: S = diag(e^{G_last}) S + K_dec^T Ub (key block `wave`) ----
-        {
-            const int i = 16 * wave + l16;
-            const f32x4v dec = GDN ? f32x4v{sm.fac[F_FN][0], sm.fac[F_FN][0], sm.fac[F_FN][0], sm.fac[F_FN][0]}
-                                   : ld4f(&sm.fac[F_FN][16 * wave + 4 * q4]);
-#pragma unroll
-            for (int jb = 0; jb < NJB; ++jb) accS[jb] *= dec;
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const int j0 = 32 * kk + 8 * q4;
-                const float el = sm.fac[F_ELR + (j0 >> 4)][GDN ? 0 : i];  // e^{G_last - B} of the rows' block
-                bf16x8 bkd;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) bkd[e] = (__bf16)((float)sm.kb[j0 + e][i] * el);
-#pragma unroll
-                for (int jb = 0; jb < NJB; ++jb)
-                    accS[jb] = mfma_bf16(bkd, ld8(&sm.c.m.w.ubt[16 * jb + l16][32 * kk + 8 * q4]), accS[jb]);
-            }
-        }
         lds_barrier();
         store_raw<GDN, NC, ACT>(sm, raw, max(min(CH, T - c0 - CH), 0), tid, a, cg);
         lds_barrier();
