@@ -35,31 +35,43 @@ constexpr int fused_cpt() { return D >= 128 ? 2 : 1; }
 template <int D>
 constexpr int fused_threads() { return 8 * D / fused_cpt<D>(); }
 
-template <int D, bool BF, bool GDN>
-__global__ __launch_bounds__(fused_threads<D>()) void seq_fused_kernel(MixerArgs a) {
+// G value heads per workgroup: G = 1, one workgroup per (sequence, value head); G > 1
+// (GDN with G = H / Hk), one workgroup per (sequence, key head) holding every value
+// head of that key head, which convolves q / k once and rolls their ring rows itself.
+// Each value head's NT1 threads map exactly as the G = 1 kernel's (same arithmetic).
+template <int D, bool BF, bool GDN, int G = 1>
+__global__ __launch_bounds__(fused_threads<D>() * G) void seq_fused_kernel(MixerArgs a) {
+    static_assert(G == 1 || GDN, "grouped value heads are a GDN layout");
     constexpr int CPT = fused_cpt<D>();
-    constexpr int NT = fused_threads<D>();
-    constexpr int NG = NT / 8;  // 8-lane column groups; column of (group g, slot c) = g + c*NG
+    constexpr int NT1 = fused_threads<D>();  // threads per value head
+    constexpr int NT = NT1 * G;
+    constexpr int NG = NT1 / 8;  // 8-lane column groups; column of (group g, slot c) = g + c*NG
     constexpr int NW = NT / 64;
     constexpr int KPL = D / 8;
     constexpr int EW = GDN ? 1 : D;
-    __shared__ float pre[3][TB_FUSED][D];  // conv outputs q, k, v (q, k l2-normalised in place)
-    __shared__ float es[TB_FUSED][EW];     // exp(g)
-    __shared__ float os[TB_FUSED][D];      // scan readout
-    __shared__ float bs[TB_FUSED], kqs[TB_FUSED];
-    __shared__ float wins[3 * D][KMAX - 1];  // conv windows between token blocks
+    constexpr int NP = 2 + G;                   // conv planes: q, k, and the G value heads
+    __shared__ float pre[NP][TB_FUSED][D];      // conv outputs q, k, v (q, k l2-normalised in place)
+    __shared__ float es[TB_FUSED][G * EW];      // exp(g), value head hg at hg * EW
+    __shared__ float os[TB_FUSED][G * D];       // scan readout
+    __shared__ float bs[TB_FUSED][G], kqs[TB_FUSED];
+    __shared__ float wins[NP * D][KMAX - 1];    // conv windows between token blocks
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int h = blockIdx.x % a.H, b = seq_of(a, blockIdx.x / a.H), bh = b * a.H + h;
+    const int hg = G == 1 ? 0 : tid / NT1;      // value head within the workgroup
+    const int tl = G == 1 ? tid : tid % NT1;    // thread within the value head's threads
+    const int HB = a.H / G;                     // workgroups per sequence
+    const int hx = blockIdx.x % HB, b = seq_of(a, blockIdx.x / HB);
+    auto vhead = [&](int g) { return G == 1 ? hx : hx + g * a.Hk; };
+    const int h = vhead(hg), bh = b * a.H + h;  // this thread's value head
     const int H = a.H, K = a.K;
     const size_t qkv = (size_t)H * D;
     const size_t head_off = (size_t)h * D;
-    const int grp = wave * 8 + (lane >> 3), s = lane & 7;
-    // q / k rows are Hk*D wide and this value head reads key head h % Hk
-    const size_t kw = (size_t)a.Hk * D, khead = (size_t)(h % a.Hk) * D;
+    const int grp = (tl >> 6) * 8 + (lane >> 3), s = lane & 7;
+    // q / k rows are Hk*D wide and value head h reads key head h % Hk
+    const size_t kw = (size_t)a.Hk * D, khead = (size_t)(hx % a.Hk) * D;
     const size_t rrow = ring_rows(a);
     auto prow = [&](int plane, int ch) -> size_t {  // conv-weight / ring row
-        return plane < 2 ? plane * kw + khead + ch : 2 * kw + head_off + ch;
+        return plane < 2 ? plane * kw + khead + ch : 2 * kw + (size_t)vhead(plane - 2) * D + ch;
     };
 
     // Issue the state loads first so their HBM latency overlaps the conv / l2 work.
@@ -68,18 +80,20 @@ __global__ __launch_bounds__(fused_threads<D>()) void seq_fused_kernel(MixerArgs
     for (int c = 0; c < CPT; ++c)
         load_keys<D>(S[c], a.state_in + ((size_t)bh * D + grp + c * NG) * D, s);
 
-    // The gate column of this thread is fixed (NT is a multiple of D); its activation
-    // parameters arrive with the ring rows, which are waited for right below (read
-    // before the state, their pointers' scalar load would hold the state loads back).
-    static_assert(NT % D == 0, "one gate column per thread");
-    const GateCol gp = gate_col(a, h, GDN ? h : head_off + tid % D);
+    // The gate column of this thread is fixed (NT1 is a multiple of D; GDN: the threads
+    // tid < G * TB_FUSED take token tid % TB_FUSED of value head tid / TB_FUSED); its
+    // activation parameters arrive with the ring rows, which are waited for right below
+    // (read before the state, their pointers' scalar load would hold the state loads back).
+    static_assert(NT1 % D == 0, "one gate column per thread");
+    const int ge = min(tid / TB_FUSED, G - 1), te = tid % TB_FUSED;  // GDN gate / beta slots
+    const GateCol gp = gate_col(a, GDN ? vhead(ge) : h, GDN ? vhead(ge) : head_off + tid % D);
 
     size_t rstart;  // first activation row of this sequence
     int T;          // its row count
     seq_span(a, b, &rstart, &T);
 
-    // Conv windows of this head's 3*D (plane, channel) rows start as the old ring.
-    for (int r = tid; r < 3 * D; r += NT) {
+    // Conv windows of the workgroup's NP*D (plane, channel) rows start as the old ring.
+    for (int r = tid; r < NP * D; r += NT) {
         const int plane = r / D, ch = r % D;
         const float* ring_row = a.ring + ((size_t)b * rrow + prow(plane, ch)) * (K - 1);
         ConvChannel cc;
@@ -91,14 +105,15 @@ __global__ __launch_bounds__(fused_threads<D>()) void seq_fused_kernel(MixerArgs
     for (int t0 = 0; t0 < T; t0 += TB_FUSED) {
         const int nt = min(TB_FUSED, T - t0);
         const size_t row0 = rstart + t0;
-        for (int r = tid; r < 3 * D; r += NT) {
+        for (int r = tid; r < NP * D; r += NT) {
             const int plane = r / D, ch = r % D;
             const void* xsrc = plane == 0 ? a.q : (plane == 1 ? a.k : a.v);
             ConvChannel cc;
             conv_load_taps(cc, a.conv_w + prow(plane, ch) * K, K);
 #pragma unroll
             for (int e = 0; e < KMAX - 1; ++e) cc.win[e] = wins[r][e];
-            const size_t xw = plane < 2 ? kw : qkv, xc = (plane < 2 ? khead : head_off) + ch;
+            const size_t xw = plane < 2 ? kw : qkv;
+            const size_t xc = (plane < 2 ? khead : (size_t)vhead(plane - 2) * D) + ch;
             for (int tt = 0; tt < nt; ++tt) {
                 const float x = ld_act<BF>(xsrc, (row0 + tt) * xw + xc);
                 pre[plane][tt][ch] = silu_f(conv_push(cc, x));
@@ -107,34 +122,39 @@ __global__ __launch_bounds__(fused_threads<D>()) void seq_fused_kernel(MixerArgs
             for (int e = 0; e < KMAX - 1; ++e) wins[r][e] = cc.win[e];
         }
         if constexpr (GDN) {
-            if (tid < nt) es[tid][0] = exp_f(gate_in(a, gp, ld_act<BF>(a.g, (row0 + tid) * H + h)));
+            if (tid < G * TB_FUSED && te < nt) {
+                const int hv = vhead(ge);
+                es[te][ge] = exp_f(gate_in(a, gp, ld_act<BF>(a.g, (row0 + te) * H + hv)));
+                bs[te][ge] = beta_in(a, ld_act<BF>(a.beta, (row0 + te) * H + hv));
+            }
         } else {
             for (int idx = tid; idx < nt * D; idx += NT) {
                 const int tt = idx / D, i = idx % D;
                 es[tt][i] = exp_f(gate_in(a, gp, ld_act<BF>(a.g, (row0 + tt) * qkv + head_off + i)));
             }
+            if (tid < nt) bs[tid][0] = beta_in(a, ld_act<BF>(a.beta, (row0 + tid) * H + h));
         }
-        if (tid < nt) bs[tid] = beta_in(a, ld_act<BF>(a.beta, (row0 + tid) * H + h));
         __syncthreads();
         for (int tt = wave; tt < nt; tt += NW) l2_qk_row<D>(pre[0][tt], pre[1][tt], lane, &kqs[tt]);
         __syncthreads();
         for (int tt = 0; tt < nt; ++tt) {
             float vj[CPT], o[CPT];
 #pragma unroll
-            for (int c = 0; c < CPT; ++c) vj[c] = pre[2][tt][grp + c * NG];
-            scan_step_cols<D, GDN, CPT>(S, pre[0][tt], pre[1][tt], es[tt], vj, bs[tt], kqs[tt],
+            for (int c = 0; c < CPT; ++c) vj[c] = pre[2 + hg][tt][grp + c * NG];
+            scan_step_cols<D, GDN, CPT>(S, pre[0][tt], pre[1][tt], &es[tt][hg * EW], vj, bs[tt][hg], kqs[tt],
                                         a.scale, s, o);
             if (s == 0) {
 #pragma unroll
-                for (int c = 0; c < CPT; ++c) os[tt][grp + c * NG] = o[c];
+                for (int c = 0; c < CPT; ++c) os[tt][hg * D + grp + c * NG] = o[c];
             }
         }
         __syncthreads();
         if (a.readout) {
-            for (int tt = wave; tt < nt; tt += NW) {
-                const size_t off = (row0 + tt) * qkv + head_off;
+            for (int idx = wave; idx < nt * G; idx += NW) {
+                const int tt = idx / G, g = idx % G;
+                const size_t off = (row0 + tt) * qkv + (size_t)vhead(g) * D;
                 const GateRow gz = load_gate_row<D, BF>(a, off, lane);
-                gated_rmsnorm_row<D, BF, GDN>(os[tt], gz, a, off, lane, a.o_core);
+                gated_rmsnorm_row<D, BF, GDN>(&os[tt][g * D], gz, a, off, lane, a.o_core);
             }
         }
         __syncthreads();
@@ -144,12 +164,12 @@ __global__ __launch_bounds__(fused_threads<D>()) void seq_fused_kernel(MixerArgs
     for (int c = 0; c < CPT; ++c)
         store_keys<D>(a.state_out + ((size_t)bh * D + grp + c * NG) * D, S[c], s);
     // The windows now hold the last K-1 raw inputs of [old ring ++ x]. Each v row was
-    // read only by this workgroup (window init); so were the q / k rows unless key
-    // heads are shared (Hk < H), in which case they are rolled by a kernel of their
-    // own after this one (another workgroup may still be reading them).
-    for (int r = tid; r < 3 * D; r += NT) {
+    // read only by this workgroup (window init); so were the q / k rows unless another
+    // workgroup shares the key head (G == 1 with Hk < H), in which case they are rolled
+    // by a kernel of their own after this one (that workgroup may still be reading them).
+    for (int r = tid; r < NP * D; r += NT) {
         const int plane = r / D, ch = r % D;
-        if (plane < 2 && a.Hk != a.H) continue;
+        if (plane < 2 && G == 1 && a.Hk != a.H) continue;
         float* ring_row = a.ring + ((size_t)b * rrow + prow(plane, ch)) * (K - 1);
         ConvChannel cc;
 #pragma unroll
@@ -319,6 +339,13 @@ __global__ __launch_bounds__(256) void norm_kernel(MixerArgs a, const float* o) 
 
 template <int D, bool BF, bool GDN>
 hipError_t fused_launch(const MixerArgs& a) {
+    if constexpr (GDN) {
+        if (a.H == 2 * a.Hk) {  // both value heads of a key head in one workgroup
+            hipLaunchKernelGGL((seq_fused_kernel<D, BF, GDN, 2>), dim3(a.B * a.Hk), dim3(2 * fused_threads<D>()),
+                               0, a.stream, a);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((seq_fused_kernel<D, BF, GDN>), dim3(a.B * a.H), dim3(fused_threads<D>()), 0,
                        a.stream, a);
     const hipError_t e = hipGetLastError();
