@@ -533,9 +533,10 @@ def run_varlen_leg() -> dict:
 
 
 def run_prefill_legs() -> dict:
-    """Each prefill workload on the chunked and the sequential arm: time of the whole
-    arm (every kernel it launches), tokens/s, algorithmic HBM GB/s and, for the
-    chunked arm, the dense-tile contraction TFLOP/s as a fraction of the bf16 peak."""
+    """Each prefill workload on the chunked and the sequential arm, and on the segmented
+    arm where AUTO takes it: time of the whole arm (every kernel it launches), tokens/s,
+    algorithmic HBM GB/s and, for the chunked arms, the dense-tile contraction TFLOP/s
+    of the unsegmented algorithm as a fraction of the bf16 peak."""
     import torch
 
     import gated_delta_rule_68_amd as kda
@@ -549,13 +550,16 @@ def run_prefill_legs() -> dict:
         rec = {"workload": f"{'GDN' if cfg.gdn else 'KDA'} prefill B={cfg.B} T={cfg.T} "
                            f"H={cfg.H} D={cfg.D} {cfg.dtype}",
                "algorithmic_bytes": prefill_bytes(cfg), "dense_tile_flops": chunk_flops(cfg)}
-        for mode in (kda.KDA_MODE_CHUNKED, kda.KDA_MODE_SEQUENTIAL):
+        auto = kda.prefill_arm(cfg.B, cfg.T, cfg.H, cfg.D, 1, kda.KDA_MODE_AUTO, gdn=cfg.gdn)
+        for mode in (kda.KDA_MODE_CHUNKED, kda.KDA_MODE_SEGMENTED, kda.KDA_MODE_SEQUENTIAL):
             if kda.prefill_arm(cfg.B, cfg.T, cfg.H, cfg.D, 1, mode, gdn=cfg.gdn) < 0:
                 continue
+            if mode == kda.KDA_MODE_SEGMENTED and kda.ARM_NAMES.get(auto) != "segmented":
+                continue  # timed where AUTO takes it
             ms, arm = run_prefill(cfg, mode, reps=3 if cfg.T * cfg.B > 50000 else 5, d=d)
             r = {"ms": ms, "tokens_per_s": cfg.B * cfg.T / (ms * 1e-3),
                  "hbm_gbs": prefill_bytes(cfg) / (ms * 1e-3) / 1e9}
-            if arm == "chunked":
+            if arm in ("chunked", "segmented"):
                 tf = chunk_flops(cfg) / (ms * 1e-3) / 1e12
                 r.update({"mfma_tflops": tf, "mfma_frac": tf / BF16_PEAK_TFLOPS,
                           "mfma_frac_of_measured_gemm": tf / legs["measured_gemm_tflops"],

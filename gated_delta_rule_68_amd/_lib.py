@@ -13,8 +13,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libkda.so")
 
 KDA_DTYPE_F32, KDA_DTYPE_BF16 = 0, 1
-KDA_MODE_AUTO, KDA_MODE_SEQUENTIAL, KDA_MODE_CHUNKED = 0, 1, 2
-ARM_NAMES = {1: "seq_fused", 2: "seq_split", 3: "chunked"}
+KDA_MODE_AUTO, KDA_MODE_SEQUENTIAL, KDA_MODE_CHUNKED, KDA_MODE_SEGMENTED = 0, 1, 2, 3
+ARM_NAMES = {1: "seq_fused", 2: "seq_split", 3: "chunked", 4: "segmented"}
 
 _lib = None
 

@@ -44,10 +44,21 @@ int check_shape(int B, int T, int H, int D, int K) {
 // very short prefills where its extra launches would dominate.
 // The chunked arm (D = 128) computes its contractions with bf16 operands, so AUTO
 // takes it only for bf16 activations and prefills of at least two chunks.
+// Few (b, h) pairs leave most compute units idle in the chunked arm; AUTO then cuts
+// each sequence into at least three segments of at least kSegAutoChunks chunks and
+// takes the segmented arm (kda_internal.h, seg_plan). The explicit mode accepts
+// segments of one chunk.
+constexpr int kSegAutoChunks = 8;
+kda::SegPlan plan_for(int B, int T, int H, int mode) {
+    return kda::seg_plan((long)B * H, T, mode == KDA_MODE_SEGMENTED ? 1 : kSegAutoChunks);
+}
+
 int pick_arm(int B, int T, int H, int D, bool bf16, int mode) {
     const bool chunk_ok = kda::kChunkedArmBuilt && D == 128;
     if (mode == KDA_MODE_CHUNKED) return chunk_ok ? kda::ARM_CHUNKED : -1;
-    if (mode == KDA_MODE_AUTO && chunk_ok && bf16 && T >= 128) return kda::ARM_CHUNKED;
+    if (mode == KDA_MODE_SEGMENTED) return chunk_ok ? kda::ARM_SEGMENTED : -1;
+    if (mode == KDA_MODE_AUTO && chunk_ok && bf16 && T >= 128)
+        return plan_for(B, T, H, mode).n >= 3 ? kda::ARM_SEGMENTED : kda::ARM_CHUNKED;
     if (mode != KDA_MODE_AUTO && mode != KDA_MODE_SEQUENTIAL) return -1;
     if (T <= 16 || (long)B * H >= 1024) return kda::ARM_SEQ_FUSED;
     return kda::ARM_SEQ_SPLIT;
@@ -66,17 +77,20 @@ int check_heads(int H, int Hk) { return Hk >= 1 && Hk <= H && H % Hk == 0 ? KDA_
 int pick_arm_varlen(int D, bool bf16, int mode) {
     const bool chunk_ok = kda::kChunkedArmBuilt && D == 128;
     if (mode == KDA_MODE_CHUNKED) return chunk_ok ? kda::ARM_CHUNKED : -1;
+    if (mode == KDA_MODE_SEGMENTED) return -1;  // segments of equal-length sequences only
     if (mode == KDA_MODE_AUTO && chunk_ok && bf16) return kda::ARM_CHUNKED;
     if (mode != KDA_MODE_AUTO && mode != KDA_MODE_SEQUENTIAL) return -1;
     return kda::ARM_SEQ_FUSED;
 }
 
 // rows: activation rows of all sequences (B*T, or T for a packed batch).
-size_t workspace_for(int B, int T, int H, int Hk, int D, bool gdn, int arm, size_t rows = 0) {
+size_t workspace_for(int B, int T, int H, int Hk, int D, bool gdn, int arm, size_t rows = 0,
+                     int mode = KDA_MODE_AUTO) {
     if (rows == 0) rows = (size_t)B * T;
     switch (arm) {
         case kda::ARM_SEQ_SPLIT: return kda::split_workspace(B, T, H, Hk, D, gdn).total;
         case kda::ARM_CHUNKED: return kda::chunked_workspace_bytes(B, rows, H, D);
+        case kda::ARM_SEGMENTED: return kda::segmented_workspace_bytes(B, H, D, plan_for(B, T, H, mode).n);
         default: return 0;
     }
 }
@@ -110,7 +124,8 @@ int validate(const MixerArgs& a, bool decode, int mode, int* arm_out) {
     const size_t rrows = kda::ring_rows(a);
     const size_t gate_n = a.gdn ? rows * a.H : act;
     const size_t state_n = (size_t)a.B * a.H * a.D * a.D;
-    const size_t need_ws = workspace_for(a.B, a.T, a.H, a.Hk, a.D, a.gdn, arm, rows) + (packed ? order_bytes(a.B) : 0);
+    const size_t need_ws = workspace_for(a.B, a.T, a.H, a.Hk, a.D, a.gdn, arm, rows, mode) +
+                           (packed ? order_bytes(a.B) : 0);
     if (need_ws > 0 && (!a.ws || a.ws_bytes < need_ws)) return KDA_ERR_WORKSPACE;
 
     auto R = [](const void* p, size_t bytes, bool w, int id) {
@@ -147,9 +162,15 @@ int validate(const MixerArgs& a, bool decode, int mode, int* arm_out) {
     return KDA_OK;
 }
 
-int run(const MixerArgs& a, int arm) {
+int run(MixerArgs a, int arm, int mode = KDA_MODE_AUTO) {
     hipError_t e;
+    if (arm == kda::ARM_SEGMENTED) {
+        const kda::SegPlan p = plan_for(a.B, a.T, a.H, mode);
+        a.seg_n = p.n;
+        a.seg_len = p.len;
+    }
     switch (arm) {
+        case kda::ARM_SEGMENTED: e = kda::launch_segmented(a); break;
         case kda::ARM_SEQ_FUSED: e = kda::launch_seq_fused(a); break;
         case kda::ARM_SEQ_SPLIT: e = kda::launch_seq_split(a); break;
         case kda::ARM_CHUNKED: e = kda::launch_chunked(a); break;
@@ -198,7 +219,7 @@ int entry(bool gdn, bool decode, const void* q, const void* k, const void* v, co
         const hipError_t e = kda::launch_seq_order(a, order);
         if (e != hipSuccess) return KDA_ERR_RUNTIME_BASE + (int)e;
     }
-    return run(a, arm);
+    return run(a, arm, mode);
 }
 
 // Rollback of a verify round: ring <- ring_snap, then the sequential arm replays the
@@ -288,7 +309,7 @@ size_t ws_query(bool gdn, int B, int T, int H, int D, int dtype, int mode, int H
     if (check_heads(H, Hk)) return (size_t)-1;
     const int arm = pick_arm(B, T, H, D, dtype == KDA_DTYPE_BF16, mode);
     if (arm < 0) return (size_t)-1;
-    return workspace_for(B, T, H, Hk, D, gdn, arm);
+    return workspace_for(B, T, H, Hk, D, gdn, arm, 0, mode);
 }
 
 int arm_query(int B, int T, int H, int D, int dtype, int mode) {

@@ -241,10 +241,11 @@ struct ChunkRaw {
 // Parts of one chunk's rows, so that the requests can be spread over the phases of
 // the previous chunk: a burst of all of them stalls every wavefront at the issue.
 enum RawPart { RAW_Q, RAW_K, RAW_G, RAW_V, RAW_BETA };
-// rowb, T: first activation row and row count (>= 1) of the sequence.
+// rowb, T: first activation row and row count (>= 1) of the sequence. v rows are
+// read from vsrc with row stride vstride (a.v and H*D, or a zero row and 0).
 template <bool BF, bool GDN, int NC, RawPart PART>
 __device__ __forceinline__ void load_raw_part(ChunkRaw<GDN, NC>& cr, const MixerArgs& a, size_t rowb, int T,
-                                              int h, int c0, int jv0, int tid) {
+                                              int h, int c0, int jv0, int tid, const void* vsrc, size_t vstride) {
     using CR = ChunkRaw<GDN, NC>;
     const int H = a.H;
     const size_t qkv = (size_t)H * DK, head_off = (size_t)h * DK;
@@ -264,7 +265,7 @@ __device__ __forceinline__ void load_raw_part(ChunkRaw<GDN, NC>& cr, const Mixer
         for (int it = 0; it < CR::NV; ++it) {
             const int idx = min(tid + NTHR * it, CR::VITEMS - 1);
             const int r = idx / (NC / 8), c8 = (idx % (NC / 8)) * 8;
-            cr.v[it] = ld_act8<BF>(a.v, (rowb + min(c0 + r, T - 1)) * qkv + head_off + jv0 + c8);
+            cr.v[it] = ld_act8<BF>(vsrc, (rowb + min(c0 + r, T - 1)) * vstride + head_off + jv0 + c8);
         }
     } else {
         const int rr = tid & (CH - 1);
@@ -275,12 +276,12 @@ __device__ __forceinline__ void load_raw_part(ChunkRaw<GDN, NC>& cr, const Mixer
 }
 template <bool BF, bool GDN, int NC>
 __device__ __forceinline__ void load_raw(ChunkRaw<GDN, NC>& cr, const MixerArgs& a, size_t rowb, int T,
-                                         int h, int c0, int jv0, int tid) {
-    load_raw_part<BF, GDN, NC, RAW_Q>(cr, a, rowb, T, h, c0, jv0, tid);
-    load_raw_part<BF, GDN, NC, RAW_K>(cr, a, rowb, T, h, c0, jv0, tid);
-    load_raw_part<BF, GDN, NC, RAW_G>(cr, a, rowb, T, h, c0, jv0, tid);
-    load_raw_part<BF, GDN, NC, RAW_V>(cr, a, rowb, T, h, c0, jv0, tid);
-    load_raw_part<BF, GDN, NC, RAW_BETA>(cr, a, rowb, T, h, c0, jv0, tid);
+                                         int h, int c0, int jv0, int tid, const void* vsrc, size_t vstride) {
+    load_raw_part<BF, GDN, NC, RAW_Q>(cr, a, rowb, T, h, c0, jv0, tid, vsrc, vstride);
+    load_raw_part<BF, GDN, NC, RAW_K>(cr, a, rowb, T, h, c0, jv0, tid, vsrc, vstride);
+    load_raw_part<BF, GDN, NC, RAW_G>(cr, a, rowb, T, h, c0, jv0, tid, vsrc, vstride);
+    load_raw_part<BF, GDN, NC, RAW_V>(cr, a, rowb, T, h, c0, jv0, tid, vsrc, vstride);
+    load_raw_part<BF, GDN, NC, RAW_BETA>(cr, a, rowb, T, h, c0, jv0, tid, vsrc, vstride);
 }
 
 // The raw rows of a chunk (n valid rows) from registers into LDS; the gates and beta
@@ -497,11 +498,72 @@ __device__ __forceinline__ void merge_column(M& m, int lane) {
     }
 }
 
+// The run of one workgroup of the segmented arm (seg_plan / seg_layout in
+// kda_internal.h): its (b, h) pair, rows [ro, ro + len) of the sequence, where its
+// state comes from and goes to, whether v is replaced by zeros (the M runs) and
+// whether the outputs are written (else they go to a dummy row).
+struct SegRun {
+    int pair, ro, len;
+    const float* s_in;
+    float* s_out;
+    bool zero_v, readout;
+};
+
+// Pass 1: blocks [0, P) run segment 0 of pair b; block P + 16 g + 8 kind + j runs the
+// B (kind 0) or M (kind 1) run of slot 8 g + j = (s - 1) P + pair: the two runs of one
+// slot are 8 blocks apart and so on the same XCD, whose L2 then serves both with the
+// same rows. Pass 3: block (s - 1) P + pair runs segment s. Returns false for the
+// padding blocks of the grid.
+__device__ __forceinline__ bool seg_run(const MixerArgs& a, SegRun* r) {
+    const int P = a.B * a.H, n = a.seg_n, L = a.seg_len;
+    const size_t blk = (size_t)DK * DK;
+    char* ws = reinterpret_cast<char*>(a.seg_ws);
+    const SegLayout lay = seg_layout(P, a.H, DK, n);
+    float* slots = reinterpret_cast<float*>(ws + lay.slots);
+    auto S = [&](int s, int p) { return slots + ((size_t)(s - 1) * P + p) * blk; };
+    auto M = [&](int s, int p) { return slots + ((size_t)(n - 1 + s - 1) * P + p) * blk; };
+    auto Bs = [&](int s, int p) { return slots + ((size_t)(2 * n - 3 + s - 1) * P + p) * blk; };
+    const int d = blockIdx.x;
+    r->zero_v = false;
+    r->readout = true;
+    if (a.seg_pass == 1) {
+        if (d < P) {
+            r->pair = d;
+            r->ro = 0;
+            r->len = n == 1 ? a.T : L;
+            r->s_in = a.state_in + (size_t)d * blk;
+            r->s_out = n == 1 ? a.state_out + (size_t)d * blk : S(1, d);
+            return true;
+        }
+        const int e = d - P, kind = (e % 16) / 8, slot = (e / 16) * 8 + e % 8;
+        if (n < 3 || slot >= (n - 2) * P) return false;
+        const int p = slot % P, sg = 1 + slot / P;
+        r->pair = p;
+        r->ro = sg * L;
+        r->len = L;
+        r->readout = false;
+        r->zero_v = kind == 1;
+        r->s_in = reinterpret_cast<const float*>(ws + (kind ? lay.ident : lay.zero));
+        r->s_out = kind ? M(sg, p) : Bs(sg, p);
+        return true;
+    }
+    if (d >= (n - 1) * P) return false;
+    const int p = d % P, sg = 1 + d / P;
+    r->pair = p;
+    r->ro = sg * L;
+    r->len = sg == n - 1 ? a.T - sg * L : L;
+    r->s_in = S(sg, p);
+    r->s_out = sg == n - 1 ? a.state_out + (size_t)p * blk : Bs(sg, p);  // B_s is spent by then
+    return true;
+}
+
 // ACT (KDA only): the gates arrive as pre-activations and are activated in P1; the
-// given-gate kernel carries none of that code.
-template <bool BF, bool GDN, int NC, int KT, bool ACT>
+// given-gate kernel carries none of that code. SEG: a workgroup of the segmented arm
+// (NC = 128), mapped by seg_run.
+template <bool BF, bool GDN, int NC, int KT, bool ACT, bool SEG = false>
 __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) {
     static_assert(!(GDN && ACT), "GDN gates are activated where they are stored");
+    static_assert(!SEG || NC == DK, "segments run every value column in one workgroup");
     constexpr int NCOL = DK / NC;
     constexpr int NJB = NC / 16;  // value-column 16-blocks of this split
     constexpr int HLD = 2 * DK + NC;
@@ -509,9 +571,18 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
     using CR = ChunkRaw<GDN, NC>;
 
     int bh, split;
-    block_coords(NCOL, a.B * a.H, &bh, &split);
-    if (bh < 0) return;  // whole block exits before any barrier
-    bh = seq_of(a, bh / a.H) * a.H + bh % a.H;  // packed batches: longest sequences first
+    SegRun sr{};
+    if constexpr (SEG) {
+        if (!seg_run(a, &sr)) return;  // whole block exits before any barrier
+        bh = sr.pair;
+        split = 0;
+    } else {
+        block_coords(NCOL, a.B * a.H, &bh, &split);
+        if (bh < 0) return;  // whole block exits before any barrier
+        bh = seq_of(a, bh / a.H) * a.H + bh % a.H;  // packed batches: longest sequences first
+    }
+    const float* s_in = SEG ? sr.s_in : a.state_in + (size_t)bh * DK * DK;
+    float* s_out = SEG ? sr.s_out : a.state_out + (size_t)bh * DK * DK;
 
     int tid = threadIdx.x, lane = tid & 63;
     const int wave = tid >> 6;
@@ -521,6 +592,10 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
     size_t rowb;  // first activation row of this sequence
     int T;        // its row count
     seq_span(a, b, &rowb, &T);
+    if constexpr (SEG) {
+        rowb += sr.ro;
+        T = sr.len;
+    }
     // Re-materialise the lane indices at every phase: otherwise the compiler hoists
     // each phase's lane-dependent LDS addresses out of the chunk loop and keeps them
     // all alive at once, which overflows the register file.
@@ -532,6 +607,15 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
     const size_t head_off = (size_t)h * DK;
     const size_t kw = (size_t)a.Hk * DK, khead = (size_t)(h % a.Hk) * DK;  // q / k: key head h % Hk
     const int jv0 = split * NC;  // first value column of this split
+    // v rows, and the outputs' base and row stride (runs without readout write every
+    // row to one dummy row)
+    const bool zero_v = SEG && sr.zero_v, readout = !SEG || sr.readout;
+    char* const seg_ws = reinterpret_cast<char*>(a.seg_ws);
+    const void* const vsrc = zero_v ? static_cast<const void*>(seg_ws) : a.v;
+    const size_t vstride = zero_v ? 0 : qkv;
+    void* const outp = readout ? a.out : static_cast<void*>(seg_ws + (SEG ? seg_layout(0, a.H, DK, 1).dummy : 0));
+    float* const obp = readout ? o_buf : static_cast<float*>(outp);
+    const size_t orow = readout ? qkv : 0;
 
     // ---- state: S tiles (key block `wave`, value block jb): lane holds keys
     // 16 wave + 4 q4 .. +3 of value column 16 jb + l16 ----
@@ -539,21 +623,31 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb) {
         const int jv = jv0 + jb * 16 + l16;
-        accS[jb] = ld4f(&a.state_in[((size_t)bh * DK + jv) * DK + 16 * wave + 4 * q4]);
+        accS[jb] = ld4f(&s_in[(size_t)jv * DK + 16 * wave + 4 * q4]);
     }
     // Wavefront (sw, hv) = (wave % 4, wave / 4) owns rows 16*sw.. of U / Ub / O and the
     // value blocks [hv*NJB2, (hv+1)*NJB2).
     constexpr int NJB2 = NJB / 2;
     const int sw = wave & 3, hv = wave >> 2;
 
-    // ---- conv history of the first chunk: the old ring (slot K-1-d is d rows back) ----
-    {
+    // ---- conv history of the first chunk: the old ring (slot K-1-d is d rows back),
+    // or for a segment past the sequence start the raw rows before it ----
+    if (!SEG || sr.ro == 0) {
         const float* ring_b = a.ring + (size_t)b * ring_rows(a) * (K - 1);
         for (int idx = tid; idx < (KT - 1) * HLD; idx += NTHR) {
             const int d = idx / HLD + 1, col = idx % HLD;
             const size_t fr = col < 2 * DK ? (size_t)(col / DK) * kw + khead + col % DK
                                            : 2 * kw + head_off + jv0 + (col - 2 * DK);
             sm.hist[d - 1][col] = (__bf16)(d <= K - 1 ? ring_b[fr * (K - 1) + K - 1 - d] : 0.0f);
+        }
+    } else {
+        for (int idx = tid; idx < (KT - 1) * HLD; idx += NTHR) {
+            const int d = idx / HLD + 1, col = idx % HLD;
+            const size_t row = rowb - (size_t)min(d, K - 1);  // segments start >= 64 rows in
+            const float x = col < DK       ? ld_act<BF>(a.q, row * kw + khead + col)
+                            : col < 2 * DK ? ld_act<BF>(a.k, row * kw + khead + col - DK)
+                                           : ld_act<BF>(vsrc, row * vstride + head_off + jv0 + col - 2 * DK);
+            sm.hist[d - 1][col] = (__bf16)(d <= K - 1 ? x : 0.0f);
         }
     }
 
@@ -596,13 +690,13 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
 #pragma unroll
         for (int jb = 0; jb < NJB; ++jb) {
             const int jv = jv0 + jb * 16 + l16;
-            *reinterpret_cast<f32x4v*>(&a.state_out[((size_t)bh * DK + jv) * DK + 16 * wave + 4 * q4]) = accS[jb];
+            *reinterpret_cast<f32x4v*>(&s_out[(size_t)jv * DK + 16 * wave + 4 * q4]) = accS[jb];
         }
         return;  // uniform over the workgroup, before any barrier
     }
 
     CR raw;
-    load_raw<BF, GDN, NC>(raw, a, rowb, T, h, 0, jv0, tid);
+    load_raw<BF, GDN, NC>(raw, a, rowb, T, h, 0, jv0, tid, vsrc, vstride);
     store_raw<GDN, NC, ACT>(sm, raw, min(CH, T), tid, a, cg);
     __syncthreads();
 
@@ -826,7 +920,7 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
         // (unconditional, like the store into LDS at the end of the iteration: past the
         // last chunk the rows clamp to T-1 and are never used, and a branch would make
         // the compiler wait for every outstanding load and store at its join)
-        load_raw_part<BF, GDN, NC, RAW_Q>(raw, a, rowb, T, h, c0 + CH, jv0, tid);
+        load_raw_part<BF, GDN, NC, RAW_Q>(raw, a, rowb, T, h, c0 + CH, jv0, tid, vsrc, vstride);
         KDA_LAUNDER_LANE();
         // ---- P3: T = (I + A)^-1, A = diag(beta) L, in 16x16 blocks; meanwhile the v conv ----
         if (wave < 4) {
@@ -914,7 +1008,7 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
         lds_barrier();
 
         KDA_LAUNDER_LANE();
-        load_raw_part<BF, GDN, NC, RAW_K>(raw, a, rowb, T, h, c0 + CH, jv0, tid);
+        load_raw_part<BF, GDN, NC, RAW_K>(raw, a, rowb, T, h, c0 + CH, jv0, tid, vsrc, vstride);
         // ---- P4: W = T (beta e^{G} k) -> -W in LDS (key block `wave`);
         //      U = T (beta v) in registers (rows 16*sw.., value blocks of half hv) ----
         if (n == CH) {  // the last KT-1 raw v rows become the next chunk's history
@@ -962,7 +1056,7 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
         lds_barrier();
 
         KDA_LAUNDER_LANE();
-        load_raw_part<BF, GDN, NC, RAW_G>(raw, a, rowb, T, h, c0 + CH, jv0, tid);
+        load_raw_part<BF, GDN, NC, RAW_G>(raw, a, rowb, T, h, c0 + CH, jv0, tid, vsrc, vstride);
         // ---- P5: S^T to LDS in bf16, then Ub = U - W S ----
 #pragma unroll
         for (int jb = 0; jb < NJB; ++jb) {
@@ -1014,8 +1108,8 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
         lds_barrier();
 
         KDA_LAUNDER_LANE();
-        load_raw_part<BF, GDN, NC, RAW_V>(raw, a, rowb, T, h, c0 + CH, jv0, tid);
-        load_raw_part<BF, GDN, NC, RAW_BETA>(raw, a, rowb, T, h, c0 + CH, jv0, tid);
+        load_raw_part<BF, GDN, NC, RAW_V>(raw, a, rowb, T, h, c0 + CH, jv0, tid, vsrc, vstride);
+        load_raw_part<BF, GDN, NC, RAW_BETA>(raw, a, rowb, T, h, c0 + CH, jv0, tid, vsrc, vstride);
         // ---- P6: O = scale (Q+ S + P Ub), rows 16*sw.., value blocks of half hv ----
         {
             const int s = 16 * sw + l16;
@@ -1099,7 +1193,7 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
                     ss = sum_row16(ss);
                     const float inv = rsqrtf(fmaf(ss, 1.0f / DK, a.rms_eps));
                     {
-                        const size_t off = (row0 + r) * qkv + head_off + c8;
+                        const size_t off = (row0 + r) * orow + head_off + c8;
                         float y[8];
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
@@ -1111,14 +1205,14 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
                             bf16x8 yb;
 #pragma unroll
                             for (int e = 0; e < 8; ++e) yb[e] = (__bf16)y[e];
-                            st8(static_cast<__bf16*>(a.out) + off, yb);
+                            st8(static_cast<__bf16*>(outp) + off, yb);
                         } else {
-                            float4* d = reinterpret_cast<float4*>(static_cast<float*>(a.out) + off);
+                            float4* d = reinterpret_cast<float4*>(static_cast<float*>(outp) + off);
                             d[0] = make_float4(y[0], y[1], y[2], y[3]);
                             d[1] = make_float4(y[4], y[5], y[6], y[7]);
                         }
-                        if (o_buf) {
-                            float4* d = reinterpret_cast<float4*>(o_buf + off);
+                        if (obp) {
+                            float4* d = reinterpret_cast<float4*>(obp + off);
                             d[0] = make_float4(o8[0], o8[1], o8[2], o8[3]);
                             d[1] = make_float4(o8[4], o8[5], o8[6], o8[7]);
                         }
@@ -1145,7 +1239,7 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
 #pragma unroll
     for (int jb = 0; jb < NJB; ++jb) {
         const int jv = jv0 + jb * 16 + l16;
-        *reinterpret_cast<f32x4v*>(&a.state_out[((size_t)bh * DK + jv) * DK + 16 * wave + 4 * q4]) = accS[jb];
+        *reinterpret_cast<f32x4v*>(&s_out[(size_t)jv * DK + 16 * wave + 4 * q4]) = accS[jb];
     }
 }
 #undef KDA_LAUNDER_LANE
@@ -1196,7 +1290,107 @@ hipError_t chunk_launch(const MixerArgs& a) {
     return launch_ring_roll(a, false);
 }
 
+// The constant blocks of the segmented arm's workspace: zeros (state and v row of
+// the M runs) and the identity (entry state of the M runs). A kernel rather than a
+// memset, so that the call can be captured in a graph.
+__global__ void seg_init_kernel(float* zero, size_t nzero, float* ident) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < nzero) zero[i] = 0.0f;
+    if (i < (size_t)DK * DK) ident[i] = (i / DK == i % DK) ? 1.0f : 0.0f;
+}
+
+// Entry states of the middle segments: S_{s+1} = M_s S_s + B_s for s = 1 .. n-2, in
+// fp32. Workgroup (pair, 16-column block cb): thread t computes key i = t % 128 of
+// columns cb*16 + 8 (t / 128) .. +7. State blocks are [value][key], so M_s (the
+// final state of the run from the identity) holds M[i][k] at [k][i].
+constexpr int SCAN_COLS = 16;
+__global__ __launch_bounds__(256) void seg_scan_kernel(MixerArgs a) {
+    const int P = a.B * a.H, n = a.seg_n;
+    const int pair = blockIdx.x / (DK / SCAN_COLS), cb = blockIdx.x % (DK / SCAN_COLS);
+    if (pair >= P) return;
+    const size_t blk = (size_t)DK * DK;
+    const SegLayout lay = seg_layout(P, a.H, DK, n);
+    float* slots = reinterpret_cast<float*>(reinterpret_cast<char*>(a.seg_ws) + lay.slots);
+    auto S = [&](int s) { return slots + ((size_t)(s - 1) * P + pair) * blk; };
+    auto M = [&](int s) { return slots + ((size_t)(n - 1 + s - 1) * P + pair) * blk; };
+    auto Bs = [&](int s) { return slots + ((size_t)(2 * n - 3 + s - 1) * P + pair) * blk; };
+    __shared__ float sc[SCAN_COLS][DK];  // the current entry state's columns [j][k]
+    const int t = threadIdx.x, i = t % DK, j0 = (t / DK) * 8;
+    const size_t col0 = (size_t)cb * SCAN_COLS;
+    for (int e = 0; e < 8; ++e) sc[j0 + e][i] = S(1)[(col0 + j0 + e) * DK + i];
+    for (int s = 1; s <= n - 2; ++s) {
+        __syncthreads();
+        const float* m = M(s);
+        float acc[8];
+        for (int e = 0; e < 8; ++e) acc[e] = Bs(s)[(col0 + j0 + e) * DK + i];
+        for (int k = 0; k < DK; ++k) {
+            const float mik = m[(size_t)k * DK + i];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = fmaf(mik, sc[j0 + e][k], acc[e]);
+        }
+        for (int e = 0; e < 8; ++e) S(s + 1)[(col0 + j0 + e) * DK + i] = acc[e];
+        __syncthreads();
+        for (int e = 0; e < 8; ++e) sc[j0 + e][i] = acc[e];
+    }
+}
+
+template <bool BF, bool GDN>
+hipError_t seg_pass(const MixerArgs& a, int grid) {
+    if (grid <= 0) return hipSuccess;
+    const bool act = !GDN && a.gate_form != GATE_GIVEN;
+    const dim3 g(grid), blk(NTHR);
+    float* ob = a.o_core;
+    if (a.K == 4) {
+        if (act) hipLaunchKernelGGL((chunk_kernel<BF, GDN, DK, 4, !GDN, true>), g, blk, 0, a.stream, a, ob);
+        else hipLaunchKernelGGL((chunk_kernel<BF, GDN, DK, 4, false, true>), g, blk, 0, a.stream, a, ob);
+    } else {
+        if (act) hipLaunchKernelGGL((chunk_kernel<BF, GDN, DK, KMAX, !GDN, true>), g, blk, 0, a.stream, a, ob);
+        else hipLaunchKernelGGL((chunk_kernel<BF, GDN, DK, KMAX, false, true>), g, blk, 0, a.stream, a, ob);
+    }
+    return hipGetLastError();
+}
+
+template <bool BF, bool GDN>
+hipError_t seg_launch(MixerArgs a) {
+    const int P = a.B * a.H, n = a.seg_n;
+    const SegLayout lay = seg_layout(P, a.H, DK, n);
+    a.seg_ws = static_cast<float*>(a.ws);
+    char* ws = static_cast<char*>(a.ws);
+    const size_t nzero = (lay.ident - lay.zero) / 4;
+    const size_t ninit = nzero > (size_t)DK * DK ? nzero : (size_t)DK * DK;
+    hipLaunchKernelGGL(seg_init_kernel, dim3((unsigned)((ninit + 255) / 256)), dim3(256), 0, a.stream,
+                       reinterpret_cast<float*>(ws + lay.zero), nzero, reinterpret_cast<float*>(ws + lay.ident));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a.seg_pass = 1;
+    const int mid = n >= 3 ? (n - 2) * P : 0;
+    e = seg_pass<BF, GDN>(a, P + 16 * ((mid + 7) / 8));
+    if (e != hipSuccess) return e;
+    if (n >= 3) {
+        hipLaunchKernelGGL(seg_scan_kernel, dim3(P * (DK / SCAN_COLS)), dim3(256), 0, a.stream, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (n >= 2) {
+        a.seg_pass = 3;
+        e = seg_pass<BF, GDN>(a, (n - 1) * P);
+        if (e != hipSuccess) return e;
+    }
+    return launch_ring_roll(a, false);
+}
+
 }  // namespace
+
+size_t segmented_workspace_bytes(int B, int H, int D, int n) {
+    if (D != DK) return 0;
+    return seg_layout((long)B * H, H, D, n).total;
+}
+
+hipError_t launch_segmented(const MixerArgs& a) {
+    if (a.D != DK || a.cu_seqlens || a.seg_n < 1 || a.seg_len < CH || !a.ws) return hipErrorInvalidValue;
+    if (a.bf16) return a.gdn ? seg_launch<true, true>(a) : seg_launch<true, false>(a);
+    return a.gdn ? seg_launch<false, true>(a) : seg_launch<false, false>(a);
+}
 
 size_t chunked_workspace_bytes(int nseq, size_t rows, int H, int D) {
     if (D != DK || chunk_ncol(nseq, H) == 1) return 0;

@@ -56,7 +56,57 @@ struct MixerArgs {
     // launch_seq_order), so that the first workgroups dispatched take the longest work;
     // null: in index order.
     const int* seq_order;
+    // Segmented chunked prefill (ARM_SEGMENTED): segment count and rows per segment of
+    // the plan, the pass a launch runs (1 or 3) and the workspace holding the segment
+    // states (SegLayout).
+    int seg_n, seg_len, seg_pass;
+    float* seg_ws;
 };
+
+// Segmented chunked prefill. The state map of a run of tokens is affine in its
+// entry state, S_out = M S_in + B: the recurrence's decay and delta-rule update act
+// on the key index by left multiplication and add a term that does not depend on S.
+// Each sequence is cut into n segments of len rows (the last one takes the rest).
+// Pass 1 runs segment 0 from the given state and, for every middle segment s, the
+// same tokens twice: from a zero state (its final state is B_s) and from the
+// identity with v = 0 (its final state is M_s). A scan then forms the entry states
+// S_{s+1} = M_s S_s + B_s, and pass 3 runs segments 1 .. n-1 from them with readout.
+// Pass 1 has pairs * (2n - 3) workgroups; n is the largest count that keeps them in
+// one wave over the 256 compute units, with at least min_chunks chunks of 64 rows
+// per segment and at most kSegMax segments.
+constexpr int kSegMax = 32;
+constexpr int kSegCUs = 256;
+struct SegPlan {
+    int n, len;
+};
+__host__ __device__ inline SegPlan seg_plan(long pairs, int T, int min_chunks) {
+    const int nch = (T + 63) / 64;
+    long cap = pairs > kSegCUs ? 1 : (kSegCUs / pairs + 3) / 2;
+    cap = cap < kSegMax ? cap : kSegMax;
+    long n = nch / (min_chunks > 0 ? min_chunks : 1);
+    n = n < cap ? n : cap;
+    if (n < 1) n = 1;
+    return SegPlan{(int)n, (int)(nch / n) * 64};
+}
+// Byte offsets of the segmented arm's workspace: a zero block (also the zero v row of
+// the M runs), the identity, a dummy output row for runs without readout, then the
+// fp32 D x D state blocks [slot][pair] of S_1 .. S_{n-1}, M_1 .. M_{n-2},
+// B_1 .. B_{n-2} (state layout [value][key]).
+struct SegLayout {
+    size_t zero, ident, dummy, slots, total;
+};
+__host__ __device__ inline SegLayout seg_layout(long pairs, int H, int D, int n) {
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t blk = (size_t)D * D * 4, row = (size_t)H * D * 4;
+    SegLayout l;
+    l.zero = 0;
+    l.ident = al(blk > row ? blk : row);
+    l.dummy = l.ident + al(blk);
+    l.slots = l.dummy + al(row);
+    const size_t nslot = n >= 2 ? (size_t)(n - 1) + 2 * (size_t)(n >= 3 ? n - 2 : 0) : 0;
+    l.total = l.slots + nslot * (size_t)pairs * blk;
+    return l;
+}
 
 // Sequence processed by the workgroups of dispatch rank r.
 __device__ inline int seq_of(const MixerArgs& a, int r) { return a.seq_order ? a.seq_order[r] : r; }
@@ -92,7 +142,7 @@ __host__ __device__ inline size_t ring_rows(const MixerArgs& a) { return (size_t
 enum GateForm { GATE_GIVEN = 0, GATE_SIGMOID = 1, GATE_SOFTPLUS = 2 };
 
 // Arms (values match the KDA_ARM_* codes of the public header).
-enum Arm { ARM_SEQ_FUSED = 1, ARM_SEQ_SPLIT = 2, ARM_CHUNKED = 3 };
+enum Arm { ARM_SEQ_FUSED = 1, ARM_SEQ_SPLIT = 2, ARM_CHUNKED = 3, ARM_SEGMENTED = 4 };
 
 // Workspace carve-up of the split sequential arm: fp32 arrays, each starting on a
 // 256-byte boundary.
@@ -107,10 +157,16 @@ extern const bool kChunkedArmBuilt;
 // Workspace of the chunked arm: nseq sequences of H heads, rows activation rows in all.
 size_t chunked_workspace_bytes(int nseq, size_t rows, int H, int D);
 
+// Workspace of the segmented arm for B sequences of H heads cut into n segments.
+size_t segmented_workspace_bytes(int B, int H, int D, int n);
+
 // Launchers: enqueue on a.stream, return the first launch error (hipSuccess if none).
 hipError_t launch_seq_fused(const MixerArgs& a);
 hipError_t launch_seq_split(const MixerArgs& a);
 hipError_t launch_chunked(const MixerArgs& a);
+// Segmented chunked prefill; a.seg_n / a.seg_len hold the plan and a.ws its
+// workspace (seg_layout).
+hipError_t launch_segmented(const MixerArgs& a);
 // Gated RMSNorm of a fp32 pre-norm output o [B][T][H*D] into a.out.
 hipError_t launch_norm(const MixerArgs& a, const float* o);
 // Rank the B sequences of a packed batch by length, longest first (ties by index),

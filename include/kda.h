@@ -79,9 +79,18 @@ extern "C" {
 /* ---- dtype and prefill mode ---- */
 #define KDA_DTYPE_F32 0
 #define KDA_DTYPE_BF16 1
-#define KDA_MODE_AUTO 0       /* library picks sequential or chunked from the shape */
+#define KDA_MODE_AUTO 0       /* library picks sequential, chunked or segmented from the shape */
 #define KDA_MODE_SEQUENTIAL 1 /* token-by-token scan (bit-identical to chained decodes) */
 #define KDA_MODE_CHUNKED 2    /* chunk-64 WY form, bf16 MFMA operands, fp32 state (D = 128) */
+/* The chunked form with every sequence cut into segments that run in parallel (D = 128,
+ * equal-length sequences; not for packed batches). A run of tokens maps its entry state
+ * affinely, S_out = M S_in + B: the decay and the delta-rule update of stage 5 above act
+ * on the key index by left multiplication. The segments' M and B are computed in
+ * parallel, a scan forms each segment's entry state, and the segments run again from
+ * it with readout. AUTO takes it for few (b, h) pairs and long sequences; this mode
+ * forces it, with segments as short as one chunk. Same accuracy contract as
+ * KDA_MODE_CHUNKED. */
+#define KDA_MODE_SEGMENTED 3
 
 /* Gate activation of the *_gated entry points (the plain entry points take g and
  * beta already activated). x is the gate pre-activation read from `g`, b the beta
@@ -101,6 +110,7 @@ extern "C" {
 #define KDA_ARM_SEQ_FUSED 1   /* one kernel per (b, h): conv, l2, scan, norm and ring fused */
 #define KDA_ARM_SEQ_SPLIT 2   /* pre-kernel, column-split scan, norm kernel */
 #define KDA_ARM_CHUNKED 3     /* chunked prefill */
+#define KDA_ARM_SEGMENTED 4   /* chunked prefill, segments of each sequence in parallel */
 
 /*
  * kda_prefill - run the mixer over T tokens of B sequences.
@@ -109,8 +119,8 @@ extern "C" {
  *   scale multiplies the readout (head_dim^-1/2 in the source model);
  *   rms_eps is the RMSNorm epsilon.
  *   mode: KDA_MODE_*. The sequential mode gives results bit-identical to T
- *   successive kda_decode calls. The chunked mode agrees with it to bf16-operand
- *   accuracy and requires D == 128.
+ *   successive kda_decode calls. The chunked and segmented modes agree with it to
+ *   bf16-operand accuracy and require D == 128.
  *   workspace: device buffer of at least kda_prefill_workspace_bytes(...) bytes
  *   (may be NULL when that is 0). Its contents on entry are ignored.
  * Returns KDA_OK or a status code above.
@@ -322,7 +332,8 @@ size_t gdn_gqa_workspace_bytes(int B, int T, int H, int Hk, int D, int dtype, in
  * layout; kda_prefill_varlen has Hk = H). gate_form / gate_a / gate_bias / gate_lb
  * as for gdn_prefill_gqa (0: g and beta given).
  * Arms: KDA_MODE_SEQUENTIAL runs the fused sequential arm (one workgroup per
- * (sequence, head)); KDA_MODE_CHUNKED the chunked arm (D = 128); KDA_MODE_AUTO the
+ * (sequence, head)); KDA_MODE_CHUNKED the chunked arm (D = 128); KDA_MODE_SEGMENTED is
+ * rejected (KDA_ERR_DTYPE_MODE); KDA_MODE_AUTO the
  * chunked arm for bf16 activations at D = 128, else the fused arm. Each sequence is
  * processed exactly as a call on that sequence alone would process it on the same arm
  * (the fused arm bit for bit). workspace: at least *_prefill_varlen_workspace_bytes

@@ -74,12 +74,12 @@ def test_fp32_inputs_chunked():
 
 
 def test_prefill_full_size():
-    """Single-sequence prefill T=4626, H=64 (4 column splits): sampled heads against the
-    oracle, everything against the sequential arm."""
+    """Single-sequence prefill T=4626, H=64 on the chunked arm (4 column splits):
+    sampled heads against the oracle, everything against the sequential arm."""
     cfg = CONFIGS["kda_prefill"]
     inp, dev = inputs_for(cfg)
-    assert kda.prefill_arm(cfg.B, cfg.T, cfg.H, cfg.D, 1, kda.KDA_MODE_AUTO) == 3
-    got = run_gpu(cfg, dev, mode=kda.KDA_MODE_AUTO)
+    assert kda.prefill_arm(cfg.B, cfg.T, cfg.H, cfg.D, 1, CHK) == 3
+    got = run_gpu(cfg, dev, mode=CHK)
     torch.cuda.synchronize()
     ref, ch, rows, bsel, hh = oracle_run(inp, heads=[0, 33, 63])
     errs = compare_to_oracle(cfg, got, ref, ch, rows, bsel, hh, tol=TOL)

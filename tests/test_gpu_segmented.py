@@ -1,0 +1,130 @@
+"""GPU parity of the segmented chunked prefill (KDA_MODE_SEGMENTED): each sequence is
+cut into segments that run in parallel, and the segments are joined by the affine state
+scan. The segmented run is checked against the fp64 oracle. Segments of one chunk give
+several scan steps and a ragged last segment. The segmented arm is also checked against
+the sequential arm at the single-sequence prefill workload, which AUTO sends to it."""
+import pytest
+import torch
+
+import gated_delta_rule_68_amd as kda
+import oracle
+from gated_delta_rule_68_amd.synth import CONFIGS
+from gated_delta_rule_68_amd.torch_io import to_f64
+from tests.gpu_util import DEV, compare_to_oracle, inputs_for, oracle_run, run_gpu
+from tests.test_gpu_gates import compare as compare_gated
+from tests.test_gpu_gates import gate_params, oracle_gated, run_gated
+from tests.test_gpu_gqa import compare as compare_gqa
+from tests.test_gpu_gqa import oracle_heads, run_gqa
+
+pytestmark = pytest.mark.gpu
+SEG, SEQ, CHK = kda.KDA_MODE_SEGMENTED, kda.KDA_MODE_SEQUENTIAL, kda.KDA_MODE_CHUNKED
+TOL = 2e-2  # bf16-operand arm
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+def _check(cfg, heads=None, tol=TOL, **run_kw):
+    inp, dev = inputs_for(cfg)
+    got = run_gpu(cfg, dev, mode=SEG, **run_kw)
+    torch.cuda.synchronize()
+    ref, ch, rows, bsel, hh = oracle_run(inp, heads=heads, threads=16)
+    errs = compare_to_oracle(cfg, got, ref, ch, rows, bsel, hh, tol=tol)
+    _print("errs", errs)
+    return got, dev
+
+
+# At B*H = 2 the plan takes one segment per chunk: T = 50 is one segment, 100 two (no
+# scan step), 300 five (three scan steps, a 44-row last segment), 700 eleven.
+@pytest.mark.parametrize("T", [50, 100, 300, 700])
+@pytest.mark.parametrize("gdn", [False, True])
+def test_one_chunk_segments_vs_oracle(T, gdn):
+    cfg = CONFIGS["kda_decode"].with_(B=1, H=2, T=T, gdn=gdn)
+    _print("case", cfg)
+    _check(cfg)
+
+
+@pytest.mark.parametrize("gdn", [False, True])
+def test_three_segments_many_pairs_vs_oracle(gdn):
+    """B*H = 80: three segments (one wave of 240 pass-1 workgroups), sampled heads."""
+    cfg = CONFIGS["kda_decode"].with_(B=2, H=40, T=300, gdn=gdn)
+    _check(cfg, heads=[0, 17, 39])
+
+
+def test_wide_conv_fp32_and_alternating_gates_vs_oracle():
+    """K = 6 (history of five rows read from the rows before each segment), fp32
+    activations, and gates pushed to both ends of [-5, 0] on alternate heads."""
+    cfg = CONFIGS["kda_long"].with_(B=1, T=330, H=4, K=6, dtype="fp32", random_init=True)
+    _check(cfg)
+
+
+def test_in_place_state_vs_oracle():
+    cfg = CONFIGS["kda_decode"].with_(B=1, H=3, T=260)
+    _check(cfg, inplace=True)
+
+
+@pytest.mark.parametrize("gdn", [False, True])
+def test_gated_vs_oracle(gdn):
+    cfg = CONFIGS["kda_decode"].with_(B=1, H=3, T=300, gdn=gdn)
+    inp, dev = inputs_for(cfg)
+    form = kda.KDA_GATE_SIGMOID
+    ga, gb, g, beta = gate_params(inp, dev, form)
+    got = run_gated(cfg, dev, ga, gb, form, mode=SEG)
+    torch.cuda.synchronize()
+    ref, ch, rows, bsel = oracle_gated(inp, g, beta, heads=[0, 1, 2])
+    compare_gated(cfg, got, ref, ch, rows, bsel, [0, 1, 2], TOL)
+
+
+def test_grouped_heads_vs_oracle():
+    cfg = CONFIGS["gdn_prefill"].with_(B=2, T=300, H=8, Hk=4, random_init=True)
+    inp, dev = inputs_for(cfg)
+    got = run_gqa(cfg, dev, mode=SEG)
+    torch.cuda.synchronize()
+    heads = list(range(cfg.H))
+    ref, vc, rows, bsel = oracle_heads(inp, heads, [0, 1])
+    compare_gqa(got, ref, vc, rows, bsel, heads, TOL)
+
+
+def test_prefill_workload_auto_is_segmented():
+    """Single-sequence prefill T = 4626, H = 64: AUTO takes three segments. Sampled heads
+    against the oracle, everything against the sequential arm and the unsegmented
+    chunked arm."""
+    cfg = CONFIGS["kda_prefill"]
+    assert kda.prefill_arm(cfg.B, cfg.T, cfg.H, cfg.D, kda.KDA_DTYPE_BF16, kda.KDA_MODE_AUTO) == 4
+    inp, dev = inputs_for(cfg)
+    got = run_gpu(cfg, dev, mode=kda.KDA_MODE_AUTO)
+    torch.cuda.synchronize()
+    ref, ch, rows, bsel, hh = oracle_run(inp, heads=[0, 33, 63])
+    _print("oracle errs", compare_to_oracle(cfg, got, ref, ch, rows, bsel, hh, tol=TOL))
+    for mode in (SEQ, CHK):
+        other = run_gpu(cfg, dev, mode=mode)
+        errs = {k: oracle.rel_linf(to_f64(got[k]), to_f64(other[k])) for k in ("out", "o_core", "state", "ring")}
+        _print("vs mode", mode, errs)
+        assert max(errs.values()) <= TOL and errs["ring"] == 0.0
+
+
+def test_segmented_gdn_few_pairs_auto():
+    """GDN, one sequence of 2048 rows, 16 heads: AUTO takes four segments of eight
+    chunks; checked against the sequential arm."""
+    cfg = CONFIGS["gdn_prefill"].with_(B=1, T=2048, H=16)
+    assert kda.prefill_arm(cfg.B, cfg.T, cfg.H, cfg.D, kda.KDA_DTYPE_BF16, kda.KDA_MODE_AUTO, gdn=True) == 4
+    inp, dev = inputs_for(cfg)
+    got = run_gpu(cfg, dev, mode=kda.KDA_MODE_AUTO)
+    ref = run_gpu(cfg, dev, mode=SEQ)
+    torch.cuda.synchronize()
+    errs = {k: oracle.rel_linf(to_f64(got[k]), to_f64(ref[k])) for k in ("out", "o_core", "state", "ring")}
+    _print("vs sequential", errs)
+    assert max(errs.values()) <= TOL and errs["ring"] == 0.0
+
+
+def test_repeated_calls_reuse_the_workspace():
+    """The workspace's constant blocks are rebuilt by every call: a second call on a
+    workspace full of the first call's values gives the same result bit for bit."""
+    cfg = CONFIGS["kda_decode"].with_(B=1, H=2, T=300)
+    inp, dev = inputs_for(cfg)
+    a = run_gpu(cfg, dev, mode=SEG)
+    b = run_gpu(cfg, dev, mode=SEG)
+    torch.cuda.synchronize()
+    for k in ("out", "o_core", "state", "ring"):
+        assert torch.equal(a[k], b[k]), k
