@@ -587,7 +587,9 @@ def main():
                     help="only run the 1 GiB device copy (counter calibration)")
     ap.add_argument("--prefill-only", metavar="WORKLOAD",
                     help="only run this prefill workload (kda_prefill, gdn_prefill, kda_long) on "
-                         "the chunked arm, --steps times after one warm-up (for profilers)")
+                         "the arm of --prefill-mode, --steps times after one warm-up (for profilers)")
+    ap.add_argument("--prefill-mode", choices=("chunked", "segmented", "auto"), default="chunked",
+                    help="prefill mode of --prefill-only (default: chunked)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -611,7 +613,9 @@ def main():
         import gated_delta_rule_68_amd as kda
 
         cfg = CONFIGS[args.prefill_only]
-        ms, arm = run_prefill(cfg, kda.KDA_MODE_CHUNKED, reps=max(1, args.steps))
+        mode = {"chunked": kda.KDA_MODE_CHUNKED, "segmented": kda.KDA_MODE_SEGMENTED,
+                "auto": kda.KDA_MODE_AUTO}[args.prefill_mode]
+        ms, arm = run_prefill(cfg, mode, reps=max(1, args.steps))
         print(json.dumps({"workload": args.prefill_only, "arm": arm, "ms": ms,
                           "tokens_per_s": cfg.B * cfg.T / (ms * 1e-3)}), flush=True)
         return

@@ -44,13 +44,17 @@ int check_shape(int B, int T, int H, int D, int K) {
 // very short prefills where its extra launches would dominate.
 // The chunked arm (D = 128) computes its contractions with bf16 operands, so AUTO
 // takes it only for bf16 activations and prefills of at least two chunks.
-// Few (b, h) pairs leave most compute units idle in the chunked arm; AUTO then cuts
-// each sequence into at least three segments of at least kSegAutoChunks chunks and
-// takes the segmented arm (kda_internal.h, seg_plan). The explicit mode accepts
-// segments of one chunk.
+// Few (b, h) pairs leave most compute units idle in the chunked arm. AUTO takes the
+// segmented arm (kda_internal.h, seg_plan) when its plan, with segments of at least
+// kSegAutoChunks chunks, shortens the critical path to at most 85% of the chunk
+// count. The explicit mode accepts segments of one chunk.
 constexpr int kSegAutoChunks = 8;
 kda::SegPlan plan_for(int B, int T, int H, int mode) {
     return kda::seg_plan((long)B * H, T, mode == KDA_MODE_SEGMENTED ? 1 : kSegAutoChunks);
+}
+bool segments_pay(int B, int T, int H) {
+    const kda::SegPlan p = plan_for(B, T, H, KDA_MODE_AUTO);
+    return p.n >= 3 && p.cost * 100 <= 85 * ((T + 63) / 64);
 }
 
 int pick_arm(int B, int T, int H, int D, bool bf16, int mode) {
@@ -58,7 +62,7 @@ int pick_arm(int B, int T, int H, int D, bool bf16, int mode) {
     if (mode == KDA_MODE_CHUNKED) return chunk_ok ? kda::ARM_CHUNKED : -1;
     if (mode == KDA_MODE_SEGMENTED) return chunk_ok ? kda::ARM_SEGMENTED : -1;
     if (mode == KDA_MODE_AUTO && chunk_ok && bf16 && T >= 128)
-        return plan_for(B, T, H, mode).n >= 3 ? kda::ARM_SEGMENTED : kda::ARM_CHUNKED;
+        return segments_pay(B, T, H) ? kda::ARM_SEGMENTED : kda::ARM_CHUNKED;
     if (mode != KDA_MODE_AUTO && mode != KDA_MODE_SEQUENTIAL) return -1;
     if (T <= 16 || (long)B * H >= 1024) return kda::ARM_SEQ_FUSED;
     return kda::ARM_SEQ_SPLIT;
@@ -167,6 +171,7 @@ int run(MixerArgs a, int arm, int mode = KDA_MODE_AUTO) {
     if (arm == kda::ARM_SEGMENTED) {
         const kda::SegPlan p = plan_for(a.B, a.T, a.H, mode);
         a.seg_n = p.n;
+        a.seg_len0 = p.len0;
         a.seg_len = p.len;
     }
     switch (arm) {

@@ -509,13 +509,14 @@ struct SegRun {
     bool zero_v, readout;
 };
 
-// Pass 1: blocks [0, P) run segment 0 of pair b; block P + 16 g + 8 kind + j runs the
+// Pass 1: blocks [0, P) run segment 0 of pair b (dispatched first: they are the
+// longest); block P + 16 g + 8 kind + j runs the
 // B (kind 0) or M (kind 1) run of slot 8 g + j = (s - 1) P + pair: the two runs of one
 // slot are 8 blocks apart and so on the same XCD, whose L2 then serves both with the
 // same rows. Pass 3: block (s - 1) P + pair runs segment s. Returns false for the
 // padding blocks of the grid.
 __device__ __forceinline__ bool seg_run(const MixerArgs& a, SegRun* r) {
-    const int P = a.B * a.H, n = a.seg_n, L = a.seg_len;
+    const int P = a.B * a.H, n = a.seg_n, L0 = a.seg_len0, L = a.seg_len;
     const size_t blk = (size_t)DK * DK;
     char* ws = reinterpret_cast<char*>(a.seg_ws);
     const SegLayout lay = seg_layout(P, a.H, DK, n);
@@ -530,7 +531,7 @@ __device__ __forceinline__ bool seg_run(const MixerArgs& a, SegRun* r) {
         if (d < P) {
             r->pair = d;
             r->ro = 0;
-            r->len = n == 1 ? a.T : L;
+            r->len = n == 1 ? a.T : L0;
             r->s_in = a.state_in + (size_t)d * blk;
             r->s_out = n == 1 ? a.state_out + (size_t)d * blk : S(1, d);
             return true;
@@ -539,7 +540,7 @@ __device__ __forceinline__ bool seg_run(const MixerArgs& a, SegRun* r) {
         if (n < 3 || slot >= (n - 2) * P) return false;
         const int p = slot % P, sg = 1 + slot / P;
         r->pair = p;
-        r->ro = sg * L;
+        r->ro = L0 + (sg - 1) * L;
         r->len = L;
         r->readout = false;
         r->zero_v = kind == 1;
@@ -550,8 +551,8 @@ __device__ __forceinline__ bool seg_run(const MixerArgs& a, SegRun* r) {
     if (d >= (n - 1) * P) return false;
     const int p = d % P, sg = 1 + d / P;
     r->pair = p;
-    r->ro = sg * L;
-    r->len = sg == n - 1 ? a.T - sg * L : L;
+    r->ro = L0 + (sg - 1) * L;
+    r->len = sg == n - 1 ? a.T - r->ro : L;
     r->s_in = S(sg, p);
     r->s_out = sg == n - 1 ? a.state_out + (size_t)p * blk : Bs(sg, p);  // B_s is spent by then
     return true;
@@ -1302,8 +1303,10 @@ __global__ void seg_init_kernel(float* zero, size_t nzero, float* ident) {
 // Entry states of the middle segments: S_{s+1} = M_s S_s + B_s for s = 1 .. n-2, in
 // fp32. Workgroup (pair, 16-column block cb): thread t computes key i = t % 128 of
 // columns cb*16 + 8 (t / 128) .. +7. State blocks are [value][key], so M_s (the
-// final state of the run from the identity) holds M[i][k] at [k][i].
-constexpr int SCAN_COLS = 16;
+// final state of the run from the identity) holds M[i][k] at [k][i]: a wavefront's
+// loads of M are coalesced over i, and the current state's columns sit in LDS as
+// [k][column], read as two 16-byte broadcasts per k.
+constexpr int SCAN_COLS = 16, SCAN_KB = 8;
 __global__ __launch_bounds__(256) void seg_scan_kernel(MixerArgs a) {
     const int P = a.B * a.H, n = a.seg_n;
     const int pair = blockIdx.x / (DK / SCAN_COLS), cb = blockIdx.x % (DK / SCAN_COLS);
@@ -1314,23 +1317,31 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(MixerArgs a) {
     auto S = [&](int s) { return slots + ((size_t)(s - 1) * P + pair) * blk; };
     auto M = [&](int s) { return slots + ((size_t)(n - 1 + s - 1) * P + pair) * blk; };
     auto Bs = [&](int s) { return slots + ((size_t)(2 * n - 3 + s - 1) * P + pair) * blk; };
-    __shared__ float sc[SCAN_COLS][DK];  // the current entry state's columns [j][k]
+    __shared__ __align__(16) float sc[DK][SCAN_COLS];  // the current entry state [k][j]
     const int t = threadIdx.x, i = t % DK, j0 = (t / DK) * 8;
     const size_t col0 = (size_t)cb * SCAN_COLS;
-    for (int e = 0; e < 8; ++e) sc[j0 + e][i] = S(1)[(col0 + j0 + e) * DK + i];
+    for (int e = 0; e < 8; ++e) sc[i][j0 + e] = S(1)[(col0 + j0 + e) * DK + i];
     for (int s = 1; s <= n - 2; ++s) {
         __syncthreads();
-        const float* m = M(s);
+        const float* m = M(s) + i;
         float acc[8];
         for (int e = 0; e < 8; ++e) acc[e] = Bs(s)[(col0 + j0 + e) * DK + i];
-        for (int k = 0; k < DK; ++k) {
-            const float mik = m[(size_t)k * DK + i];
+        for (int k0 = 0; k0 < DK; k0 += SCAN_KB) {
+            float mv[SCAN_KB];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] = fmaf(mik, sc[j0 + e][k], acc[e]);
+            for (int kk = 0; kk < SCAN_KB; ++kk) mv[kk] = m[(size_t)(k0 + kk) * DK];
+#pragma unroll
+            for (int kk = 0; kk < SCAN_KB; ++kk) {
+                const float4 lo = *reinterpret_cast<const float4*>(&sc[k0 + kk][j0]);
+                const float4 hi = *reinterpret_cast<const float4*>(&sc[k0 + kk][j0 + 4]);
+                const float sv[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] = fmaf(mv[kk], sv[e], acc[e]);
+            }
         }
         for (int e = 0; e < 8; ++e) S(s + 1)[(col0 + j0 + e) * DK + i] = acc[e];
         __syncthreads();
-        for (int e = 0; e < 8; ++e) sc[j0 + e][i] = acc[e];
+        for (int e = 0; e < 8; ++e) sc[i][j0 + e] = acc[e];
     }
 }
 
@@ -1387,7 +1398,8 @@ size_t segmented_workspace_bytes(int B, int H, int D, int n) {
 }
 
 hipError_t launch_segmented(const MixerArgs& a) {
-    if (a.D != DK || a.cu_seqlens || a.seg_n < 1 || a.seg_len < CH || !a.ws) return hipErrorInvalidValue;
+    if (a.D != DK || a.cu_seqlens || a.seg_n < 1 || a.seg_len0 < 1 || (a.seg_n > 1 && a.seg_len < CH) || !a.ws)
+        return hipErrorInvalidValue;
     if (a.bf16) return a.gdn ? seg_launch<true, true>(a) : seg_launch<true, false>(a);
     return a.gdn ? seg_launch<false, true>(a) : seg_launch<false, false>(a);
 }

@@ -56,37 +56,54 @@ struct MixerArgs {
     // launch_seq_order), so that the first workgroups dispatched take the longest work;
     // null: in index order.
     const int* seq_order;
-    // Segmented chunked prefill (ARM_SEGMENTED): segment count and rows per segment of
-    // the plan, the pass a launch runs (1 or 3) and the workspace holding the segment
-    // states (SegLayout).
-    int seg_n, seg_len, seg_pass;
+    // Segmented chunked prefill (ARM_SEGMENTED): segment count, rows of segment 0 and
+    // of the others (seg_plan), the pass a launch runs (1 or 3) and the workspace
+    // holding the segment states (SegLayout).
+    int seg_n, seg_len0, seg_len, seg_pass;
     float* seg_ws;
 };
 
 // Segmented chunked prefill. The state map of a run of tokens is affine in its
 // entry state, S_out = M S_in + B: the recurrence's decay and delta-rule update act
 // on the key index by left multiplication and add a term that does not depend on S.
-// Each sequence is cut into n segments of len rows (the last one takes the rest).
-// Pass 1 runs segment 0 from the given state and, for every middle segment s, the
-// same tokens twice: from a zero state (its final state is B_s) and from the
-// identity with v = 0 (its final state is M_s). A scan then forms the entry states
-// S_{s+1} = M_s S_s + B_s, and pass 3 runs segments 1 .. n-1 from them with readout.
-// Pass 1 has pairs * (2n - 3) workgroups; n is the largest count that keeps them in
-// one wave over the 256 compute units, with at least min_chunks chunks of 64 rows
-// per segment and at most kSegMax segments.
+// Each sequence is cut into n segments: segment 0 of len0 rows, then segments of len
+// rows (the last one takes the rest). Pass 1 runs segment 0 from the given state
+// and, for every middle segment s, the same tokens twice: from a zero state (its
+// final state is B_s) and from the identity with v = 0 (its final state is M_s). A
+// scan then forms the entry states S_{s+1} = M_s S_s + B_s, and pass 3 runs
+// segments 1 .. n-1 from them with readout.
+//
+// One workgroup fills a compute unit. Pass 3 must fit one wave over the 256 units,
+// (n-1) pairs <= 256. In pass 1 the pairs' segment-0 runs hold `pairs` units and the
+// 2 (n-2) pairs middle runs take the other 256 - pairs units in r rounds (workgroups
+// start in index order as units free up, the segment-0 runs first), so segment 0
+// can be r times as long as the others. The plan minimises the chunk times of the
+// critical path, max(len0, r len) + len, over n <= kSegMax and segment lengths of at
+// least min_chunks chunks.
 constexpr int kSegMax = 32;
 constexpr int kSegCUs = 256;
 struct SegPlan {
-    int n, len;
+    int n, len0, len;  // segment count; rows of segment 0 and of the others
+    int cost;          // chunk times of the critical path (the chunk count when n == 1)
 };
 __host__ __device__ inline SegPlan seg_plan(long pairs, int T, int min_chunks) {
     const int nch = (T + 63) / 64;
-    long cap = pairs > kSegCUs ? 1 : (kSegCUs / pairs + 3) / 2;
-    cap = cap < kSegMax ? cap : kSegMax;
-    long n = nch / (min_chunks > 0 ? min_chunks : 1);
-    n = n < cap ? n : cap;
-    if (n < 1) n = 1;
-    return SegPlan{(int)n, (int)(nch / n) * 64};
+    SegPlan best{1, T, 0, nch};
+    if (min_chunks < 1) min_chunks = 1;
+    if (pairs >= kSegCUs) return best;
+    const long free_cu = kSegCUs - pairs;
+    for (int n = 3; n <= kSegMax && (long)(n - 1) * pairs <= kSegCUs; ++n) {
+        const long mid = 2 * pairs * (n - 2);
+        const int r = (int)((mid + free_cu - 1) / free_cu);
+        const int x0 = nch / (r + n - 1);
+        for (int x = x0; x <= x0 + 1; ++x) {
+            const int l0 = nch - (n - 1) * x;
+            if (x < min_chunks || l0 < 1) continue;
+            const int cost = (l0 > r * x ? l0 : r * x) + x;
+            if (cost < best.cost) best = SegPlan{n, l0 * 64, x * 64, cost};
+        }
+    }
+    return best;
 }
 // Byte offsets of the segmented arm's workspace: a zero block (also the zero v row of
 // the M runs), the identity, a dummy output row for runs without readout, then the

@@ -139,11 +139,13 @@ def test_queries():
 
 
 def test_segmented_queries():
-    # AUTO takes the segmented arm when at least three segments of eight chunks keep
-    # pass 1 (pairs * (2n - 3) workgroups) within 256: one sequence, 64 heads, 73 chunks
-    assert kda.prefill_arm(1, 4626, 64, 128, 1, 0) == 4
-    assert kda.prefill_arm(2, 4626, 64, 128, 1, 0) == 3  # 128 pairs: two segments at most
-    assert kda.prefill_arm(1, 1000, 64, 128, 1, 0) == 3  # 16 chunks: two segments of eight
+    # AUTO takes the segmented arm when its plan (segments of at least eight chunks)
+    # shortens the critical path to 85% of the chunk count or less
+    assert kda.prefill_arm(1, 4626, 64, 128, 1, 0) == 4  # 64 pairs, 73 chunks: 5 segments
+    assert kda.prefill_arm(2, 4626, 64, 128, 1, 0) == 4  # 128 pairs: 3 segments
+    assert kda.prefill_arm(4, 8192, 32, 128, 1, 0, gdn=True) == 4
+    assert kda.prefill_arm(8, 16384, 64, 128, 1, 0) == 3  # 512 pairs fill the chip
+    assert kda.prefill_arm(1, 1000, 64, 128, 1, 0) == 3  # 16 chunks: too short
     assert kda.prefill_arm(1, 4626, 64, 128, 0, 0) == 2  # fp32 activations: sequential
     assert kda.prefill_arm(1, 300, 2, 128, 1, 3) == 4
     assert kda.prefill_arm(1, 300, 2, 16, 1, 3) == -1
@@ -151,8 +153,8 @@ def test_segmented_queries():
     # (n-1) + 2(n-2) state blocks per pair: B*H = 2, T = 300 gives n = 5 segments
     blk = 128 * 128 * 4
     assert kda.workspace_bytes(1, 300, 2, 128, 1, 3) == blk + blk + 1024 + (4 + 6) * 2 * blk
-    # the prefill workload: n = 3
-    assert kda.workspace_bytes(1, 4626, 64, 128, 1, 0) == blk + blk + 64 * 128 * 4 + (2 + 2) * 64 * blk
+    # the prefill workload: n = 5
+    assert kda.workspace_bytes(1, 4626, 64, 128, 1, 0) == blk + blk + 64 * 128 * 4 + (4 + 6) * 64 * blk
     assert kda.workspace_bytes(1, 4626, 64, 128, 1, 0, gdn=True) == kda.workspace_bytes(1, 4626, 64, 128, 1, 0)
     # packed batches have no segmented arm
     assert kda.varlen_workspace_bytes(3, 500, 4, 128, 1, 3) == ctypes.c_size_t(-1).value

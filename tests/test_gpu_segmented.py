@@ -3,6 +3,7 @@ cut into segments that run in parallel, and the segments are joined by the affin
 scan. The segmented run is checked against the fp64 oracle. Segments of one chunk give
 several scan steps and a ragged last segment. The segmented arm is also checked against
 the sequential arm at the single-sequence prefill workload, which AUTO sends to it."""
+import numpy as np
 import pytest
 import torch
 
@@ -10,6 +11,7 @@ import gated_delta_rule_68_amd as kda
 import oracle
 from gated_delta_rule_68_amd.synth import CONFIGS
 from gated_delta_rule_68_amd.torch_io import to_f64
+from oracle import gates
 from tests.gpu_util import DEV, compare_to_oracle, inputs_for, oracle_run, run_gpu
 from tests.test_gpu_gates import compare as compare_gated
 from tests.test_gpu_gates import gate_params, oracle_gated, run_gated
@@ -35,8 +37,9 @@ def _check(cfg, heads=None, tol=TOL, **run_kw):
     return got, dev
 
 
-# At B*H = 2 the plan takes one segment per chunk: T = 50 is one segment, 100 two (no
-# scan step), 300 five (three scan steps, a 44-row last segment), 700 eleven.
+# At B*H = 2 the explicit mode takes one-chunk segments where they shorten the
+# critical path: T = 50 and 100 run as one segment, 300 as five (three scan steps, a
+# 44-row last segment), 700 as eleven.
 @pytest.mark.parametrize("T", [50, 100, 300, 700])
 @pytest.mark.parametrize("gdn", [False, True])
 def test_one_chunk_segments_vs_oracle(T, gdn):
@@ -46,8 +49,9 @@ def test_one_chunk_segments_vs_oracle(T, gdn):
 
 
 @pytest.mark.parametrize("gdn", [False, True])
-def test_three_segments_many_pairs_vs_oracle(gdn):
-    """B*H = 80: three segments (one wave of 240 pass-1 workgroups), sampled heads."""
+def test_many_pairs_vs_oracle(gdn):
+    """B*H = 80: four segments; the 320 middle runs of pass 1 take two rounds beside the
+    segment-0 runs. Sampled heads."""
     cfg = CONFIGS["kda_decode"].with_(B=2, H=40, T=300, gdn=gdn)
     _check(cfg, heads=[0, 17, 39])
 
@@ -86,8 +90,47 @@ def test_grouped_heads_vs_oracle():
     compare_gqa(got, ref, vc, rows, bsel, heads, TOL)
 
 
+def _slow_gates(inp, dev, a=-0.002):
+    """Softplus gates with multiplier a: e^g stays within 1% of 1, so a segment's
+    transition M is far from zero and the entry states carry the whole history.
+    (Under the workloads' gates M underflows to zero within a few hundred rows.)"""
+    cfg = inp.cfg
+    av = np.full(cfg.H, a, np.float32)
+    g = gates.gate_softplus(inp.gate_x, av, inp.dt_bias, -5.0, cfg.D, cfg.gdn)
+    return torch.from_numpy(av).to(DEV), dev["dt_bias"], g, gates.beta_sigmoid(inp.beta_x)
+
+
+@pytest.mark.parametrize("T", [300, 700])
+@pytest.mark.parametrize("gdn", [False, True])
+def test_slow_decay_history_across_segments_vs_oracle(T, gdn):
+    """Slow gates and a random entry state: the outputs of later segments depend on
+    the whole history through the scan (forgetting it moves them by about 50%)."""
+    cfg = CONFIGS["kda_decode"].with_(B=1, H=2, T=T, gdn=gdn)
+    inp, dev = inputs_for(cfg)
+    ga, gb, g, beta = _slow_gates(inp, dev)
+    form = kda.KDA_GATE_SOFTPLUS
+    got = run_gated(cfg, dev, ga, gb, form, mode=SEG)
+    torch.cuda.synchronize()
+    ref, ch, rows, bsel = oracle_gated(inp, g, beta, heads=[0, 1])
+    compare_gated(cfg, got, ref, ch, rows, bsel, [0, 1], TOL)
+
+
+def test_slow_decay_prefill_workload_vs_oracle():
+    """The single-sequence workload's shape and AUTO plan (five segments) with slow
+    gates: sampled heads against the oracle."""
+    cfg = CONFIGS["kda_prefill"].with_(random_init=True)
+    assert kda.prefill_arm(cfg.B, cfg.T, cfg.H, cfg.D, kda.KDA_DTYPE_BF16, kda.KDA_MODE_AUTO) == 4
+    inp, dev = inputs_for(cfg)
+    ga, gb, g, beta = _slow_gates(inp, dev)
+    got = run_gated(cfg, dev, ga, gb, kda.KDA_GATE_SOFTPLUS, mode=kda.KDA_MODE_AUTO)
+    torch.cuda.synchronize()
+    heads = [0, 33, 63]
+    ref, ch, rows, bsel = oracle_gated(inp, g, beta, heads=heads)
+    compare_gated(cfg, got, ref, ch, rows, bsel, heads, TOL)
+
+
 def test_prefill_workload_auto_is_segmented():
-    """Single-sequence prefill T = 4626, H = 64: AUTO takes three segments. Sampled heads
+    """Single-sequence prefill T = 4626, H = 64: AUTO takes five segments. Sampled heads
     against the oracle, everything against the sequential arm and the unsegmented
     chunked arm."""
     cfg = CONFIGS["kda_prefill"]
@@ -102,6 +145,23 @@ def test_prefill_workload_auto_is_segmented():
         errs = {k: oracle.rel_linf(to_f64(got[k]), to_f64(other[k])) for k in ("out", "o_core", "state", "ring")}
         _print("vs mode", mode, errs)
         assert max(errs.values()) <= TOL and errs["ring"] == 0.0
+
+
+def test_gdn_workload_auto_is_segmented():
+    """GDN prefill B = 4, T = 8192, H = 32 (128 pairs): AUTO takes three segments, the
+    first twice as long as the others. Sampled heads against the oracle, everything
+    against the sequential arm."""
+    cfg = CONFIGS["gdn_prefill"]
+    assert kda.prefill_arm(cfg.B, cfg.T, cfg.H, cfg.D, kda.KDA_DTYPE_BF16, kda.KDA_MODE_AUTO, gdn=True) == 4
+    inp, dev = inputs_for(cfg)
+    got = run_gpu(cfg, dev, mode=kda.KDA_MODE_AUTO)
+    torch.cuda.synchronize()
+    ref, ch, rows, bsel, hh = oracle_run(inp, heads=[7], batches=[1, 2])
+    _print("oracle errs", compare_to_oracle(cfg, got, ref, ch, rows, bsel, hh, tol=TOL))
+    seq = run_gpu(cfg, dev, mode=SEQ)
+    errs = {k: oracle.rel_linf(to_f64(got[k]), to_f64(seq[k])) for k in ("out", "o_core", "state", "ring")}
+    _print("vs sequential", errs)
+    assert max(errs.values()) <= TOL and errs["ring"] == 0.0
 
 
 def test_segmented_gdn_few_pairs_auto():
