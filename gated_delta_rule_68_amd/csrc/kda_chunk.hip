@@ -608,8 +608,9 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
     const size_t head_off = (size_t)h * DK;
     const size_t kw = (size_t)a.Hk * DK, khead = (size_t)(h % a.Hk) * DK;  // q / k: key head h % Hk
     const int jv0 = split * NC;  // first value column of this split
-    // v rows, and the outputs' base and row stride (runs without readout write every
-    // row to one dummy row)
+    // v rows, and the outputs' base and row stride. Runs without readout skip the
+    // output stores (a branch on a workgroup-uniform value, taken the same way in
+    // every chunk); the dummy row only keeps their addresses valid.
     const bool zero_v = SEG && sr.zero_v, readout = !SEG || sr.readout;
     char* const seg_ws = reinterpret_cast<char*>(a.seg_ws);
     const void* const vsrc = zero_v ? static_cast<const void*>(seg_ws) : a.v;
@@ -1178,6 +1179,7 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
             const float* of = reinterpret_cast<const float*>(&sm.e);
             if constexpr (NCOL == 1) {
                 static_assert(NE == NZ && NITEMS == NE * NTHR, "z prefetch covers the epilogue items");
+                if (readout) {
                 const int c8 = (tid % (NC / 8)) * 8;  // the same columns for every item of a thread
                 const bf16x8* zz = zpre;
 #pragma unroll
@@ -1218,6 +1220,7 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
                             d[1] = make_float4(o8[4], o8[5], o8[6], o8[7]);
                         }
                     }
+                }
                 }
             } else {
 #pragma unroll
