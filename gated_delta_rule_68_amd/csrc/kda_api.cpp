@@ -54,7 +54,7 @@ kda::SegPlan plan_for(int B, int T, int H, int mode) {
 }
 bool segments_pay(int B, int T, int H) {
     const kda::SegPlan p = plan_for(B, T, H, KDA_MODE_AUTO);
-    return p.n >= 3 && p.cost * 100 <= 85 * ((T + 63) / 64);
+    return p.n >= 3 && (long)p.cost * 100 <= 85 * (((long)T + 63) / 64);
 }
 
 int pick_arm(int B, int T, int H, int D, bool bf16, int mode) {

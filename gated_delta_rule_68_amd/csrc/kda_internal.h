@@ -87,7 +87,7 @@ struct SegPlan {
     int cost;          // chunk times of the critical path (the chunk count when n == 1)
 };
 __host__ __device__ inline SegPlan seg_plan(long pairs, int T, int min_chunks) {
-    const int nch = (T + 63) / 64;
+    const int nch = (int)(((long)T + 63) / 64);
     SegPlan best{1, T, 0, nch};
     if (min_chunks < 1) min_chunks = 1;
     if (pairs >= kSegCUs) return best;

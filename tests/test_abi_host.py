@@ -160,6 +160,32 @@ def test_segmented_queries():
     assert kda.varlen_workspace_bytes(3, 500, 4, 128, 1, 3) == ctypes.c_size_t(-1).value
 
 
+def _segments_from_workspace(B, T, H, mode):
+    """The segment count n of a segmented call, read back from its workspace size:
+    constant blocks, then (n-1) + 2(n-2) state blocks per pair."""
+    blk, row = 128 * 128 * 4, H * 128 * 4
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    const = al(max(blk, row)) + al(blk) + al(row)
+    ws = kda.workspace_bytes(B, T, H, 128, 1, mode)
+    slots, rem = divmod(ws - const, B * H * blk)
+    assert rem == 0 and slots >= 0
+    return 1 if slots == 0 else (slots + 5) // 3
+
+
+@pytest.mark.parametrize("B,H", [(1, 1), (1, 8), (1, 64), (2, 64), (4, 32), (1, 100), (3, 85), (2, 128)])
+@pytest.mark.parametrize("T", [1, 64, 300, 4626, 70000])
+def test_segment_plan_invariants(B, H, T):
+    """Every plan fits pass 3 in one wave over 256 compute units, keeps at most 32
+    segments of at least one chunk, and AUTO never picks the segmented arm with fewer
+    than three segments or at 256 pairs and more."""
+    P, nch = B * H, (T + 63) // 64
+    n = _segments_from_workspace(B, T, H, 3)
+    assert n == 1 or (3 <= n <= 32 and (n - 1) * P <= 256 and n <= nch), (n, P, nch)
+    if kda.prefill_arm(B, T, H, 128, 1, 0) == 4:
+        na = _segments_from_workspace(B, T, H, 0)
+        assert 3 <= na <= 32 and (na - 1) * P <= 256 and P < 256 and nch > 8 * (na - 1)
+
+
 def call_rollback(a, gdn=False, T_stash=3, keep=2):
     f = kda.lib().gdn_rollback if gdn else kda.lib().kda_rollback
     return f(a["q"], a["k"], a["v"], a["g"], a["beta"], a["conv_w"], a["ring_snap"], a["state_snap"],
