@@ -1309,10 +1309,13 @@ __global__ void seg_init_kernel(float* zero, size_t nzero, float* ident) {
 // final state of the run from the identity) holds M[i][k] at [k][i]: a wavefront's
 // loads of M are coalesced over i, and the current state's columns sit in LDS as
 // [k][column], read as two 16-byte broadcasts per k.
-constexpr int SCAN_COLS = 16, SCAN_KB = 8;
+// The DK / SCAN_COLS workgroups of one pair share blockIdx % 8, so they run on one XCD
+// and its L2 fetches the pair's M_s and B_s once for all of them.
+constexpr int SCAN_COLS = 16, SCAN_KB = 8, SCAN_NCB = DK / SCAN_COLS;
 __global__ __launch_bounds__(256) void seg_scan_kernel(MixerArgs a) {
     const int P = a.B * a.H, n = a.seg_n;
-    const int pair = blockIdx.x / (DK / SCAN_COLS), cb = blockIdx.x % (DK / SCAN_COLS);
+    const int x = blockIdx.x;
+    const int pair = (x / (8 * SCAN_NCB)) * 8 + x % 8, cb = (x / 8) % SCAN_NCB;
     if (pair >= P) return;
     const size_t blk = (size_t)DK * DK;
     const SegLayout lay = seg_layout(P, a.H, DK, n);
@@ -1381,7 +1384,7 @@ hipError_t seg_launch(MixerArgs a) {
     e = seg_pass<BF, GDN>(a, P + 16 * ((mid + 7) / 8));
     if (e != hipSuccess) return e;
     if (n >= 3) {
-        hipLaunchKernelGGL(seg_scan_kernel, dim3(P * (DK / SCAN_COLS)), dim3(256), 0, a.stream, a);
+        hipLaunchKernelGGL(seg_scan_kernel, dim3(((P + 7) / 8) * 8 * SCAN_NCB), dim3(256), 0, a.stream, a);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
