@@ -1303,15 +1303,16 @@ __global__ void seg_init_kernel(float* zero, size_t nzero, float* ident) {
     if (i < (size_t)DK * DK) ident[i] = (i / DK == i % DK) ? 1.0f : 0.0f;
 }
 
-// Entry states of the middle segments: S_{s+1} = M_s S_s + B_s for s = 1 .. n-2, in
-// fp32. Workgroup (pair, 16-column block cb): thread t computes key i = t % 128 of
-// columns cb*16 + 8 (t / 128) .. +7. State blocks are [value][key], so M_s (the
-// final state of the run from the identity) holds M[i][k] at [k][i]: a wavefront's
-// loads of M are coalesced over i, and the current state's columns sit in LDS as
-// [k][column], read as two 16-byte broadcasts per k.
-// The DK / SCAN_COLS workgroups of one pair share blockIdx % 8, so they run on one XCD
-// and its L2 fetches the pair's M_s and B_s once for all of them.
-constexpr int SCAN_COLS = 16, SCAN_KB = 8, SCAN_NCB = DK / SCAN_COLS;
+// Entry states of the middle segments: S_{s+1} = M_s S_s + B_s for s = 1 .. n-2, on
+// the fp32 MFMA (v_mfma_f32_16x16x4f32: exact fp32 products, fp32 accumulation).
+// Workgroup (pair, 32-column block cb), four wavefronts; wavefront w computes keys
+// 32 w .. +31 (two 16-row blocks) of the block's 32 columns (two 16-column blocks).
+// State blocks are [value][key], so M_s (the final state of the run from the identity)
+// holds M[i][k] at [k][i]: the A fragment M[i = l16][k = q4] of a 4-wide k slice is a
+// 64-byte run per q4. The current state sits in LDS as [k][column] (row pitch 48 floats:
+// the four k rows of a B fragment fall in distinct banks). The workgroups of one pair
+// share blockIdx % 8, so they run on one XCD and its L2 fetches M_s and B_s once.
+constexpr int SCAN_COLS = 32, SCAN_NCB = DK / SCAN_COLS, SCAN_LD = 48;
 __global__ __launch_bounds__(256) void seg_scan_kernel(MixerArgs a) {
     const int P = a.B * a.H, n = a.seg_n;
     const int x = blockIdx.x;
@@ -1323,31 +1324,55 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(MixerArgs a) {
     auto S = [&](int s) { return slots + ((size_t)(s - 1) * P + pair) * blk; };
     auto M = [&](int s) { return slots + ((size_t)(n - 1 + s - 1) * P + pair) * blk; };
     auto Bs = [&](int s) { return slots + ((size_t)(2 * n - 3 + s - 1) * P + pair) * blk; };
-    __shared__ __align__(16) float sc[DK][SCAN_COLS];  // the current entry state [k][j]
-    const int t = threadIdx.x, i = t % DK, j0 = (t / DK) * 8;
+    __shared__ __align__(16) float sc[DK][SCAN_LD];  // the current entry state [k][column]
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6, q4 = lane >> 4, l16 = lane & 15;
     const size_t col0 = (size_t)cb * SCAN_COLS;
-    for (int e = 0; e < 8; ++e) sc[i][j0 + e] = S(1)[(col0 + j0 + e) * DK + i];
+    {  // S_1 columns col0 .. +31 into LDS: thread t reads keys 16 (t % 8) .. +15 of column t / 8
+        const int j = t / 8, k0 = (t % 8) * 16;
+        const float* src = S(1) + (col0 + j) * DK + k0;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const float4 x4 = *reinterpret_cast<const float4*>(src + 4 * v);
+            sc[k0 + 4 * v][j] = x4.x;
+            sc[k0 + 4 * v + 1][j] = x4.y;
+            sc[k0 + 4 * v + 2][j] = x4.z;
+            sc[k0 + 4 * v + 3][j] = x4.w;
+        }
+    }
+    // result tile (rb, cc): keys 32 w + 16 rb + 4 q4 + r, column col0 + 16 cc + l16
+    auto tile = [&](float* blkp, int rb, int cc) {
+        return blkp + (col0 + 16 * cc + l16) * DK + 32 * w + 16 * rb + 4 * q4;
+    };
     for (int s = 1; s <= n - 2; ++s) {
         __syncthreads();
-        const float* m = M(s) + i;
-        float acc[8];
-        for (int e = 0; e < 8; ++e) acc[e] = Bs(s)[(col0 + j0 + e) * DK + i];
-        for (int k0 = 0; k0 < DK; k0 += SCAN_KB) {
-            float mv[SCAN_KB];
+        const float* m = M(s) + 32 * w + l16;
+        f32x4v acc[2][2];
 #pragma unroll
-            for (int kk = 0; kk < SCAN_KB; ++kk) mv[kk] = m[(size_t)(k0 + kk) * DK];
+        for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-            for (int kk = 0; kk < SCAN_KB; ++kk) {
-                const float4 lo = *reinterpret_cast<const float4*>(&sc[k0 + kk][j0]);
-                const float4 hi = *reinterpret_cast<const float4*>(&sc[k0 + kk][j0 + 4]);
-                const float sv[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] = fmaf(mv[kk], sv[e], acc[e]);
-            }
+            for (int cc = 0; cc < 2; ++cc) acc[rb][cc] = ld4f(tile(Bs(s), rb, cc));
+#pragma unroll 8
+        for (int k4 = 0; k4 < DK; k4 += 4) {
+            const size_t kr = (size_t)(k4 + q4) * DK;
+            const float a0 = m[kr], a1 = m[kr + 16];  // M[32w + l16][k], M[32w + 16 + l16][k]
+            const float b0 = sc[k4 + q4][l16], b1 = sc[k4 + q4][16 + l16];
+            acc[0][0] = mfma_f32(a0, b0, acc[0][0]);
+            acc[0][1] = mfma_f32(a0, b1, acc[0][1]);
+            acc[1][0] = mfma_f32(a1, b0, acc[1][0]);
+            acc[1][1] = mfma_f32(a1, b1, acc[1][1]);
         }
-        for (int e = 0; e < 8; ++e) S(s + 1)[(col0 + j0 + e) * DK + i] = acc[e];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc)
+                *reinterpret_cast<f32x4v*>(tile(S(s + 1), rb, cc)) = acc[rb][cc];
         __syncthreads();
-        for (int e = 0; e < 8; ++e) sc[i][j0 + e] = acc[e];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sc[32 * w + 16 * rb + 4 * q4 + r][16 * cc + l16] = acc[rb][cc][r];
     }
 }
 
