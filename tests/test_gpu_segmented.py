@@ -63,6 +63,13 @@ def test_wide_conv_fp32_and_alternating_gates_vs_oracle():
     _check(cfg)
 
 
+def test_gdn_widest_conv_vs_oracle():
+    """GDN with K = 8: the widest conv history, read from the seven rows before each
+    segment."""
+    cfg = CONFIGS["gdn_prefill"].with_(B=1, T=330, H=3, K=8, random_init=True)
+    _check(cfg)
+
+
 def test_in_place_state_vs_oracle():
     cfg = CONFIGS["kda_decode"].with_(B=1, H=3, T=260)
     _check(cfg, inplace=True)
