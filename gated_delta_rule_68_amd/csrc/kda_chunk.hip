@@ -498,10 +498,26 @@ __device__ __forceinline__ void merge_column(M& m, int lane) {
     }
 }
 
-// The run of one workgroup of the segmented arm (seg_plan / seg_layout in
-// kda_internal.h): its (b, h) pair, rows [ro, ro + len) of the sequence, where its
-// state comes from and goes to, whether v is replaced by zeros (the M runs) and
-// whether the outputs are written (else they go to a dummy row).
+// The D x D fp32 state blocks of the segmented arm's workspace (seg_layout in
+// kda_internal.h), in state layout [value][key]: the entry states S_s (s = 1 .. n-1)
+// and the transitions M_s and offsets B_s (s = 1 .. n-2) of pair p.
+struct SegSlots {
+    float* base;
+    int P, n;
+    __device__ float* blk(size_t i, int p) const { return base + (i * P + p) * ((size_t)DK * DK); }
+    __device__ float* S(int s, int p) const { return blk(s - 1, p); }
+    __device__ float* M(int s, int p) const { return blk(n - 1 + s - 1, p); }
+    __device__ float* B(int s, int p) const { return blk(2 * n - 3 + s - 1, p); }
+};
+__device__ __forceinline__ SegSlots seg_slots(const MixerArgs& a) {
+    const int P = a.B * a.H;
+    char* ws = reinterpret_cast<char*>(a.seg_ws);
+    return SegSlots{reinterpret_cast<float*>(ws + seg_layout(P, a.H, DK, a.seg_n).slots), P, a.seg_n};
+}
+
+// The run of one workgroup of the segmented arm: its (b, h) pair, rows [ro, ro + len)
+// of the sequence, where its state comes from and goes to, whether v is replaced by
+// zeros (the M runs) and whether the outputs are written.
 struct SegRun {
     int pair, ro, len;
     const float* s_in;
@@ -510,20 +526,16 @@ struct SegRun {
 };
 
 // Pass 1: blocks [0, P) run segment 0 of pair b (dispatched first: they are the
-// longest); block P + 16 g + 8 kind + j runs the
-// B (kind 0) or M (kind 1) run of slot 8 g + j = (s - 1) P + pair: the two runs of one
-// slot are 8 blocks apart and so on the same XCD, whose L2 then serves both with the
-// same rows. Pass 3: block (s - 1) P + pair runs segment s. Returns false for the
-// padding blocks of the grid.
+// longest). Block P + 16 g + 8 kind + j runs the B (kind 0) or M (kind 1) run of slot
+// 8 g + j = (s - 1) P + pair: the two runs of one slot are 8 blocks apart and so on
+// the same XCD, whose L2 then serves both with the same rows. Pass 3: block
+// (s - 1) P + pair runs segment s. Returns false for the padding blocks of the grid.
 __device__ __forceinline__ bool seg_run(const MixerArgs& a, SegRun* r) {
     const int P = a.B * a.H, n = a.seg_n, L0 = a.seg_len0, L = a.seg_len;
     const size_t blk = (size_t)DK * DK;
     char* ws = reinterpret_cast<char*>(a.seg_ws);
     const SegLayout lay = seg_layout(P, a.H, DK, n);
-    float* slots = reinterpret_cast<float*>(ws + lay.slots);
-    auto S = [&](int s, int p) { return slots + ((size_t)(s - 1) * P + p) * blk; };
-    auto M = [&](int s, int p) { return slots + ((size_t)(n - 1 + s - 1) * P + p) * blk; };
-    auto Bs = [&](int s, int p) { return slots + ((size_t)(2 * n - 3 + s - 1) * P + p) * blk; };
+    const SegSlots sl = seg_slots(a);
     const int d = blockIdx.x;
     r->zero_v = false;
     r->readout = true;
@@ -533,7 +545,7 @@ __device__ __forceinline__ bool seg_run(const MixerArgs& a, SegRun* r) {
             r->ro = 0;
             r->len = n == 1 ? a.T : L0;
             r->s_in = a.state_in + (size_t)d * blk;
-            r->s_out = n == 1 ? a.state_out + (size_t)d * blk : S(1, d);
+            r->s_out = n == 1 ? a.state_out + (size_t)d * blk : sl.S(1, d);
             return true;
         }
         const int e = d - P, kind = (e % 16) / 8, slot = (e / 16) * 8 + e % 8;
@@ -545,7 +557,7 @@ __device__ __forceinline__ bool seg_run(const MixerArgs& a, SegRun* r) {
         r->readout = false;
         r->zero_v = kind == 1;
         r->s_in = reinterpret_cast<const float*>(ws + (kind ? lay.ident : lay.zero));
-        r->s_out = kind ? M(sg, p) : Bs(sg, p);
+        r->s_out = kind ? sl.M(sg, p) : sl.B(sg, p);
         return true;
     }
     if (d >= (n - 1) * P) return false;
@@ -553,8 +565,8 @@ __device__ __forceinline__ bool seg_run(const MixerArgs& a, SegRun* r) {
     r->pair = p;
     r->ro = L0 + (sg - 1) * L;
     r->len = sg == n - 1 ? a.T - r->ro : L;
-    r->s_in = S(sg, p);
-    r->s_out = sg == n - 1 ? a.state_out + (size_t)p * blk : Bs(sg, p);  // B_s is spent by then
+    r->s_in = sl.S(sg, p);
+    r->s_out = sg == n - 1 ? a.state_out + (size_t)p * blk : sl.B(sg, p);  // B_s is spent by then
     return true;
 }
 
@@ -1318,12 +1330,10 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(MixerArgs a) {
     const int x = blockIdx.x;
     const int pair = (x / (8 * SCAN_NCB)) * 8 + x % 8, cb = (x / 8) % SCAN_NCB;
     if (pair >= P) return;
-    const size_t blk = (size_t)DK * DK;
-    const SegLayout lay = seg_layout(P, a.H, DK, n);
-    float* slots = reinterpret_cast<float*>(reinterpret_cast<char*>(a.seg_ws) + lay.slots);
-    auto S = [&](int s) { return slots + ((size_t)(s - 1) * P + pair) * blk; };
-    auto M = [&](int s) { return slots + ((size_t)(n - 1 + s - 1) * P + pair) * blk; };
-    auto Bs = [&](int s) { return slots + ((size_t)(2 * n - 3 + s - 1) * P + pair) * blk; };
+    const SegSlots sl = seg_slots(a);
+    auto S = [&](int s) { return sl.S(s, pair); };
+    auto M = [&](int s) { return sl.M(s, pair); };
+    auto Bs = [&](int s) { return sl.B(s, pair); };
     __shared__ __align__(16) float sc[DK][SCAN_LD];  // the current entry state [k][column]
     const int t = threadIdx.x, lane = t & 63, w = t >> 6, q4 = lane >> 4, l16 = lane & 15;
     const size_t col0 = (size_t)cb * SCAN_COLS;

@@ -185,6 +185,18 @@ def test_segmented_gdn_few_pairs_auto():
     assert max(errs.values()) <= TOL and errs["ring"] == 0.0
 
 
+def test_without_o_core_same_outputs():
+    """o_core = NULL: the same out, ring and state bit for bit as with it."""
+    cfg = CONFIGS["kda_decode"].with_(B=1, H=2, T=300)
+    inp, dev = inputs_for(cfg)
+    a = run_gpu(cfg, dev, mode=SEG)
+    b = run_gpu(cfg, dev, mode=SEG, o_core=False)
+    torch.cuda.synchronize()
+    assert b["o_core"] is None
+    for k in ("out", "state", "ring"):
+        assert torch.equal(a[k], b[k]), k
+
+
 def test_repeated_calls_reuse_the_workspace():
     """The workspace's constant blocks are rebuilt by every call: a second call on a
     workspace full of the first call's values gives the same result bit for bit."""
