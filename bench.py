@@ -146,6 +146,62 @@ def cpu_baseline(cfg, inp, budget_s: float = 12.0):
                       f"same seeded inputs in {el:.1f} s, fp64, threads split the batch"}
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# The oracle on every workload: (workload, rows timed, thread counts, runs). The oracle
+# threads over whole sequences only, so a workload of B sequences uses at most B
+# threads. The sequential definition costs the same per token at any position, so a
+# leading slice of T rows gives the workload's tokens/s; the slices keep each leg to
+# seconds.
+CPU_LEGS = (("tiny_kda", None, (1,), 3),
+            ("kda_decode", None, (1, 16), 3),
+            ("kda_prefill", 512, (1,), 3),
+            ("gdn_prefill", 1024, (4,), 1),
+            ("kda_long", 512, (8,), 1))
+
+
+def cpu_baselines() -> dict:
+    """Time the fp64 oracle on each workload's seeded inputs (bounded slices)."""
+    import numpy as np
+
+    import oracle
+    from gated_delta_rule_68_amd.synth import CONFIGS, make_inputs
+
+    ncpu = os.cpu_count() or 1
+    rec = {"cpu_model": _cpu_model(), "host_cpus": ncpu, "legs": []}
+    for name, T, thread_counts, runs in CPU_LEGS:
+        cfg = CONFIGS[name]
+        inp = make_inputs(cfg, T=T)
+        rows = T or cfg.T
+        arrs = [np.ascontiguousarray(getattr(inp, n), np.float64)
+                for n in ("q", "k", "v", "g", "beta", "conv_w", "ring", "state", "z", "norm_w")]
+        scale = 1.0 / math.sqrt(cfg.D)
+        for th in thread_counts:
+            th = max(1, min(th, cfg.B, ncpu))
+            times = []
+            for _ in range(runs):
+                t0 = time.perf_counter()
+                oracle.mixer(*arrs, scale, RMS_EPS, gdn=cfg.gdn, threads=th)
+                times.append(time.perf_counter() - t0)
+            s = sorted(times)[len(times) // 2]
+            leg = {"workload": name, "B": cfg.B, "T_timed": rows, "T_workload": cfg.T,
+                   "H": cfg.H, "D": cfg.D, "threads": th, "runs": runs, "s": s,
+                   "tokens_per_s": cfg.B * rows / s}
+            log(f"oracle {leg}")
+            rec["legs"].append(leg)
+        del inp, arrs
+    return rec
+
+
 def run_decode(cfg, steps, warmup):
     import torch
 
@@ -590,12 +646,18 @@ def main():
                          "the arm of --prefill-mode, --steps times after one warm-up (for profilers)")
     ap.add_argument("--prefill-mode", choices=("chunked", "segmented", "auto"), default="chunked",
                     help="prefill mode of --prefill-only (default: chunked)")
+    ap.add_argument("--cpu-baselines", action="store_true",
+                    help="only time the fp64 oracle on the host cores, on every workload "
+                         "(bounded slices; no GPU used)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the mixer shards by (sequence, head) with no exchange; see DESIGN.md)",
+              "(the mixer shards by (sequence, head) with no exchange)",
               file=sys.stderr)
         sys.exit(2)
+    if args.cpu_baselines:
+        print(json.dumps({"cpu_baselines": cpu_baselines()}), flush=True)
+        return
 
     import torch
 
