@@ -178,6 +178,85 @@ __global__ __launch_bounds__(fused_threads<D>() * G) void seq_fused_kernel(Mixer
     }
 }
 
+// One-token step at D = 128, one value head per workgroup (G = 1): the fused kernel's
+// work for T = 1, calling the same helpers on the same values in the same order (so
+// the bits equal those of the fused and split arms), with nothing kept for a second
+// token. Its few live registers let three 512-thread workgroups share a CU, three
+// 64 KiB head states in flight per CU instead of two. The new ring rows are written
+// as soon as the conv has read the old ones (each row is read only by its own
+// thread; q / k rows shared with other value heads, Hk < H, are left to the roll
+// kernel that runs after this one).
+constexpr int DEC_D = 128, DEC_THREADS = 512;
+template <bool BF, bool GDN>
+__global__ __launch_bounds__(DEC_THREADS, 6) void seq_decode_kernel(MixerArgs a) {
+    constexpr int D = DEC_D, CPT = 2, NG = DEC_THREADS / 8, KPL = D / 8, EW = GDN ? 1 : D;
+    static_assert(fused_cpt<D>() == CPT && fused_threads<D>() == DEC_THREADS, "the fused kernel's lane map");
+    __shared__ float pre[3][D];  // conv outputs q, k, v (q, k l2-normalised in place)
+    __shared__ float es[EW];     // exp(g)
+    __shared__ float os[D];      // scan readout
+    __shared__ float bs, kqs;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int h = blockIdx.x % a.H, b = seq_of(a, blockIdx.x / a.H);
+    const int bh = b * a.H + h, K = a.K;
+    const size_t qkv = (size_t)a.H * D, head_off = (size_t)h * D;
+    const int grp = (tid >> 6) * 8 + (lane >> 3), s = lane & 7;
+    const size_t kw = (size_t)a.Hk * D, khead = (size_t)(h % a.Hk) * D;
+
+    float S[CPT][KPL];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) load_keys<D>(S[c], a.state_in + ((size_t)bh * D + grp + c * NG) * D, s);
+
+    const GateCol gp = gate_col(a, h, GDN ? (size_t)h : head_off + tid % D);
+    size_t row0;
+    int T;
+    seq_span(a, b, &row0, &T);
+
+    if (tid < 3 * D) {  // conv + SiLU of plane tid / D, channel tid % D
+        const int plane = tid / D, ch = tid % D;
+        const size_t prow = plane < 2 ? plane * kw + khead + ch : 2 * kw + head_off + ch;
+        float* ring_row = a.ring + ((size_t)b * ring_rows(a) + prow) * (K - 1);
+        ConvChannel cc;
+        conv_window_from_ring(cc, ring_row, K);
+        conv_load_taps(cc, a.conv_w + prow * K, K);
+        const void* xsrc = plane == 0 ? a.q : (plane == 1 ? a.k : a.v);
+        const size_t xc = plane < 2 ? row0 * kw + khead + ch : row0 * qkv + head_off + ch;
+        pre[plane][ch] = silu_f(conv_push(cc, ld_act<BF>(xsrc, xc)));
+        if (plane == 2 || a.Hk == a.H) conv_window_to_ring(cc, ring_row, K);
+    }
+    if constexpr (GDN) {
+        if (tid == 0) {
+            es[0] = exp_f(gate_in(a, gp, ld_act<BF>(a.g, row0 * a.H + h)));
+            bs = beta_in(a, ld_act<BF>(a.beta, row0 * a.H + h));
+        }
+    } else {
+        if (tid < D) es[tid] = exp_f(gate_in(a, gp, ld_act<BF>(a.g, row0 * qkv + head_off + tid)));
+        if (tid == 0) bs = beta_in(a, ld_act<BF>(a.beta, row0 * a.H + h));
+    }
+    __syncthreads();
+    if (tid < 64) l2_qk_row<D>(pre[0], pre[1], lane, &kqs);
+    __syncthreads();
+    {
+        float vj[CPT], o[CPT];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) vj[c] = pre[2][grp + c * NG];
+        scan_step_cols<D, GDN, CPT>(S, pre[0], pre[1], es, vj, bs, kqs, a.scale, s, o);
+        if (s == 0) {
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) os[grp + c * NG] = o[c];
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) store_keys<D>(a.state_out + ((size_t)bh * D + grp + c * NG) * D, S[c], s);
+    if (!a.readout) return;
+    __syncthreads();
+    if (tid < 64) {
+        const size_t off = row0 * qkv + head_off;
+        const GateRow gz = load_gate_row<D, BF>(a, off, lane);
+        gated_rmsnorm_row<D, BF, GDN>(os, gz, a, off, lane, a.o_core);
+    }
+}
+
 // ------------------------------------------------------------------ split arm
 template <int D>
 constexpr int pre_threads() { return ((3 * D + 63) / 64) * 64; }
@@ -346,8 +425,11 @@ hipError_t fused_launch(const MixerArgs& a) {
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((seq_fused_kernel<D, BF, GDN>), dim3(a.B * a.H), dim3(fused_threads<D>()), 0,
-                       a.stream, a);
+    if (D == DEC_D && a.T == 1 && !a.cu_seqlens)
+        hipLaunchKernelGGL((seq_decode_kernel<BF, GDN>), dim3(a.B * a.H), dim3(DEC_THREADS), 0, a.stream, a);
+    else
+        hipLaunchKernelGGL((seq_fused_kernel<D, BF, GDN>), dim3(a.B * a.H), dim3(fused_threads<D>()), 0,
+                           a.stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.Hk == a.H) return e;
     return launch_ring_roll(a, true);  // shared q / k rows, after every reader
