@@ -4,6 +4,7 @@
 // for all T tokens - conv + SiLU (q, k, v), l2 (q, k), the delta-rule scan on
 // register-resident state, the gated RMSNorm, and the ring roll - so decode is a
 // single kernel that streams each 64 KiB head state from HBM once and back once.
+// A one-token variant of it (seq_decode_kernel) takes the decode step at D = 128.
 //
 // Split arm (prefill with few (b, h) pairs): a pre-kernel over (b, h, 32-token
 // block) writes the conv/l2 results to the workspace, a scan kernel splits each
