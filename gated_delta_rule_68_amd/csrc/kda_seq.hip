@@ -4,7 +4,8 @@
 // for all T tokens - conv + SiLU (q, k, v), l2 (q, k), the delta-rule scan on
 // register-resident state, the gated RMSNorm, and the ring roll - so decode is a
 // single kernel that streams each 64 KiB head state from HBM once and back once.
-// A one-token variant of it (seq_decode_kernel) takes the decode step at D = 128.
+// A variant of it for calls of at most 16 tokens (seq_short_kernel) takes the decode
+// step and short calls at D = 128.
 //
 // Split arm (prefill with few (b, h) pairs): a pre-kernel over (b, h, 32-token
 // block) writes the conv/l2 results to the workspace, a scan kernel splits each
@@ -179,25 +180,29 @@ __global__ __launch_bounds__(fused_threads<D>() * G) void seq_fused_kernel(Mixer
     }
 }
 
-// One-token step at D = 128, one value head per workgroup (G = 1): the fused kernel's
-// work for T = 1, calling the same helpers on the same values in the same order (so
-// the bits equal those of the fused and split arms), with nothing kept for a second
-// token. Its few live registers let three 512-thread workgroups share a CU, three
-// 64 KiB head states in flight per CU instead of two. The new ring rows are written
-// as soon as the conv has read the old ones (each row is read only by its own
-// thread; q / k rows shared with other value heads, Hk < H, are left to the roll
-// kernel that runs after this one).
-constexpr int DEC_D = 128, DEC_THREADS = 512;
-template <bool BF, bool GDN>
-__global__ __launch_bounds__(DEC_THREADS, 6) void seq_decode_kernel(MixerArgs a) {
-    constexpr int D = DEC_D, CPT = 2, NG = DEC_THREADS / 8, KPL = D / 8, EW = GDN ? 1 : D;
-    static_assert(fused_cpt<D>() == CPT && fused_threads<D>() == DEC_THREADS, "the fused kernel's lane map");
-    __shared__ float pre[3][D];  // conv outputs q, k, v (q, k l2-normalised in place)
-    __shared__ float es[EW];     // exp(g)
-    __shared__ float os[D];      // scan readout
-    __shared__ float bs, kqs;
+// Short calls at D = 128, one value head per workgroup (G = 1): the fused kernel's work
+// for T <= TM tokens (the decode step is TM = 1; speculative verify and rollback
+// replays take TM = 8 or 16), calling the same helpers on the same values in the same
+// order, so the bits equal those of the fused and split arms. Every raw row of the call
+// is requested at once, right behind the state, and nothing is kept for a later token
+// block: with few live registers three 512-thread workgroups share a CU, three 64 KiB
+// head states in flight per CU instead of two. The new ring rows are written as soon
+// as the conv has read the old ones (each row is read only by its own thread; q / k
+// rows shared with other value heads, Hk < H, are left to the roll kernel that runs
+// after this one). Rows past T are clamped copies of row T-1 and are not used.
+constexpr int SHORT_D = 128, SHORT_THREADS = 512, SHORT_TMAX = 16;
+template <bool BF, bool GDN, int TM>
+__global__ __launch_bounds__(SHORT_THREADS, 6) void seq_short_kernel(MixerArgs a) {
+    constexpr int D = SHORT_D, CPT = 2, NG = SHORT_THREADS / 8, KPL = D / 8, EW = GDN ? 1 : D;
+    constexpr int NW = SHORT_THREADS / 64;
+    static_assert(fused_cpt<D>() == CPT && fused_threads<D>() == SHORT_THREADS, "the fused kernel's lane map");
+    static_assert(SHORT_THREADS % D == 0, "one gate column per thread");
+    __shared__ float pre[3][TM][D];  // conv outputs q, k, v (q, k l2-normalised in place)
+    __shared__ float es[TM][EW];     // exp(g)
+    __shared__ float os[TM][D];      // scan readout
+    __shared__ float bs[TM], kqs[TM];
 
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = blockIdx.x % a.H, b = seq_of(a, blockIdx.x / a.H);
     const int bh = b * a.H + h, K = a.K;
     const size_t qkv = (size_t)a.H * D, head_off = (size_t)h * D;
@@ -210,8 +215,9 @@ __global__ __launch_bounds__(DEC_THREADS, 6) void seq_decode_kernel(MixerArgs a)
 
     const GateCol gp = gate_col(a, h, GDN ? (size_t)h : head_off + tid % D);
     size_t row0;
-    int T;
-    seq_span(a, b, &row0, &T);
+    int Tspan;
+    seq_span(a, b, &row0, &Tspan);
+    const int T = TM == 1 ? 1 : Tspan;  // 1 <= T <= TM (the launch checks it)
 
     if (tid < 3 * D) {  // conv + SiLU of plane tid / D, channel tid % D
         const int plane = tid / D, ch = tid % D;
@@ -221,41 +227,61 @@ __global__ __launch_bounds__(DEC_THREADS, 6) void seq_decode_kernel(MixerArgs a)
         conv_window_from_ring(cc, ring_row, K);
         conv_load_taps(cc, a.conv_w + prow * K, K);
         const void* xsrc = plane == 0 ? a.q : (plane == 1 ? a.k : a.v);
-        const size_t xc = plane < 2 ? row0 * kw + khead + ch : row0 * qkv + head_off + ch;
-        pre[plane][ch] = silu_f(conv_push(cc, ld_act<BF>(xsrc, xc)));
+        const size_t xw = plane < 2 ? kw : qkv, xc = (plane < 2 ? khead : head_off) + ch;
+        float x[TM];
+#pragma unroll
+        for (int t = 0; t < TM; ++t) x[t] = ld_act<BF>(xsrc, (row0 + min(t, T - 1)) * xw + xc);
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
+            if (t < T) pre[plane][t][ch] = silu_f(conv_push(cc, x[t]));
         if (plane == 2 || a.Hk == a.H) conv_window_to_ring(cc, ring_row, K);
     }
     if constexpr (GDN) {
-        if (tid == 0) {
-            es[0] = exp_f(gate_in(a, gp, ld_act<BF>(a.g, row0 * a.H + h)));
-            bs = beta_in(a, ld_act<BF>(a.beta, row0 * a.H + h));
+        if (tid < T) {
+            es[tid][0] = exp_f(gate_in(a, gp, ld_act<BF>(a.g, (row0 + tid) * a.H + h)));
+            bs[tid] = beta_in(a, ld_act<BF>(a.beta, (row0 + tid) * a.H + h));
         }
     } else {
-        if (tid < D) es[tid] = exp_f(gate_in(a, gp, ld_act<BF>(a.g, row0 * qkv + head_off + tid)));
-        if (tid == 0) bs = beta_in(a, ld_act<BF>(a.beta, row0 * a.H + h));
+        for (int idx = tid; idx < T * D; idx += SHORT_THREADS) {
+            const int t = idx / D, i = idx % D;
+            es[t][i] = exp_f(gate_in(a, gp, ld_act<BF>(a.g, (row0 + t) * qkv + head_off + i)));
+        }
+        if (tid < T) bs[tid] = beta_in(a, ld_act<BF>(a.beta, (row0 + tid) * a.H + h));
     }
     __syncthreads();
-    if (tid < 64) l2_qk_row<D>(pre[0], pre[1], lane, &kqs);
+    for (int t = wave; t < T; t += NW) l2_qk_row<D>(pre[0][t], pre[1][t], lane, &kqs[t]);
     __syncthreads();
-    {
+    for (int t = 0; t < T; ++t) {
         float vj[CPT], o[CPT];
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) vj[c] = pre[2][grp + c * NG];
-        scan_step_cols<D, GDN, CPT>(S, pre[0], pre[1], es, vj, bs, kqs, a.scale, s, o);
+        for (int c = 0; c < CPT; ++c) vj[c] = pre[2][t][grp + c * NG];
+        scan_step_cols<D, GDN, CPT>(S, pre[0][t], pre[1][t], es[t], vj, bs[t], kqs[t], a.scale, s, o);
         if (s == 0) {
 #pragma unroll
-            for (int c = 0; c < CPT; ++c) os[grp + c * NG] = o[c];
+            for (int c = 0; c < CPT; ++c) os[t][grp + c * NG] = o[c];
         }
     }
 #pragma unroll
     for (int c = 0; c < CPT; ++c) store_keys<D>(a.state_out + ((size_t)bh * D + grp + c * NG) * D, S[c], s);
     if (!a.readout) return;
     __syncthreads();
-    if (tid < 64) {
-        const size_t off = row0 * qkv + head_off;
+    for (int t = wave; t < T; t += NW) {
+        const size_t off = (row0 + t) * qkv + head_off;
         const GateRow gz = load_gate_row<D, BF>(a, off, lane);
-        gated_rmsnorm_row<D, BF, GDN>(os, gz, a, off, lane, a.o_core);
+        gated_rmsnorm_row<D, BF, GDN>(os[t], gz, a, off, lane, a.o_core);
     }
+}
+
+template <bool BF, bool GDN>
+hipError_t short_launch(const MixerArgs& a) {
+    const dim3 grid(a.B * a.H), block(SHORT_THREADS);
+    if (a.T == 1)
+        hipLaunchKernelGGL((seq_short_kernel<BF, GDN, 1>), grid, block, 0, a.stream, a);
+    else if (a.T <= 8)
+        hipLaunchKernelGGL((seq_short_kernel<BF, GDN, 8>), grid, block, 0, a.stream, a);
+    else
+        hipLaunchKernelGGL((seq_short_kernel<BF, GDN, SHORT_TMAX>), grid, block, 0, a.stream, a);
+    return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ split arm
@@ -426,12 +452,14 @@ hipError_t fused_launch(const MixerArgs& a) {
             return hipGetLastError();
         }
     }
-    if (D == DEC_D && a.T == 1 && !a.cu_seqlens)
-        hipLaunchKernelGGL((seq_decode_kernel<BF, GDN>), dim3(a.B * a.H), dim3(DEC_THREADS), 0, a.stream, a);
-    else
+    hipError_t e;
+    if (D == SHORT_D && a.T >= 1 && a.T <= SHORT_TMAX && !a.cu_seqlens) {
+        e = short_launch<BF, GDN>(a);
+    } else {
         hipLaunchKernelGGL((seq_fused_kernel<D, BF, GDN>), dim3(a.B * a.H), dim3(fused_threads<D>()), 0,
                            a.stream, a);
-    const hipError_t e = hipGetLastError();
+        e = hipGetLastError();
+    }
     if (e != hipSuccess || a.Hk == a.H) return e;
     return launch_ring_roll(a, true);  // shared q / k rows, after every reader
 }
