@@ -689,7 +689,7 @@ def main():
     tokens_per_step = cfg.B * cfg.T
     nbytes = decode_bytes(cfg)
     achieved = nbytes / (kern_avg_ms * 1e-3) / 1e9
-    traffic = traffic_from_profile("seq_decode_kernel_kda_decode")
+    traffic = traffic_from_profile("seq_short_kernel_kda_decode")
     line = {
         "metric": METRIC,
         "value": tokens_per_step / (ms_per_step * 1e-3),
@@ -709,7 +709,7 @@ def main():
                    "buffers_cycled": NBUF, "arm": "seq_fused"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "seq_decode_kernel<bf16,kda>",
+                     "kernel": "seq_short_kernel<bf16,kda,1>",
                      "kernel_avg_us": kern_avg_ms * 1e3, "kernel_median_us": kern_med_ms * 1e3,
                      "algorithmic_bytes": nbytes, "measured_copy_gbs": measure_copy()},
     }
