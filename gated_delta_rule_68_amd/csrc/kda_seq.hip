@@ -272,6 +272,108 @@ __global__ __launch_bounds__(SHORT_THREADS, 6) void seq_short_kernel(MixerArgs a
     }
 }
 
+// Short calls of GDN with two value heads per key head (H = 2 Hk): one 512-thread
+// workgroup per (sequence, key head) holds both value heads, each thread two columns
+// of each (the fused kernel's column map, once per head), so the q / k conv runs once
+// and the workgroup rolls its own q / k ring rows. Two workgroups share a CU: four
+// head states in flight per CU, where the 1024-thread fused kernel holds two.
+template <bool BF, int TM>
+__global__ __launch_bounds__(SHORT_THREADS, 4) void seq_short_pair_kernel(MixerArgs a) {
+    constexpr int D = SHORT_D, CPT = 2, NG = SHORT_THREADS / 8, KPL = D / 8, G = 2;
+    constexpr int NW = SHORT_THREADS / 64;
+    static_assert((2 + G) * D == SHORT_THREADS, "one conv channel per thread");
+    __shared__ float pre[2 + G][TM][D];  // conv outputs q, k, v of value head 0, 1
+    __shared__ float es[TM][G];          // exp(g) per value head
+    __shared__ float os[TM][G * D];      // scan readout
+    __shared__ float bs[TM][G], kqs[TM];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hx = blockIdx.x % a.Hk, b = seq_of(a, blockIdx.x / a.Hk);
+    const int K = a.K;
+    const size_t qkv = (size_t)a.H * D, kw = (size_t)a.Hk * D, khead = (size_t)hx * D;
+    const int grp = (tid >> 6) * 8 + (lane >> 3), s = lane & 7;
+    auto vhead = [&](int g) { return hx + g * a.Hk; };
+
+    float S[G][CPT][KPL];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int c = 0; c < CPT; ++c)
+            load_keys<D>(S[g][c], a.state_in + ((size_t)(b * a.H + vhead(g)) * D + grp + c * NG) * D, s);
+
+    const int ge = min(tid / TM, G - 1), te = tid % TM;  // gate / beta slot of threads tid < G * TM
+    const GateCol gp = gate_col(a, vhead(ge), vhead(ge));
+    size_t row0;
+    int Tspan;
+    seq_span(a, b, &row0, &Tspan);
+    const int T = TM == 1 ? 1 : Tspan;  // 1 <= T <= TM (the launch checks it)
+
+    {  // conv + SiLU of plane tid / D (q, k, v of head 0, v of head 1), channel tid % D
+        const int plane = tid / D, ch = tid % D;
+        const size_t vo = plane < 2 ? 0 : (size_t)vhead(plane - 2) * D;
+        const size_t prow = plane < 2 ? plane * kw + khead + ch : 2 * kw + vo + ch;
+        float* ring_row = a.ring + ((size_t)b * ring_rows(a) + prow) * (K - 1);
+        ConvChannel cc;
+        conv_window_from_ring(cc, ring_row, K);
+        conv_load_taps(cc, a.conv_w + prow * K, K);
+        const void* xsrc = plane == 0 ? a.q : (plane == 1 ? a.k : a.v);
+        const size_t xw = plane < 2 ? kw : qkv, xc = (plane < 2 ? khead : vo) + ch;
+        float x[TM];
+#pragma unroll
+        for (int t = 0; t < TM; ++t) x[t] = ld_act<BF>(xsrc, (row0 + min(t, T - 1)) * xw + xc);
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
+            if (t < T) pre[plane][t][ch] = silu_f(conv_push(cc, x[t]));
+        conv_window_to_ring(cc, ring_row, K);
+    }
+    if (tid < G * TM && te < T) {
+        const int hv = vhead(ge);
+        es[te][ge] = exp_f(gate_in(a, gp, ld_act<BF>(a.g, (row0 + te) * a.H + hv)));
+        bs[te][ge] = beta_in(a, ld_act<BF>(a.beta, (row0 + te) * a.H + hv));
+    }
+    __syncthreads();
+    for (int t = wave; t < T; t += NW) l2_qk_row<D>(pre[0][t], pre[1][t], lane, &kqs[t]);
+    __syncthreads();
+    for (int t = 0; t < T; ++t) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            float vj[CPT], o[CPT];
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) vj[c] = pre[2 + g][t][grp + c * NG];
+            scan_step_cols<D, true, CPT>(S[g], pre[0][t], pre[1][t], &es[t][g], vj, bs[t][g], kqs[t], a.scale, s, o);
+            if (s == 0) {
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) os[t][g * D + grp + c * NG] = o[c];
+            }
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int c = 0; c < CPT; ++c)
+            store_keys<D>(a.state_out + ((size_t)(b * a.H + vhead(g)) * D + grp + c * NG) * D, S[g][c], s);
+    if (!a.readout) return;
+    __syncthreads();
+    for (int idx = wave; idx < T * G; idx += NW) {
+        const int t = idx / G, g = idx % G;
+        const size_t off = (row0 + t) * qkv + (size_t)vhead(g) * D;
+        const GateRow gz = load_gate_row<D, BF>(a, off, lane);
+        gated_rmsnorm_row<D, BF, true>(&os[t][g * D], gz, a, off, lane, a.o_core);
+    }
+}
+
+template <bool BF>
+hipError_t short_pair_launch(const MixerArgs& a) {
+    const dim3 grid(a.B * a.Hk), block(SHORT_THREADS);
+    if (a.T == 1)
+        hipLaunchKernelGGL((seq_short_pair_kernel<BF, 1>), grid, block, 0, a.stream, a);
+    else if (a.T <= 8)
+        hipLaunchKernelGGL((seq_short_pair_kernel<BF, 8>), grid, block, 0, a.stream, a);
+    else
+        hipLaunchKernelGGL((seq_short_pair_kernel<BF, SHORT_TMAX>), grid, block, 0, a.stream, a);
+    return hipGetLastError();
+}
+
 template <bool BF, bool GDN>
 hipError_t short_launch(const MixerArgs& a) {
     const dim3 grid(a.B * a.H), block(SHORT_THREADS);
@@ -447,6 +549,7 @@ template <int D, bool BF, bool GDN>
 hipError_t fused_launch(const MixerArgs& a) {
     if constexpr (GDN) {
         if (a.H == 2 * a.Hk) {  // both value heads of a key head in one workgroup
+            if (D == SHORT_D && a.T >= 1 && a.T <= SHORT_TMAX && !a.cu_seqlens) return short_pair_launch<BF>(a);
             hipLaunchKernelGGL((seq_fused_kernel<D, BF, GDN, 2>), dim3(a.B * a.Hk), dim3(2 * fused_threads<D>()),
                                0, a.stream, a);
             return hipGetLastError();
