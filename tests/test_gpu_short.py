@@ -1,0 +1,98 @@
+"""Short sequential calls at D = 128 (the decode step, speculative verify, rollback
+replays): calls of 1..16 tokens run the short-call kernels (token slots TM = 1, 8, 16;
+GDN with two value heads per key head on the pair kernel), longer calls the T-token
+fused kernel. These tests pin the slot boundaries (T = 8 / 9 and 16 / 17) bit for bit
+against chained one-token decodes, and against the fp64 oracle with the widest conv
+(T < K-1 mixes old ring slots and new rows)."""
+import pytest
+import torch
+
+import gated_delta_rule_68_amd as kda
+from gated_delta_rule_68_amd.synth import CONFIGS
+from tests.gpu_util import assert_bitwise, compare_to_oracle, inputs_for, oracle_run, run_gpu
+from tests.test_gpu_gqa import compare, oracle_heads, run_gqa
+
+pytestmark = pytest.mark.gpu
+SEQ = kda.KDA_MODE_SEQUENTIAL
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+def _chain(cfg, dev, T, grouped):
+    """T chained one-token decodes from the config's initial ring and state."""
+    ring, state = dev["ring"].clone(), dev["state"].clone()
+    outs, cores = [], []
+    for t in range(T):
+        if grouped:
+            r = run_gqa(cfg, dev, decode=True, t0=t, T=1, ring=ring, state=state)
+        else:
+            r = run_gpu(cfg, dev, decode=True, t0=t, T=1, ring=ring, state=state, inplace=True)
+        outs.append(r["out"])
+        cores.append(r["o_core"])
+    return {"out": torch.cat(outs, 1), "o_core": torch.cat(cores, 1), "ring": ring, "state": state}
+
+
+# (name, config overrides): KDA and GDN one head per workgroup; GDN with two value
+# heads per key head (pair kernel); GDN with four (one workgroup per value head and
+# the q / k ring roll launch after it)
+VARIANTS = [("kda", dict(gdn=False, H=4)), ("gdn", dict(gdn=True, H=4)),
+            ("gdn_pair", dict(gdn=True, H=4, Hk=2)), ("gdn_g4", dict(gdn=True, H=8, Hk=2))]
+
+
+@pytest.mark.parametrize("T", [2, 8, 9, 16])
+@pytest.mark.parametrize("name,over", VARIANTS, ids=[v[0] for v in VARIANTS])
+def test_short_call_equals_chained_decodes(name, over, T):
+    cfg = CONFIGS["kda_decode"].with_(B=3, T=T, **over)
+    _print("case", name, cfg)
+    inp, dev = inputs_for(cfg)
+    grouped = cfg.hk != cfg.H
+    one = run_gqa(cfg, dev, mode=SEQ) if grouped else run_gpu(cfg, dev, mode=SEQ)
+    torch.cuda.synchronize()
+    assert_bitwise(one, _chain(cfg, dev, T, grouped))
+
+
+@pytest.mark.parametrize("gdn", [False, True])
+def test_fused_kernel_past_the_slots_equals_chained_decodes(gdn):
+    """T = 17 with B*H >= 1024 (H = 64, B = 16) takes the T-token fused kernel; chained
+    decodes take the short-call kernel: same bits."""
+    cfg = CONFIGS["kda_decode"].with_(B=16, T=17, gdn=gdn)
+    _print("case", cfg)
+    assert kda.prefill_arm(cfg.B, cfg.T, cfg.H, cfg.D, kda.KDA_DTYPE_BF16, SEQ) == 1  # seq_fused
+    inp, dev = inputs_for(cfg)
+    one = run_gpu(cfg, dev, mode=SEQ)
+    torch.cuda.synchronize()
+    assert_bitwise(one, _chain(cfg, dev, cfg.T, False))
+
+
+@pytest.mark.parametrize("T", [1, 3, 9, 16])
+@pytest.mark.parametrize("name,over", VARIANTS, ids=[v[0] for v in VARIANTS])
+def test_short_call_widest_conv_vs_oracle(name, over, T):
+    """K = 8, random ring and state, bf16 at D = 128: every head against the oracle."""
+    cfg = CONFIGS["kda_decode"].with_(B=2, T=T, K=8, **over)
+    _print("case", name, cfg)
+    inp, dev = inputs_for(cfg)
+    if cfg.hk != cfg.H:
+        got = run_gqa(cfg, dev, mode=SEQ)
+        torch.cuda.synchronize()
+        heads = list(range(cfg.H))
+        ref, vc, rows, bsel = oracle_heads(inp, heads, list(range(cfg.B)))
+        compare(got, ref, vc, rows, bsel, heads, 2e-2)
+    else:
+        got = run_gpu(cfg, dev, mode=SEQ)
+        torch.cuda.synchronize()
+        ref, ch, rows, bsel, heads = oracle_run(inp)
+        _print("errs", compare_to_oracle(cfg, got, ref, ch, rows, bsel, heads))
+
+
+@pytest.mark.parametrize("T", [1, 8])
+def test_short_call_without_readout_outputs_same_state(T):
+    """o_core omitted: the state and ring are the same bits (the readout is the
+    kernel's last phase)."""
+    cfg = CONFIGS["kda_decode"].with_(B=2, H=4, T=T)
+    inp, dev = inputs_for(cfg)
+    a = run_gpu(cfg, dev, mode=SEQ)
+    b = run_gpu(cfg, dev, mode=SEQ, o_core=False)
+    torch.cuda.synchronize()
+    assert_bitwise(a, b, keys=("out", "ring", "state"))
