@@ -272,6 +272,140 @@ __global__ __launch_bounds__(SHORT_THREADS, 6) void seq_short_kernel(MixerArgs a
     }
 }
 
+// Longer calls at D = 128, one value head per workgroup (G = 1), packed batches
+// included: the short-call kernel's structure over blocks of 16 tokens. A block's raw
+// rows and conv taps are all requested at its start; the conv windows carry over in
+// LDS between blocks. Same helpers, same values, same order as the
+// fused kernel (its bits). At most 80 VGPRs and 51 KiB of LDS: three workgroups per CU.
+constexpr int BLOCK_TB = 16;
+template <bool BF, bool GDN>
+__global__ __launch_bounds__(SHORT_THREADS, 6) void seq_blocks_kernel(MixerArgs a) {
+    constexpr int D = SHORT_D, CPT = 2, NG = SHORT_THREADS / 8, KPL = D / 8, EW = GDN ? 1 : D;
+    constexpr int NW = SHORT_THREADS / 64, TB = BLOCK_TB, RPW = TB / NW;
+    static_assert(fused_cpt<D>() == CPT && fused_threads<D>() == SHORT_THREADS, "the fused kernel's lane map");
+    static_assert(TB % NW == 0, "norm rows per wavefront");
+    __shared__ float pre[3][TB][D];          // conv outputs q, k, v (q, k l2-normalised in place)
+    __shared__ float es[TB][EW];             // exp(g)
+    __shared__ float os[TB][D];              // scan readout
+    __shared__ float bs[TB], kqs[TB];
+    __shared__ float wins[3 * D][KMAX - 1];  // conv windows between blocks
+
+    // The thread index is re-materialised at every phase (an opaque copy): otherwise the
+    // compiler hoists every phase's per-thread addresses out of the block loop and keeps
+    // them all alive at once, which spills.
+    int tid = threadIdx.x;
+#define KDA_LAUNDER_TID() asm volatile("" : "+v"(tid))
+    const int h = blockIdx.x % a.H, b = seq_of(a, blockIdx.x / a.H);
+    const int bh = b * a.H + h, K = a.K;
+    const size_t qkv = (size_t)a.H * D, head_off = (size_t)h * D;
+    const size_t kw = (size_t)a.Hk * D, khead = (size_t)(h % a.Hk) * D;
+    // conv row of threads tid < 3 D: plane tid / D (q, k, v), channel tid % D
+    auto ring_row_of = [&](int t) -> float* {
+        const int plane = t / D, ch = t % D;
+        const size_t prow = plane < 2 ? plane * kw + khead + ch : 2 * kw + head_off + ch;
+        return a.ring + ((size_t)b * ring_rows(a) + prow) * (K - 1);
+    };
+    auto state_row = [&](int t, int c) -> size_t {  // offset of this thread's column c
+        return ((size_t)bh * D + (t >> 6) * 8 + ((t & 63) >> 3) + c * NG) * D;
+    };
+
+    float S[CPT][KPL];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) load_keys<D>(S[c], a.state_in + state_row(tid, c), tid & 7);
+
+    const GateCol gp = gate_col(a, h, GDN ? (size_t)h : head_off + tid % D);
+    size_t rstart;
+    int T;
+    seq_span(a, b, &rstart, &T);
+
+    if (tid < 3 * D) {
+        ConvChannel cc;
+        conv_window_from_ring(cc, ring_row_of(tid), K);
+#pragma unroll
+        for (int e = 0; e < KMAX - 1; ++e) wins[tid][e] = cc.win[e];
+    }
+    for (int t0 = 0; t0 < T; t0 += TB) {
+        const int nt = min(TB, T - t0);
+        const size_t row0 = rstart + t0;
+        KDA_LAUNDER_TID();
+        if (tid < 3 * D) {  // conv + SiLU of plane tid / D, channel tid % D
+            const int plane = tid / D, ch = tid % D;
+            const size_t prow = plane < 2 ? plane * kw + khead + ch : 2 * kw + head_off + ch;
+            ConvChannel cc;
+            conv_load_taps(cc, a.conv_w + prow * K, K);
+            const void* xsrc = plane == 0 ? a.q : (plane == 1 ? a.k : a.v);
+            const size_t xw = plane < 2 ? kw : qkv, xc = (plane < 2 ? khead : head_off) + ch;
+            float x[TB];
+#pragma unroll
+            for (int t = 0; t < TB; ++t) x[t] = ld_act<BF>(xsrc, (row0 + min(t, nt - 1)) * xw + xc);
+#pragma unroll
+            for (int e = 0; e < KMAX - 1; ++e) cc.win[e] = wins[tid][e];
+#pragma unroll
+            for (int t = 0; t < TB; ++t)
+                if (t < nt) pre[plane][t][ch] = silu_f(conv_push(cc, x[t]));
+#pragma unroll
+            for (int e = 0; e < KMAX - 1; ++e) wins[tid][e] = cc.win[e];
+        }
+        KDA_LAUNDER_TID();
+        if constexpr (GDN) {
+            if (tid < nt) {
+                es[tid][0] = exp_f(gate_in(a, gp, ld_act<BF>(a.g, (row0 + tid) * a.H + h)));
+                bs[tid] = beta_in(a, ld_act<BF>(a.beta, (row0 + tid) * a.H + h));
+            }
+        } else {
+            for (int idx = tid; idx < nt * D; idx += SHORT_THREADS) {
+                const int t = idx / D, i = idx % D;
+                es[t][i] = exp_f(gate_in(a, gp, ld_act<BF>(a.g, (row0 + t) * qkv + head_off + i)));
+            }
+            if (tid < nt) bs[tid] = beta_in(a, ld_act<BF>(a.beta, (row0 + tid) * a.H + h));
+        }
+        __syncthreads();
+        KDA_LAUNDER_TID();
+        for (int t = tid >> 6; t < nt; t += NW) l2_qk_row<D>(pre[0][t], pre[1][t], tid & 63, &kqs[t]);
+        __syncthreads();
+        KDA_LAUNDER_TID();
+        {
+            const int grp = (tid >> 6) * 8 + ((tid & 63) >> 3), s = tid & 7;
+            for (int t = 0; t < nt; ++t) {
+                float vj[CPT], o[CPT];
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) vj[c] = pre[2][t][grp + c * NG];
+                scan_step_cols<D, GDN, CPT>(S, pre[0][t], pre[1][t], es[t], vj, bs[t], kqs[t], a.scale, s, o);
+                if (s == 0) {
+#pragma unroll
+                    for (int c = 0; c < CPT; ++c) os[t][grp + c * NG] = o[c];
+                }
+            }
+        }
+        __syncthreads();
+        KDA_LAUNDER_TID();
+        if (a.readout) {
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) {
+                const int t = (tid >> 6) + r * NW;
+                if (t < nt) {
+                    const size_t off = (row0 + t) * qkv + head_off;
+                    const GateRow gz = load_gate_row<D, BF>(a, off, tid & 63);
+                    gated_rmsnorm_row<D, BF, GDN>(os[t], gz, a, off, tid & 63, a.o_core);
+                }
+            }
+        }
+        __syncthreads();
+    }
+    KDA_LAUNDER_TID();
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) store_keys<D>(a.state_out + state_row(tid, c), S[c], tid & 7);
+    // the windows hold the last K-1 raw inputs of [old ring ++ x]; q / k rows shared
+    // with other value heads (Hk < H) are rolled by the roll kernel after this one
+    if (tid < 3 * D && (tid >= 2 * D || a.Hk == a.H)) {
+        ConvChannel cc;
+#pragma unroll
+        for (int e = 0; e < KMAX - 1; ++e) cc.win[e] = wins[tid][e];
+        conv_window_to_ring(cc, ring_row_of(tid), K);
+    }
+#undef KDA_LAUNDER_TID
+}
+
 // Short calls of GDN with two value heads per key head (H = 2 Hk): one 512-thread
 // workgroup per (sequence, key head) holds both value heads, each thread two columns
 // of each (the fused kernel's column map, once per head), so the q / k conv runs once
@@ -558,6 +692,9 @@ hipError_t fused_launch(const MixerArgs& a) {
     hipError_t e;
     if (D == SHORT_D && a.T >= 1 && a.T <= SHORT_TMAX && !a.cu_seqlens) {
         e = short_launch<BF, GDN>(a);
+    } else if (D == SHORT_D) {
+        hipLaunchKernelGGL((seq_blocks_kernel<BF, GDN>), dim3(a.B * a.H), dim3(SHORT_THREADS), 0, a.stream, a);
+        e = hipGetLastError();
     } else {
         hipLaunchKernelGGL((seq_fused_kernel<D, BF, GDN>), dim3(a.B * a.H), dim3(fused_threads<D>()), 0,
                            a.stream, a);
