@@ -29,10 +29,9 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // ------------------------------------------------------------------ fused arm
 // Value columns per thread of the fused kernel at D = 128. Two columns (512
-// threads, ~117 VGPRs, two workgroups per CU) measured fastest on the decode step for
-// this kernel: one column (1024 threads) keeps too little state in flight per CU, four
-// or eight columns raise the register count until occupancy drops. The short-call and
-// block kernels below keep the same column map with fewer live registers.
+// threads, ~117 VGPRs, two workgroups per CU) measured fastest on the decode step:
+// one column (1024 threads) keeps too little state in flight per CU, four or eight
+// columns raise the register count until occupancy drops.
 template <int D>
 constexpr int fused_cpt() { return D >= 128 ? 2 : 1; }
 template <int D>
