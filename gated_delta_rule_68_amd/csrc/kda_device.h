@@ -121,10 +121,19 @@ __device__ __forceinline__ float gate_in(const MixerArgs& a, const GateCol& p, f
 
 // Butterfly sums. Every lane of the group ends with the same bits (each step adds
 // the same two operands, only in swapped order).
+// The 8-lane sum runs on DPP (no LDS crossbar traffic): quad_perm [1,0,3,2] and
+// [2,3,0,1] pair lane bits 0 and 1, then row_half_mirror pairs lane l with 7 - l of
+// its 8-lane group. After the first two steps every lane of a quad holds the same
+// value, so the last step adds the two quads' values exactly as a partner across lane
+// bit 2 would. The groups must be aligned to 8 lanes and the wavefront fully active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(x), CTRL, 0xf, 0xf, false));
+}
 __device__ __forceinline__ float sum_lanes8(float v) {
-    v += __shfl_xor(v, 1, 64);
-    v += __shfl_xor(v, 2, 64);
-    v += __shfl_xor(v, 4, 64);
+    v += dpp_mov<0xB1>(v);
+    v += dpp_mov<0x4E>(v);
+    v += dpp_mov<0x141>(v);
     return v;
 }
 
