@@ -137,14 +137,18 @@ __device__ __forceinline__ float sum_lanes8(float v) {
     return v;
 }
 
+// The 64-lane sum: the 8-lane steps, row_mirror (lane l with 15 - l: the two 8-lane
+// halves of a row), then v_permlane16_swap and v_permlane32_swap (lane bits 4 and 5;
+// each returns a lane's own value and its partner's, in an order that depends on the
+// lane, which an addition does not see). As above, each step pairs groups whose lanes
+// already hold one value, so the sum has the bits of the lane-xor butterfly.
 __device__ __forceinline__ float sum_lanes64(float v) {
-    v += __shfl_xor(v, 1, 64);
-    v += __shfl_xor(v, 2, 64);
-    v += __shfl_xor(v, 4, 64);
-    v += __shfl_xor(v, 8, 64);
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    return v;
+    v = sum_lanes8(v);
+    v += dpp_mov<0x140>(v);
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
 }
 
 // ---------------------------------------------------------------------------
