@@ -136,6 +136,15 @@ __device__ __forceinline__ float sum_lanes8(float v) {
     v += dpp_mov<0x141>(v);
     return v;
 }
+// The same sum through the LDS crossbar (lane xor 1, 2, 4): identical bits. Kernels
+// whose scan interleaves many column sums per thread (four columns in the grouped-head
+// pair kernel) measured faster with it, the VALU pipe being the busier one there.
+__device__ __forceinline__ float sum_lanes8_xbar(float v) {
+    v += __shfl_xor(v, 1, 64);
+    v += __shfl_xor(v, 2, 64);
+    v += __shfl_xor(v, 4, 64);
+    return v;
+}
 
 // The 64-lane sum: the 8-lane steps, row_mirror (lane l with 15 - l: the two 8-lane
 // halves of a row), then v_permlane16_swap and v_permlane32_swap (lane bits 4 and 5;
@@ -321,9 +330,9 @@ __device__ __forceinline__ void store_keys(float* row, const float (&src)[D / 8]
 // l2-normalised rows, erow holds exp(g) (D values for KDA, one for GDN), vj the
 // columns' v values, kq = k.q. The readout uses the post-update state, expanded as
 // S'^T q + beta u (k.q) where S' is the decayed state, so both reductions run in one
-// pass. The arithmetic of a column does not depend on CPT: every arm produces the
-// same bits for the same column.
-template <int D, bool GDN, int CPT>
+// pass. The arithmetic of a column does not depend on CPT or XBAR (which lane path
+// the column sums take): every arm produces the same bits for the same column.
+template <int D, bool GDN, int CPT, bool XBAR = false>
 __device__ __forceinline__ void scan_step_cols(float (&S)[CPT][D / 8], const float* qrow,
                                                const float* krow, const float* erow,
                                                const float (&vj)[CPT], float beta, float kq,
@@ -363,8 +372,8 @@ __device__ __forceinline__ void scan_step_cols(float (&S)[CPT][D / 8], const flo
     float bu[CPT];
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-        const float sk = sum_lanes8(a0[c] + a1[c]);
-        const float sq = sum_lanes8(b0[c] + b1[c]);
+        const float sk = XBAR ? sum_lanes8_xbar(a0[c] + a1[c]) : sum_lanes8(a0[c] + a1[c]);
+        const float sq = XBAR ? sum_lanes8_xbar(b0[c] + b1[c]) : sum_lanes8(b0[c] + b1[c]);
         bu[c] = beta * (vj[c] - sk);
         o[c] = scale * fmaf(bu[c], kq, sq);
     }

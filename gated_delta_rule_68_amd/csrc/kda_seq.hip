@@ -474,7 +474,7 @@ __global__ __launch_bounds__(SHORT_THREADS, 4) void seq_short_pair_kernel(MixerA
             float vj[CPT], o[CPT];
 #pragma unroll
             for (int c = 0; c < CPT; ++c) vj[c] = pre[2 + g][t][grp + c * NG];
-            scan_step_cols<D, true, CPT>(S[g], pre[0][t], pre[1][t], &es[t][g], vj, bs[t][g], kqs[t], a.scale, s, o);
+            scan_step_cols<D, true, CPT, true>(S[g], pre[0][t], pre[1][t], &es[t][g], vj, bs[t][g], kqs[t], a.scale, s, o);
             if (s == 0) {
 #pragma unroll
                 for (int c = 0; c < CPT; ++c) os[t][g * D + grp + c * NG] = o[c];
