@@ -43,12 +43,12 @@ int check_shape(int B, int T, int H, int D, int K) {
 // fused workgroup per pair; below that the column-split pipeline is used, except for
 // very short prefills where its extra launches would dominate.
 // The chunked arm (D = 128) computes its contractions with bf16 operands, so AUTO
-// takes it only for bf16 activations, from 32 tokens on, or from 17 when there are
+// takes it only for bf16 activations, from 33 tokens on, or from 17 when there are
 // fewer than 1024 (b, h) pairs (where the sequential arm would be the column-split
 // pipeline): measured faster than either sequential arm there (e.g. B = 64, H = 64:
-// 0.38 against 0.42 ms at T = 32, 0.40 against 0.87 ms at T = 64; B = 8, H = 32,
-// T = 17: 31 against 50 us), and slower below (T = 17, B = 64, H = 64: 0.38 against
-// 0.23 ms).
+// 0.38 against 0.46 ms at T = 40, 0.40 against 0.75 ms at T = 64; B = 8, H = 64,
+// T = 24: 53 against 89 us), and slower below (B = 64, H = 64: 0.38 against 0.35 ms
+// at T = 32, against 0.27 ms at T = 24).
 // Few (b, h) pairs leave most compute units idle in the chunked arm. AUTO takes the
 // segmented arm (kda_internal.h, seg_plan) when its plan, with segments of at least
 // kSegAutoChunks chunks, shortens the critical path to at most 85% of the chunk
@@ -66,7 +66,7 @@ int pick_arm(int B, int T, int H, int D, bool bf16, int mode) {
     const bool chunk_ok = kda::kChunkedArmBuilt && D == 128;
     if (mode == KDA_MODE_CHUNKED) return chunk_ok ? kda::ARM_CHUNKED : -1;
     if (mode == KDA_MODE_SEGMENTED) return chunk_ok ? kda::ARM_SEGMENTED : -1;
-    if (mode == KDA_MODE_AUTO && chunk_ok && bf16 && (T >= 32 || (T > 16 && (long)B * H < 1024)))
+    if (mode == KDA_MODE_AUTO && chunk_ok && bf16 && (T > 32 || (T > 16 && (long)B * H < 1024)))
         return segments_pay(B, T, H) ? kda::ARM_SEGMENTED : kda::ARM_CHUNKED;
     if (mode != KDA_MODE_AUTO && mode != KDA_MODE_SEQUENTIAL) return -1;
     if (T <= 16 || (long)B * H >= 1024) return kda::ARM_SEQ_FUSED;

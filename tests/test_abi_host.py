@@ -140,12 +140,12 @@ def test_queries():
 
 def test_auto_arm_boundaries():
     # bf16 at D = 128: the short-call sequential kernel up to 16 tokens; the chunked arm
-    # from 32 tokens, or from 17 with fewer than 1024 (b, h) pairs; fp32 and D = 16 stay
+    # from 33 tokens, or from 17 with fewer than 1024 (b, h) pairs; fp32 and D = 16 stay
     # sequential (fused from 1024 pairs, else the column-split pipeline)
     assert kda.prefill_arm(64, 16, 64, 128, 1, 0) == 1
     assert kda.prefill_arm(64, 17, 64, 128, 1, 0) == 1
-    assert kda.prefill_arm(64, 31, 64, 128, 1, 0) == 1
-    assert kda.prefill_arm(64, 32, 64, 128, 1, 0) == 3
+    assert kda.prefill_arm(64, 32, 64, 128, 1, 0) == 1
+    assert kda.prefill_arm(64, 33, 64, 128, 1, 0) == 3
     assert kda.prefill_arm(8, 16, 32, 128, 1, 0) == 1
     assert kda.prefill_arm(8, 17, 32, 128, 1, 0) == 3
     assert kda.prefill_arm(16, 17, 64, 128, 1, 0) == 1  # 1024 pairs
