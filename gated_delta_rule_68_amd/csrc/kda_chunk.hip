@@ -665,13 +665,12 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
         }
     }
 
-    // Conv roles. q / k (P1): wavefront w < 4 convolves k, w >= 4 convolves q, rows
-    // 16 (w % 4) .. +15 (one 16-row block), channels 2 lane and 2 lane + 1, so the
-    // l2 norm of a row is a sum over the 64 lanes of one wavefront and the block's
-    // gate prefix is a per-thread running sum. v (P3, while wavefronts 0..3 solve for
+    // Conv roles. q / k (P1): wavefront w convolves both, rows 16 (w % 4) + 8 (w / 4)
+    // .. +7 (half of one 16-row block), channels 2 lane and 2 lane + 1, so the l2 norm
+    // of a row is a sum over the 64 lanes of one wavefront and the block's gate prefix
+    // is a per-thread running sum. v (P3, while wavefronts 0..3 solve for
     // T): items (NVCH channels, 16-row block) on the threads of wavefronts 4..7, NVP
     // per thread, all of the same channels.
-    const bool kplane = wave < 4;
     constexpr int NVCH = NC == 128 ? 2 : 1;
     constexpr int NVIT = 4 * NC / NVCH, NVP = (NVIT + NTHR / 2 - 1) / (NTHR / 2);
     static_assert((NTHR / 2) % (NC / NVCH) == 0, "the v items of a thread share its channels");
@@ -723,8 +722,9 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
         // bytes). They are requested here, before any prefetch of the next chunk:
         // vector-memory counters complete in order, so a small load issued after the
         // prefetch could only be waited for together with all of it.
-        float wqk[2][KT], wv[NVCH][KT], w8[8];
-        load_taps<KT, 2>(wqk, a.conv_w, (kplane ? kw : 0) + khead + 2 * lane, K);
+        float wqk[2][2][KT], wv[NVCH][KT], w8[8];  // wqk[0]: q taps, wqk[1]: k taps
+        load_taps<KT, 2>(wqk[0], a.conv_w, khead + 2 * lane, K);
+        load_taps<KT, 2>(wqk[1], a.conv_w, kw + khead + 2 * lane, K);
         load_taps<KT, NVCH>(wv, a.conv_w, 2 * kw + head_off + jv0 + max(cv, 0), K);  // used by wavefronts 4..7
         if constexpr (NCOL == 1) {
 #pragma unroll
@@ -732,61 +732,87 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
         }
 
         KDA_LAUNDER_LANE();
-        // ---- P1: gate prefix, conv + SiLU + l2, decayed operand tiles ----
+        // ---- P1: gate prefix, conv + SiLU + l2, decayed operand tiles. The two
+        // wavefronts of a SIMD (w and w + 4) share the 16-row block 16 (w % 4): w takes
+        // its rows 0..7 and w + 4 rows 8..15, each for both q and k, so the decay
+        // exponentials of a (row, channel) serve the q and both k tiles and the two end
+        // together. ----
         {
-            const int qq = wave & 3, rb = 16 * qq, c2 = 2 * lane;
+            const int qq = wave & 3, rb = 16 * qq, c2 = 2 * lane, hr = 8 * (wave >> 2);
             constexpr int NG = GDN ? 1 : 2;
-            // gamma (gate sum of rows rb+1 .. rb+r), block total and first gate, all
-            // times log2 e
-            float gm[16][NG], tot[NG], g0[NG];
-#pragma unroll
-            for (int e = 0; e < NG; ++e) gm[0][e] = 0.0f;
-            if constexpr (GDN) {
-                float acc = 0.0f;
-#pragma unroll
-                for (int r = 1; r < 16; ++r) {
-                    acc = fmaf(sm.c.raw.gs[rb + r], LOG2E, acc);
-                    gm[r][0] = acc;
+            // the gate of row `row`, channel c2 + e, in log2 units, added to acc
+            auto add_gate = [&](float acc, int row, int e) -> float {
+                if constexpr (GDN) {
+                    return fmaf(sm.c.raw.gs[row], LOG2E, acc);
+                } else if constexpr (!ACT) {
+                    return fmaf((float)ld2(&sm.c.raw.rg[row][c2])[e], LOG2E, acc);
+                } else {
+                    const uint32_t hi = *reinterpret_cast<const uint32_t*>(&sm.c.raw.rg[row][c2]);
+                    const uint32_t lo = *reinterpret_cast<const uint32_t*>(&sm.e.pre.vb.glo[row][c2]);
+                    return acc + __uint_as_float(e ? ((hi & 0xffff0000u) | (lo >> 16)) : ((hi << 16) | (lo & 0xffffu)));
                 }
-                g0[0] = sm.c.raw.gs[rb] * LOG2E;
-                tot[0] = g0[0] + acc;
-            } else {
-                const __bf16* rg = &sm.c.raw.rg[rb][c2];
-                if constexpr (!ACT)
-                    gate_prefix_given(rg, gm, g0, tot);
-                else
-                    gate_prefix_split(rg, &sm.e.pre.vb.glo[rb][c2], gm, g0, tot);
+            };
+            // gamma of this wavefront's rows (gate sum of rows rb+1 .. rb+hr+r)
+            float gm[8][NG], acc[NG];
+#pragma unroll
+            for (int e = 0; e < NG; ++e) acc[e] = 0.0f;
+            if (hr) {
+#pragma unroll
+                for (int i = 1; i <= 8; ++i)
+#pragma unroll
+                    for (int e = 0; e < NG; ++e) acc[e] = add_gate(acc[e], rb + i, e);
             }
-            if (kplane) {
+#pragma unroll
+            for (int e = 0; e < NG; ++e) gm[0][e] = acc[e];
+#pragma unroll
+            for (int r = 1; r < 8; ++r)
+#pragma unroll
+                for (int e = 0; e < NG; ++e) {
+                    acc[e] = add_gate(acc[e], rb + hr + r, e);
+                    gm[r][e] = acc[e];
+                }
+            if (!hr) {  // block total and first gate for the factor table
+                float g0[NG];
+#pragma unroll
+                for (int i = 8; i < 16; ++i)
+#pragma unroll
+                    for (int e = 0; e < NG; ++e) acc[e] = add_gate(acc[e], rb + i, e);
+#pragma unroll
+                for (int e = 0; e < NG; ++e) g0[e] = add_gate(0.0f, rb, e);
                 if constexpr (GDN) {
                     if (lane == 0) {
-                        sm.fac[F_TOT + qq][0] = tot[0];
+                        sm.fac[F_TOT + qq][0] = g0[0] + acc[0];
                         sm.fac[F_G0 + qq][0] = g0[0];
                     }
                 } else {
-                    *reinterpret_cast<float2*>(&sm.fac[F_TOT + qq][c2]) = make_float2(tot[0], tot[1]);
+                    *reinterpret_cast<float2*>(&sm.fac[F_TOT + qq][c2]) = make_float2(g0[0] + acc[0], g0[1] + acc[1]);
                     *reinterpret_cast<float2*>(&sm.fac[F_G0 + qq][c2]) = make_float2(g0[0], g0[1]);
                 }
             }
 
-            // conv + SiLU of 16 rows x 2 channels
-            const __bf16* rawp = (kplane ? &sm.c.raw.rk[0][0] : &sm.c.raw.rq[0][0]) + c2;
-            float win[KT - 1][2];
+            // conv + SiLU of 8 rows x 2 channels of q (pl = 0) and k (pl = 1)
+            float y[2][8][2], ps[16];
 #pragma unroll
-            for (int d = 1; d < KT; ++d) {  // rows rb - d: in the chunk, or (block 0) the history
-                const bf16x2 x = qq > 0 ? ld2(rawp + (rb - d) * LDH) : ld2(&sm.hist[d - 1][(kplane ? DK : 0) + c2]);
+            for (int pl = 0; pl < 2; ++pl) {
+                const __bf16* rawp = (pl ? &sm.c.raw.rk[0][0] : &sm.c.raw.rq[0][0]) + c2;
+                float win[KT - 1][2];
 #pragma unroll
-                for (int e = 0; e < 2; ++e) win[KT - 1 - d][e] = (float)x[e];
+                for (int d = 1; d < KT; ++d) {  // row rb + hr - d: in the chunk, or the history
+                    const int r = rb + hr - d;
+                    const __bf16* src = r >= 0 ? rawp + r * LDH : &sm.hist[-r - 1][(pl ? DK : 0) + c2];
+                    const bf16x2 x = ld2(src);
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) win[KT - 1 - d][e] = (float)x[e];
+                }
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const bf16x2 xv = ld2(rawp + (rb + hr + r) * LDH);
+                    const float x[2] = {(float)xv[0], (float)xv[1]};
+                    conv_step<KT, 2>(win, x, wqk[pl], y[pl][r]);
+                    ps[8 * pl + r] = fmaf(y[pl][r][0], y[pl][r][0], y[pl][r][1] * y[pl][r][1]);
+                }
             }
-            float y[16][2], ps[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const bf16x2 xv = ld2(rawp + (rb + r) * LDH);
-                const float x[2] = {(float)xv[0], (float)xv[1]};
-                conv_step<KT, 2>(win, x, wqk, y[r]);
-                ps[r] = fmaf(y[r][0], y[r][0], y[r][1] * y[r][1]);
-            }
-            const float ss = sum16x64(ps, lane);  // sum of squares of row rb + lane / 4
+            const float ss = sum16x64(ps, lane);  // lane l: plane (l >> 2) / 8, row hr + (l >> 2) % 8
             if ((lane & 3) == 0) sm.nrm[wave][lane >> 2] = rsqrtf(ss + L2_EPS);
             lds_wave_sync();
             float nr[16];
@@ -797,21 +823,20 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
                 for (int e = 0; e < 4; ++e) nr[4 * r4 + e] = v4[e];
             }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                bf16x2 o1, o2;
+            for (int r = 0; r < 8; ++r) {
+                bf16x2 oq, oa, ob;
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
                     const float g = gm[r][GDN ? 0 : e];
-                    const float kh = y[r][e] * nr[r];
-                    o1[e] = (__bf16)(kh * exp2_f(g));
-                    if (kplane) o2[e] = (__bf16)(kh * exp2_f(-g));
+                    const float ep = exp2_f(g), en = exp2_f(-g);
+                    const float qh = y[0][r][e] * nr[r], kh = y[1][r][e] * nr[8 + r];
+                    oq[e] = (__bf16)(qh * ep);
+                    oa[e] = (__bf16)(kh * ep);
+                    ob[e] = (__bf16)(kh * en);
                 }
-                if (kplane) {
-                    st2(&sm.ka[rb + r][c2], o1);
-                    st2(&sm.kb[rb + r][c2], o2);
-                } else {
-                    st2(&sm.qa[rb + r][c2], o1);
-                }
+                st2(&sm.qa[rb + hr + r][c2], oq);
+                st2(&sm.ka[rb + hr + r][c2], oa);
+                st2(&sm.kb[rb + hr + r][c2], ob);
             }
         }
         lds_barrier();
