@@ -961,7 +961,35 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
         // the compiler wait for every outstanding load and store at its join)
         load_raw_part<BF, GDN, NC, RAW_Q>(raw, a, rowb, T, h, c0 + CH, jv0, tid, vsrc, vstride);
         KDA_LAUNDER_LANE();
-        // ---- P3: T = (I + A)^-1, A = diag(beta) L, in 16x16 blocks; meanwhile the v conv ----
+        // ---- P3: T = (I + A)^-1, A = diag(beta) L, in 16x16 blocks; meanwhile the v conv:
+        // rows 0..7 of each 16-row item here, rows 8..15 while wavefronts 0..2 merge the
+        // blocks below the diagonal (the other wavefronts would wait there). With the
+        // 8-tap window the carried window would spill, so those kernels convolve all 16
+        // rows here. ----
+        static_assert(NVP == 1, "one v item per thread of wavefronts 4..7");
+        constexpr bool VSPLIT = KT <= 4;
+        float vwin[KT - 1][NVCH];  // conv window of this thread's v item, kept for rows 8..15
+        const int qv = vt / (NC / NVCH), rbv = 16 * qv;
+        auto v_half = [&](int r0) {  // conv + SiLU of rows rbv + r0 .. +7, times beta, stored transposed
+            float bt[8];
+#pragma unroll
+            for (int r4 = 0; r4 < 2; ++r4) {
+                const f32x4v b4 = ld4f(&sm.beta[rbv + r0 + 4 * r4]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) bt[4 * r4 + e] = b4[e];
+            }
+            bf16x8 o[NVCH];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                float x[NVCH], y[NVCH];
+                ld_chan<NVCH>(&sm.e.pre.rv[rbv + r0 + r][cv], x);
+                conv_step<KT, NVCH>(vwin, x, wv, y);
+#pragma unroll
+                for (int e = 0; e < NVCH; ++e) o[e][r] = (__bf16)(bt[r] * y[e]);
+            }
+#pragma unroll
+            for (int e = 0; e < NVCH; ++e) st8(&sm.e.pre.vb.vbt[cv + e][rbv + r0], o[e]);
+        };
         if (wave < 4) {
             lds_wave_sync();  // this wavefront's own diagonal block from P2
             if (q4 == 0) {
@@ -1000,42 +1028,17 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
                 const int r = idx / (CH / 8), c8 = (idx % (CH / 8)) * 8;
                 if (c8 >= 16 * ((r >> 4) + 1)) st8(&sm.c.m.tb[r][c8], zero8());
             }
-            // v: conv + SiLU, times beta, stored transposed
+            // v: conv + SiLU, times beta, stored transposed (rows 0..7 of the item)
+            if (vt < NVIT) {
 #pragma unroll
-            for (int m = 0; m < NVP; ++m) {
-                const int item = vt + (NTHR / 2) * m;
-                if (item < NVIT) {
-                    const int qv = item / (NC / NVCH), rbv = 16 * qv;
-                    float win[KT - 1][NVCH];
+                for (int d = 1; d < KT; ++d) {
+                    float x[NVCH];
+                    ld_chan<NVCH>(qv > 0 ? &sm.e.pre.rv[rbv - d][cv] : &sm.hist[d - 1][2 * DK + cv], x);
 #pragma unroll
-                    for (int d = 1; d < KT; ++d) {
-                        float x[NVCH];
-                        ld_chan<NVCH>(qv > 0 ? &sm.e.pre.rv[rbv - d][cv] : &sm.hist[d - 1][2 * DK + cv], x);
-#pragma unroll
-                        for (int e = 0; e < NVCH; ++e) win[KT - 1 - d][e] = x[e];
-                    }
-                    float bt[16];
-#pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4) {
-                        const f32x4v b4 = ld4f(&sm.beta[rbv + 4 * r4]);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) bt[4 * r4 + e] = b4[e];
-                    }
-                    bf16x8 o[NVCH][2];
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        float x[NVCH], y[NVCH];
-                        ld_chan<NVCH>(&sm.e.pre.rv[rbv + r][cv], x);
-                        conv_step<KT, NVCH>(win, x, wv, y);
-#pragma unroll
-                        for (int e = 0; e < NVCH; ++e) o[e][r >> 3][r & 7] = (__bf16)(bt[r] * y[e]);
-                    }
-#pragma unroll
-                    for (int e = 0; e < NVCH; ++e) {
-                        st8(&sm.e.pre.vb.vbt[cv + e][rbv], o[e][0]);
-                        st8(&sm.e.pre.vb.vbt[cv + e][rbv + 8], o[e][1]);
-                    }
+                    for (int e = 0; e < NVCH; ++e) vwin[KT - 1 - d][e] = x[e];
                 }
+                v_half(0);
+                if constexpr (!VSPLIT) v_half(8);
             }
         }
         lds_barrier();
@@ -1044,6 +1047,7 @@ __global__ __launch_bounds__(NTHR) void chunk_kernel(MixerArgs a, float* o_buf) 
         if (wave == 0) merge_column<0>(sm.c.m, lane);
         else if (wave == 1) merge_column<1>(sm.c.m, lane);
         else if (wave == 2) merge_column<2>(sm.c.m, lane);
+        else if (VSPLIT && wave >= 4 && vt < NVIT) v_half(8);
         lds_barrier();
 
         KDA_LAUNDER_LANE();
