@@ -79,6 +79,10 @@ extern "C" {
 /* ---- dtype and prefill mode ---- */
 #define KDA_DTYPE_F32 0
 #define KDA_DTYPE_BF16 1
+/* AUTO: for bf16 activations at D = 128, the sequential arm up to 32 tokens (up to 16
+ * with fewer than 1024 (b, h) pairs), the chunked arm beyond, the segmented arm when its
+ * plan shortens the critical path (few pairs, long sequences); fp32 activations and
+ * D = 16 always take the sequential arm. *_prefill_arm reports the choice. */
 #define KDA_MODE_AUTO 0       /* library picks sequential, chunked or segmented from the shape */
 #define KDA_MODE_SEQUENTIAL 1 /* token-by-token scan (bit-identical to chained decodes) */
 #define KDA_MODE_CHUNKED 2    /* chunk-64 WY form, bf16 MFMA operands, fp32 state (D = 128) */
