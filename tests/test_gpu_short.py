@@ -1,7 +1,7 @@
 """Short sequential calls at D = 128 (the decode step, speculative verify, rollback
 replays): calls of 1..16 tokens run the short-call kernels (token slots TM = 1, 8, 16;
-GDN with two value heads per key head on the pair kernel), longer calls the T-token
-fused kernel. These tests pin the slot boundaries (T = 8 / 9 and 16 / 17) bit for bit
+GDN with two value heads per key head on the pair kernel), longer calls the 16-token
+block kernel. These tests pin the slot boundaries (T = 8 / 9 and 16 / 17) bit for bit
 against chained one-token decodes, and against the fp64 oracle with the widest conv
 (T < K-1 mixes old ring slots and new rows)."""
 import pytest
@@ -54,9 +54,9 @@ def test_short_call_equals_chained_decodes(name, over, T):
 
 
 @pytest.mark.parametrize("gdn", [False, True])
-def test_fused_kernel_past_the_slots_equals_chained_decodes(gdn):
-    """T = 17 with B*H >= 1024 (H = 64, B = 16) takes the T-token fused kernel; chained
-    decodes take the short-call kernel: same bits."""
+def test_block_kernel_past_the_slots_equals_chained_decodes(gdn):
+    """T = 17 with B*H >= 1024 (H = 64, B = 16) takes the fused arm's block kernel (two
+    blocks, the second of one row); chained decodes take the short-call kernel: same bits."""
     cfg = CONFIGS["kda_decode"].with_(B=16, T=17, gdn=gdn)
     _print("case", cfg)
     assert kda.prefill_arm(cfg.B, cfg.T, cfg.H, cfg.D, kda.KDA_DTYPE_BF16, SEQ) == 1  # seq_fused
@@ -96,3 +96,17 @@ def test_short_call_without_readout_outputs_same_state(T):
     b = run_gpu(cfg, dev, mode=SEQ, o_core=False)
     torch.cuda.synchronize()
     assert_bitwise(a, b, keys=("out", "ring", "state"))
+
+
+@pytest.mark.parametrize("T,arm", [(32, 1), (33, 3)], ids=["sequential", "chunked"])
+def test_auto_around_the_chunked_threshold_vs_oracle(T, arm):
+    """1024 (b, h) pairs, bf16 at D = 128: AUTO keeps the sequential arm at 32 tokens and
+    takes the chunked arm at 33; both against the oracle on sampled sequences and heads."""
+    cfg = CONFIGS["kda_decode"].with_(B=16, T=T)
+    assert kda.prefill_arm(cfg.B, cfg.T, cfg.H, cfg.D, kda.KDA_DTYPE_BF16, kda.KDA_MODE_AUTO) == arm
+    _print("case", cfg, "arm", arm)
+    inp, dev = inputs_for(cfg)
+    got = run_gpu(cfg, dev, mode=kda.KDA_MODE_AUTO)
+    torch.cuda.synchronize()
+    ref, ch, rows, bsel, heads = oracle_run(inp, heads=[0, 37, 63], batches=[0, 15])
+    _print("errs", compare_to_oracle(cfg, got, ref, ch, rows, bsel, heads))
