@@ -2,13 +2,16 @@
 
 A step is one batched KDA decode step (B=64 sequences x 1 token, H=64, D=128, bf16
 activations, fp32 state updated in place, conv kernel 4): conv + SiLU + l2, the
-delta-rule scan, the gated RMSNorm and the ring roll, all in the library's fused
+delta-rule scan, the gated RMSNorm and the ring roll, all in the library's one-token
 decode kernel. Inputs are seeded synthetic data (gated_delta_rule_68_amd.synth)
 already resident in HBM; NBUF independent copies of every buffer are cycled so
 that the 268 MB of state cannot stay in the 256 MB last-level cache between steps.
+The steps are replayed from a captured HIP graph of NBUF steps, as a serving loop
+runs them (--eager: one launch per step); HIP events bracket each replay.
 
-Prints ONE JSON line (rank 0). Extra legs: the single-sequence prefill (T=4626)
-and the oracle's CPU rate on a bounded sample.
+Prints ONE JSON line (rank 0). Extra legs: the prefill workloads on every arm, verify
+and rollback, fused gates, grouped heads, packed batches, and the oracle's CPU rate on
+a bounded sample.
 """
 from __future__ import annotations
 
@@ -202,7 +205,7 @@ def cpu_baselines() -> dict:
     return rec
 
 
-def run_decode(cfg, steps, warmup):
+def run_decode(cfg, steps, warmup, graph=False):
     import torch
 
     import gated_delta_rule_68_amd as kda
@@ -224,6 +227,38 @@ def run_decode(cfg, steps, warmup):
         kda.kda_decode(d["q"], d["k"], d["v"], d["g"], d["beta"], d["conv_w"], d["ring"],
                        d["state"], d["state"], d["z"], d["norm_w"], d["out"], None,
                        scale=scale, rms_eps=RMS_EPS)
+
+    if graph and steps % NBUF == 0:
+        # A serving loop replays the decode step from a captured graph: one graph holds
+        # NBUF steps (one per buffer set); HIP events bracket each replay, so a step's
+        # kernel time is a replay's time / NBUF (the kernels plus the gaps between them).
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(NBUF):
+                step(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(NBUF):
+                step(i)
+        for _ in range(max(1, -(-warmup // NBUF))):
+            g.replay()
+        torch.cuda.synchronize()
+        reps = steps // NBUF
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(reps):
+            ev[i][0].record()
+            g.replay()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        kern_ms = sorted(a.elapsed_time(b) / NBUF for a, b in ev)
+        return inp, wall, sum(kern_ms) / len(kern_ms), kern_ms[len(kern_ms) // 2]
 
     for i in range(warmup):
         step(i)
@@ -646,6 +681,8 @@ def main():
                          "the arm of --prefill-mode, --steps times after one warm-up (for profilers)")
     ap.add_argument("--prefill-mode", choices=("chunked", "segmented", "auto"), default="chunked",
                     help="prefill mode of --prefill-only (default: chunked)")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the decode steps as separate launches instead of graph replays")
     ap.add_argument("--cpu-baselines", action="store_true",
                     help="only time the fp64 oracle on the host cores, on every workload "
                          "(bounded slices; no GPU used)")
@@ -684,7 +721,8 @@ def main():
 
     cfg = CONFIGS["kda_decode"]
     log(f"decode: {cfg}")
-    inp, wall, kern_avg_ms, kern_med_ms = run_decode(cfg, args.steps, args.warmup)
+    graphed = not args.eager and args.steps % NBUF == 0
+    inp, wall, kern_avg_ms, kern_med_ms = run_decode(cfg, args.steps, args.warmup, graph=graphed)
     ms_per_step = 1e3 * wall / args.steps
     tokens_per_step = cfg.B * cfg.T
     nbytes = decode_bytes(cfg)
@@ -706,7 +744,8 @@ def main():
         "config": {"workload": "KDA batched decode step", "activations": "bf16",
                    "B": cfg.B, "T": cfg.T, "H": cfg.H,
                    "D": cfg.D, "conv_kernel": cfg.K, "state": "fp32, in place",
-                   "buffers_cycled": NBUF, "arm": "seq_fused"},
+                   "buffers_cycled": NBUF, "arm": "seq_fused",
+                   "launch": f"HIP graph of {NBUF} steps, replayed" if graphed else "one launch per step"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "seq_short_kernel<bf16,kda,1>",
