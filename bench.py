@@ -302,7 +302,8 @@ def run_prefill(cfg, mode, reps=5, d=None):
         b.record()
         return a, b
 
-    once()
+    for _ in range(3):  # warm-up runs
+        once()
     torch.cuda.synchronize()
     evs = [once() for _ in range(reps)]
     torch.cuda.synchronize()
@@ -647,7 +648,7 @@ def run_prefill_legs() -> dict:
                 continue
             if mode == kda.KDA_MODE_SEGMENTED and kda.ARM_NAMES.get(auto) != "segmented":
                 continue  # timed where AUTO takes it
-            ms, arm = run_prefill(cfg, mode, reps=3 if cfg.T * cfg.B > 50000 else 5, d=d)
+            ms, arm = run_prefill(cfg, mode, reps=10, d=d)
             r = {"ms": ms, "tokens_per_s": cfg.B * cfg.T / (ms * 1e-3),
                  "hbm_gbs": prefill_bytes(cfg) / (ms * 1e-3) / 1e9}
             if arm in ("chunked", "segmented"):
