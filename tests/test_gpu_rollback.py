@@ -42,6 +42,9 @@ def _chain(cfg, dev, T):
 CASES = [
     ("kda_bf16_d128", dict(B=2, H=3, T=8)),
     ("kda_fp32_d16", dict(B=2, H=3, T=8, D=16, dtype="fp32")),
+    # 1024 (b, h) pairs and 20 stored rows: replays of 19 and 20 rows run the block
+    # kernel (readout off, stored-row pitch 20)
+    ("kda_bf16_d128_1024_pairs", dict(B=16, H=64, T=20)),
 ]
 
 
