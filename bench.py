@@ -66,20 +66,20 @@ def chunk_flops(cfg, C=64) -> float:
     return 2.0 * (5 * C * cfg.D + 3 * cfg.D * cfg.D) * cfg.B * cfg.T * cfg.H
 
 
-def traffic_from_profile(name: str):
-    """HBM bytes per launch from a committed rocprofv3 counter summary
-    (profiles/<name>_traffic.json), if it was taken on the current kernel sources;
-    else None."""
+def profile_record(name: str) -> dict:
+    """The committed rocprofv3 summary of a kernel (profiles/<name>_traffic.json: HBM
+    bytes per launch from the counters, average duration from the kernel trace), if it
+    was taken on the current kernel sources; else an empty dict."""
     path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
     if not os.path.exists(path):
-        return None
+        return {}
     rec = json.load(open(path))
     h = hashlib.sha256()
     for f in rec.get("source_files", []):
         h.update(open(os.path.join(ROOT, "gated_delta_rule_68_amd", "csrc", f), "rb").read())
     if rec.get("source_sha256") != h.hexdigest():
-        return None
-    return rec.get("bytes_per_launch")
+        return {}
+    return rec
 
 
 COPY_BYTES = 1 << 30
@@ -144,7 +144,7 @@ def cpu_baseline(cfg, inp, budget_s: float = 12.0):
         if el >= budget_s or steps >= 400:
             break
     return {"value": cfg.B * cfg.T * steps / el, "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": _cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"{steps} full decode steps (B={cfg.B}, H={cfg.H}, D={cfg.D}) of the "
                       f"same seeded inputs in {el:.1f} s, fp64, threads split the batch"}
 
@@ -728,7 +728,7 @@ def main():
     tokens_per_step = cfg.B * cfg.T
     nbytes = decode_bytes(cfg)
     achieved = nbytes / (kern_avg_ms * 1e-3) / 1e9
-    traffic = traffic_from_profile("seq_short_kernel_kda_decode")
+    prof = profile_record("seq_short_kernel_kda_decode")
     line = {
         "metric": METRIC,
         "value": tokens_per_step / (ms_per_step * 1e-3),
@@ -745,12 +745,19 @@ def main():
         "config": {"workload": "KDA batched decode step", "activations": "bf16",
                    "B": cfg.B, "T": cfg.T, "H": cfg.H,
                    "D": cfg.D, "conv_kernel": cfg.K, "state": "fp32, in place",
-                   "buffers_cycled": NBUF, "arm": "seq_fused",
+                   "buffers_cycled": NBUF,
+                   "arm": "seq_fused (kernel seq_short_kernel, one token per call)",
                    "launch": f"HIP graph of {NBUF} steps, replayed" if graphed else "one launch per step"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": prof.get("bytes_per_launch"),
                      "kernel": "seq_short_kernel<bf16,kda,1>",
-                     "kernel_avg_us": kern_avg_ms * 1e3, "kernel_median_us": kern_med_ms * 1e3,
+                     # HIP events on the launch stream around each graph replay of NBUF
+                     # launches, divided by NBUF: the kernel plus the gaps between launches
+                     # (an upper bound of the kernel's own duration)
+                     "launch_avg_us": kern_avg_ms * 1e3, "launch_median_us": kern_med_ms * 1e3,
+                     "launch_time": (f"HIP events around each replay of {NBUF} launches, / {NBUF}" if graphed
+                                     else "HIP events around each launch"),
+                     "rocprof_kernel_avg_us": prof.get("avg_us_trace"),
                      "algorithmic_bytes": nbytes, "measured_copy_gbs": measure_copy()},
     }
     if not args.no_prefill:

@@ -58,48 +58,54 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
                                "(the mixer has no non-HIP fallback)")
-        l = ctypes.CDLL(LIB_PATH)
-        for n in ("kda_prefill", "gdn_prefill"):
-            getattr(l, n).argtypes = _PREFILL_ARGS
-            getattr(l, n).restype = _i
-        for n in ("kda_decode", "gdn_decode"):
-            getattr(l, n).argtypes = _DECODE_ARGS
-            getattr(l, n).restype = _i
-        for n in ("kda_prefill_workspace_bytes", "gdn_prefill_workspace_bytes"):
-            getattr(l, n).argtypes = [_i] * 6
-            getattr(l, n).restype = _sz
-        for n in ("kda_prefill_arm", "gdn_prefill_arm"):
-            getattr(l, n).argtypes = [_i] * 6
-            getattr(l, n).restype = _i
-        for n in ("kda_prefill_gated", "gdn_prefill_gated"):
-            getattr(l, n).argtypes = _GATED_PREFILL_ARGS
-            getattr(l, n).restype = _i
-        for n in ("kda_decode_gated", "gdn_decode_gated"):
-            getattr(l, n).argtypes = _GATED_DECODE_ARGS
-            getattr(l, n).restype = _i
-        for n in ("kda_rollback", "gdn_rollback"):
-            getattr(l, n).argtypes = _ROLLBACK_ARGS
-            getattr(l, n).restype = _i
-        for n in ("kda_rollback_gated", "gdn_rollback_gated"):
-            getattr(l, n).argtypes = _GATED_ROLLBACK_ARGS
-            getattr(l, n).restype = _i
-        l.gdn_prefill_gqa.argtypes, l.gdn_prefill_gqa.restype = _GQA_PREFILL_ARGS, _i
-        l.gdn_decode_gqa.argtypes, l.gdn_decode_gqa.restype = _GQA_DECODE_ARGS, _i
-        l.gdn_rollback_gqa.argtypes, l.gdn_rollback_gqa.restype = _GQA_ROLLBACK_ARGS, _i
-        l.gdn_gqa_workspace_bytes.argtypes, l.gdn_gqa_workspace_bytes.restype = [_i] * 7, _sz
-        l.kda_prefill_varlen.argtypes, l.kda_prefill_varlen.restype = _VARLEN_KDA_ARGS, _i
-        l.gdn_prefill_varlen.argtypes, l.gdn_prefill_varlen.restype = _VARLEN_GDN_ARGS, _i
-        l.kda_prefill_varlen_workspace_bytes.argtypes = [_i] * 6
-        l.kda_prefill_varlen_workspace_bytes.restype = _sz
-        l.gdn_prefill_varlen_workspace_bytes.argtypes = [_i] * 7
-        l.gdn_prefill_varlen_workspace_bytes.restype = _sz
-        for n in ("kda_rollback_workspace_bytes", "gdn_rollback_workspace_bytes"):
-            getattr(l, n).argtypes = [_i] * 5
-            getattr(l, n).restype = _sz
-        l.kda_status_string.argtypes = [_i]
-        l.kda_status_string.restype = ctypes.c_char_p
-        _lib = l
+        _lib = bind(LIB_PATH)
     return _lib
+
+
+def bind(path: str) -> ctypes.CDLL:
+    """Load the build of the library at `path` and declare every export's argument and
+    result types."""
+    l = ctypes.CDLL(path)
+    for n in ("kda_prefill", "gdn_prefill"):
+        getattr(l, n).argtypes = _PREFILL_ARGS
+        getattr(l, n).restype = _i
+    for n in ("kda_decode", "gdn_decode"):
+        getattr(l, n).argtypes = _DECODE_ARGS
+        getattr(l, n).restype = _i
+    for n in ("kda_prefill_workspace_bytes", "gdn_prefill_workspace_bytes"):
+        getattr(l, n).argtypes = [_i] * 6
+        getattr(l, n).restype = _sz
+    for n in ("kda_prefill_arm", "gdn_prefill_arm"):
+        getattr(l, n).argtypes = [_i] * 6
+        getattr(l, n).restype = _i
+    for n in ("kda_prefill_gated", "gdn_prefill_gated"):
+        getattr(l, n).argtypes = _GATED_PREFILL_ARGS
+        getattr(l, n).restype = _i
+    for n in ("kda_decode_gated", "gdn_decode_gated"):
+        getattr(l, n).argtypes = _GATED_DECODE_ARGS
+        getattr(l, n).restype = _i
+    for n in ("kda_rollback", "gdn_rollback"):
+        getattr(l, n).argtypes = _ROLLBACK_ARGS
+        getattr(l, n).restype = _i
+    for n in ("kda_rollback_gated", "gdn_rollback_gated"):
+        getattr(l, n).argtypes = _GATED_ROLLBACK_ARGS
+        getattr(l, n).restype = _i
+    l.gdn_prefill_gqa.argtypes, l.gdn_prefill_gqa.restype = _GQA_PREFILL_ARGS, _i
+    l.gdn_decode_gqa.argtypes, l.gdn_decode_gqa.restype = _GQA_DECODE_ARGS, _i
+    l.gdn_rollback_gqa.argtypes, l.gdn_rollback_gqa.restype = _GQA_ROLLBACK_ARGS, _i
+    l.gdn_gqa_workspace_bytes.argtypes, l.gdn_gqa_workspace_bytes.restype = [_i] * 7, _sz
+    l.kda_prefill_varlen.argtypes, l.kda_prefill_varlen.restype = _VARLEN_KDA_ARGS, _i
+    l.gdn_prefill_varlen.argtypes, l.gdn_prefill_varlen.restype = _VARLEN_GDN_ARGS, _i
+    l.kda_prefill_varlen_workspace_bytes.argtypes = [_i] * 6
+    l.kda_prefill_varlen_workspace_bytes.restype = _sz
+    l.gdn_prefill_varlen_workspace_bytes.argtypes = [_i] * 7
+    l.gdn_prefill_varlen_workspace_bytes.restype = _sz
+    for n in ("kda_rollback_workspace_bytes", "gdn_rollback_workspace_bytes"):
+        getattr(l, n).argtypes = [_i] * 5
+        getattr(l, n).restype = _sz
+    l.kda_status_string.argtypes = [_i]
+    l.kda_status_string.restype = ctypes.c_char_p
+    return l
 
 
 def status_string(rc: int) -> str:

@@ -62,15 +62,33 @@ bool segments_pay(int B, int T, int H) {
     return p.n >= 3 && (long)p.cost * 100 <= 85 * (((long)T + 63) / 64);
 }
 
-int pick_arm(int B, int T, int H, int D, bool bf16, int mode) {
-    const bool chunk_ok = kda::kChunkedArmBuilt && D == 128;
+//
+// The chunked and segmented arms take bf16 activations only: their contractions run
+// on bf16 operands, which cannot meet the fp32 accuracy bar (rel L-inf <= 1e-3), so
+// fp32 activations always take a sequential arm and the explicit modes reject them.
+// Their decay factorisation needs g >= -5 (kda_chunk.hip). Given gates carry that
+// as a precondition; activated gates are bounded by gate_lb, and a bound below -5
+// (gates_ok false) sends AUTO to the fused sequential arm, which needs no workspace
+// (so a workspace sized by the query for given gates still suffices), while the
+// explicit chunked and segmented modes reject the call.
+int pick_arm(int B, int T, int H, int D, bool bf16, int mode, bool gates_ok = true) {
+    const bool chunk_ok = kda::kChunkedArmBuilt && D == 128 && bf16 && gates_ok;
     if (mode == KDA_MODE_CHUNKED) return chunk_ok ? kda::ARM_CHUNKED : -1;
     if (mode == KDA_MODE_SEGMENTED) return chunk_ok ? kda::ARM_SEGMENTED : -1;
-    if (mode == KDA_MODE_AUTO && chunk_ok && bf16 && (T > 32 || (T > 16 && (long)B * H < 1024)))
-        return segments_pay(B, T, H) ? kda::ARM_SEGMENTED : kda::ARM_CHUNKED;
     if (mode != KDA_MODE_AUTO && mode != KDA_MODE_SEQUENTIAL) return -1;
+    const bool chunk_len = T > 32 || (T > 16 && (long)B * H < 1024);
+    if (mode == KDA_MODE_AUTO && chunk_len && D == 128 && bf16) {
+        if (!gates_ok) return kda::ARM_SEQ_FUSED;
+        return segments_pay(B, T, H) ? kda::ARM_SEGMENTED : kda::ARM_CHUNKED;
+    }
     if (T <= 16 || (long)B * H >= 1024) return kda::ARM_SEQ_FUSED;
     return kda::ARM_SEQ_SPLIT;
+}
+
+// Whether activated gates stay inside the chunked arm's range (g >= -5): gate_lb is
+// their lower bound in both activation forms (NaN fails the test).
+bool gates_in_chunk_range(int gate_form, float gate_lb) {
+    return gate_form == kda::GATE_GIVEN || gate_lb >= -5.0f;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -83,11 +101,11 @@ int check_heads(int H, int Hk) { return Hk >= 1 && Hk <= H && H % Hk == 0 ? KDA_
 // Arm of a packed variable-length batch: the fused sequential arm (one workgroup per
 // (sequence, head), whatever the lengths) or the chunked arm; AUTO takes the chunked
 // arm for bf16 activations at D = 128.
-int pick_arm_varlen(int D, bool bf16, int mode) {
-    const bool chunk_ok = kda::kChunkedArmBuilt && D == 128;
+int pick_arm_varlen(int D, bool bf16, int mode, bool gates_ok = true) {
+    const bool chunk_ok = kda::kChunkedArmBuilt && D == 128 && bf16 && gates_ok;
     if (mode == KDA_MODE_CHUNKED) return chunk_ok ? kda::ARM_CHUNKED : -1;
     if (mode == KDA_MODE_SEGMENTED) return -1;  // segments of equal-length sequences only
-    if (mode == KDA_MODE_AUTO && chunk_ok && bf16) return kda::ARM_CHUNKED;
+    if (mode == KDA_MODE_AUTO && chunk_ok) return kda::ARM_CHUNKED;
     if (mode != KDA_MODE_AUTO && mode != KDA_MODE_SEQUENTIAL) return -1;
     return kda::ARM_SEQ_FUSED;
 }
@@ -114,8 +132,10 @@ int validate(const MixerArgs& a, bool decode, int mode, int* arm_out) {
     if (!rc && packed) rc = check_shape(a.B, 1, a.H, a.D, a.K);
     if (rc) return rc;
     if (decode && a.T != 1) return KDA_ERR_DECODE_T;
+    const bool gates_ok = gates_in_chunk_range(a.gate_form, a.gate_lb);
     const int arm = decode ? (int)kda::ARM_SEQ_FUSED
-                           : (packed ? pick_arm_varlen(a.D, a.bf16, mode) : pick_arm(a.B, a.T, a.H, a.D, a.bf16, mode));
+                           : (packed ? pick_arm_varlen(a.D, a.bf16, mode, gates_ok)
+                                     : pick_arm(a.B, a.T, a.H, a.D, a.bf16, mode, gates_ok));
     if (arm < 0) return KDA_ERR_DTYPE_MODE;
 
     if (a.gate_form != kda::GATE_GIVEN && (!a.gate_a || !a.gate_bias)) return KDA_ERR_NULL;

@@ -82,10 +82,19 @@ extern "C" {
 /* AUTO: for bf16 activations at D = 128, the sequential arm up to 32 tokens (up to 16
  * with fewer than 1024 (b, h) pairs), the chunked arm beyond, the segmented arm when its
  * plan shortens the critical path (few pairs, long sequences); fp32 activations and
- * D = 16 always take the sequential arm. *_prefill_arm reports the choice. */
+ * D = 16 always take the sequential arm. *_prefill_arm reports the choice for given
+ * gates. Gated calls (KDA_GATE_*) whose gate_lb is below -5 (or NaN) run on the fused
+ * sequential arm wherever AUTO would take the chunked or segmented arm: that arm needs
+ * no workspace, so a workspace sized by *_prefill_workspace_bytes still suffices.
+ *
+ * The chunked and segmented modes take bf16 activations only (their contractions use
+ * bf16 operands, which cannot meet the fp32 accuracy bar): with KDA_DTYPE_F32 they
+ * return KDA_ERR_DTYPE_MODE. Their decay factorisation needs every log gate >= -5:
+ * for given gates that is a precondition (gates below it need KDA_MODE_SEQUENTIAL:
+ * the library cannot see device values), and gated calls with gate_lb < -5 are refused with KDA_ERR_DTYPE_MODE. */
 #define KDA_MODE_AUTO 0       /* library picks sequential, chunked or segmented from the shape */
 #define KDA_MODE_SEQUENTIAL 1 /* token-by-token scan (bit-identical to chained decodes) */
-#define KDA_MODE_CHUNKED 2    /* chunk-64 WY form, bf16 MFMA operands, fp32 state (D = 128) */
+#define KDA_MODE_CHUNKED 2    /* chunk-64 WY form, bf16 MFMA operands, fp32 state (D = 128, bf16) */
 /* The chunked form with every sequence cut into segments that run in parallel (D = 128,
  * equal-length sequences; not for packed batches). A run of tokens maps its entry state
  * affinely, S_out = M S_in + B: the decay and the delta-rule update of stage 5 above act
@@ -124,7 +133,8 @@ extern "C" {
  *   rms_eps is the RMSNorm epsilon.
  *   mode: KDA_MODE_*. The sequential mode gives results bit-identical to T
  *   successive kda_decode calls. The chunked and segmented modes agree with it to
- *   bf16-operand accuracy and require D == 128.
+ *   bf16-operand accuracy (rel L-inf <= 2e-2) and require D == 128 and bf16
+ *   activations (else KDA_ERR_DTYPE_MODE).
  *   workspace: device buffer of at least kda_prefill_workspace_bytes(...) bytes
  *   (may be NULL when that is 0). Its contents on entry are ignored.
  * Returns KDA_OK or a status code above.
@@ -182,8 +192,9 @@ int gdn_prefill_arm(int B, int T, int H, int D, int dtype, int mode);
  * the kernels as they are read (see KDA_GATE_*). gate_a is [H] fp32, gate_bias is
  * [H*D] (KDA) or [H] (GDN) fp32, both 16-byte aligned. gate_form must be
  * KDA_GATE_SIGMOID or KDA_GATE_SOFTPLUS (else KDA_ERR_DTYPE_MODE). Everything else is
- * as for the plain entry points; the chunked arm's precondition g >= -5 applies to the
- * activated gate.
+ * as for the plain entry points. The chunked arm needs activated gates >= -5, which
+ * gate_lb >= -5 guarantees in both forms: with gate_lb < -5 (or NaN) AUTO runs the
+ * sequential arm and the explicit chunked / segmented modes return KDA_ERR_DTYPE_MODE.
  */
 int kda_prefill_gated(const void* q, const void* k, const void* v, const void* gate_x,
                       const void* beta_x, const float* gate_a, const float* gate_bias,

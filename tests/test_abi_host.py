@@ -89,6 +89,10 @@ CASES = [
     ("dtype 2", dict(dtype=2), 40008),
     ("mode 7", dict(mode=7), 40008),
     ("chunked D=16", dict(mode=2, D=16), 40008),
+    # the chunked and segmented arms take bf16 activations only (fp32 cannot meet its
+    # 1e-3 bar through bf16 MFMA operands): fp32 through the explicit modes is refused
+    ("chunked fp32", dict(mode=2, D=128, dtype=0), 40008),
+    ("segmented fp32", dict(mode=3, D=128, dtype=0), 40008),
     ("out overlaps q", dict(out=BASE + 64), 40009),
     ("state partial overlap", dict(state_out=BASE + 7 * (1 << 32) + 256), 40009),
     ("ring overlaps conv_w", dict(ring=BASE + 5 * (1 << 32) + 16), 40009),
@@ -152,6 +156,10 @@ def test_auto_arm_boundaries():
     assert kda.prefill_arm(64, 64, 64, 128, 0, 0) == 1  # fp32
     assert kda.prefill_arm(8, 64, 32, 128, 0, 0) == 2
     assert kda.prefill_arm(8, 64, 32, 16, 1, 0) == 2  # D = 16
+    # the explicit chunked and segmented modes refuse fp32 activations
+    assert kda.prefill_arm(8, 64, 32, 128, 0, 2) == -1
+    assert kda.prefill_arm(8, 64, 32, 128, 0, 3) == -1
+    assert kda.workspace_bytes(8, 64, 32, 128, 0, 2) == ctypes.c_size_t(-1).value
 
 
 def test_segmented_queries():
@@ -278,6 +286,26 @@ def test_gated_contract(what, over, kw, rc, gdn, decode):
     a = fake_args(T=1 if decode else 3)
     a.update({k: (0 if v is None else v) for k, v in over.items()})
     assert call_gated(a, gdn, decode, **kw) == rc
+
+
+# The chunked arm's decay factorisation needs g >= -5; activated gates are bounded
+# below by gate_lb, so the explicit chunked / segmented modes refuse a lower bound
+# below -5 (AUTO runs such calls on the fused sequential arm instead).
+GATED_CHUNK_CASES = [
+    ("chunked lb -5.5", dict(mode=2, D=128, dtype=1), dict(lb=-5.5), 40008),
+    ("segmented lb -inf", dict(mode=3, D=128, dtype=1), dict(lb=float("-inf")), 40008),
+    ("chunked lb nan", dict(mode=2, D=128, dtype=1), dict(lb=float("nan"), form=2), 40008),
+    ("chunked fp32 gated", dict(mode=2, D=128, dtype=0), dict(lb=-5.0), 40008),
+]
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="fake pointers only where no GPU is visible")
+@pytest.mark.parametrize("gdn", [False, True])
+@pytest.mark.parametrize("what,over,kw,rc", GATED_CHUNK_CASES, ids=[c[0] for c in GATED_CHUNK_CASES])
+def test_gated_chunk_modes_need_bounded_gates(what, over, kw, rc, gdn):
+    a = fake_args(T=100)
+    a.update(over)
+    assert call_gated(a, gdn, False, **kw) == rc
 
 
 def call_rollback_gated(a, gdn=False, T_stash=3, keep=2, form=2, lb=-5.0):

@@ -63,14 +63,28 @@ def test_alternating_gates_vs_oracle(gdn):
     _print("errs", errs)
 
 
-def test_fp32_inputs_chunked():
-    """fp32 activations through the chunked arm: bf16-operand accuracy."""
-    cfg = CONFIGS["kda_decode"].with_(B=2, H=4, T=150, dtype="fp32")
+@pytest.mark.parametrize("gdn", [False, True])
+def test_fp32_inputs_take_a_sequential_arm_at_the_fp32_bar(gdn):
+    """fp32 activations at D = 128: the chunked and segmented modes refuse them (their
+    bf16 MFMA operands cannot meet 1e-3) with nothing written, and AUTO runs them on a
+    sequential arm, which meets the fp32 bar against the oracle."""
+    cfg = CONFIGS["kda_decode"].with_(B=2, H=4, T=150, dtype="fp32", gdn=gdn)
     inp, dev = inputs_for(cfg)
-    got = run_gpu(cfg, dev, mode=CHK)
+    for mode in (CHK, kda.KDA_MODE_SEGMENTED):
+        assert kda.prefill_arm(cfg.B, cfg.T, cfg.H, cfg.D, kda.KDA_DTYPE_F32, mode, gdn=gdn) == -1
+        sentinel = torch.full_like(dev["state"], 7.0)
+        with pytest.raises(kda.KdaError) as e:
+            run_gpu(cfg, dev, mode=mode, state=sentinel, inplace=True)
+        assert e.value.rc == 40008
+        torch.cuda.synchronize()
+        assert bool((sentinel == 7.0).all()), "a refused call wrote the state"
+    arm = kda.prefill_arm(cfg.B, cfg.T, cfg.H, cfg.D, kda.KDA_DTYPE_F32, kda.KDA_MODE_AUTO, gdn=gdn)
+    assert kda.ARM_NAMES[arm].startswith("seq"), arm
+    got = run_gpu(cfg, dev, mode=kda.KDA_MODE_AUTO)
     torch.cuda.synchronize()
     ref, ch, rows, bsel, hh = oracle_run(inp, threads=16)
-    compare_to_oracle(cfg, got, ref, ch, rows, bsel, hh, tol=TOL)
+    errs = compare_to_oracle(cfg, got, ref, ch, rows, bsel, hh, tol=1e-3)
+    _print("fp32 AUTO", kda.ARM_NAMES[arm], errs)
 
 
 def test_prefill_full_size():

@@ -9,8 +9,8 @@ import pytest
 import torch
 
 import gated_delta_rule_68_amd as kda
-from tests.test_abi_host import (CASES, GATED_CASES, GATED_ROLLBACK_CASES, ROLLBACK_CASES, call_decode,
-                                 call_gated, call_prefill, call_rollback, call_rollback_gated)
+from tests.test_abi_host import (CASES, GATED_CASES, GATED_CHUNK_CASES, GATED_ROLLBACK_CASES, ROLLBACK_CASES,
+                                 call_decode, call_gated, call_prefill, call_rollback, call_rollback_gated)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -152,4 +152,13 @@ def test_gated_rollback_rejected_before_copy_or_launch(arena, what, over, kw, rc
     a = real_args(arena)
     a.update(rebase(arena, over))
     assert call_rollback_gated(a, gdn, **kw) == rc
+    assert outputs_untouched(arena) is None
+
+
+@pytest.mark.parametrize("gdn", [False, True])
+@pytest.mark.parametrize("what,over,kw,rc", GATED_CHUNK_CASES, ids=[c[0] for c in GATED_CHUNK_CASES])
+def test_gated_chunk_modes_refuse_unbounded_gates(arena, what, over, kw, rc, gdn):
+    a = real_args(arena, T=100)
+    a.update(over)
+    assert call_gated(a, gdn, False, **kw) == rc
     assert outputs_untouched(arena) is None

@@ -37,7 +37,7 @@ def gate_params(inp, dev, form):
     return ga, dev["dt_bias"], g, gates.beta_sigmoid(inp.beta_x)
 
 
-def run_gated(cfg, dev, ga, gb, form, mode=SEQ, decode=False, t0=0, T=None, ring=None, state=None):
+def run_gated(cfg, dev, ga, gb, form, mode=SEQ, decode=False, t0=0, T=None, ring=None, state=None, lb=LB):
     T = cfg.T if T is None else T
     sl = slice(t0, t0 + T)
     acts = {n: dev[n][:, sl].clone(memory_format=torch.contiguous_format)
@@ -48,7 +48,7 @@ def run_gated(cfg, dev, ga, gb, form, mode=SEQ, decode=False, t0=0, T=None, ring
     outs = alloc_outputs(cfg, T, DEV, o_core=True)
     args = (acts["q"], acts["k"], acts["v"], acts["gate_x"], acts["beta_x"], ga, gb, dev["conv_w"], ring,
             s_in, s_out, acts["z"], dev["norm_w"], outs["out"], outs["o_core"])
-    kw = dict(gate_form=form, gate_lb=LB, scale=scale_of(cfg), rms_eps=RMS_EPS)
+    kw = dict(gate_form=form, gate_lb=lb, scale=scale_of(cfg), rms_eps=RMS_EPS)
     if decode:
         (kda.gdn_decode_gated if cfg.gdn else kda.kda_decode_gated)(*args, **kw)
     else:
@@ -90,6 +90,31 @@ def test_gated_prefill_vs_oracle(form, gdn, mode, T):
     inp, dev = inputs_for(cfg)
     ga, gb, g, beta = gate_params(inp, dev, form)
     got = run_gated(cfg, dev, ga, gb, form, mode=mode)
+    torch.cuda.synchronize()
+    ref, ch, rows, bsel = oracle_gated(inp, g, beta, heads=[0, 1, 2])
+    compare(cfg, got, ref, ch, rows, bsel, [0, 1, 2], TOL["bf16"])
+
+
+@pytest.mark.parametrize("gdn", [False, True])
+def test_gated_unbounded_gates_auto_vs_oracle(gdn):
+    """Softplus gates with no lower bound (gate_lb = -inf) and pre-activations shifted
+    up by 3, so that most log gates lie between about -50 and -3, far below the chunked
+    arm's -5. AUTO at bf16, D = 128, T = 200 (which would take the chunked arm for given
+    gates) runs them on the fused sequential arm and matches the oracle."""
+    cfg = CONFIGS["kda_decode"].with_(B=2, H=3, T=200, gdn=gdn)
+    inp, dev = inputs_for(cfg)
+    assert kda.ARM_NAMES[kda.prefill_arm(cfg.B, cfg.T, cfg.H, cfg.D, kda.KDA_DTYPE_BF16,
+                                         kda.KDA_MODE_AUTO, gdn=gdn)] in ("chunked", "segmented")
+    shifted = (inp.gate_x.astype(np.float32) + 3.0)
+    dev = dict(dev)
+    dev["gate_x"] = torch.from_numpy(shifted).to(DEV, dev["gate_x"].dtype)
+    gx = to_f64(dev["gate_x"].cpu())  # the values the kernels read (bf16-rounded)
+    a = -np.exp(inp.A_log.astype(np.float64))
+    ga = torch.from_numpy(a.astype(np.float32)).to(DEV)
+    g = gates.gate_softplus(gx, a.astype(np.float32), inp.dt_bias, -np.inf, cfg.D, cfg.gdn)
+    assert float(np.mean(g < -5.0)) > 0.5, "most gates should lie below -5"
+    beta = gates.beta_sigmoid(inp.beta_x)
+    got = run_gated(cfg, dev, ga, dev["dt_bias"], kda.KDA_GATE_SOFTPLUS, mode=kda.KDA_MODE_AUTO, lb=-np.inf)
     torch.cuda.synchronize()
     ref, ch, rows, bsel = oracle_gated(inp, g, beta, heads=[0, 1, 2])
     compare(cfg, got, ref, ch, rows, bsel, [0, 1, 2], TOL["bf16"])

@@ -56,10 +56,10 @@ def test_many_pairs_vs_oracle(gdn):
     _check(cfg, heads=[0, 17, 39])
 
 
-def test_wide_conv_fp32_and_alternating_gates_vs_oracle():
-    """K = 6 (history of five rows read from the rows before each segment), fp32
-    activations, and gates pushed to both ends of [-5, 0] on alternate heads."""
-    cfg = CONFIGS["kda_long"].with_(B=1, T=330, H=4, K=6, dtype="fp32", random_init=True)
+def test_wide_conv_and_alternating_gates_vs_oracle():
+    """K = 6 (history of five rows read from the rows before each segment) and gates
+    pushed to both ends of [-5, 0] on alternate heads."""
+    cfg = CONFIGS["kda_long"].with_(B=1, T=330, H=4, K=6, random_init=True)
     _check(cfg)
 
 

@@ -1,0 +1,59 @@
+"""The host half of the C ABI under AddressSanitizer and UndefinedBehaviorSanitizer.
+
+Every source of the library is compiled with -fsanitize=address,undefined on its host
+side (kda_api.cpp's validation, range and overlap arithmetic, the arm choice, the
+workspace and segment-plan queries, the launchers' host code; the device code is built
+as usual, unsanitized), and tests/test_abi_host.py runs against that build in a child
+process with the sanitizer runtime preloaded. Its cases call every entry point
+with fake, never dereferenced device addresses and are all refused before any launch,
+so no GPU is needed. Any sanitizer report fails the test."""
+import glob
+import os
+from concurrent.futures import ThreadPoolExecutor
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "gated_delta_rule_68_amd", "csrc")
+HIPCC = "/opt/rocm/bin/hipcc"
+SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-shared-libasan",
+       "-fno-omit-frame-pointer", "-fno-sanitize-recover=all"]
+
+
+def _asan_runtime():
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return hits[-1] if hits else None
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC) or _asan_runtime() is None, reason="needs hipcc and its ASan runtime")
+def test_host_contract_cases_under_asan_ubsan(tmp_path):
+    common = [HIPCC, "-std=c++17", "-O1", "-g", "-fPIC", "-I", os.path.join(ROOT, "include"), "-I", CSRC, *SAN]
+    def compile_one(src):
+        obj = str(tmp_path / (os.path.splitext(src)[0] + ".o"))
+        dev = (["-x", "hip", "--offload-arch=gfx950", "-ffp-contract=off", "-Xclang", "-target-feature",
+                "-Xclang", "-packed-fp32-ops"] if src.endswith(".hip") else [])
+        subprocess.run(common + dev + ["-c", os.path.join(CSRC, src), "-o", obj], check=True,
+                       capture_output=True, text=True)
+        return obj
+
+    with ThreadPoolExecutor(3) as ex:
+        objs = list(ex.map(compile_one, ("kda_api.cpp", "kda_seq.hip", "kda_chunk.hip")))
+    lib = str(tmp_path / "libkda_san.so")
+    subprocess.run([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *SAN, *objs, "-o", lib], check=True,
+                   capture_output=True, text=True)
+
+    env = dict(os.environ)
+    env.update(LD_PRELOAD=_asan_runtime(), KDA_TEST_SANITIZED_LIB=lib,
+               ASAN_OPTIONS="detect_leaks=0:halt_on_error=1:abort_on_error=1",
+               UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1", HIP_VISIBLE_DEVICES="")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-p", "no:cacheprovider", "-m", "not gpu",
+                        os.path.join(ROOT, "tests", "test_abi_host.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    out = r.stdout + r.stderr
+    print(out[-3000:])
+    assert r.returncode == 0, out[-3000:]
+    assert "AddressSanitizer" not in out and "runtime error:" not in out, out[-3000:]
+    assert " passed" in out
