@@ -6,5 +6,5 @@ from ._lib import (  # noqa: F401
     kda_prefill_gated, gdn_rollback_gated, kda_rollback_gated, KDA_GATE_GIVEN, gdn_prefill_gqa,
     gdn_decode_gqa, gdn_rollback_gqa, gqa_workspace_bytes, prefill_varlen, varlen_workspace_bytes,
     KDA_MODE_SEQUENTIAL, KdaError, gdn_decode, gdn_prefill, gdn_rollback, kda_decode, kda_prefill,
-    kda_rollback, lib, prefill_arm, rollback_workspace_bytes, status_string, workspace_bytes,
+    kda_rollback, lib, prefill_arm, kda_prefill_noalloc, KDA_NOALLOC_SCRATCH_BYTES, rollback_workspace_bytes, status_string, workspace_bytes,
 )

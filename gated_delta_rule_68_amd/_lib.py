@@ -42,7 +42,9 @@ EXPORTS = ("kda_prefill", "kda_decode", "gdn_prefill", "gdn_decode",
            "gdn_prefill_gated", "kda_decode_gated", "gdn_decode_gated", "kda_rollback_gated",
            "gdn_rollback_gated", "gdn_prefill_gqa", "gdn_decode_gqa", "gdn_rollback_gqa",
            "gdn_gqa_workspace_bytes", "kda_prefill_varlen", "gdn_prefill_varlen",
-           "kda_prefill_varlen_workspace_bytes", "gdn_prefill_varlen_workspace_bytes", "kda_status_string")
+           "kda_prefill_varlen_workspace_bytes", "gdn_prefill_varlen_workspace_bytes", "kda_status_string",
+           "kda_prefill_noalloc")
+KDA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class KdaError(RuntimeError):
@@ -72,6 +74,8 @@ def bind(path: str) -> ctypes.CDLL:
     for n in ("kda_decode", "gdn_decode"):
         getattr(l, n).argtypes = _DECODE_ARGS
         getattr(l, n).restype = _i
+    l.kda_prefill_noalloc.argtypes = _PREFILL_ARGS[:-3] + [_vp]  # no workspace, its size
+    l.kda_prefill_noalloc.restype = _i
     for n in ("kda_prefill_workspace_bytes", "gdn_prefill_workspace_bytes"):
         getattr(l, n).argtypes = [_i] * 6
         getattr(l, n).restype = _sz
@@ -159,6 +163,19 @@ def _prefill(name, q, k, v, g, beta, conv_w, conv_ring, state_in, state_out, z, 
         _ptr(workspace), ws_bytes, _stream_handle(stream))
     if check and rc != 0:
         raise KdaError(rc, name)
+    return rc
+
+
+def kda_prefill_noalloc(q, k, v, g, beta, conv_w, conv_ring, state_in, state_out, z, norm_w, out,
+                        o_core=None, *, scale, rms_eps, mode=KDA_MODE_AUTO, stream=None, check=True):
+    """kda_prefill with its workspace taken from the library's static scratch buffer."""
+    B, T, H, D, K = _geometry(q, state_in, conv_w)
+    rc = lib().kda_prefill_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(conv_w), _ptr(conv_ring),
+        _ptr(state_in), _ptr(state_out), _ptr(z), _ptr(norm_w), _ptr(out), _ptr(o_core),
+        B, T, H, D, K, float(scale), float(rms_eps), _dtype_code(q), int(mode), _stream_handle(stream))
+    if check and rc != 0:
+        raise KdaError(rc, "kda_prefill_noalloc")
     return rc
 
 

@@ -122,7 +122,9 @@ size_t workspace_for(int B, int T, int H, int Hk, int D, bool gdn, int arm, size
     }
 }
 
-int validate(const MixerArgs& a, bool decode, int mode, int* arm_out) {
+// need_out (optional) receives the workspace bytes the call needs, once the shape,
+// arm and pointer alignment have passed.
+int validate(const MixerArgs& a, bool decode, int mode, int* arm_out, size_t* need_out = nullptr) {
     if (!a.q || !a.k || !a.v || !a.g || !a.beta || !a.conv_w || !a.ring || !a.state_in ||
         !a.state_out || !a.z || !a.norm_w || !a.out)
         return KDA_ERR_NULL;
@@ -155,6 +157,7 @@ int validate(const MixerArgs& a, bool decode, int mode, int* arm_out) {
     const size_t state_n = (size_t)a.B * a.H * a.D * a.D;
     const size_t need_ws = workspace_for(a.B, a.T, a.H, a.Hk, a.D, a.gdn, arm, rows, mode) +
                            (packed ? order_bytes(a.B) : 0);
+    if (need_out) *need_out = need_ws;
     if (need_ws > 0 && (!a.ws || a.ws_bytes < need_ws)) return KDA_ERR_WORKSPACE;
 
     auto R = [](const void* p, size_t bytes, bool w, int id) {
@@ -222,7 +225,7 @@ int entry(bool gdn, bool decode, const void* q, const void* k, const void* v, co
           float* state_out, const void* z, const float* norm_w, void* out, float* o_core,
           int B, int T, int H, int D, int K, float scale, float rms_eps, int dtype, int mode,
           void* workspace, size_t workspace_bytes, void* stream, GateArgs ga = kGiven, int Hk = 0,
-          const int* cu_seqlens = nullptr) {
+          const int* cu_seqlens = nullptr, bool static_ws = false) {
     if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return KDA_ERR_DTYPE_MODE;
     if (ga.form != kda::GATE_GIVEN && ga.form != KDA_GATE_SIGMOID && ga.form != KDA_GATE_SOFTPLUS)
         return KDA_ERR_DTYPE_MODE;
@@ -239,7 +242,20 @@ int entry(bool gdn, bool decode, const void* q, const void* k, const void* v, co
         a.gate_bias = conv_w;
     }
     int arm = 0;
-    const int rc = validate(a, decode, mode, &arm);
+    size_t need = 0;
+    int rc = validate(a, decode, mode, &arm, &need);
+    if (static_ws && rc == KDA_ERR_WORKSPACE) {
+        // The workspace comes from the library's static scratch: sized first, so a call
+        // the contract refuses looks nothing up; then the contract is checked again with
+        // the scratch in place (its range against every other buffer).
+        if (need > kda::static_scratch_bytes()) return KDA_ERR_SCRATCH;
+        void* p = nullptr;
+        const hipError_t e = kda::static_scratch(a.stream, &p);
+        if (e != hipSuccess) return KDA_ERR_RUNTIME_BASE + (int)e;
+        a.ws = p;
+        a.ws_bytes = kda::static_scratch_bytes();
+        rc = validate(a, decode, mode, &arm);
+    }
     if (rc) return rc;
     if (a.cu_seqlens) {  // rank the sequences first; the arm's own workspace follows
         int* order = static_cast<int*>(a.ws);
@@ -370,6 +386,16 @@ int gdn_prefill(const void* q, const void* k, const void* v, const void* g, cons
     return entry(true, false, q, k, v, g, beta, conv_w, conv_ring, state_in, state_out, z,
                  norm_w, out, o_core, B, T, H, D, K, scale, rms_eps, dtype, mode, workspace,
                  workspace_bytes, stream);
+}
+
+int kda_prefill_noalloc(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                        const float* conv_w, float* conv_ring, const float* state_in, float* state_out,
+                        const void* z, const float* norm_w, void* out, float* o_core, int B, int T,
+                        int H, int D, int K, float scale, float rms_eps, int dtype, int mode,
+                        void* stream) {
+    return entry(false, false, q, k, v, g, beta, conv_w, conv_ring, state_in, state_out, z,
+                 norm_w, out, o_core, B, T, H, D, K, scale, rms_eps, dtype, mode, nullptr, 0,
+                 stream, kGiven, 0, nullptr, true);
 }
 
 int kda_decode(const void* q, const void* k, const void* v, const void* g, const void* beta,
@@ -561,6 +587,9 @@ const char* kda_status_string(int rc) {
         case KDA_ERR_WORKSPACE: return "workspace missing or smaller than the query returned";
         case KDA_ERR_ALIGN: return "every pointer must be 16-byte aligned";
         case KDA_ERR_DTYPE_MODE: return "unknown dtype or mode, or mode not valid for this shape";
+        case KDA_ERR_SCRATCH:
+            return "the call needs more workspace than the static scratch of kda_prefill_noalloc "
+                   "(KDA_NOALLOC_SCRATCH_BYTES); use kda_prefill with a workspace";
         case KDA_ERR_ALIAS:
             return "buffers overlap (only state_in == state_out, or a rollback's snapshot and "
                    "live ring / state, may be the same buffer)";

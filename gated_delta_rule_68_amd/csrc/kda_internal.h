@@ -177,6 +177,11 @@ size_t chunked_workspace_bytes(int nseq, size_t rows, int H, int D);
 // Workspace of the segmented arm for B sequences of H heads cut into n segments.
 size_t segmented_workspace_bytes(int B, int H, int D, int n);
 
+// The static scratch buffer of the allocation-free prefill (kda_scratch.hip): its size,
+// and its device address on the device of `stream` (looked up once per device).
+size_t static_scratch_bytes();
+hipError_t static_scratch(hipStream_t stream, void** ptr);
+
 // Launchers: enqueue on a.stream, return the first launch error (hipSuccess if none).
 hipError_t launch_seq_fused(const MixerArgs& a);
 hipError_t launch_seq_split(const MixerArgs& a);

@@ -75,6 +75,7 @@ extern "C" {
 #define KDA_ERR_ALIGN 40007        /* a pointer is not 16-byte aligned */
 #define KDA_ERR_DTYPE_MODE 40008   /* unknown dtype or mode, or mode not valid here */
 #define KDA_ERR_ALIAS 40009        /* two buffers overlap (other than the allowed in-place pairs) */
+#define KDA_ERR_SCRATCH 40010      /* kda_prefill_noalloc: the call needs more than the static scratch */
 
 /* ---- dtype and prefill mode ---- */
 #define KDA_DTYPE_F32 0
@@ -176,6 +177,30 @@ int gdn_decode(const void* q, const void* k, const void* v, const void* g,
                const float* norm_w, void* out, float* o_core,
                int B, int T, int H, int D, int K, float scale, float rms_eps,
                int dtype, void* stream);
+
+/*
+ * kda_prefill_noalloc - kda_prefill for callers that cannot allocate device memory
+ *   (code under HIP graph capture, tight serving loops, harnesses that forbid
+ *   hipMalloc): the same arguments without the workspace, which comes from a static
+ *   device buffer of KDA_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it
+ *   runs on until the process ends. The call allocates nothing (no hipMalloc, no
+ *   allocating library routine) and otherwise behaves as kda_prefill with a workspace:
+ *   same arms, kernels and results.
+ *   A call whose arm needs more workspace than the buffer (kda_prefill_workspace_bytes
+ *   > KDA_NOALLOC_SCRATCH_BYTES) returns KDA_ERR_SCRATCH before any launch.
+ *   Every call on one GPU shares that GPU's buffer: calls that overlap in time on one
+ *   GPU (different host threads or streams with no ordering between them) race, so
+ *   order them on one stream. The buffer keeps the last call's contents; the arms
+ *   never read workspace contents they did not write in the same call.
+ *   The buffer is on the device of `stream` (the current device for NULL).
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int kda_prefill_noalloc(const void* q, const void* k, const void* v, const void* g,
+                        const void* beta, const float* conv_w, float* conv_ring,
+                        const float* state_in, float* state_out, const void* z,
+                        const float* norm_w, void* out, float* o_core,
+                        int B, int T, int H, int D, int K, float scale, float rms_eps,
+                        int dtype, int mode, void* stream);
 
 /* Workspace bytes a prefill with these arguments needs (0 if none). Returns
  * (size_t)-1 for arguments the prefill would reject. */

@@ -33,7 +33,7 @@ def test_library_exports_every_header_symbol():
 
 def test_status_strings():
     assert kda.status_string(0) == "ok"
-    for rc in range(40001, 40010):
+    for rc in range(40001, 40011):
         s = kda.status_string(rc)
         assert s and s != "unknown status code", rc
     assert "HIP" in kda.status_string(10001)
@@ -107,6 +107,19 @@ def test_prefill_contract(what, over, rc, gdn):
     a = fake_args()
     a.update({k: (0 if v is None else v) for k, v in over.items()})
     assert call_prefill(a, gdn) == rc
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="fake pointers only where no GPU is visible")
+@pytest.mark.parametrize("what,over,rc", CASES, ids=[c[0] for c in CASES])
+def test_prefill_noalloc_contract(what, over, rc):
+    """The allocation-free prefill refuses every contract violation the plain prefill
+    does, with the same code and before it looks up its scratch buffer."""
+    a = fake_args()
+    a.update({k: (0 if v is None else v) for k, v in over.items()})
+    f = kda.lib().kda_prefill_noalloc
+    assert f(a["q"], a["k"], a["v"], a["g"], a["beta"], a["conv_w"], a["ring"], a["state_in"], a["state_out"],
+             a["z"], a["norm_w"], a["out"], a["o_core"], a["B"], a["T"], a["H"], a["D"], a["K"], 0.25, 1e-5,
+             a["dtype"], a["mode"], None) == rc
 
 
 @pytest.mark.skipif(_gpu_visible(), reason="fake pointers only where no GPU is visible")

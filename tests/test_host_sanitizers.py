@@ -39,8 +39,9 @@ def test_host_contract_cases_under_asan_ubsan(tmp_path):
                        capture_output=True, text=True)
         return obj
 
-    with ThreadPoolExecutor(3) as ex:
-        objs = list(ex.map(compile_one, ("kda_api.cpp", "kda_seq.hip", "kda_chunk.hip")))
+    from gated_delta_rule_68_amd.build import SOURCES
+    with ThreadPoolExecutor(len(SOURCES)) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
     lib = str(tmp_path / "libkda_san.so")
     subprocess.run([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *SAN, *objs, "-o", lib], check=True,
                    capture_output=True, text=True)
