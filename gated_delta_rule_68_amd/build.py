@@ -24,7 +24,7 @@ ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-I", INCLUDE, "-I", CSRC]
 DEVICE = ["-x", "hip", f"--offload-arch={ARCH}", "-ffp-contract=off",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-SOURCES = ["kda_api.cpp", "kda_seq.hip", "kda_chunk.hip", "kda_scratch.hip"]
+SOURCES = ["kda_api.cpp", "kda_seq.hip", "kda_chunk.hip", "kda_c32.hip", "kda_scratch.hip"]
 
 
 def _compile(src: str) -> str:

@@ -1,0 +1,814 @@
+// Chunked prefill of the KDA / GDN mixer for gfx950 in chunks of 32 rows: bf16
+// activations, D = 128, conv kernels of up to 4 taps, one (sequence, head) per
+// workgroup of 16 wavefronts in two specialised groups.
+//
+// The recurrence is taken in its WY / UT form (memra-engine kda.rs, module notes on the
+// chunked twin: a cumulative log gate per channel, k scaled by exp(-Gcum) and q by
+// exp(+Gcum), a triangular intra-chunk solve; for GDN one scalar gate per row). Per
+// chunk of 32 rows with carried state S (key i x value j), G the inclusive cumulative
+// log gate from the chunk start and G_l its value at the last row:
+//   L[s][j] = sum_i k_s[i] k_j[i] e^{G_s[i]-G_j[i]}  (j < s),  P the same with q_s, j <= s
+//   T  = (I + diag(beta) L)^-1
+//   Ub = T diag(beta) (V - K+ S)            K+_j = k_j e^{G_j}
+//   O  = scale (Q+ S + P Ub)                Q+_s = q_s e^{G_s}
+//   S  = diag(e^{G_l}) S + K_dec^T Ub       K_dec_j = k_j e^{G_l - G_j}
+// K+, Q+ and K_dec have factors <= 1. For L and P (KDA) the rows form two 16-row
+// blocks; with R_a the cumulative gate before block a and gamma = G - R_a (at most 16
+// gates, >= -80 for gates >= -5), k e^{-gamma} <= e^{80} stays inside the bf16 range:
+//   L, P block (a, a):  (k, q) e^{gamma}  .  k e^{-gamma}
+//   L, P block (1, 0):  (k, q) e^{gamma}  .  (k e^{-gamma}) e^{R_1}
+// For GDN the gate is a scalar per row, so L = (k k^T) * E and P = (q k^T) * E with
+// E[s][j] = e^{G_s - G_j} taken on the 32 x 32 products, and the row factors of K+,
+// Q+ and K_dec are applied to the MFMA results instead of the operands.
+//
+// Work layout: wavefronts 0..7 (two per SIMD) prepare chunk c+1 while wavefronts 8..15
+// (two per SIMD) run chunk c's state-dependent work, so every SIMD holds VALU-heavy
+// and MFMA-heavy wavefronts at once, two of each to hide each other's latencies. A
+// step has three phases between workgroup barriers:
+//   phase  preparing group (chunk c+1)             state group (chunk c)
+//   1      conv + SiLU of q, k, l2 norms, gates    v conv, diagonal blocks of T, Q+ S, K+ S
+//   2      decay factors, operand tiles            T_10, Ub, O, state update
+//   3      L and P (MFMA)                          gated RMSNorm and stores
+// The preparing wavefront w convolves rows 4w .. 4w+3, two channels per lane, straight
+// from registers: each lane reads its channels of its rows and of the 3 rows before
+// them (the conv history; the old ring before the sequence start), so no raw rows are
+// staged in LDS; the l2 norms are sums over the 64 lanes of a wavefront. The state
+// lives in the state group's MFMA accumulators, owned by value column (state wavefront
+// w holds value columns 16w .. 16w+15 for all 128 keys). Packed to bf16, those
+// accumulators are directly the operand of Q+ S and K+ S (keys in the accumulator
+// order), and Ub's accumulators directly the operands of P Ub and K_dec^T Ub, so the
+// state-dependent work needs no LDS exchange of its own. Tiles whose contraction index
+// meets an accumulator are stored with that index permuted within each 32-wide slice
+// (perm32), so every MFMA fragment is one 16-byte LDS read. Tiles that one group
+// writes while the other reads the previous chunk's are double-buffered.
+#include "kda_chunk_common.h"
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int C = 32;            // rows per chunk
+constexpr int DK = CHUNK_DK;     // 128
+constexpr int NT = 1024;         // 16 wavefronts: 0..7 prepare, 8..15 carry the state
+constexpr int GT = 512;          // threads of one group
+constexpr int NW = 8;            // wavefronts of one group
+constexpr int RW = C / NW;       // rows per preparing (and v conv) wavefront: 4
+constexpr int KT = 4;            // conv window of this kernel (K <= 4)
+constexpr int HALO = KT - 1;     // conv history rows
+constexpr int NR = RW + HALO;    // rows a lane reads per conv plane
+constexpr int LDR = DK + 8;      // bf16 pitch of [32][128] tiles
+constexpr int LDJ = C + 8;       // bf16 pitch of [128][32] tiles
+constexpr int LDT = 20;          // fp32 pitch of the 16 x 16 solve blocks
+
+// Physical position of index k within a 32-wide slice: the accumulator order of two
+// stacked 16-row MFMA results (lane q4 holds rows 4 q4 .. +3 of each), so that lane
+// q4's 16-byte read at 8 q4 returns exactly the rows its accumulators hold.
+__device__ __forceinline__ int perm32(int k) { return ((k & 15) >> 2) * 8 + (k >> 4) * 4 + (k & 3); }
+__device__ __forceinline__ int pchan(int c) { return (c & ~31) | perm32(c & 31); }
+
+template <bool GDN>
+struct C32Lds {
+    // written in phase 2 by the preparing group, read in phase 3 (and qp / kp by the
+    // state group in the next step's phase 1)
+    alignas(16) __bf16 qa[C][LDR];             // KDA: q^ e^{gamma}; GDN: q^ (channels permuted)
+    __bf16 ka[C][LDR];             // KDA: k^ e^{gamma}; GDN: k^
+    __bf16 kb[GDN ? 1 : C][LDR];   // k^ e^{-gamma}
+    __bf16 qp[GDN ? 1 : C][LDR];   // Q+
+    __bf16 kp[GDN ? 1 : C][LDR];   // K+
+    // double-buffered by chunk parity
+    __bf16 kdt[2][DK][LDJ];        // KDA: K_dec^T; GDN: k^T  ([key][row], rows permuted)
+    float beta[2][C];
+    float ffn[2][GDN ? 4 : DK];    // KDA: e^{G_l} per key
+    float gcum[2][C];              // GDN: G per row (log2 units)
+    // single-buffered (written in phase 3, read by the state group in the next step;
+    // v^T written and read by the state group within one step)
+    __bf16 vbt[DK][LDJ];           // v^T (conv output, no beta)
+    __bf16 pb[C][LDJ];             // P [s][j] (j permuted)
+    float lf10[16][LDT];           // A_10 = diag(beta) L, rows 16.., columns 0..15
+    float ltd[2][16 * 16 + 4];     // A_aa transposed: [a][c * 16 + r] = A[16a + r][16a + c]
+    float tdiag[2][16][LDT];       // T_aa (fp32), the state group's own
+    float fd10[GDN ? 4 : DK];      // KDA: e^{R_1} per channel (permuted)
+    float gsum[NW][DK];            // KDA: gate sums of each wavefront's rows; GDN: [0][r] row prefix, [1][w] totals
+    float nrm[NW][8];              // 1 / ||row|| of the l2 norms, per preparing wavefront
+    float taps[3][DK][KT];         // conv taps of the q, k, v channels (each lane reads back its own)
+    float normw[DK];               // norm weight (written by the state group, read back by each lane)
+    union {
+        float hist[3][HALO][DK];   // conv history before the sequence (first chunk)
+        float ost[C][DK + 4];      // O staging for the norm
+    } u;
+};
+
+__device__ __forceinline__ float lo_bf(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float hi_bf(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// The value of quad lane src in every lane of its quad (DPP quad_perm [src x 4]); src
+// is a constant once the caller's loop is unrolled.
+__device__ __forceinline__ float quad_bcast(float x, int src) {
+    switch (src) {
+        case 0: return dpp<0x00>(x);
+        case 1: return dpp<0x55>(x);
+        case 2: return dpp<0xAA>(x);
+        default: return dpp<0xFF>(x);
+    }
+}
+
+// Two 16-row accumulator tiles (rows 4 q4 + r of each) as one bf16 operand in the
+// perm32 slot order.
+__device__ __forceinline__ bf16x8 pack2(f32x4v t0, f32x4v t1) {
+    return bf16x8{(__bf16)t0[0], (__bf16)t0[1], (__bf16)t0[2], (__bf16)t0[3],
+                  (__bf16)t1[0], (__bf16)t1[1], (__bf16)t1[2], (__bf16)t1[3]};
+}
+
+// What one workgroup works on.
+struct C32Job {
+    size_t rowb;           // first activation row of the run
+    int T;                 // its rows
+    int lo;                // lowest row index a conv history may read (0 or -HALO)
+    int b, h;
+    bool ring_start;       // the run starts at the sequence start: history from the ring
+    bool readout;          // outputs are written
+    const void* vsrc;      // v rows (the zero row for the segmented arm's M runs)
+    size_t vstride;
+    const float* s_in;
+    float* s_out;
+};
+
+// Raw rows of one plane: a lane's two channels (one dword of bf16) of rows
+// RW w - 3 .. RW w + RW - 1 of the chunk at c0, from a clamped row (rows past T repeat
+// row T-1, rows before the run clamp to job.lo). Nothing is consumed before the next
+// chunk, so the loads stay in flight.
+__device__ __forceinline__ void load_rows(uint32_t (&x)[NR], const void* base, size_t stride, size_t col,
+                                          const C32Job& j, int c0, int w) {
+    const __bf16* p = static_cast<const __bf16*>(base) + col;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        const int rel = min(max(c0 + RW * w - HALO + i, j.lo), j.T - 1);
+        x[i] = *reinterpret_cast<const uint32_t*>(p + (size_t)((long long)j.rowb + rel) * stride);
+    }
+}
+
+// conv + SiLU of the lane's two channels over its RW rows: the window starts from the
+// halo rows (or, for the first chunk of a run at the sequence start, from the ring
+// copy in LDS: `hist` non-null); wt[e][KT-1] multiplies the current input.
+__device__ __forceinline__ void conv_rows(const uint32_t (&x)[NR], const float* hist, const float (&wt)[2][KT],
+                                          float (&y)[RW][2]) {
+    float win[HALO][2];
+#pragma unroll
+    for (int i = 0; i < HALO; ++i) {
+        win[i][0] = lo_bf(x[i]);
+        win[i][1] = hi_bf(x[i]);
+    }
+    if (hist) {
+#pragma unroll
+        for (int i = 0; i < HALO; ++i) {
+            win[i][0] = hist[i * DK];
+            win[i][1] = hist[i * DK + 1];
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+        const float xc[2] = {lo_bf(x[HALO + r]), hi_bf(x[HALO + r])};
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int t = 0; t < HALO; ++t) acc = fmaf(wt[e][t], win[t][e], acc);
+            acc = fmaf(wt[e][KT - 1], xc[e], acc);
+            y[r][e] = silu_f(acc);
+        }
+#pragma unroll
+        for (int t = 0; t < HALO - 1; ++t)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) win[t][e] = win[t + 1][e];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) win[HALO - 1][e] = xc[e];
+    }
+}
+
+// The KDA gates of the lane's two channels over its RW rows, activated (FORM) and in
+// log2 units, as running sums gp[r][e]; rows at or past n are zero.
+template <int FORM>
+__device__ __forceinline__ void kda_gate_prefix(const uint32_t (&g)[RW], int row0, int n, float lb2, float m,
+                                                float k1, const float (&k0)[2], float (&gp)[RW][2]) {
+    float acc[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+        const float x[2] = {lo_bf(g[r]), hi_bf(g[r])};
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            float v;
+            if constexpr (FORM == GATE_GIVEN) v = x[e] * LOG2E;
+            else v = gate_act_log2<FORM>(lb2, m, k1, k0[e], x[e]);
+            acc[e] += row0 + r < n ? v : 0.0f;
+            gp[r][e] = acc[e];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------
+// Wavefronts 0..7: the state-independent preparation of each chunk.
+// ---------------------------------------------------------------------------------
+template <bool GDN, bool ACT>
+__device__ __forceinline__ void c32_prepare(C32Lds<GDN>& sm, const MixerArgs& a, const C32Job& jb, int w,
+                                            int lane) {
+    const int q4 = lane >> 4, l16 = lane & 15, c2 = 2 * lane, K = a.K, H = a.H, h = jb.h;
+    const size_t qkv = (size_t)H * DK, hoff = (size_t)h * DK;
+    const size_t kw = (size_t)a.Hk * DK, khead = (size_t)(h % a.Hk) * DK;
+    const int nch = (jb.T + C - 1) / C;
+    const int pr0 = RW * w;  // this wavefront's first row of a chunk
+
+    // gate-activation constants (read once, before the row loads)
+    float gm = 0.0f, gbias = 0.0f, k1 = 0.0f, lb2 = 0.0f, k0[2] = {0.0f, 0.0f};
+    if constexpr (GDN) {
+        if (a.gate_form != GATE_GIVEN) {
+            gm = gate_head_factor(a, h);
+            gbias = a.gate_bias[h];
+        }
+    }
+    if constexpr (ACT) {
+        gm = gate_head_factor(a, h);
+        lb2 = a.gate_lb * LOG2E;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const float bias = a.gate_bias[hoff + c2 + e];
+            if (a.gate_form == GATE_SIGMOID) gate_log2_consts<GATE_SIGMOID>(gm, bias, &k1, &k0[e]);
+            else gate_log2_consts<GATE_SOFTPLUS>(gm, bias, &k1, &k0[e]);
+        }
+    }
+
+    // conv history before the sequence start (the old ring; slot K-1-d is d rows back),
+    // oldest first; preparing wavefront 0 reads the q / k planes in its first chunk,
+    // state wavefront 0 the v plane (in the next step)
+    if (jb.ring_start && w == 0) {
+        const float* ring_b = a.ring + (size_t)jb.b * ring_rows(a) * (K - 1);
+#pragma unroll
+        for (int pl = 0; pl < 3; ++pl)
+#pragma unroll
+            for (int d = 1; d <= HALO; ++d)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const size_t fr = plane_row(a, pl, h, c2 + e);
+                    const float x = ring_b[fr * (K - 1) + max(K - 1 - d, 0)];
+                    sm.u.hist[pl][HALO - d][c2 + e] = d <= K - 1 ? x : 0.0f;
+                }
+        lds_wave_sync();
+    }
+
+    // raw rows of the first chunk; beta and the GDN gate stay raw bf16 bits until they
+    // are used (converting them at the load would wait for every row load before them)
+    uint32_t rq[NR], rk[NR], rg[GDN ? 1 : RW];
+    uint32_t rbeta = 0, rgs = 0;
+    auto load_chunk = [&](int c0) {
+        load_rows(rq, a.q, kw, khead + c2, jb, c0, w);
+        load_rows(rk, a.k, kw, khead + c2, jb, c0, w);
+        if constexpr (!GDN) {
+            const __bf16* g = static_cast<const __bf16*>(a.g) + hoff + c2;
+#pragma unroll
+            for (int i = 0; i < RW; ++i)
+                rg[i] = *reinterpret_cast<const uint32_t*>(g + (jb.rowb + min(c0 + pr0 + i, jb.T - 1)) * qkv);
+        }
+        const size_t hr = (jb.rowb + min(c0 + pr0 + (lane & (RW - 1)), jb.T - 1)) * H + h;
+        rbeta = static_cast<const unsigned short*>(a.beta)[hr];
+        if constexpr (GDN) rgs = static_cast<const unsigned short*>(a.g)[hr];
+    };
+    load_chunk(0);
+    // conv taps of the lane's q and k channels, parked in LDS for the whole run (each
+    // lane reads back only what it wrote)
+    {
+        float wt[2][KT];
+        load_taps<KT, 2>(wt, a.conv_w, khead + c2, K);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) *reinterpret_cast<f32x4v*>(&sm.taps[0][c2 + e][0]) = f32x4v{wt[e][0], wt[e][1], wt[e][2], wt[e][3]};
+        load_taps<KT, 2>(wt, a.conv_w, kw + khead + c2, K);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) *reinterpret_cast<f32x4v*>(&sm.taps[1][c2 + e][0]) = f32x4v{wt[e][0], wt[e][1], wt[e][2], wt[e][3]};
+    }
+    auto taps_of = [&](int pl, float (&wt)[2][KT]) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const f32x4v t = ld4f(&sm.taps[pl][c2 + e][0]);
+#pragma unroll
+            for (int j = 0; j < KT; ++j) wt[e][j] = t[j];
+        }
+    };
+
+    for (int s = 0; s <= nch; ++s) {
+        const int c0 = s * C, n = min(C, jb.T - c0), par = s & 1;
+        const bool live = s < nch;
+        // ---- phase 1: conv + SiLU of q and k, l2 norms, gate prefix ----
+        float yq[RW][2], yk[RW][2];
+        float gp[GDN ? 1 : RW][2];
+        if (live) {
+            const bool from_hist = jb.ring_start && s == 0 && w == 0;
+            {
+                float wt[2][KT];
+                taps_of(0, wt);
+                conv_rows(rq, from_hist ? &sm.u.hist[0][0][c2] : nullptr, wt, yq);
+                taps_of(1, wt);
+                conv_rows(rk, from_hist ? &sm.u.hist[1][0][c2] : nullptr, wt, yk);
+            }
+            float ps[8];
+#pragma unroll
+            for (int r = 0; r < RW; ++r) {
+                ps[r] = fmaf(yq[r][0], yq[r][0], yq[r][1] * yq[r][1]);
+                ps[RW + r] = fmaf(yk[r][0], yk[r][0], yk[r][1] * yk[r][1]);
+            }
+            const int brow = pr0 + (lane & (RW - 1));
+            if constexpr (!GDN) {
+                if constexpr (ACT) {
+                    if (a.gate_form == GATE_SIGMOID)
+                        kda_gate_prefix<GATE_SIGMOID>(rg, pr0, n, lb2, gm, k1, k0, gp);
+                    else
+                        kda_gate_prefix<GATE_SOFTPLUS>(rg, pr0, n, lb2, gm, k1, k0, gp);
+                } else {
+                    kda_gate_prefix<GATE_GIVEN>(rg, pr0, n, lb2, gm, k1, k0, gp);
+                }
+                *reinterpret_cast<float2*>(&sm.gsum[w][c2]) = make_float2(gp[RW - 1][0], gp[RW - 1][1]);
+            } else {
+                const float gx = __uint_as_float(rgs << 16);
+                float gv = a.gate_form != GATE_GIVEN ? gate_act_core(a.gate_form, a.gate_lb, gm, gbias, gx) : gx;
+                gv = (lane < RW && brow < n) ? gv * LOG2E : 0.0f;
+#pragma unroll
+                for (int off = 1; off < RW; off *= 2) {
+                    const float t = __shfl_up(gv, off, RW);
+                    if ((lane & (RW - 1)) >= off) gv += t;
+                }
+                if (lane < RW) sm.gsum[0][brow] = gv;
+                if (lane == RW - 1) sm.gsum[1][w] = gv;
+            }
+            const float bval = beta_in(a, __uint_as_float(rbeta << 16));
+            if (lane < RW) sm.beta[par][brow] = brow < n ? bval : 0.0f;
+            // l2 norms: lane l gets plane (l >> 3) / RW, row (l >> 3) % RW of this wavefront
+            const float ss = sum8x64(ps, lane);
+            if ((lane & 7) == 0) sm.nrm[w][lane >> 3] = rsqrtf(ss + L2_EPS);
+            // the next chunk's rows (the registers above are consumed)
+            asm volatile("" ::: "memory");
+            load_chunk(c0 + C);
+        }
+        lds_barrier();  // B1
+
+        // ---- phase 2: decay factors and operand tiles ----
+        if (live) {
+            float nr[8];
+            {
+                const f32x4v v0 = ld4f(&sm.nrm[w][0]), v1 = ld4f(&sm.nrm[w][4]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    nr[e] = v0[e];
+                    nr[4 + e] = v1[e];
+                }
+            }
+            const int pc = pchan(c2);
+            if constexpr (!GDN) {
+                float off[2] = {0.0f, 0.0f}, tot[2] = {0.0f, 0.0f}, r1[2] = {0.0f, 0.0f};
+#pragma unroll
+                for (int ww = 0; ww < NW; ++ww) {
+                    const float2 s2 = *reinterpret_cast<const float2*>(&sm.gsum[ww][c2]);
+                    const float sv[2] = {s2.x, s2.y};
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        if (ww < w) off[e] += sv[e];
+                        if (ww < NW / 2) r1[e] += sv[e];  // rows 0..15
+                        tot[e] += sv[e];
+                    }
+                }
+                const bool blk1 = w >= NW / 2;
+                float ra[2], fa[2], fl[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    ra[e] = blk1 ? r1[e] : 0.0f;
+                    fa[e] = exp2_f(ra[e]);
+                    fl[e] = exp2_f(tot[e] - ra[e]);
+                }
+                if (w == 0) {
+                    *reinterpret_cast<float2*>(&sm.ffn[par][c2]) = make_float2(exp2_f(tot[0]), exp2_f(tot[1]));
+                    *reinterpret_cast<float2*>(&sm.fd10[pc]) = make_float2(exp2_f(r1[0]), exp2_f(r1[1]));
+                }
+                float kd[2][RW];
+#pragma unroll
+                for (int r = 0; r < RW; ++r) {
+                    bf16x2 oqa, oqp, oka, okp, okb;
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const float gam = off[e] + gp[r][e] - ra[e];
+                        const float e1 = exp2_f(gam), e2 = exp2_f(-gam);
+                        const float qh = yq[r][e] * nr[r], kh = yk[r][e] * nr[RW + r];
+                        const float qa = qh * e1, ka = kh * e1, kbv = kh * e2;
+                        oqa[e] = (__bf16)qa;
+                        oqp[e] = (__bf16)(qa * fa[e]);
+                        oka[e] = (__bf16)ka;
+                        okp[e] = (__bf16)(ka * fa[e]);
+                        okb[e] = (__bf16)kbv;
+                        kd[e][r] = kbv * fl[e];
+                    }
+                    const int row = pr0 + r;
+                    st2(&sm.qa[row][pc], oqa);
+                    st2(&sm.qp[row][pc], oqp);
+                    st2(&sm.ka[row][pc], oka);
+                    st2(&sm.kp[row][pc], okp);
+                    st2(&sm.kb[row][pc], okb);
+                }
+                // K_dec^T: the wavefront's 4 rows are contiguous in the permuted order
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const bf16x4 v4{(__bf16)kd[e][0], (__bf16)kd[e][1], (__bf16)kd[e][2], (__bf16)kd[e][3]};
+                    *reinterpret_cast<bf16x4*>(&sm.kdt[par][c2 + e][perm32(pr0)]) = v4;
+                }
+            } else {
+                if (w == 0 && lane < C) {
+                    float g = sm.gsum[0][lane];
+#pragma unroll
+                    for (int ww = 0; ww < NW - 1; ++ww)
+                        if (ww < lane / RW) g += sm.gsum[1][ww];
+                    sm.gcum[par][lane] = g;
+                }
+                float kk[2][RW];
+#pragma unroll
+                for (int r = 0; r < RW; ++r) {
+                    bf16x2 oq, ok;
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        oq[e] = (__bf16)(yq[r][e] * nr[r]);
+                        kk[e][r] = yk[r][e] * nr[RW + r];
+                        ok[e] = (__bf16)kk[e][r];
+                    }
+                    st2(&sm.qa[pr0 + r][pc], oq);
+                    st2(&sm.ka[pr0 + r][pc], ok);
+                }
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const bf16x4 v4{(__bf16)kk[e][0], (__bf16)kk[e][1], (__bf16)kk[e][2], (__bf16)kk[e][3]};
+                    *reinterpret_cast<bf16x4*>(&sm.kdt[par][c2 + e][perm32(pr0)]) = v4;
+                }
+            }
+        }
+        lds_barrier();  // B2
+
+        // ---- phase 3: L and P, one 16 x 16 block product per wavefront 0..5:
+        // L(0,0), P(0,0), L(1,1), P(1,1), L(1,0), P(1,0) ----
+        if (live && w < 6) {
+            const bool doL = (w & 1) == 0;
+            const int ab = w < 2 ? 0 : 1, bb = (w == 2 || w == 3) ? 1 : 0;  // row block, column block
+            const int srow = 16 * ab + l16;
+            const __bf16* brow_p = GDN ? &sm.ka[16 * bb + l16][0] : &sm.kb[16 * bb + l16][0];
+            const __bf16* arow_p = doL ? &sm.ka[srow][0] : &sm.qa[srow][0];
+            f32x4v acc = zero4();
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int i0 = 32 * kk + 8 * q4;
+                bf16x8 bk = ld8(brow_p + i0);
+                if constexpr (!GDN) {
+                    if (w >= 4) {  // block (1, 0): k e^{-gamma} of block 0 times e^{R_1}
+                        const f32x4v d0 = ld4f(&sm.fd10[i0]), d1 = ld4f(&sm.fd10[i0 + 4]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            bk[e] = (__bf16)((float)bk[e] * d0[e]);
+                            bk[4 + e] = (__bf16)((float)bk[4 + e] * d1[e]);
+                        }
+                    }
+                }
+                acc = mfma_bf16(bk, ld8(arow_p + i0), acc);  // lane: X[srow][16 bb + 4 q4 + r]
+            }
+            const int j0 = 16 * bb + 4 * q4;
+            if (doL) {
+                const float bs = sm.beta[par][srow];
+                f32x4v lv;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = j0 + r;
+                    float ef = 1.0f;
+                    if constexpr (GDN) ef = exp2_f(fminf(sm.gcum[par][srow] - sm.gcum[par][j], 0.0f));
+                    lv[r] = j < srow ? bs * (acc[r] * ef) : 0.0f;
+                }
+                if (ab == bb) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sm.ltd[ab][(4 * q4 + r) * 16 + l16] = lv[r];
+                } else {
+                    *reinterpret_cast<f32x4v*>(&sm.lf10[l16][4 * q4]) = lv;
+                }
+            } else {
+                bf16x4 pv;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = j0 + r;
+                    float ef = 1.0f;
+                    if constexpr (GDN) ef = exp2_f(fminf(sm.gcum[par][srow] - sm.gcum[par][j], 0.0f));
+                    pv[r] = (__bf16)(j <= srow ? acc[r] * ef : 0.0f);
+                }
+                *reinterpret_cast<bf16x4*>(&sm.pb[srow][perm32(j0)]) = pv;
+                if (w == 1) {  // P block (0, 1) above the diagonal
+                    const __bf16 z = (__bf16)0.0f;
+                    *reinterpret_cast<bf16x4*>(&sm.pb[srow][perm32(16 + 4 * q4)]) = bf16x4{z, z, z, z};
+                }
+            }
+        }
+        lds_barrier();  // B3
+    }
+}
+
+// ---------------------------------------------------------------------------------
+// Wavefronts 8..15: the state; in step s the v conv and the state-dependent work of
+// chunk s-1.
+// ---------------------------------------------------------------------------------
+template <bool GDN>
+__device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, const C32Job& jb, int w,
+                                          int lane) {
+    const int tid = w * 64 + lane;  // 0..511 within the group
+    const int q4 = lane >> 4, l16 = lane & 15, c2 = 2 * lane, K = a.K;
+    const size_t qkv = (size_t)a.H * DK, hoff = (size_t)jb.h * DK;
+    const size_t kw = (size_t)a.Hk * DK;
+    const int nch = (jb.T + C - 1) / C;
+    const int vcol = 16 * w + l16;  // this lane's value column
+
+    // ---- state: accS[kt] holds keys 16 kt + 4 q4 .. +3 of value column vcol ----
+    f32x4v accS[8];
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt) accS[kt] = ld4f(&jb.s_in[(size_t)vcol * DK + 16 * kt + 4 * q4]);
+    // the epilogue's item: row tid / 16 (clamped), columns c8 .. c8 + 7
+    const int c8 = (tid & 15) * 8, erow = tid >> 4;
+    // the norm weight of the lane's columns and the conv taps of its v channels, parked
+    // in LDS for the whole run (each lane reads back only what it wrote)
+    {
+        const f32x4v n0 = ld4f(&a.norm_w[c8]), n1 = ld4f(&a.norm_w[c8 + 4]);
+        *reinterpret_cast<f32x4v*>(&sm.normw[c8]) = n0;
+        *reinterpret_cast<f32x4v*>(&sm.normw[c8 + 4]) = n1;
+        float wt[2][KT];
+        load_taps<KT, 2>(wt, a.conv_w, 2 * kw + hoff + c2, K);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) *reinterpret_cast<f32x4v*>(&sm.taps[2][c2 + e][0]) = f32x4v{wt[e][0], wt[e][1], wt[e][2], wt[e][3]};
+    }
+    uint32_t rv[NR];
+    load_rows(rv, jb.vsrc, jb.vstride, hoff + c2, jb, 0, w);
+
+    bf16x8 zpre;
+    f32x4v oacc[2], racc[2];  // [mt] O^T, K+ S
+    for (int s = 0; s <= nch; ++s) {
+        const int c = s - 1, par = c & 1;  // the chunk of the state work
+        const bool live = s >= 1;
+        const int c0 = c * C, n = min(C, jb.T - c0);
+        const size_t row0 = jb.rowb + c0;
+        // ---- phase 1: v conv; diagonal blocks of T; Q+ S as O^T and K+ S ----
+        if (live) {
+            {
+                float yv[RW][2], wv[2][KT];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const f32x4v t = ld4f(&sm.taps[2][c2 + e][0]);
+#pragma unroll
+                    for (int j = 0; j < KT; ++j) wv[e][j] = t[j];
+                }
+                const bool from_hist = jb.ring_start && c == 0 && w == 0;
+                conv_rows(rv, from_hist ? &sm.u.hist[2][0][c2] : nullptr, wv, yv);
+                // v^T: the wavefront's 4 rows are contiguous in the permuted order
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const bf16x4 v4{(__bf16)yv[0][e], (__bf16)yv[1][e], (__bf16)yv[2][e], (__bf16)yv[3][e]};
+                    *reinterpret_cast<bf16x4*>(&sm.vbt[c2 + e][perm32(RW * w)]) = v4;
+                }
+            }
+            // this chunk's output gates (for phase 3), then the next chunk's v rows
+            asm volatile("" ::: "memory");
+            zpre = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.z) +
+                                                   (row0 + min(erow, n - 1)) * qkv + jb.h * DK + c8);
+            load_rows(rv, jb.vsrc, jb.vstride, hoff + c2, jb, c0 + C, w);
+            if (w < 2) {
+                // T_ww = (I + A_ww)^-1 by forward substitution in column (axpy) order, all
+                // 64 lanes: lane (col = lane / 4, rg = lane % 4) holds rows 4 rg .. 4 rg + 3 of
+                // column col; step cc takes the pivot x[cc] from its owner in the quad
+                // (DPP broadcast) and updates the rows below it. Column cc of A_ww is row cc
+                // of the transposed copy, read one step ahead.
+                const int col = lane >> 2, rg = lane & 3;
+                const float* at = sm.ltd[w];
+                float x[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x[i] = (4 * rg + i == col) ? 1.0f : 0.0f;
+                f32x4v nxt = ld4f(at + 4 * rg);
+#pragma unroll
+                for (int cc = 0; cc < 15; ++cc) {
+                    const f32x4v cur = nxt;
+                    if (cc + 1 < 15) nxt = ld4f(at + (cc + 1) * 16 + 4 * rg);
+                    const float piv = quad_bcast(x[cc & 3], cc >> 2);  // from the quad lane owning row cc
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float upd = fmaf(-cur[i], piv, x[i]);
+                        x[i] = 4 * rg + i > cc ? upd : x[i];
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sm.tdiag[w][4 * rg + i][col] = x[i];
+            }
+            // O^T (lane: O[16 mt + l16][16 w + 4 q4 + r]) and K+ S (lane: R[16 mt + 4 q4 + r]
+            // [vcol]); the state packed to bf16 is the operand with its keys in the
+            // accumulator (perm32) order
+            bf16x8 sbop[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) sbop[kk] = pack2(accS[2 * kk], accS[2 * kk + 1]);
+            const __bf16* qsrc = GDN ? &sm.qa[0][0] : &sm.qp[0][0];
+            const __bf16* ksrc = GDN ? &sm.ka[0][0] : &sm.kp[0][0];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                oacc[mt] = zero4();
+                racc[mt] = zero4();
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const int off = (16 * mt + l16) * LDR + 32 * kk + 8 * q4;
+                    oacc[mt] = mfma_bf16(sbop[kk], ld8(qsrc + off), oacc[mt]);
+                    racc[mt] = mfma_bf16(ld8(ksrc + off), sbop[kk], racc[mt]);
+                }
+            }
+        }
+        lds_barrier();  // B1
+
+        // ---- phase 2: T_10, Ub = T diag(beta) (V - K+ S), O, state update ----
+        if (live) {
+            // T_10 = -T_11 A_10 T_00, formed transposed in registers: Y = A_10^T T_11^T
+            // (slot k = 4 kk + q4), then T_10^T = T_00^T Y (negated) with Y fed back as
+            // the B operand (slot k = 4 q4 + kk); the lane ends with T_10[l16][4 q4 + r].
+            f32x4v y = zero4();
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) y = mfma_f32(sm.lf10[4 * kk + q4][l16], sm.tdiag[1][l16][4 * kk + q4], y);
+            f32x4v t10 = zero4();
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) t10 = mfma_f32(sm.tdiag[0][4 * q4 + kk][l16], y[kk], t10);
+            // T as A fragments: rows 16 mt + l16, slots e < 4 -> column 4 q4 + e,
+            // e >= 4 -> column 16 + 4 q4 + e - 4
+            const f32x4v t00 = ld4f(&sm.tdiag[0][l16][4 * q4]), t11 = ld4f(&sm.tdiag[1][l16][4 * q4]);
+            const __bf16 z = (__bf16)0.0f;
+            const bf16x8 ta0{(__bf16)t00[0], (__bf16)t00[1], (__bf16)t00[2], (__bf16)t00[3], z, z, z, z};
+            const bf16x8 ta1{(__bf16)(-t10[0]), (__bf16)(-t10[1]), (__bf16)(-t10[2]), (__bf16)(-t10[3]),
+                             (__bf16)t11[0], (__bf16)t11[1], (__bf16)t11[2], (__bf16)t11[3]};
+
+            const f32x4v be0 = ld4f(&sm.beta[par][4 * q4]), be1 = ld4f(&sm.beta[par][16 + 4 * q4]);
+            f32x4v gr0 = f32x4v{1.0f, 1.0f, 1.0f, 1.0f}, gr1 = gr0;  // GDN: e^{G_j} of the lane's rows
+            float gl = 0.0f;
+            if constexpr (GDN) {
+                const f32x4v g0 = ld4f(&sm.gcum[par][4 * q4]), g1 = ld4f(&sm.gcum[par][16 + 4 * q4]);
+                gl = sm.gcum[par][C - 1];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    gr0[r] = exp2_f(g0[r]);
+                    gr1[r] = exp2_f(g1[r]);
+                }
+            }
+            bf16x8 xb;
+            {
+                const bf16x8 vv = ld8(&sm.vbt[vcol][8 * q4]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    xb[r] = (__bf16)(be0[r] * ((float)vv[r] - racc[0][r] * gr0[r]));
+                    xb[4 + r] = (__bf16)(be1[r] * ((float)vv[4 + r] - racc[1][r] * gr1[r]));
+                }
+            }
+            // Ub[16 mt + 4 q4 + r][vcol]
+            const f32x4v ub0 = mfma_bf16(ta0, xb, zero4()), ub1 = mfma_bf16(ta1, xb, zero4());
+            const bf16x8 ubo = pack2(ub0, ub1);  // Ub as operand
+            bf16x8 ubs = ubo;                    // for the state update (GDN: rows times e^{G_l - G_j})
+            if constexpr (GDN) {
+                f32x4v u0, u1;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    u0[r] = ub0[r] * exp2_f(gl - sm.gcum[par][4 * q4 + r]);
+                    u1[r] = ub1[r] * exp2_f(gl - sm.gcum[par][16 + 4 * q4 + r]);
+                }
+                ubs = pack2(u0, u1);
+            }
+            // O^T = (Q+ S)^T + Ub^T P^T (GDN: Q+ S is q S with rows times e^{G_s})
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                if constexpr (GDN) oacc[mt] *= exp2_f(sm.gcum[par][16 * mt + l16]);
+                oacc[mt] = mfma_bf16(ubo, ld8(&sm.pb[16 * mt + l16][8 * q4]), oacc[mt]);
+            }
+            // S = diag(e^{G_l}) S + K_dec^T Ub
+            const float fg = GDN ? exp2_f(gl) : 0.0f;
+#pragma unroll
+            for (int kt = 0; kt < 8; ++kt) {
+                const f32x4v dec = GDN ? f32x4v{fg, fg, fg, fg} : ld4f(&sm.ffn[par][16 * kt + 4 * q4]);
+                accS[kt] *= dec;
+                accS[kt] = mfma_bf16(ld8(&sm.kdt[par][16 * kt + l16][8 * q4]), ubs, accS[kt]);
+            }
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+                *reinterpret_cast<f32x4v*>(&sm.u.ost[16 * mt + l16][16 * w + 4 * q4]) = a.scale * oacc[mt];
+        }
+        lds_barrier();  // B2
+
+        // ---- phase 3: gated RMSNorm and stores (rows past n store copies of row n-1) ----
+        if (live && jb.readout) {
+            const int r = min(erow, n - 1);  // the 16 lanes of a DPP row share r
+            float o8[8], w8[8];
+            const f32x4v oa = ld4f(&sm.u.ost[r][c8]), ob = ld4f(&sm.u.ost[r][c8 + 4]);
+            const f32x4v wa = ld4f(&sm.normw[c8]), wb = ld4f(&sm.normw[c8 + 4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                w8[e] = wa[e];
+                w8[4 + e] = wb[e];
+            }
+            float ss = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                o8[e] = oa[e];
+                o8[4 + e] = ob[e];
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss = fmaf(o8[e], o8[e], ss);
+            ss = sum_row16(ss);
+            const float inv = rsqrtf(fmaf(ss, 1.0f / DK, a.rms_eps));
+            const size_t off = (row0 + r) * qkv + hoff + c8;
+            bf16x8 yb;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float zf = (float)zpre[e];
+                const float gate = GDN ? silu_f(zf) : sigmoid_f(zf);
+                yb[e] = (__bf16)(((o8[e] * inv) * w8[e]) * gate);
+            }
+            st8(static_cast<__bf16*>(a.out) + off, yb);
+            if (a.o_core) {
+                float4* d = reinterpret_cast<float4*>(a.o_core + off);
+                d[0] = make_float4(o8[0], o8[1], o8[2], o8[3]);
+                d[1] = make_float4(o8[4], o8[5], o8[6], o8[7]);
+            }
+        }
+        lds_barrier();  // B3
+    }
+
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt)
+        *reinterpret_cast<f32x4v*>(&jb.s_out[(size_t)vcol * DK + 16 * kt + 4 * q4]) = accS[kt];
+}
+
+template <bool GDN, bool ACT, bool SEG>
+__global__ __launch_bounds__(NT) void c32_kernel(MixerArgs a) {
+    static_assert(!(GDN && ACT), "GDN gates are activated per row at run time");
+    __shared__ C32Lds<GDN> sm;
+
+    int bh;
+    SegRun sr{};
+    if constexpr (SEG) {
+        if (!seg_run(a, &sr)) return;  // whole block exits before any barrier
+        bh = sr.pair;
+    } else {
+        bh = blockIdx.x;
+        if (bh >= a.B * a.H) return;
+        bh = seq_of(a, bh / a.H) * a.H + bh % a.H;  // packed batches: longest sequences first
+    }
+    C32Job jb;
+    jb.b = bh / a.H;
+    jb.h = bh % a.H;
+    seq_span(a, jb.b, &jb.rowb, &jb.T);
+    if constexpr (SEG) {
+        jb.rowb += sr.ro;
+        jb.T = sr.len;
+    }
+    jb.ring_start = !SEG || sr.ro == 0;
+    jb.lo = jb.ring_start ? 0 : -HALO;
+    jb.readout = !SEG || sr.readout;
+    const bool zero_v = SEG && sr.zero_v;
+    jb.vsrc = zero_v ? static_cast<const void*>(a.seg_ws) : a.v;
+    jb.vstride = zero_v ? 0 : (size_t)a.H * DK;
+    jb.s_in = SEG ? sr.s_in : a.state_in + (size_t)bh * DK * DK;
+    jb.s_out = SEG ? sr.s_out : a.state_out + (size_t)bh * DK * DK;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave-uniform: every row index built from it is scalar arithmetic
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (jb.T == 0) {  // an empty sequence of a packed batch: the state passes through
+        const f32x4v* src = reinterpret_cast<const f32x4v*>(jb.s_in);
+        f32x4v* dst = reinterpret_cast<f32x4v*>(jb.s_out);
+        for (int i = tid; i < DK * DK / 4; i += NT) dst[i] = src[i];
+        return;  // uniform over the workgroup, before any barrier
+    }
+    if (wave < NW) c32_prepare<GDN, ACT>(sm, a, jb, wave, lane);
+    else c32_state<GDN>(sm, a, jb, wave - NW, lane);
+}
+
+template <bool GDN, bool SEG>
+hipError_t c32_launch(const MixerArgs& a, int grid) {
+    static_assert(sizeof(C32Lds<GDN>) <= 160 * 1024, "LDS of one workgroup");
+    if (grid <= 0) return hipSuccess;
+    const dim3 g(grid), blk(NT);
+    if (!GDN && a.gate_form != GATE_GIVEN)
+        hipLaunchKernelGGL((c32_kernel<GDN, !GDN, SEG>), g, blk, 0, a.stream, a);
+    else
+        hipLaunchKernelGGL((c32_kernel<GDN, false, SEG>), g, blk, 0, a.stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool chunked32_fits(const MixerArgs& a) { return a.bf16 && a.D == DK && a.K <= KT; }
+
+hipError_t launch_chunked32(const MixerArgs& a) {
+    if (!chunked32_fits(a)) return hipErrorInvalidValue;
+    const int grid = a.B * a.H;
+    const hipError_t e = a.gdn ? c32_launch<true, false>(a, grid) : c32_launch<false, false>(a, grid);
+    if (e != hipSuccess) return e;
+    return launch_ring_roll(a, false);
+}
+
+hipError_t launch_seg_pass32(const MixerArgs& a, int grid) {
+    return a.gdn ? c32_launch<true, true>(a, grid) : c32_launch<false, true>(a, grid);
+}
+
+}  // namespace kda

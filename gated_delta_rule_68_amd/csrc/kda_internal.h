@@ -189,6 +189,12 @@ hipError_t launch_chunked(const MixerArgs& a);
 // Segmented chunked prefill; a.seg_n / a.seg_len hold the plan and a.ws its
 // workspace (seg_layout).
 hipError_t launch_segmented(const MixerArgs& a);
+// The 32-row chunk kernel (kda_c32.hip): bf16 activations, D = 128, K <= 4. The
+// chunked and segmented arms run it wherever it fits, the 64-row kernel otherwise.
+bool chunked32_fits(const MixerArgs& a);
+hipError_t launch_chunked32(const MixerArgs& a);
+// One pass of the segmented arm on the 32-row kernel (a.seg_pass, grid as planned).
+hipError_t launch_seg_pass32(const MixerArgs& a, int grid);
 // Gated RMSNorm of a fp32 pre-norm output o [B][T][H*D] into a.out.
 hipError_t launch_norm(const MixerArgs& a, const float* o);
 // Rank the B sequences of a packed batch by length, longest first (ties by index),
