@@ -41,6 +41,8 @@
 // meets an accumulator are stored with that index permuted within each 32-wide slice
 // (perm32), so every MFMA fragment is one 16-byte LDS read. Tiles that one group
 // writes while the other reads the previous chunk's are double-buffered.
+#include <type_traits>
+
 #include "kda_chunk_common.h"
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -77,6 +79,7 @@ struct C32Lds {
     __bf16 kb[GDN ? 1 : C][LDR];   // k^ e^{-gamma}
     __bf16 qp[GDN ? 1 : C][LDR];   // Q+
     __bf16 kp[GDN ? 1 : C][LDR];   // K+
+    __bf16 kb1[GDN ? 1 : C / 2][LDR];  // rows 0..15: k^ e^{-gamma} e^{R_1} (L, P block (1, 0))
     // double-buffered by chunk parity
     __bf16 kdt[2][DK][LDJ];        // KDA: K_dec^T; GDN: k^T  ([key][row], rows permuted)
     float beta[2][C];
@@ -89,7 +92,6 @@ struct C32Lds {
     float lf10[16][LDT];           // A_10 = diag(beta) L, rows 16.., columns 0..15
     float ltd[2][16 * 16 + 4];     // A_aa transposed: [a][c * 16 + r] = A[16a + r][16a + c]
     float tdiag[2][16][LDT];       // T_aa (fp32), the state group's own
-    float fd10[GDN ? 4 : DK];      // KDA: e^{R_1} per channel (permuted)
     float gsum[NW][DK];            // KDA: gate sums of each wavefront's rows; GDN: [0][r] row prefix, [1][w] totals
     float nrm[NW][8];              // 1 / ||row|| of the l2 norms, per preparing wavefront
     float taps[3][DK][KT];         // conv taps of the q, k, v channels (each lane reads back its own)
@@ -103,14 +105,19 @@ struct C32Lds {
 __device__ __forceinline__ float lo_bf(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float hi_bf(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
-// The value of quad lane src in every lane of its quad (DPP quad_perm [src x 4]); src
-// is a constant once the caller's loop is unrolled.
+// The value of quad lane src in every lane of its quad (DPP quad_perm [src x 4]; every
+// lane reads a lane of its own quad, so no lane keeps an old value); src is a constant
+// once the caller's loop is unrolled.
+template <int CTRL>
+__device__ __forceinline__ float mov_dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
 __device__ __forceinline__ float quad_bcast(float x, int src) {
     switch (src) {
-        case 0: return dpp<0x00>(x);
-        case 1: return dpp<0x55>(x);
-        case 2: return dpp<0xAA>(x);
-        default: return dpp<0xFF>(x);
+        case 0: return mov_dpp<0x00>(x);
+        case 1: return mov_dpp<0x55>(x);
+        case 2: return mov_dpp<0xAA>(x);
+        default: return mov_dpp<0xFF>(x);
     }
 }
 
@@ -129,23 +136,26 @@ struct C32Job {
     int b, h;
     bool ring_start;       // the run starts at the sequence start: history from the ring
     bool readout;          // outputs are written
-    const void* vsrc;      // v rows (the zero row for the segmented arm's M runs)
-    size_t vstride;
+    uint32_t vbytes;       // range of the v loads: 0 for the segmented arm's M runs (v = 0)
     const float* s_in;
     float* s_out;
 };
 
-// Raw rows of one plane: a lane's two channels (one dword of bf16) of rows
-// RW w - 3 .. RW w + RW - 1 of the chunk at c0, from a clamped row (rows past T repeat
-// row T-1, rows before the run clamp to job.lo). Nothing is consumed before the next
-// chunk, so the loads stay in flight.
-__device__ __forceinline__ void load_rows(uint32_t (&x)[NR], const void* base, size_t stride, size_t col,
-                                          const C32Job& j, int c0, int w) {
-    const __bf16* p = static_cast<const __bf16*>(base) + col;
+// Raw rows of one plane: a lane's two channels (one dword of bf16, `lane_off` bytes into
+// the row) of rows RW w - 3 .. RW w + RW - 1 of the chunk at c0, from a clamped row (rows
+// past T repeat row T-1, rows before the run clamp to job.lo). Row indices are
+// wave-uniform: the buffer starts at the lowest row any wavefront reads, and each row is
+// a scalar offset from it. Nothing is consumed before the next chunk, so the loads stay
+// in flight.
+__device__ __forceinline__ void load_rows(uint32_t (&x)[NR], const void* base, size_t stride, size_t col0,
+                                          uint32_t lane_off, uint32_t bytes, const C32Job& j, int c0, int w) {
+    const int rb = min(max(c0 - HALO, j.lo), j.T - 1);
+    const auto rs = buf_rsrc(static_cast<const __bf16*>(base) + ((size_t)((long long)j.rowb + rb) * stride + col0), bytes);
+    const uint32_t pitch = (uint32_t)(stride * sizeof(__bf16));
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
         const int rel = min(max(c0 + RW * w - HALO + i, j.lo), j.T - 1);
-        x[i] = *reinterpret_cast<const uint32_t*>(p + (size_t)((long long)j.rowb + rel) * stride);
+        x[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)lane_off, (int)((uint32_t)(rel - rb) * pitch), 0);
     }
 }
 
@@ -260,18 +270,26 @@ __device__ __forceinline__ void c32_prepare(C32Lds<GDN>& sm, const MixerArgs& a,
     // are used (converting them at the load would wait for every row load before them)
     uint32_t rq[NR], rk[NR], rg[GDN ? 1 : RW];
     uint32_t rbeta = 0, rgs = 0;
+    const uint32_t lane_off = 4u * lane;  // the lane's two channels, in bytes
     auto load_chunk = [&](int c0) {
-        load_rows(rq, a.q, kw, khead + c2, jb, c0, w);
-        load_rows(rk, a.k, kw, khead + c2, jb, c0, w);
+        load_rows(rq, a.q, kw, khead, lane_off, BUF_ALL, jb, c0, w);
+        load_rows(rk, a.k, kw, khead, lane_off, BUF_ALL, jb, c0, w);
+        const int gb = min(c0 + pr0, jb.T - 1);  // the wavefront's first row, clamped
         if constexpr (!GDN) {
-            const __bf16* g = static_cast<const __bf16*>(a.g) + hoff + c2;
+            const auto rs = buf_rsrc(static_cast<const __bf16*>(a.g) + ((jb.rowb + gb) * qkv + hoff), BUF_ALL);
 #pragma unroll
             for (int i = 0; i < RW; ++i)
-                rg[i] = *reinterpret_cast<const uint32_t*>(g + (jb.rowb + min(c0 + pr0 + i, jb.T - 1)) * qkv);
+                rg[i] = __builtin_amdgcn_raw_buffer_load_b32(
+                    rs, (int)lane_off, (int)((uint32_t)(min(c0 + pr0 + i, jb.T - 1) - gb) * (uint32_t)(qkv * 2)), 0);
         }
-        const size_t hr = (jb.rowb + min(c0 + pr0 + (lane & (RW - 1)), jb.T - 1)) * H + h;
-        rbeta = static_cast<const unsigned short*>(a.beta)[hr];
-        if constexpr (GDN) rgs = static_cast<const unsigned short*>(a.g)[hr];
+        // beta (and the GDN gate) of row pr0 + lane % RW
+        const int boff = (min(c0 + pr0 + (lane & (RW - 1)), jb.T - 1) - gb) * H * 2;
+        const size_t hr0 = (jb.rowb + gb) * H + h;
+        rbeta = __builtin_amdgcn_raw_buffer_load_b16(buf_rsrc(static_cast<const unsigned short*>(a.beta) + hr0, BUF_ALL),
+                                                     boff, 0, 0);
+        if constexpr (GDN)
+            rgs = __builtin_amdgcn_raw_buffer_load_b16(buf_rsrc(static_cast<const unsigned short*>(a.g) + hr0, BUF_ALL),
+                                                       boff, 0, 0);
     };
     load_chunk(0);
     // conv taps of the lane's q and k channels, parked in LDS for the whole run (each
@@ -294,13 +312,13 @@ __device__ __forceinline__ void c32_prepare(C32Lds<GDN>& sm, const MixerArgs& a,
         }
     };
 
-    for (int s = 0; s <= nch; ++s) {
+    // one step per chunk; the state group's last step (chunk nch - 1) follows the loop
+    for (int s = 0; s < nch; ++s) {
         const int c0 = s * C, n = min(C, jb.T - c0), par = s & 1;
-        const bool live = s < nch;
         // ---- phase 1: conv + SiLU of q and k, l2 norms, gate prefix ----
         float yq[RW][2], yk[RW][2];
         float gp[GDN ? 1 : RW][2];
-        if (live) {
+        {
             const bool from_hist = jb.ring_start && s == 0 && w == 0;
             {
                 float wt[2][KT];
@@ -350,7 +368,7 @@ __device__ __forceinline__ void c32_prepare(C32Lds<GDN>& sm, const MixerArgs& a,
         lds_barrier();  // B1
 
         // ---- phase 2: decay factors and operand tiles ----
-        if (live) {
+        {
             float nr[8];
             {
                 const f32x4v v0 = ld4f(&sm.nrm[w][0]), v1 = ld4f(&sm.nrm[w][4]);
@@ -362,60 +380,77 @@ __device__ __forceinline__ void c32_prepare(C32Lds<GDN>& sm, const MixerArgs& a,
             }
             const int pc = pchan(c2);
             if constexpr (!GDN) {
-                float off[2] = {0.0f, 0.0f}, tot[2] = {0.0f, 0.0f}, r1[2] = {0.0f, 0.0f};
+                // gate sums before this wavefront's rows (off), of rows 0..15 (r1) and of
+                // the chunk (tot); w is wave-uniform
+                float acc[2] = {0.0f, 0.0f}, off[2] = {0.0f, 0.0f}, r1[2] = {0.0f, 0.0f};
 #pragma unroll
                 for (int ww = 0; ww < NW; ++ww) {
+                    if (ww == w) {
+                        off[0] = acc[0];
+                        off[1] = acc[1];
+                    }
+                    if (ww == NW / 2) {
+                        r1[0] = acc[0];
+                        r1[1] = acc[1];
+                    }
                     const float2 s2 = *reinterpret_cast<const float2*>(&sm.gsum[ww][c2]);
-                    const float sv[2] = {s2.x, s2.y};
+                    acc[0] += s2.x;
+                    acc[1] += s2.y;
+                }
+                float er1[2];  // e^{R_1}
+#pragma unroll
+                for (int e = 0; e < 2; ++e) er1[e] = exp2_f(r1[e]);
+                if (w == 0) *reinterpret_cast<float2*>(&sm.ffn[par][c2]) = make_float2(exp2_f(acc[0]), exp2_f(acc[1]));
+                // Block a's rows: gamma = G - R_a; Q+ and K+ are the block-relative tiles
+                // times e^{R_a} (R_0 = 0, so block 0 stores them unscaled), and block 0
+                // also stores k e^{-gamma} e^{R_1}, the operand of the L and P block (1, 0).
+                auto tiles = [&](auto blk1c) {
+                    constexpr bool blk1 = decltype(blk1c)::value;
+                    float kd[2][RW], fl[2];  // fl: e^{G_l - R_a}
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) fl[e] = exp2_f(acc[e] - (blk1 ? r1[e] : 0.0f));
+#pragma unroll
+                    for (int r = 0; r < RW; ++r) {
+                        bf16x2 oqa, oqp, oka, okp, okb, okb1;
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) {
+                            const float gam = off[e] + gp[r][e] - (blk1 ? r1[e] : 0.0f);
+                            const float e1 = exp2_f(gam), e2 = exp2_f(-gam);
+                            const float qh = yq[r][e] * nr[r], kh = yk[r][e] * nr[RW + r];
+                            const float qa = qh * e1, ka = kh * e1, kbv = kh * e2;
+                            oqa[e] = (__bf16)qa;
+                            oka[e] = (__bf16)ka;
+                            okb[e] = (__bf16)kbv;
+                            if constexpr (blk1) {
+                                oqp[e] = (__bf16)(qa * er1[e]);
+                                okp[e] = (__bf16)(ka * er1[e]);
+                            } else {
+                                okb1[e] = (__bf16)(kbv * er1[e]);
+                            }
+                            kd[e][r] = kbv * fl[e];
+                        }
+                        const int row = pr0 + r;
+                        st2(&sm.qa[row][pc], oqa);
+                        st2(&sm.ka[row][pc], oka);
+                        st2(&sm.kb[row][pc], okb);
+                        if constexpr (blk1) {
+                            st2(&sm.qp[row][pc], oqp);
+                            st2(&sm.kp[row][pc], okp);
+                        } else {
+                            st2(&sm.qp[row][pc], oqa);
+                            st2(&sm.kp[row][pc], oka);
+                            st2(&sm.kb1[row][pc], okb1);
+                        }
+                    }
+                    // K_dec^T: the wavefront's 4 rows are contiguous in the permuted order
 #pragma unroll
                     for (int e = 0; e < 2; ++e) {
-                        if (ww < w) off[e] += sv[e];
-                        if (ww < NW / 2) r1[e] += sv[e];  // rows 0..15
-                        tot[e] += sv[e];
+                        const bf16x4 v4{(__bf16)kd[e][0], (__bf16)kd[e][1], (__bf16)kd[e][2], (__bf16)kd[e][3]};
+                        *reinterpret_cast<bf16x4*>(&sm.kdt[par][c2 + e][perm32(pr0)]) = v4;
                     }
-                }
-                const bool blk1 = w >= NW / 2;
-                float ra[2], fa[2], fl[2];
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    ra[e] = blk1 ? r1[e] : 0.0f;
-                    fa[e] = exp2_f(ra[e]);
-                    fl[e] = exp2_f(tot[e] - ra[e]);
-                }
-                if (w == 0) {
-                    *reinterpret_cast<float2*>(&sm.ffn[par][c2]) = make_float2(exp2_f(tot[0]), exp2_f(tot[1]));
-                    *reinterpret_cast<float2*>(&sm.fd10[pc]) = make_float2(exp2_f(r1[0]), exp2_f(r1[1]));
-                }
-                float kd[2][RW];
-#pragma unroll
-                for (int r = 0; r < RW; ++r) {
-                    bf16x2 oqa, oqp, oka, okp, okb;
-#pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        const float gam = off[e] + gp[r][e] - ra[e];
-                        const float e1 = exp2_f(gam), e2 = exp2_f(-gam);
-                        const float qh = yq[r][e] * nr[r], kh = yk[r][e] * nr[RW + r];
-                        const float qa = qh * e1, ka = kh * e1, kbv = kh * e2;
-                        oqa[e] = (__bf16)qa;
-                        oqp[e] = (__bf16)(qa * fa[e]);
-                        oka[e] = (__bf16)ka;
-                        okp[e] = (__bf16)(ka * fa[e]);
-                        okb[e] = (__bf16)kbv;
-                        kd[e][r] = kbv * fl[e];
-                    }
-                    const int row = pr0 + r;
-                    st2(&sm.qa[row][pc], oqa);
-                    st2(&sm.qp[row][pc], oqp);
-                    st2(&sm.ka[row][pc], oka);
-                    st2(&sm.kp[row][pc], okp);
-                    st2(&sm.kb[row][pc], okb);
-                }
-                // K_dec^T: the wavefront's 4 rows are contiguous in the permuted order
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const bf16x4 v4{(__bf16)kd[e][0], (__bf16)kd[e][1], (__bf16)kd[e][2], (__bf16)kd[e][3]};
-                    *reinterpret_cast<bf16x4*>(&sm.kdt[par][c2 + e][perm32(pr0)]) = v4;
-                }
+                };
+                if (w >= NW / 2) tiles(std::true_type{});
+                else tiles(std::false_type{});
             } else {
                 if (w == 0 && lane < C) {
                     float g = sm.gsum[0][lane];
@@ -448,29 +483,23 @@ __device__ __forceinline__ void c32_prepare(C32Lds<GDN>& sm, const MixerArgs& a,
 
         // ---- phase 3: L and P, one 16 x 16 block product per wavefront 0..5:
         // L(0,0), P(0,0), L(1,1), P(1,1), L(1,0), P(1,0) ----
-        if (live && w < 6) {
+        if (w < 6) {
             const bool doL = (w & 1) == 0;
             const int ab = w < 2 ? 0 : 1, bb = (w == 2 || w == 3) ? 1 : 0;  // row block, column block
             const int srow = 16 * ab + l16;
-            const __bf16* brow_p = GDN ? &sm.ka[16 * bb + l16][0] : &sm.kb[16 * bb + l16][0];
+            // the column operand: k^ (GDN); k^ e^{-gamma} of block bb, for block (1, 0) times e^{R_1}
+            const __bf16* brow_p = GDN ? &sm.ka[16 * bb + l16][0] : (w >= 4 ? &sm.kb1[l16][0] : &sm.kb[16 * bb + l16][0]);
             const __bf16* arow_p = doL ? &sm.ka[srow][0] : &sm.qa[srow][0];
-            f32x4v acc = zero4();
+            bf16x8 bo[4], ao[4];
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                const int i0 = 32 * kk + 8 * q4;
-                bf16x8 bk = ld8(brow_p + i0);
-                if constexpr (!GDN) {
-                    if (w >= 4) {  // block (1, 0): k e^{-gamma} of block 0 times e^{R_1}
-                        const f32x4v d0 = ld4f(&sm.fd10[i0]), d1 = ld4f(&sm.fd10[i0 + 4]);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            bk[e] = (__bf16)((float)bk[e] * d0[e]);
-                            bk[4 + e] = (__bf16)((float)bk[4 + e] * d1[e]);
-                        }
-                    }
-                }
-                acc = mfma_bf16(bk, ld8(arow_p + i0), acc);  // lane: X[srow][16 bb + 4 q4 + r]
+                bo[kk] = ld8(brow_p + 32 * kk + 8 * q4);
+                ao[kk] = ld8(arow_p + 32 * kk + 8 * q4);
             }
+            __builtin_amdgcn_sched_barrier(0);
+            f32x4v acc = zero4();
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) acc = mfma_bf16(bo[kk], ao[kk], acc);  // lane: X[srow][16 bb + 4 q4 + r]
             const int j0 = 16 * bb + 4 * q4;
             if (doL) {
                 const float bs = sm.beta[par][srow];
@@ -506,6 +535,10 @@ __device__ __forceinline__ void c32_prepare(C32Lds<GDN>& sm, const MixerArgs& a,
         }
         lds_barrier();  // B3
     }
+    // the state group's step for the last chunk
+    lds_barrier();
+    lds_barrier();
+    lds_barrier();
 }
 
 // ---------------------------------------------------------------------------------
@@ -526,7 +559,7 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
     f32x4v accS[8];
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt) accS[kt] = ld4f(&jb.s_in[(size_t)vcol * DK + 16 * kt + 4 * q4]);
-    // the epilogue's item: row tid / 16 (clamped), columns c8 .. c8 + 7
+    // the epilogue's item: row tid / 16, columns c8 .. c8 + 7
     const int c8 = (tid & 15) * 8, erow = tid >> 4;
     // the norm weight of the lane's columns and the conv taps of its v channels, parked
     // in LDS for the whole run (each lane reads back only what it wrote)
@@ -539,108 +572,169 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
 #pragma unroll
         for (int e = 0; e < 2; ++e) *reinterpret_cast<f32x4v*>(&sm.taps[2][c2 + e][0]) = f32x4v{wt[e][0], wt[e][1], wt[e][2], wt[e][3]};
     }
+    // The loop below waits for its prefetched v rows behind the three stores of the
+    // previous chunk's epilogue (vector-memory counters complete in order). Its entry
+    // must show the compiler the same order, or the merged count waits for everything:
+    // the state has landed before the first rows are requested (the empty asm reads it),
+    // and three stores into an empty range (no memory access) follow them.
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt) asm volatile("" ::"v"(accS[kt]));
+    const uint32_t lane_off = 4u * lane;  // the lane's two v channels, in bytes
+    const size_t vstride = (size_t)a.H * DK;
     uint32_t rv[NR];
-    load_rows(rv, jb.vsrc, jb.vstride, hoff + c2, jb, 0, w);
+    load_rows(rv, a.v, vstride, hoff, lane_off, jb.vbytes, jb, 0, w);
+    // the epilogue's z loads and out / o_core stores: row erow of the chunk, columns
+    // c8 .. c8 + 7; rows at or past the chunk's end fall outside the buffer's range (no
+    // access), and so does every store of a run without readout or of a null o_core
+    const uint32_t eoff = (uint32_t)(erow * qkv + c8) * 2u;
+    const uint32_t orow = (uint32_t)(qkv * 2);  // bytes of one bf16 row
+    const bool ocore = jb.readout && a.o_core;
+    {
+        const auto none = buf_rsrc(a.out, 0u);
+        const u32x4v zero{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 3; ++i) __builtin_amdgcn_raw_buffer_store_b128(zero, none, (int)eoff + 16 * i, 0, 0);
+    }
 
+    // step 0: the preparing group's first chunk
+    lds_barrier();
+    lds_barrier();
+    lds_barrier();
     bf16x8 zpre;
     f32x4v oacc[2], racc[2];  // [mt] O^T, K+ S
-    for (int s = 0; s <= nch; ++s) {
-        const int c = s - 1, par = c & 1;  // the chunk of the state work
-        const bool live = s >= 1;
-        const int c0 = c * C, n = min(C, jb.T - c0);
+    for (int c = 0; c < nch; ++c) {
+        const int par = c & 1, c0 = c * C, n = min(C, jb.T - c0);
         const size_t row0 = jb.rowb + c0;
         // ---- phase 1: v conv; diagonal blocks of T; Q+ S as O^T and K+ S ----
-        if (live) {
-            {
-                float yv[RW][2], wv[2][KT];
+        {
+            float yv[RW][2], wv[2][KT];
 #pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const f32x4v t = ld4f(&sm.taps[2][c2 + e][0]);
+            for (int e = 0; e < 2; ++e) {
+                const f32x4v t = ld4f(&sm.taps[2][c2 + e][0]);
 #pragma unroll
-                    for (int j = 0; j < KT; ++j) wv[e][j] = t[j];
-                }
-                const bool from_hist = jb.ring_start && c == 0 && w == 0;
-                conv_rows(rv, from_hist ? &sm.u.hist[2][0][c2] : nullptr, wv, yv);
-                // v^T: the wavefront's 4 rows are contiguous in the permuted order
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const bf16x4 v4{(__bf16)yv[0][e], (__bf16)yv[1][e], (__bf16)yv[2][e], (__bf16)yv[3][e]};
-                    *reinterpret_cast<bf16x4*>(&sm.vbt[c2 + e][perm32(RW * w)]) = v4;
-                }
+                for (int j = 0; j < KT; ++j) wv[e][j] = t[j];
             }
-            // this chunk's output gates (for phase 3), then the next chunk's v rows
-            asm volatile("" ::: "memory");
-            zpre = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.z) +
-                                                   (row0 + min(erow, n - 1)) * qkv + jb.h * DK + c8);
-            load_rows(rv, jb.vsrc, jb.vstride, hoff + c2, jb, c0 + C, w);
-            if (w < 2) {
-                // T_ww = (I + A_ww)^-1 by forward substitution in column (axpy) order, all
-                // 64 lanes: lane (col = lane / 4, rg = lane % 4) holds rows 4 rg .. 4 rg + 3 of
-                // column col; step cc takes the pivot x[cc] from its owner in the quad
-                // (DPP broadcast) and updates the rows below it. Column cc of A_ww is row cc
-                // of the transposed copy, read one step ahead.
-                const int col = lane >> 2, rg = lane & 3;
-                const float* at = sm.ltd[w];
-                float x[4];
+            const bool from_hist = jb.ring_start && c == 0 && w == 0;
+            conv_rows(rv, from_hist ? &sm.u.hist[2][0][c2] : nullptr, wv, yv);
+            // v^T: the wavefront's 4 rows are contiguous in the permuted order
 #pragma unroll
-                for (int i = 0; i < 4; ++i) x[i] = (4 * rg + i == col) ? 1.0f : 0.0f;
-                f32x4v nxt = ld4f(at + 4 * rg);
-#pragma unroll
-                for (int cc = 0; cc < 15; ++cc) {
-                    const f32x4v cur = nxt;
-                    if (cc + 1 < 15) nxt = ld4f(at + (cc + 1) * 16 + 4 * rg);
-                    const float piv = quad_bcast(x[cc & 3], cc >> 2);  // from the quad lane owning row cc
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float upd = fmaf(-cur[i], piv, x[i]);
-                        x[i] = 4 * rg + i > cc ? upd : x[i];
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sm.tdiag[w][4 * rg + i][col] = x[i];
+            for (int e = 0; e < 2; ++e) {
+                const bf16x4 v4{(__bf16)yv[0][e], (__bf16)yv[1][e], (__bf16)yv[2][e], (__bf16)yv[3][e]};
+                *reinterpret_cast<bf16x4*>(&sm.vbt[c2 + e][perm32(RW * w)]) = v4;
             }
-            // O^T (lane: O[16 mt + l16][16 w + 4 q4 + r]) and K+ S (lane: R[16 mt + 4 q4 + r]
-            // [vcol]); the state packed to bf16 is the operand with its keys in the
-            // accumulator (perm32) order
+        }
+        // this chunk's output gates (for phase 3), then the next chunk's v rows
+        asm volatile("" ::: "memory");
+        {
+            const auto zr = buf_rsrc(static_cast<const __bf16*>(a.z) + (row0 * qkv + hoff), (uint32_t)n * orow);
+            const auto zv = __builtin_amdgcn_raw_buffer_load_b128(zr, (int)eoff, 0, 0);
+            zpre = __builtin_bit_cast(bf16x8, zv);
+        }
+        load_rows(rv, a.v, vstride, hoff, lane_off, jb.vbytes, jb, c0 + C, w);
+        if (w == 2 || w == 3) {
+            // T_bb = (I + A_bb)^-1 (block bb = w - 2) by forward substitution in column
+            // (axpy) order, all 64 lanes: lane (col = lane / 4, rg = lane % 4) holds rows
+            // 4 rg .. 4 rg + 3 of column col; step cc takes the pivot x[cc] from its owner
+            // in the quad (DPP broadcast) and subtracts A[r][cc] x[cc] from every row r.
+            // A_bb is strictly lower triangular, so rows r <= cc subtract exact zeros.
+            // Column cc of A_bb is row cc of the transposed copy, read one step ahead.
+            const int col = lane >> 2, rg = lane & 3, bb = w - 2;
+            const float* at = sm.ltd[bb];
+            float x[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[i] = (4 * rg + i == col) ? 1.0f : 0.0f;
+            f32x4v nxt = ld4f(at + 4 * rg);
+#pragma unroll
+            for (int cc = 0; cc < 15; ++cc) {
+                const f32x4v cur = nxt;
+                if (cc + 1 < 15) nxt = ld4f(at + (cc + 1) * 16 + 4 * rg);
+                const float piv = quad_bcast(x[cc & 3], cc >> 2);  // from the quad lane owning row cc
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x[i] = fmaf(-cur[i], piv, x[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sm.tdiag[bb][4 * rg + i][col] = x[i];
+        }
+        // O^T (lane: O[16 mt + l16][16 w + 4 q4 + r]) and K+ S (lane: R[16 mt + 4 q4 + r]
+        // [vcol]); the state packed to bf16 is the operand with its keys in the
+        // accumulator (perm32) order
+        {
             bf16x8 sbop[4];
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) sbop[kk] = pack2(accS[2 * kk], accS[2 * kk + 1]);
             const __bf16* qsrc = GDN ? &sm.qa[0][0] : &sm.qp[0][0];
             const __bf16* ksrc = GDN ? &sm.ka[0][0] : &sm.kp[0][0];
+            // LDS operands in batches issued together (a scheduling fence keeps the
+            // reads ahead of their uses, so each batch costs one round trip)
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
                 oacc[mt] = zero4();
                 racc[mt] = zero4();
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const int off = (16 * mt + l16) * LDR + 32 * kk + 8 * q4;
-                    oacc[mt] = mfma_bf16(sbop[kk], ld8(qsrc + off), oacc[mt]);
-                    racc[mt] = mfma_bf16(ld8(ksrc + off), sbop[kk], racc[mt]);
+                for (int kh = 0; kh < 2; ++kh) {
+                    bf16x8 qf[2], kf[2];
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        const int off = (16 * mt + l16) * LDR + 32 * (2 * kh + i) + 8 * q4;
+                        qf[i] = ld8(qsrc + off);
+                        kf[i] = ld8(ksrc + off);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        oacc[mt] = mfma_bf16(sbop[2 * kh + i], qf[i], oacc[mt]);
+                        racc[mt] = mfma_bf16(kf[i], sbop[2 * kh + i], racc[mt]);
+                    }
+                }
+            }
+            // the decay of the state update, diag(e^{G_l}) S (the old S is packed above)
+            if constexpr (GDN) {
+                const float fg = exp2_f(sm.gcum[par][C - 1]);
+#pragma unroll
+                for (int kt = 0; kt < 8; ++kt) accS[kt] *= fg;
+            } else {
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh) {
+                    f32x4v d[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) d[i] = ld4f(&sm.ffn[par][16 * (4 * kh + i) + 4 * q4]);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) accS[4 * kh + i] *= d[i];
                 }
             }
         }
         lds_barrier();  // B1
 
         // ---- phase 2: T_10, Ub = T diag(beta) (V - K+ S), O, state update ----
-        if (live) {
+        {
             // T_10 = -T_11 A_10 T_00, formed transposed in registers: Y = A_10^T T_11^T
             // (slot k = 4 kk + q4), then T_10^T = T_00^T Y (negated) with Y fed back as
             // the B operand (slot k = 4 q4 + kk); the lane ends with T_10[l16][4 q4 + r].
+            float la[4], lb[4], lc[4];  // the operands first: one LDS round trip
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                la[kk] = sm.lf10[4 * kk + q4][l16];
+                lb[kk] = sm.tdiag[1][l16][4 * kk + q4];
+                lc[kk] = sm.tdiag[0][4 * q4 + kk][l16];
+            }
+            const f32x4v t00 = ld4f(&sm.tdiag[0][l16][4 * q4]), t11 = ld4f(&sm.tdiag[1][l16][4 * q4]);
+            const f32x4v be0 = ld4f(&sm.beta[par][4 * q4]), be1 = ld4f(&sm.beta[par][16 + 4 * q4]);
+            const bf16x8 vv = ld8(&sm.vbt[vcol][8 * q4]);
+            __builtin_amdgcn_sched_barrier(0);
             f32x4v y = zero4();
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) y = mfma_f32(sm.lf10[4 * kk + q4][l16], sm.tdiag[1][l16][4 * kk + q4], y);
+            for (int kk = 0; kk < 4; ++kk) y = mfma_f32(la[kk], lb[kk], y);
             f32x4v t10 = zero4();
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) t10 = mfma_f32(sm.tdiag[0][4 * q4 + kk][l16], y[kk], t10);
+            for (int kk = 0; kk < 4; ++kk) t10 = mfma_f32(lc[kk], y[kk], t10);
             // T as A fragments: rows 16 mt + l16, slots e < 4 -> column 4 q4 + e,
             // e >= 4 -> column 16 + 4 q4 + e - 4
-            const f32x4v t00 = ld4f(&sm.tdiag[0][l16][4 * q4]), t11 = ld4f(&sm.tdiag[1][l16][4 * q4]);
             const __bf16 z = (__bf16)0.0f;
             const bf16x8 ta0{(__bf16)t00[0], (__bf16)t00[1], (__bf16)t00[2], (__bf16)t00[3], z, z, z, z};
             const bf16x8 ta1{(__bf16)(-t10[0]), (__bf16)(-t10[1]), (__bf16)(-t10[2]), (__bf16)(-t10[3]),
                              (__bf16)t11[0], (__bf16)t11[1], (__bf16)t11[2], (__bf16)t11[3]};
 
-            const f32x4v be0 = ld4f(&sm.beta[par][4 * q4]), be1 = ld4f(&sm.beta[par][16 + 4 * q4]);
             f32x4v gr0 = f32x4v{1.0f, 1.0f, 1.0f, 1.0f}, gr1 = gr0;  // GDN: e^{G_j} of the lane's rows
             float gl = 0.0f;
             if constexpr (GDN) {
@@ -653,13 +747,10 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
                 }
             }
             bf16x8 xb;
-            {
-                const bf16x8 vv = ld8(&sm.vbt[vcol][8 * q4]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    xb[r] = (__bf16)(be0[r] * ((float)vv[r] - racc[0][r] * gr0[r]));
-                    xb[4 + r] = (__bf16)(be1[r] * ((float)vv[4 + r] - racc[1][r] * gr1[r]));
-                }
+            for (int r = 0; r < 4; ++r) {
+                xb[r] = (__bf16)(be0[r] * ((float)vv[r] - racc[0][r] * gr0[r]));
+                xb[4 + r] = (__bf16)(be1[r] * ((float)vv[4 + r] - racc[1][r] * gr1[r]));
             }
             // Ub[16 mt + 4 q4 + r][vcol]
             const f32x4v ub0 = mfma_bf16(ta0, xb, zero4()), ub1 = mfma_bf16(ta1, xb, zero4());
@@ -675,18 +766,24 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
                 ubs = pack2(u0, u1);
             }
             // O^T = (Q+ S)^T + Ub^T P^T (GDN: Q+ S is q S with rows times e^{G_s})
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                if constexpr (GDN) oacc[mt] *= exp2_f(sm.gcum[par][16 * mt + l16]);
-                oacc[mt] = mfma_bf16(ubo, ld8(&sm.pb[16 * mt + l16][8 * q4]), oacc[mt]);
+            {
+                const bf16x8 p0 = ld8(&sm.pb[l16][8 * q4]), p1 = ld8(&sm.pb[16 + l16][8 * q4]);
+                if constexpr (GDN) {
+                    oacc[0] *= exp2_f(sm.gcum[par][l16]);
+                    oacc[1] *= exp2_f(sm.gcum[par][16 + l16]);
+                }
+                oacc[0] = mfma_bf16(ubo, p0, oacc[0]);
+                oacc[1] = mfma_bf16(ubo, p1, oacc[1]);
             }
-            // S = diag(e^{G_l}) S + K_dec^T Ub
-            const float fg = GDN ? exp2_f(gl) : 0.0f;
+            // S = diag(e^{G_l}) S + K_dec^T Ub (the decay was applied in phase 1)
 #pragma unroll
-            for (int kt = 0; kt < 8; ++kt) {
-                const f32x4v dec = GDN ? f32x4v{fg, fg, fg, fg} : ld4f(&sm.ffn[par][16 * kt + 4 * q4]);
-                accS[kt] *= dec;
-                accS[kt] = mfma_bf16(ld8(&sm.kdt[par][16 * kt + l16][8 * q4]), ubs, accS[kt]);
+            for (int kh = 0; kh < 2; ++kh) {
+                bf16x8 kd[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) kd[i] = ld8(&sm.kdt[par][16 * (4 * kh + i) + l16][8 * q4]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) accS[4 * kh + i] = mfma_bf16(kd[i], ubs, accS[4 * kh + i]);
             }
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
@@ -694,11 +791,10 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
         }
         lds_barrier();  // B2
 
-        // ---- phase 3: gated RMSNorm and stores (rows past n store copies of row n-1) ----
-        if (live && jb.readout) {
-            const int r = min(erow, n - 1);  // the 16 lanes of a DPP row share r
+        // ---- phase 3: gated RMSNorm and stores ----
+        {
             float o8[8], w8[8];
-            const f32x4v oa = ld4f(&sm.u.ost[r][c8]), ob = ld4f(&sm.u.ost[r][c8 + 4]);
+            const f32x4v oa = ld4f(&sm.u.ost[erow][c8]), ob = ld4f(&sm.u.ost[erow][c8 + 4]);
             const f32x4v wa = ld4f(&sm.normw[c8]), wb = ld4f(&sm.normw[c8 + 4]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -713,9 +809,8 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) ss = fmaf(o8[e], o8[e], ss);
-            ss = sum_row16(ss);
+            ss = sum_row16(ss);  // the 16 lanes of a DPP row share erow
             const float inv = rsqrtf(fmaf(ss, 1.0f / DK, a.rms_eps));
-            const size_t off = (row0 + r) * qkv + hoff + c8;
             bf16x8 yb;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -723,12 +818,14 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
                 const float gate = GDN ? silu_f(zf) : sigmoid_f(zf);
                 yb[e] = (__bf16)(((o8[e] * inv) * w8[e]) * gate);
             }
-            st8(static_cast<__bf16*>(a.out) + off, yb);
-            if (a.o_core) {
-                float4* d = reinterpret_cast<float4*>(a.o_core + off);
-                d[0] = make_float4(o8[0], o8[1], o8[2], o8[3]);
-                d[1] = make_float4(o8[4], o8[5], o8[6], o8[7]);
-            }
+            const uint32_t rows = jb.readout ? (uint32_t)n : 0u;
+            const auto outr = buf_rsrc(static_cast<__bf16*>(a.out) + (row0 * qkv + hoff), rows * orow);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4v, yb), outr, (int)eoff, 0, 0);
+            const auto ocr = buf_rsrc(ocore ? a.o_core + (row0 * qkv + hoff) : nullptr, ocore ? (uint32_t)n * 2u * orow : 0u);
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4v{__float_as_uint(o8[0]), __float_as_uint(o8[1]), __float_as_uint(o8[2]), __float_as_uint(o8[3])},
+                                                   ocr, (int)(2u * eoff), 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4v{__float_as_uint(o8[4]), __float_as_uint(o8[5]), __float_as_uint(o8[6]), __float_as_uint(o8[7])},
+                                                   ocr, (int)(2u * eoff + 16u), 0, 0);
         }
         lds_barrier();  // B3
     }
@@ -765,8 +862,7 @@ __global__ __launch_bounds__(NT) void c32_kernel(MixerArgs a) {
     jb.lo = jb.ring_start ? 0 : -HALO;
     jb.readout = !SEG || sr.readout;
     const bool zero_v = SEG && sr.zero_v;
-    jb.vsrc = zero_v ? static_cast<const void*>(a.seg_ws) : a.v;
-    jb.vstride = zero_v ? 0 : (size_t)a.H * DK;
+    jb.vbytes = zero_v ? 0u : BUF_ALL;
     jb.s_in = SEG ? sr.s_in : a.state_in + (size_t)bh * DK * DK;
     jb.s_out = SEG ? sr.s_out : a.state_out + (size_t)bh * DK * DK;
 

@@ -15,6 +15,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 
 // MFMA 16x16x32 operand layout (lane l, q4 = l / 16, l16 = l % 16): an A fragment
 // holds A[l16][8 q4 .. 8 q4 + 7] of a 16x32 tile, a B fragment B[8 q4 .. + 7][l16] of a
@@ -39,6 +40,16 @@ __device__ __forceinline__ bf16x8 zero8() {
     const __bf16 z = (__bf16)0.0f;
     return bf16x8{z, z, z, z, z, z, z, z};
 }
+
+// Raw buffer resource over `bytes` bytes from p (gfx9 word 3: 32-bit data format, no
+// swizzle, no stride). Accesses at or past `bytes` do not touch memory: stores are
+// dropped and loads return zero. Loads and stores through it take a wave-uniform scalar
+// offset and a per-lane vector offset, so a row index that is the same across a
+// wavefront costs scalar arithmetic only.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t BUF_ALL = 0xffffffffu;  // no range limit (the caller keeps offsets in range)
 
 // Workgroup barrier that orders LDS only: it waits for this wave's LDS operations and
 // not for its outstanding global loads, so prefetched rows stay in flight across the
