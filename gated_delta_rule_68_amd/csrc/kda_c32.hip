@@ -21,10 +21,11 @@
 // E[s][j] = e^{G_s - G_j} taken on the 32 x 32 products, and the row factors of K+,
 // Q+ and K_dec are applied to the MFMA results instead of the operands.
 //
-// Work layout: wavefronts 0..7 (two per SIMD) prepare chunk c+1 while wavefronts 8..15
+// Work layout: wavefronts 8..15 (two per SIMD) prepare chunk c+1 while wavefronts 0..7
 // (two per SIMD) run chunk c's state-dependent work, so every SIMD holds VALU-heavy
-// and MFMA-heavy wavefronts at once, two of each to hide each other's latencies. A
-// step has three phases between workgroup barriers:
+// and MFMA-heavy wavefronts at once, two of each to hide each other's latencies. The
+// state group's work is the longer chain in every phase; it issues first (older
+// wavefronts, raised priority). A step has three phases between workgroup barriers:
 //   phase  preparing group (chunk c+1)             state group (chunk c)
 //   1      conv + SiLU of q, k, l2 norms, gates    v conv, diagonal blocks of T, Q+ S, K+ S
 //   2      decay factors, operand tiles            T_10, Ub, O, state update
@@ -53,7 +54,7 @@ namespace {
 
 constexpr int C = 32;            // rows per chunk
 constexpr int DK = CHUNK_DK;     // 128
-constexpr int NT = 1024;         // 16 wavefronts: 0..7 prepare, 8..15 carry the state
+constexpr int NT = 1024;         // 16 wavefronts: 0..7 carry the state, 8..15 prepare
 constexpr int GT = 512;          // threads of one group
 constexpr int NW = 8;            // wavefronts of one group
 constexpr int RW = C / NW;       // rows per preparing (and v conv) wavefront: 4
@@ -92,6 +93,7 @@ struct C32Lds {
     float lf10[16][LDT];           // A_10 = diag(beta) L, rows 16.., columns 0..15
     float ltd[2][16 * 16 + 4];     // A_aa transposed: [a][c * 16 + r] = A[16a + r][16a + c]
     float tdiag[2][16][LDT];       // T_aa (fp32), the state group's own
+    bf16x8 tfrag[2][64];           // T as the MFMA A fragments of a state wavefront's lanes
     float gsum[NW][DK];            // KDA: gate sums of each wavefront's rows; GDN: [0][r] row prefix, [1][w] totals
     float nrm[NW][8];              // 1 / ||row|| of the l2 norms, per preparing wavefront
     float taps[3][DK][KT];         // conv taps of the q, k, v channels (each lane reads back its own)
@@ -218,7 +220,7 @@ __device__ __forceinline__ void kda_gate_prefix(const uint32_t (&g)[RW], int row
 }
 
 // ---------------------------------------------------------------------------------
-// Wavefronts 0..7: the state-independent preparation of each chunk.
+// Wavefronts 8..15: the state-independent preparation of each chunk.
 // ---------------------------------------------------------------------------------
 template <bool GDN, bool ACT>
 __device__ __forceinline__ void c32_prepare(C32Lds<GDN>& sm, const MixerArgs& a, const C32Job& jb, int w,
@@ -542,7 +544,7 @@ __device__ __forceinline__ void c32_prepare(C32Lds<GDN>& sm, const MixerArgs& a,
 }
 
 // ---------------------------------------------------------------------------------
-// Wavefronts 8..15: the state; in step s the v conv and the state-dependent work of
+// Wavefronts 0..7: the state; in step s the v conv and the state-dependent work of
 // chunk s-1.
 // ---------------------------------------------------------------------------------
 template <bool GDN>
@@ -623,6 +625,68 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
                 *reinterpret_cast<bf16x4*>(&sm.vbt[c2 + e][perm32(RW * w)]) = v4;
             }
         }
+        if (w == 2) {
+            __builtin_amdgcn_s_setprio(3);  // the longest chain of the phase
+            // T_aa = (I + A_aa)^-1 for both diagonal blocks, the two independent chains
+            // interleaved: forward substitution in column (axpy) order, all 64 lanes; lane
+            // (col = lane / 4, rg = lane % 4) holds rows 4 rg .. 4 rg + 3 of column col.
+            // Step cc takes the pivot x[cc] from its owner in the quad (DPP broadcast) and
+            // subtracts A[r][cc] x[cc] from every row r. A_aa is strictly lower triangular,
+            // so rows r <= cc subtract exact zeros. Column cc of A_aa is row cc of the
+            // transposed copy, read one step ahead.
+            // this block's lane-derived LDS addresses are formed here, not held in
+            // registers across the loop (the opaque copy keeps them from being hoisted)
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            const int col = ln >> 2, rg = ln & 3, bq4 = ln >> 4, bl16 = ln & 15;
+            float x[2][4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[0][i] = x[1][i] = (4 * rg + i == col) ? 1.0f : 0.0f;
+            f32x4v nxt[2] = {ld4f(&sm.ltd[0][4 * rg]), ld4f(&sm.ltd[1][4 * rg])};
+#pragma unroll
+            for (int cc = 0; cc < 15; ++cc) {
+                const f32x4v cur[2] = {nxt[0], nxt[1]};
+                if (cc + 1 < 15) {
+                    nxt[0] = ld4f(&sm.ltd[0][(cc + 1) * 16 + 4 * rg]);
+                    nxt[1] = ld4f(&sm.ltd[1][(cc + 1) * 16 + 4 * rg]);
+                }
+#pragma unroll
+                for (int bb = 0; bb < 2; ++bb) {
+                    const float piv = quad_bcast(x[bb][cc & 3], cc >> 2);  // from the quad lane owning row cc
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) x[bb][i] = fmaf(-cur[bb][i], piv, x[bb][i]);
+                }
+            }
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sm.tdiag[bb][4 * rg + i][col] = x[bb][i];
+            lds_wave_sync();  // the reads below cross lanes of this wavefront
+            // T_10 = -T_11 A_10 T_00, formed transposed in registers: Y = A_10^T T_11^T
+            // (slot k = 4 kk + q4), then T_10^T = T_00^T Y (negated) with Y fed back as
+            // the B operand (slot k = 4 q4 + kk); the lane ends with T_10[l16][4 q4 + r].
+            float la[4], lb[4], lc[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                la[kk] = sm.lf10[4 * kk + bq4][bl16];
+                lb[kk] = sm.tdiag[1][bl16][4 * kk + bq4];
+                lc[kk] = sm.tdiag[0][4 * bq4 + kk][bl16];
+            }
+            const f32x4v t00 = ld4f(&sm.tdiag[0][bl16][4 * bq4]), t11 = ld4f(&sm.tdiag[1][bl16][4 * bq4]);
+            f32x4v y = zero4();
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) y = mfma_f32(la[kk], lb[kk], y);
+            f32x4v t10 = zero4();
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) t10 = mfma_f32(lc[kk], y[kk], t10);
+            // T as the A fragments of every state wavefront (lane: rows 16 mt + l16; slots
+            // e < 4 -> column 4 q4 + e, e >= 4 -> column 16 + 4 q4 + e - 4)
+            const __bf16 z = (__bf16)0.0f;
+            sm.tfrag[0][ln] = bf16x8{(__bf16)t00[0], (__bf16)t00[1], (__bf16)t00[2], (__bf16)t00[3], z, z, z, z};
+            sm.tfrag[1][ln] = bf16x8{(__bf16)(-t10[0]), (__bf16)(-t10[1]), (__bf16)(-t10[2]), (__bf16)(-t10[3]),
+                                       (__bf16)t11[0], (__bf16)t11[1], (__bf16)t11[2], (__bf16)t11[3]};
+            __builtin_amdgcn_s_setprio(2);
+        }
         // this chunk's output gates (for phase 3), then the next chunk's v rows
         asm volatile("" ::: "memory");
         {
@@ -631,30 +695,6 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
             zpre = __builtin_bit_cast(bf16x8, zv);
         }
         load_rows(rv, a.v, vstride, hoff, lane_off, jb.vbytes, jb, c0 + C, w);
-        if (w == 2 || w == 3) {
-            // T_bb = (I + A_bb)^-1 (block bb = w - 2) by forward substitution in column
-            // (axpy) order, all 64 lanes: lane (col = lane / 4, rg = lane % 4) holds rows
-            // 4 rg .. 4 rg + 3 of column col; step cc takes the pivot x[cc] from its owner
-            // in the quad (DPP broadcast) and subtracts A[r][cc] x[cc] from every row r.
-            // A_bb is strictly lower triangular, so rows r <= cc subtract exact zeros.
-            // Column cc of A_bb is row cc of the transposed copy, read one step ahead.
-            const int col = lane >> 2, rg = lane & 3, bb = w - 2;
-            const float* at = sm.ltd[bb];
-            float x[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) x[i] = (4 * rg + i == col) ? 1.0f : 0.0f;
-            f32x4v nxt = ld4f(at + 4 * rg);
-#pragma unroll
-            for (int cc = 0; cc < 15; ++cc) {
-                const f32x4v cur = nxt;
-                if (cc + 1 < 15) nxt = ld4f(at + (cc + 1) * 16 + 4 * rg);
-                const float piv = quad_bcast(x[cc & 3], cc >> 2);  // from the quad lane owning row cc
-#pragma unroll
-                for (int i = 0; i < 4; ++i) x[i] = fmaf(-cur[i], piv, x[i]);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sm.tdiag[bb][4 * rg + i][col] = x[i];
-        }
         // O^T (lane: O[16 mt + l16][16 w + 4 q4 + r]) and K+ S (lane: R[16 mt + 4 q4 + r]
         // [vcol]); the state packed to bf16 is the operand with its keys in the
         // accumulator (perm32) order
@@ -706,34 +746,12 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
         }
         lds_barrier();  // B1
 
-        // ---- phase 2: T_10, Ub = T diag(beta) (V - K+ S), O, state update ----
+        // ---- phase 2: Ub = T diag(beta) (V - K+ S), O, state update ----
         {
-            // T_10 = -T_11 A_10 T_00, formed transposed in registers: Y = A_10^T T_11^T
-            // (slot k = 4 kk + q4), then T_10^T = T_00^T Y (negated) with Y fed back as
-            // the B operand (slot k = 4 q4 + kk); the lane ends with T_10[l16][4 q4 + r].
-            float la[4], lb[4], lc[4];  // the operands first: one LDS round trip
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                la[kk] = sm.lf10[4 * kk + q4][l16];
-                lb[kk] = sm.tdiag[1][l16][4 * kk + q4];
-                lc[kk] = sm.tdiag[0][4 * q4 + kk][l16];
-            }
-            const f32x4v t00 = ld4f(&sm.tdiag[0][l16][4 * q4]), t11 = ld4f(&sm.tdiag[1][l16][4 * q4]);
+            const bf16x8 ta0 = sm.tfrag[0][lane], ta1 = sm.tfrag[1][lane];
             const f32x4v be0 = ld4f(&sm.beta[par][4 * q4]), be1 = ld4f(&sm.beta[par][16 + 4 * q4]);
             const bf16x8 vv = ld8(&sm.vbt[vcol][8 * q4]);
             __builtin_amdgcn_sched_barrier(0);
-            f32x4v y = zero4();
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) y = mfma_f32(la[kk], lb[kk], y);
-            f32x4v t10 = zero4();
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) t10 = mfma_f32(lc[kk], y[kk], t10);
-            // T as A fragments: rows 16 mt + l16, slots e < 4 -> column 4 q4 + e,
-            // e >= 4 -> column 16 + 4 q4 + e - 4
-            const __bf16 z = (__bf16)0.0f;
-            const bf16x8 ta0{(__bf16)t00[0], (__bf16)t00[1], (__bf16)t00[2], (__bf16)t00[3], z, z, z, z};
-            const bf16x8 ta1{(__bf16)(-t10[0]), (__bf16)(-t10[1]), (__bf16)(-t10[2]), (__bf16)(-t10[3]),
-                             (__bf16)t11[0], (__bf16)t11[1], (__bf16)t11[2], (__bf16)t11[3]};
 
             f32x4v gr0 = f32x4v{1.0f, 1.0f, 1.0f, 1.0f}, gr1 = gr0;  // GDN: e^{G_j} of the lane's rows
             float gl = 0.0f;
@@ -875,8 +893,15 @@ __global__ __launch_bounds__(NT) void c32_kernel(MixerArgs a) {
         for (int i = tid; i < DK * DK / 4; i += NT) dst[i] = src[i];
         return;  // uniform over the workgroup, before any barrier
     }
-    if (wave < NW) c32_prepare<GDN, ACT>(sm, a, jb, wave, lane);
-    else c32_state<GDN>(sm, a, jb, wave - NW, lane);
+    // The state group carries the critical path of every step, so it issues first: it
+    // holds the older wavefronts (the SIMD arbiter favours them) and a raised priority,
+    // and the preparing group fills the issue slots it leaves.
+    if (wave >= NW) {
+        c32_prepare<GDN, ACT>(sm, a, jb, wave - NW, lane);
+    } else {
+        __builtin_amdgcn_s_setprio(2);
+        c32_state<GDN>(sm, a, jb, wave, lane);
+    }
 }
 
 template <bool GDN, bool SEG>
