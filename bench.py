@@ -61,8 +61,9 @@ def prefill_bytes(cfg) -> int:
     return acts + state + ring + 3 * qkv * K * 4 + D * 4
 
 
-def chunk_flops(cfg, C=64) -> float:
-    """Dense-tile contraction FLOPs of the chunked form: 2(5CD + 3D^2) per token-head."""
+def chunk_flops(cfg, C=32) -> float:
+    """Dense-tile contraction FLOPs of the chunked form: 2(5CD + 3D^2) per token-head
+    (chunks of C = 32 rows: the kernel of every bf16 call with a conv of up to 4 taps)."""
     return 2.0 * (5 * C * cfg.D + 3 * cfg.D * cfg.D) * cfg.B * cfg.T * cfg.H
 
 
