@@ -102,6 +102,8 @@ struct C32Lds {
         float hist[3][HALO][DK];   // conv history before the sequence (first chunk)
         float ost[C][DK + 4];      // O staging for the norm
     } u;
+    float gpos[2][GDN ? C : 1];    // GDN: e^{G_j} per row
+    float gdec[2][GDN ? C : 1];    // GDN: e^{G_l - G_j} per row
 };
 
 __device__ __forceinline__ float lo_bf(uint32_t u) { return __uint_as_float(u << 16); }
@@ -460,6 +462,10 @@ __device__ __forceinline__ void c32_prepare(C32Lds<GDN>& sm, const MixerArgs& a,
                     for (int ww = 0; ww < NW - 1; ++ww)
                         if (ww < lane / RW) g += sm.gsum[1][ww];
                     sm.gcum[par][lane] = g;
+                    // the row factors of the state group, once per chunk
+                    const float gl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), C - 1));  // G_l
+                    sm.gpos[par][lane] = exp2_f(g);
+                    sm.gdec[par][lane] = exp2_f(gl - g);
                 }
                 float kk[2][RW];
 #pragma unroll
@@ -729,7 +735,7 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
             }
             // the decay of the state update, diag(e^{G_l}) S (the old S is packed above)
             if constexpr (GDN) {
-                const float fg = exp2_f(sm.gcum[par][C - 1]);
+                const float fg = sm.gpos[par][C - 1];  // e^{G_l}
 #pragma unroll
                 for (int kt = 0; kt < 8; ++kt) accS[kt] *= fg;
             } else {
@@ -754,15 +760,9 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
             __builtin_amdgcn_sched_barrier(0);
 
             f32x4v gr0 = f32x4v{1.0f, 1.0f, 1.0f, 1.0f}, gr1 = gr0;  // GDN: e^{G_j} of the lane's rows
-            float gl = 0.0f;
             if constexpr (GDN) {
-                const f32x4v g0 = ld4f(&sm.gcum[par][4 * q4]), g1 = ld4f(&sm.gcum[par][16 + 4 * q4]);
-                gl = sm.gcum[par][C - 1];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    gr0[r] = exp2_f(g0[r]);
-                    gr1[r] = exp2_f(g1[r]);
-                }
+                gr0 = ld4f(&sm.gpos[par][4 * q4]);
+                gr1 = ld4f(&sm.gpos[par][16 + 4 * q4]);
             }
             bf16x8 xb;
 #pragma unroll
@@ -775,20 +775,15 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
             const bf16x8 ubo = pack2(ub0, ub1);  // Ub as operand
             bf16x8 ubs = ubo;                    // for the state update (GDN: rows times e^{G_l - G_j})
             if constexpr (GDN) {
-                f32x4v u0, u1;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    u0[r] = ub0[r] * exp2_f(gl - sm.gcum[par][4 * q4 + r]);
-                    u1[r] = ub1[r] * exp2_f(gl - sm.gcum[par][16 + 4 * q4 + r]);
-                }
-                ubs = pack2(u0, u1);
+                const f32x4v d0 = ld4f(&sm.gdec[par][4 * q4]), d1 = ld4f(&sm.gdec[par][16 + 4 * q4]);
+                ubs = pack2(ub0 * d0, ub1 * d1);
             }
             // O^T = (Q+ S)^T + Ub^T P^T (GDN: Q+ S is q S with rows times e^{G_s})
             {
                 const bf16x8 p0 = ld8(&sm.pb[l16][8 * q4]), p1 = ld8(&sm.pb[16 + l16][8 * q4]);
                 if constexpr (GDN) {
-                    oacc[0] *= exp2_f(sm.gcum[par][l16]);
-                    oacc[1] *= exp2_f(sm.gcum[par][16 + l16]);
+                    oacc[0] *= sm.gpos[par][l16];
+                    oacc[1] *= sm.gpos[par][16 + l16];
                 }
                 oacc[0] = mfma_bf16(ubo, p0, oacc[0]);
                 oacc[1] = mfma_bf16(ubo, p1, oacc[1]);
