@@ -70,6 +70,11 @@ constexpr int LDT = 20;          // fp32 pitch of the 16 x 16 solve blocks
 // q4's 16-byte read at 8 q4 returns exactly the rows its accumulators hold.
 __device__ __forceinline__ int perm32(int k) { return ((k & 15) >> 2) * 8 + (k >> 4) * 4 + (k & 3); }
 __device__ __forceinline__ int pchan(int c) { return (c & ~31) | perm32(c & 31); }
+// Column of the [128][32] tiles (K_dec^T, v^T) as stored: the 16-byte block of
+// column col is XORed with bits 4-5 of the row, so the 8-byte stores of a wavefront
+// (rows two apart, one column block) spread over the LDS banks; a reader of 16 rows
+// r0 .. r0 + 15 applies one constant (r0 a multiple of 16).
+__device__ __forceinline__ int swz(int col, int row) { return col ^ (((row >> 4) & 3) << 3); }
 
 template <bool GDN>
 struct C32Lds {
@@ -91,12 +96,13 @@ struct C32Lds {
     __bf16 vbt[DK][LDJ];           // v^T (conv output, no beta)
     __bf16 pb[C][LDJ];             // P [s][j] (j permuted)
     float lf10[16][LDT];           // A_10 = diag(beta) L, rows 16.., columns 0..15
-    float ltd[2][16 * 16 + 4];     // A_aa transposed: [a][c * 16 + r] = A[16a + r][16a + c]
+    float ltd[2][16 * LDT];        // A_aa transposed: [a][c * LDT + r] = A[16a + r][16a + c]
     float tdiag[2][16][LDT];       // T_aa (fp32), the state group's own
     bf16x8 tfrag[2][64];           // T as the MFMA A fragments of a state wavefront's lanes
     float gsum[NW][DK];            // KDA: gate sums of each wavefront's rows; GDN: [0][r] row prefix, [1][w] totals
     float nrm[NW][8];              // 1 / ||row|| of the l2 norms, per preparing wavefront
-    float taps[3][DK][KT];         // conv taps of the q, k, v channels (each lane reads back its own)
+    float taps[3][2][64][KT];      // conv taps of the q, k, v planes: [plane][e][lane] for channel 2 lane + e
+                                   // (each lane reads back only its own, 16 bytes apart across lanes)
     float normw[DK];               // norm weight (written by the state group, read back by each lane)
     union {
         float hist[3][HALO][DK];   // conv history before the sequence (first chunk)
@@ -302,15 +308,15 @@ __device__ __forceinline__ void c32_prepare(C32Lds<GDN>& sm, const MixerArgs& a,
         float wt[2][KT];
         load_taps<KT, 2>(wt, a.conv_w, khead + c2, K);
 #pragma unroll
-        for (int e = 0; e < 2; ++e) *reinterpret_cast<f32x4v*>(&sm.taps[0][c2 + e][0]) = f32x4v{wt[e][0], wt[e][1], wt[e][2], wt[e][3]};
+        for (int e = 0; e < 2; ++e) *reinterpret_cast<f32x4v*>(&sm.taps[0][e][lane][0]) = f32x4v{wt[e][0], wt[e][1], wt[e][2], wt[e][3]};
         load_taps<KT, 2>(wt, a.conv_w, kw + khead + c2, K);
 #pragma unroll
-        for (int e = 0; e < 2; ++e) *reinterpret_cast<f32x4v*>(&sm.taps[1][c2 + e][0]) = f32x4v{wt[e][0], wt[e][1], wt[e][2], wt[e][3]};
+        for (int e = 0; e < 2; ++e) *reinterpret_cast<f32x4v*>(&sm.taps[1][e][lane][0]) = f32x4v{wt[e][0], wt[e][1], wt[e][2], wt[e][3]};
     }
     auto taps_of = [&](int pl, float (&wt)[2][KT]) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-            const f32x4v t = ld4f(&sm.taps[pl][c2 + e][0]);
+            const f32x4v t = ld4f(&sm.taps[pl][e][lane][0]);
 #pragma unroll
             for (int j = 0; j < KT; ++j) wt[e][j] = t[j];
         }
@@ -450,7 +456,7 @@ __device__ __forceinline__ void c32_prepare(C32Lds<GDN>& sm, const MixerArgs& a,
 #pragma unroll
                     for (int e = 0; e < 2; ++e) {
                         const bf16x4 v4{(__bf16)kd[e][0], (__bf16)kd[e][1], (__bf16)kd[e][2], (__bf16)kd[e][3]};
-                        *reinterpret_cast<bf16x4*>(&sm.kdt[par][c2 + e][perm32(pr0)]) = v4;
+                        *reinterpret_cast<bf16x4*>(&sm.kdt[par][c2 + e][swz(perm32(pr0), c2 + e)]) = v4;
                     }
                 };
                 if (w >= NW / 2) tiles(std::true_type{});
@@ -483,7 +489,7 @@ __device__ __forceinline__ void c32_prepare(C32Lds<GDN>& sm, const MixerArgs& a,
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
                     const bf16x4 v4{(__bf16)kk[e][0], (__bf16)kk[e][1], (__bf16)kk[e][2], (__bf16)kk[e][3]};
-                    *reinterpret_cast<bf16x4*>(&sm.kdt[par][c2 + e][perm32(pr0)]) = v4;
+                    *reinterpret_cast<bf16x4*>(&sm.kdt[par][c2 + e][swz(perm32(pr0), c2 + e)]) = v4;
                 }
             }
         }
@@ -521,7 +527,7 @@ __device__ __forceinline__ void c32_prepare(C32Lds<GDN>& sm, const MixerArgs& a,
                 }
                 if (ab == bb) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) sm.ltd[ab][(4 * q4 + r) * 16 + l16] = lv[r];
+                    for (int r = 0; r < 4; ++r) sm.ltd[ab][(4 * q4 + r) * LDT + l16] = lv[r];
                 } else {
                     *reinterpret_cast<f32x4v*>(&sm.lf10[l16][4 * q4]) = lv;
                 }
@@ -578,7 +584,7 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
         float wt[2][KT];
         load_taps<KT, 2>(wt, a.conv_w, 2 * kw + hoff + c2, K);
 #pragma unroll
-        for (int e = 0; e < 2; ++e) *reinterpret_cast<f32x4v*>(&sm.taps[2][c2 + e][0]) = f32x4v{wt[e][0], wt[e][1], wt[e][2], wt[e][3]};
+        for (int e = 0; e < 2; ++e) *reinterpret_cast<f32x4v*>(&sm.taps[2][e][lane][0]) = f32x4v{wt[e][0], wt[e][1], wt[e][2], wt[e][3]};
     }
     // The loop below waits for its prefetched v rows behind the three stores of the
     // previous chunk's epilogue (vector-memory counters complete in order). Its entry
@@ -618,7 +624,7 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
             float yv[RW][2], wv[2][KT];
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                const f32x4v t = ld4f(&sm.taps[2][c2 + e][0]);
+                const f32x4v t = ld4f(&sm.taps[2][e][lane][0]);
 #pragma unroll
                 for (int j = 0; j < KT; ++j) wv[e][j] = t[j];
             }
@@ -628,7 +634,7 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const bf16x4 v4{(__bf16)yv[0][e], (__bf16)yv[1][e], (__bf16)yv[2][e], (__bf16)yv[3][e]};
-                *reinterpret_cast<bf16x4*>(&sm.vbt[c2 + e][perm32(RW * w)]) = v4;
+                *reinterpret_cast<bf16x4*>(&sm.vbt[c2 + e][swz(perm32(RW * w), c2 + e)]) = v4;
             }
         }
         if (w == 2) {
@@ -653,8 +659,8 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
             for (int cc = 0; cc < 15; ++cc) {
                 const f32x4v cur[2] = {nxt[0], nxt[1]};
                 if (cc + 1 < 15) {
-                    nxt[0] = ld4f(&sm.ltd[0][(cc + 1) * 16 + 4 * rg]);
-                    nxt[1] = ld4f(&sm.ltd[1][(cc + 1) * 16 + 4 * rg]);
+                    nxt[0] = ld4f(&sm.ltd[0][(cc + 1) * LDT + 4 * rg]);
+                    nxt[1] = ld4f(&sm.ltd[1][(cc + 1) * LDT + 4 * rg]);
                 }
 #pragma unroll
                 for (int bb = 0; bb < 2; ++bb) {
@@ -756,7 +762,7 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
         {
             const bf16x8 ta0 = sm.tfrag[0][lane], ta1 = sm.tfrag[1][lane];
             const f32x4v be0 = ld4f(&sm.beta[par][4 * q4]), be1 = ld4f(&sm.beta[par][16 + 4 * q4]);
-            const bf16x8 vv = ld8(&sm.vbt[vcol][8 * q4]);
+            const bf16x8 vv = ld8(&sm.vbt[vcol][swz(8 * q4, vcol)]);
             __builtin_amdgcn_sched_barrier(0);
 
             f32x4v gr0 = f32x4v{1.0f, 1.0f, 1.0f, 1.0f}, gr1 = gr0;  // GDN: e^{G_j} of the lane's rows
@@ -793,7 +799,7 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
             for (int kh = 0; kh < 2; ++kh) {
                 bf16x8 kd[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) kd[i] = ld8(&sm.kdt[par][16 * (4 * kh + i) + l16][8 * q4]);
+                for (int i = 0; i < 4; ++i) kd[i] = ld8(&sm.kdt[par][16 * (4 * kh + i) + l16][swz(8 * q4, 16 * (4 * kh + i))]);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) accS[4 * kh + i] = mfma_bf16(kd[i], ubs, accS[4 * kh + i]);
