@@ -384,6 +384,34 @@ def _timed(fn, reps):
     return sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
 
 
+def _timed_graph(fn, nbuf, reps):
+    """Median time (ms) per call of fn(0) .. fn(nbuf - 1) captured in one HIP graph:
+    HIP events bracket each replay of the nbuf calls, and a call's time is a replay's
+    time / nbuf (the kernels plus the gaps between them), as for the decode step."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(nbuf):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(nbuf):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        g.replay()
+        b.record()
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) / nbuf for a, b in ev)[reps // 2]
+
+
 def _timed_pair(fa, fb, reps):
     """Median HIP-event times (ms) of fa(i) and fb(i), interleaved call by call (so that
     clock or cache drift affects both alike), after one untimed call of each."""
@@ -490,10 +518,11 @@ def run_gated_leg(reps: int = 50) -> dict:
 
 def run_gqa_leg(reps: int = 50) -> dict:
     """GDN with grouped heads: 32 value heads over 16 query / key heads, D=128, bf16.
-    The batched decode step (B=64, state in place, buffer sets cycled) and the chunked
-    prefill of the GDN workload (B=4, T=8192): HIP-event time of each call (the decode
-    includes the q / k ring roll launch that shared key heads need) and algorithmic
-    HBM bytes (q / k rows are Hk*D wide)."""
+    The batched decode step (B=64, state in place, buffer sets cycled), timed like the
+    decode step (a HIP graph of NBUF steps replayed, a replay's time / NBUF; the time of
+    each eager call between HIP events beside it), and the chunked prefill of the GDN
+    workload (B=4, T=8192, HIP-event time of each call); algorithmic HBM bytes (q / k
+    rows are Hk*D wide)."""
     import torch
 
     import gated_delta_rule_68_amd as kda
@@ -519,9 +548,11 @@ def run_gqa_leg(reps: int = 50) -> dict:
     B, H, D, K, kw, vw = cfg.B, cfg.H, cfg.D, cfg.K, cfg.kw, cfg.qkv
     nb = (2 * B * H * D * D * 4 + 2 * B * cfg.conv_rows * (K - 1) * 4
           + (2 * B * kw + 3 * B * vw + 2 * B * H) * 2 + cfg.conv_rows * K * 4 + D * 4)
-    ms = _timed(dec, reps)
+    eager_ms = _timed(dec, reps)
+    ms = _timed_graph(dec, NBUF, reps)
     rec["decode"] = {"workload": f"GDN decode B={B} H={H} Hk={cfg.hk} D={D} bf16", "ms": ms,
-                     "tokens_per_s": B / (ms * 1e-3), "hbm_gbs": nb / (ms * 1e-3) / 1e9,
+                     "time": f"HIP graph of {NBUF} steps replayed, a replay / {NBUF} (median)",
+                     "eager_ms": eager_ms, "tokens_per_s": B / (ms * 1e-3), "hbm_gbs": nb / (ms * 1e-3) / 1e9,
                      "hbm_frac": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": nb}
     del sets
     torch.cuda.empty_cache()

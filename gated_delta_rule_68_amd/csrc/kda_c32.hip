@@ -239,43 +239,6 @@ __device__ __forceinline__ void c32_prepare(C32Lds<GDN>& sm, const MixerArgs& a,
     const int nch = (jb.T + C - 1) / C;
     const int pr0 = RW * w;  // this wavefront's first row of a chunk
 
-    // gate-activation constants (read once, before the row loads)
-    float gm = 0.0f, gbias = 0.0f, k1 = 0.0f, lb2 = 0.0f, k0[2] = {0.0f, 0.0f};
-    if constexpr (GDN) {
-        if (a.gate_form != GATE_GIVEN) {
-            gm = gate_head_factor(a, h);
-            gbias = a.gate_bias[h];
-        }
-    }
-    if constexpr (ACT) {
-        gm = gate_head_factor(a, h);
-        lb2 = a.gate_lb * LOG2E;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const float bias = a.gate_bias[hoff + c2 + e];
-            if (a.gate_form == GATE_SIGMOID) gate_log2_consts<GATE_SIGMOID>(gm, bias, &k1, &k0[e]);
-            else gate_log2_consts<GATE_SOFTPLUS>(gm, bias, &k1, &k0[e]);
-        }
-    }
-
-    // conv history before the sequence start (the old ring; slot K-1-d is d rows back),
-    // oldest first; preparing wavefront 0 reads the q / k planes in its first chunk,
-    // state wavefront 0 the v plane (in the next step)
-    if (jb.ring_start && w == 0) {
-        const float* ring_b = a.ring + (size_t)jb.b * ring_rows(a) * (K - 1);
-#pragma unroll
-        for (int pl = 0; pl < 3; ++pl)
-#pragma unroll
-            for (int d = 1; d <= HALO; ++d)
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const size_t fr = plane_row(a, pl, h, c2 + e);
-                    const float x = ring_b[fr * (K - 1) + max(K - 1 - d, 0)];
-                    sm.u.hist[pl][HALO - d][c2 + e] = d <= K - 1 ? x : 0.0f;
-                }
-        lds_wave_sync();
-    }
-
     // raw rows of the first chunk; beta and the GDN gate stay raw bf16 bits until they
     // are used (converting them at the load would wait for every row load before them)
     uint32_t rq[NR], rk[NR], rg[GDN ? 1 : RW];
@@ -301,17 +264,62 @@ __device__ __forceinline__ void c32_prepare(C32Lds<GDN>& sm, const MixerArgs& a,
             rgs = __builtin_amdgcn_raw_buffer_load_b16(buf_rsrc(static_cast<const unsigned short*>(a.g) + hr0, BUF_ALL),
                                                        boff, 0, 0);
     };
+    // Every load of the prologue is requested before the first wait, so the first step
+    // starts after one memory round trip: the first chunk's rows, the conv taps of the
+    // lane's q and k channels (parked in LDS for the whole run, each lane reading back
+    // only what it wrote), the conv history before the sequence start (the old ring;
+    // slot K-1-d is d rows back, oldest first: preparing wavefront 0 convolves the q / k
+    // planes of the first chunk, state wavefront 0 the v plane in the next step) and the
+    // gate-activation constants.
     load_chunk(0);
-    // conv taps of the lane's q and k channels, parked in LDS for the whole run (each
-    // lane reads back only what it wrote)
-    {
-        float wt[2][KT];
-        load_taps<KT, 2>(wt, a.conv_w, khead + c2, K);
+    float wtq[2][KT], wtk[2][KT];
+    load_taps<KT, 2>(wtq, a.conv_w, khead + c2, K);
+    load_taps<KT, 2>(wtk, a.conv_w, kw + khead + c2, K);
+    const bool hist0 = jb.ring_start && w == 0;
+    float hv[3][HALO][2];
+    if (hist0) {
+        const float* ring_b = a.ring + (size_t)jb.b * ring_rows(a) * (K - 1);
 #pragma unroll
-        for (int e = 0; e < 2; ++e) *reinterpret_cast<f32x4v*>(&sm.taps[0][e][lane][0]) = f32x4v{wt[e][0], wt[e][1], wt[e][2], wt[e][3]};
-        load_taps<KT, 2>(wt, a.conv_w, kw + khead + c2, K);
+        for (int pl = 0; pl < 3; ++pl)
 #pragma unroll
-        for (int e = 0; e < 2; ++e) *reinterpret_cast<f32x4v*>(&sm.taps[1][e][lane][0]) = f32x4v{wt[e][0], wt[e][1], wt[e][2], wt[e][3]};
+            for (int d = 1; d <= HALO; ++d)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const size_t fr = plane_row(a, pl, h, c2 + e);
+                    const float x = ring_b[fr * (K - 1) + max(K - 1 - d, 0)];
+                    hv[pl][HALO - d][e] = d <= K - 1 ? x : 0.0f;
+                }
+    }
+    float gm = 0.0f, gbias = 0.0f, k1 = 0.0f, lb2 = 0.0f, k0[2] = {0.0f, 0.0f};
+    if constexpr (GDN) {
+        if (a.gate_form != GATE_GIVEN) {
+            gm = gate_head_factor(a, h);
+            gbias = a.gate_bias[h];
+        }
+    }
+    if constexpr (ACT) {
+        gm = gate_head_factor(a, h);
+        lb2 = a.gate_lb * LOG2E;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const float bias = a.gate_bias[hoff + c2 + e];
+            if (a.gate_form == GATE_SIGMOID) gate_log2_consts<GATE_SIGMOID>(gm, bias, &k1, &k0[e]);
+            else gate_log2_consts<GATE_SOFTPLUS>(gm, bias, &k1, &k0[e]);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        *reinterpret_cast<f32x4v*>(&sm.taps[0][e][lane][0]) = f32x4v{wtq[e][0], wtq[e][1], wtq[e][2], wtq[e][3]};
+        *reinterpret_cast<f32x4v*>(&sm.taps[1][e][lane][0]) = f32x4v{wtk[e][0], wtk[e][1], wtk[e][2], wtk[e][3]};
+    }
+    if (hist0) {
+#pragma unroll
+        for (int pl = 0; pl < 3; ++pl)
+#pragma unroll
+            for (int i = 0; i < HALO; ++i)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) sm.u.hist[pl][i][c2 + e] = hv[pl][i][e];
+        lds_wave_sync();
     }
     auto taps_of = [&](int pl, float (&wt)[2][KT]) {
 #pragma unroll
@@ -569,34 +577,34 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
     const int nch = (jb.T + C - 1) / C;
     const int vcol = 16 * w + l16;  // this lane's value column
 
-    // ---- state: accS[kt] holds keys 16 kt + 4 q4 .. +3 of value column vcol ----
-    f32x4v accS[8];
-#pragma unroll
-    for (int kt = 0; kt < 8; ++kt) accS[kt] = ld4f(&jb.s_in[(size_t)vcol * DK + 16 * kt + 4 * q4]);
     // the epilogue's item: row tid / 16, columns c8 .. c8 + 7
     const int c8 = (tid & 15) * 8, erow = tid >> 4;
-    // the norm weight of the lane's columns and the conv taps of its v channels, parked
-    // in LDS for the whole run (each lane reads back only what it wrote)
-    {
-        const f32x4v n0 = ld4f(&a.norm_w[c8]), n1 = ld4f(&a.norm_w[c8 + 4]);
-        *reinterpret_cast<f32x4v*>(&sm.normw[c8]) = n0;
-        *reinterpret_cast<f32x4v*>(&sm.normw[c8 + 4]) = n1;
-        float wt[2][KT];
-        load_taps<KT, 2>(wt, a.conv_w, 2 * kw + hoff + c2, K);
-#pragma unroll
-        for (int e = 0; e < 2; ++e) *reinterpret_cast<f32x4v*>(&sm.taps[2][e][lane][0]) = f32x4v{wt[e][0], wt[e][1], wt[e][2], wt[e][3]};
-    }
-    // The loop below waits for its prefetched v rows behind the three stores of the
-    // previous chunk's epilogue (vector-memory counters complete in order). Its entry
-    // must show the compiler the same order, or the merged count waits for everything:
-    // the state has landed before the first rows are requested (the empty asm reads it),
-    // and three stores into an empty range (no memory access) follow them.
-#pragma unroll
-    for (int kt = 0; kt < 8; ++kt) asm volatile("" ::"v"(accS[kt]));
+    // Every load of the prologue is requested before the first wait, so the run starts
+    // after one memory round trip: the first chunk's v rows, the norm weight and the
+    // conv taps of the lane's v channels (parked in LDS for the whole run, each lane
+    // reading back only what it wrote), then the state.
     const uint32_t lane_off = 4u * lane;  // the lane's two v channels, in bytes
     const size_t vstride = (size_t)a.H * DK;
     uint32_t rv[NR];
     load_rows(rv, a.v, vstride, hoff, lane_off, jb.vbytes, jb, 0, w);
+    const f32x4v n0 = ld4f(&a.norm_w[c8]), n1 = ld4f(&a.norm_w[c8 + 4]);
+    float wt[2][KT];
+    load_taps<KT, 2>(wt, a.conv_w, 2 * kw + hoff + c2, K);
+    // ---- state: accS[kt] holds keys 16 kt + 4 q4 .. +3 of value column vcol ----
+    f32x4v accS[8];
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt) accS[kt] = ld4f(&jb.s_in[(size_t)vcol * DK + 16 * kt + 4 * q4]);
+    // The loop below waits for its prefetched v rows behind the three stores of the
+    // previous chunk's epilogue (vector-memory counters complete in order). Its entry
+    // must show the compiler the same order, or the merged count waits for everything:
+    // the state has landed (the empty asm reads it, and so everything requested before
+    // it has too) and three stores into an empty range (no memory access) follow.
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt) asm volatile("" ::"v"(accS[kt]));
+    *reinterpret_cast<f32x4v*>(&sm.normw[c8]) = n0;
+    *reinterpret_cast<f32x4v*>(&sm.normw[c8 + 4]) = n1;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) *reinterpret_cast<f32x4v*>(&sm.taps[2][e][lane][0]) = f32x4v{wt[e][0], wt[e][1], wt[e][2], wt[e][3]};
     // the epilogue's z loads and out / o_core stores: row erow of the chunk, columns
     // c8 .. c8 + 7; rows at or past the chunk's end fall outside the buffer's range (no
     // access), and so does every store of a run without readout or of a null o_core
