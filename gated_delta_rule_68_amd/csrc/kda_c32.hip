@@ -149,6 +149,7 @@ struct C32Job {
     uint32_t vbytes;       // range of the v loads: 0 for the segmented arm's M runs (v = 0)
     const float* s_in;
     float* s_out;
+    int s_init;            // the entry state: 0 read from s_in, 1 zero, 2 identity
 };
 
 // Raw rows of one plane: a lane's two channels (one dword of bf16, `lane_off` bytes into
@@ -592,8 +593,16 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
     load_taps<KT, 2>(wt, a.conv_w, 2 * kw + hoff + c2, K);
     // ---- state: accS[kt] holds keys 16 kt + 4 q4 .. +3 of value column vcol ----
     f32x4v accS[8];
+    if (jb.s_init == 0) {
 #pragma unroll
-    for (int kt = 0; kt < 8; ++kt) accS[kt] = ld4f(&jb.s_in[(size_t)vcol * DK + 16 * kt + 4 * q4]);
+        for (int kt = 0; kt < 8; ++kt) accS[kt] = ld4f(&jb.s_in[(size_t)vcol * DK + 16 * kt + 4 * q4]);
+    } else {  // the segmented arm's runs from zero and from the identity: formed in place
+        const float one = jb.s_init == 2 ? 1.0f : 0.0f;
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) accS[kt][r] = 16 * kt + 4 * q4 + r == vcol ? one : 0.0f;
+    }
     // The loop below waits for its prefetched v rows behind the three stores of the
     // previous chunk's epilogue (vector-memory counters complete in order). Its entry
     // must show the compiler the same order, or the merged count waits for everything:
@@ -891,15 +900,25 @@ __global__ __launch_bounds__(NT) void c32_kernel(MixerArgs a) {
     const bool zero_v = SEG && sr.zero_v;
     jb.vbytes = zero_v ? 0u : BUF_ALL;
     jb.s_in = SEG ? sr.s_in : a.state_in + (size_t)bh * DK * DK;
+    jb.s_init = SEG ? sr.s_init : 0;
     jb.s_out = SEG ? sr.s_out : a.state_out + (size_t)bh * DK * DK;
 
     const int tid = threadIdx.x, lane = tid & 63;
     // wave-uniform: every row index built from it is scalar arithmetic
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    if (jb.T == 0) {  // an empty sequence of a packed batch: the state passes through
+    if (jb.T == 0) {  // an empty run: the state passes through
         const f32x4v* src = reinterpret_cast<const f32x4v*>(jb.s_in);
         f32x4v* dst = reinterpret_cast<f32x4v*>(jb.s_out);
-        for (int i = tid; i < DK * DK / 4; i += NT) dst[i] = src[i];
+        for (int i = tid; i < DK * DK / 4; i += NT) {
+            if (jb.s_init == 0) {
+                dst[i] = src[i];
+            } else {  // zero or identity ([value][key]: entry i covers keys 4 (i % 32) .. +3)
+                f32x4v x = zero4();
+#pragma unroll
+                for (int r = 0; r < 4; ++r) x[r] = jb.s_init == 2 && (4 * i + r) / DK == (4 * i + r) % DK ? 1.0f : 0.0f;
+                dst[i] = x;
+            }
+        }
         return;  // uniform over the workgroup, before any barrier
     }
     // The state group carries the critical path of every step, so it issues first: it

@@ -1272,12 +1272,15 @@ hipError_t seg_launch(MixerArgs a) {
     const SegLayout lay = seg_layout(P, a.H, DK, n);
     a.seg_ws = static_cast<float*>(a.ws);
     char* ws = static_cast<char*>(a.ws);
-    const size_t nzero = (lay.ident - lay.zero) / 4;
-    const size_t ninit = nzero > (size_t)DK * DK ? nzero : (size_t)DK * DK;
-    hipLaunchKernelGGL(seg_init_kernel, dim3((unsigned)((ninit + 255) / 256)), dim3(256), 0, a.stream,
-                       reinterpret_cast<float*>(ws + lay.zero), nzero, reinterpret_cast<float*>(ws + lay.ident));
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e = hipSuccess;
+    if (!chunked32_fits(a)) {  // the 32-row kernel forms the zero and identity states itself
+        const size_t nzero = (lay.ident - lay.zero) / 4;
+        const size_t ninit = nzero > (size_t)DK * DK ? nzero : (size_t)DK * DK;
+        hipLaunchKernelGGL(seg_init_kernel, dim3((unsigned)((ninit + 255) / 256)), dim3(256), 0, a.stream,
+                           reinterpret_cast<float*>(ws + lay.zero), nzero, reinterpret_cast<float*>(ws + lay.ident));
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     a.seg_pass = 1;
     const int mid = n >= 3 ? (n - 2) * P : 0;
     e = seg_pass<BF, GDN>(a, P + 16 * ((mid + 7) / 8));

@@ -165,6 +165,7 @@ struct SegRun {
     const float* s_in;
     float* s_out;
     bool zero_v, readout;
+    int s_init;  // the entry state: 0 read from s_in, 1 zero, 2 identity (s_in holds it too)
 };
 
 // Pass 1: blocks [0, P) run segment 0 of pair b (dispatched first: they are the
@@ -181,6 +182,7 @@ __device__ __forceinline__ bool seg_run(const MixerArgs& a, SegRun* r) {
     const int d = blockIdx.x;
     r->zero_v = false;
     r->readout = true;
+    r->s_init = 0;
     if (a.seg_pass == 1) {
         if (d < P) {
             r->pair = d;
@@ -198,6 +200,7 @@ __device__ __forceinline__ bool seg_run(const MixerArgs& a, SegRun* r) {
         r->len = L;
         r->readout = false;
         r->zero_v = kind == 1;
+        r->s_init = kind ? 2 : 1;
         r->s_in = reinterpret_cast<const float*>(ws + (kind ? lay.ident : lay.zero));
         r->s_out = kind ? sl.M(sg, p) : sl.B(sg, p);
         return true;
