@@ -929,6 +929,25 @@ __global__ __launch_bounds__(NT) void c32_kernel(MixerArgs a) {
     } else {
         __builtin_amdgcn_s_setprio(2);
         c32_state<GDN>(sm, a, jb, wave, lane);
+        // The segmented arm's last segment writes the new conv ring (the last K-1 input
+        // rows, T >= K-1 there): only pass 1 read the old one, and it has finished. The
+        // value head's v rows here; a key head's q / k rows by its first value head only.
+        if constexpr (SEG) {
+            if (seg_ring_fused(a) && sr.readout && sr.ro > 0 && sr.ro + sr.len == a.T) {
+                const int K = a.K;
+                const size_t kw = (size_t)a.Hk * DK, vw = (size_t)a.H * DK;
+                const int nrow = (jb.h < a.Hk ? 3 : 1) * DK;  // v rows, then q and k rows
+                float* ring_b = a.ring + (size_t)jb.b * ring_rows(a) * (K - 1);
+                const size_t rlast = jb.rowb - sr.ro + a.T;  // one past the sequence's last row
+                for (int i = tid; i < nrow; i += GT) {
+                    const int pl = i < DK ? 2 : i / DK - 1, ch = i % DK;
+                    const void* x = pl == 0 ? a.q : (pl == 1 ? a.k : a.v);
+                    const size_t xw = pl == 2 ? vw : kw, xc = (size_t)(pl == 2 ? jb.h : jb.h % a.Hk) * DK + ch;
+                    float* row = ring_b + plane_row(a, pl, jb.h, ch) * (K - 1);
+                    for (int d = 1; d <= K - 1; ++d) row[K - 1 - d] = ld_act<true>(x, (rlast - d) * xw + xc);
+                }
+            }
+        }
     }
 }
 

@@ -1200,6 +1200,34 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(MixerArgs a) {
     __shared__ __align__(16) float sc[DK][SCAN_LD];  // the current entry state [k][column]
     const int t = threadIdx.x, lane = t & 63, w = t >> 6, q4 = lane >> 4, l16 = lane & 15;
     const size_t col0 = (size_t)cb * SCAN_COLS;
+    // result tile (rb, cc): keys 32 w + 16 rb + 4 q4 + r, column col0 + 16 cc + l16
+    auto tile = [&](float* blkp, int rb, int cc) {
+        return blkp + (col0 + 16 * cc + l16) * DK + 32 * w + 16 * rb + 4 * q4;
+    };
+    // The wavefront's A operands of one step, M[32 w + 16 rb + l16][k = 4 k4 + q4], all
+    // requested at once (one memory round trip per step, not one per few k slices); the
+    // next step's M_s and B_s are requested as soon as the current ones are consumed.
+    float mreg[2][DK / 4];
+    auto load_m = [&](int s) {
+        const float* m = M(s) + 32 * w + l16;
+#pragma unroll
+        for (int k4 = 0; k4 < DK / 4; ++k4) {
+            const size_t kr = (size_t)(4 * k4 + q4) * DK;
+            mreg[0][k4] = m[kr];
+            mreg[1][k4] = m[kr + 16];
+        }
+    };
+    f32x4v acc[2][2];
+    auto load_b = [&](int s) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) acc[rb][cc] = ld4f(tile(Bs(s), rb, cc));
+    };
+    if (n >= 3) {
+        load_m(1);
+        load_b(1);
+    }
     {  // S_1 columns col0 .. +31 into LDS: thread t reads keys 16 (t % 8) .. +15 of column t / 8
         const int j = t / 8, k0 = (t % 8) * 16;
         const float* src = S(1) + (col0 + j) * DK + k0;
@@ -1212,28 +1240,17 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(MixerArgs a) {
             sc[k0 + 4 * v + 3][j] = x4.w;
         }
     }
-    // result tile (rb, cc): keys 32 w + 16 rb + 4 q4 + r, column col0 + 16 cc + l16
-    auto tile = [&](float* blkp, int rb, int cc) {
-        return blkp + (col0 + 16 * cc + l16) * DK + 32 * w + 16 * rb + 4 * q4;
-    };
     for (int s = 1; s <= n - 2; ++s) {
         __syncthreads();
-        const float* m = M(s) + 32 * w + l16;
-        f32x4v acc[2][2];
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc) acc[rb][cc] = ld4f(tile(Bs(s), rb, cc));
-#pragma unroll 8
-        for (int k4 = 0; k4 < DK; k4 += 4) {
-            const size_t kr = (size_t)(k4 + q4) * DK;
-            const float a0 = m[kr], a1 = m[kr + 16];  // M[32w + l16][k], M[32w + 16 + l16][k]
-            const float b0 = sc[k4 + q4][l16], b1 = sc[k4 + q4][16 + l16];
-            acc[0][0] = mfma_f32(a0, b0, acc[0][0]);
-            acc[0][1] = mfma_f32(a0, b1, acc[0][1]);
-            acc[1][0] = mfma_f32(a1, b0, acc[1][0]);
-            acc[1][1] = mfma_f32(a1, b1, acc[1][1]);
+        for (int k4 = 0; k4 < DK / 4; ++k4) {
+            const float b0 = sc[4 * k4 + q4][l16], b1 = sc[4 * k4 + q4][16 + l16];
+            acc[0][0] = mfma_f32(mreg[0][k4], b0, acc[0][0]);
+            acc[0][1] = mfma_f32(mreg[0][k4], b1, acc[0][1]);
+            acc[1][0] = mfma_f32(mreg[1][k4], b0, acc[1][0]);
+            acc[1][1] = mfma_f32(mreg[1][k4], b1, acc[1][1]);
         }
+        if (s < n - 2) load_m(s + 1);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -1246,6 +1263,7 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(MixerArgs a) {
             for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) sc[32 * w + 16 * rb + 4 * q4 + r][16 * cc + l16] = acc[rb][cc][r];
+        if (s < n - 2) load_b(s + 1);
     }
 }
 
@@ -1295,7 +1313,7 @@ hipError_t seg_launch(MixerArgs a) {
         e = seg_pass<BF, GDN>(a, (n - 1) * P);
         if (e != hipSuccess) return e;
     }
-    return launch_ring_roll(a, false);
+    return seg_ring_fused(a) ? hipSuccess : launch_ring_roll(a, false);
 }
 
 }  // namespace

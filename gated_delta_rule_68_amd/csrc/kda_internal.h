@@ -152,6 +152,14 @@ __host__ __device__ inline size_t plane_row(const MixerArgs& a, int plane, int h
     const size_t kw = (size_t)a.Hk * a.D;
     return plane < 2 ? plane * kw + (size_t)(h % a.Hk) * a.D + ch : 2 * kw + (size_t)h * a.D + ch;
 }
+// Whether the segmented arm's last segment writes the new conv ring itself, with no ring
+// roll launch: the 32-row chunk kernel runs the arm (bf16, D = 128, K <= 4), the call
+// has at least K-1 rows (the new ring is then input rows only) and at least two
+// segments (the old ring's readers, the segment-0 runs of pass 1, have all finished when
+// pass 3 writes it).
+__host__ __device__ inline bool seg_ring_fused(const MixerArgs& a) {
+    return a.bf16 && a.D == 128 && a.K <= 4 && a.T >= a.K - 1 && a.seg_n >= 2 && !a.cu_seqlens;
+}
 // Ring rows (= conv-weight rows) of one sequence.
 __host__ __device__ inline size_t ring_rows(const MixerArgs& a) { return (size_t)(2 * a.Hk + a.H) * a.D; }
 

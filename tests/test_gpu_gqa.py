@@ -15,7 +15,7 @@ from oracle import gqa
 from tests.gpu_util import DEV, RMS_EPS, TOL, assert_bitwise, inputs_for, run_gpu, scale_of
 
 pytestmark = pytest.mark.gpu
-SEQ, CHK = kda.KDA_MODE_SEQUENTIAL, kda.KDA_MODE_CHUNKED
+SEQ, CHK, SEG = kda.KDA_MODE_SEQUENTIAL, kda.KDA_MODE_CHUNKED, kda.KDA_MODE_SEGMENTED
 
 
 def _print(*a):
@@ -83,9 +83,12 @@ GROUPS = [(8, 4), (8, 2)]
 
 
 @pytest.mark.parametrize("H,Hk", GROUPS, ids=["g2", "g4"])
-@pytest.mark.parametrize("mode,T,B", [(SEQ, 9, 2), (SEQ, 70, 1), (CHK, 150, 2)],
-                         ids=["fused", "split", "chunked"])
+@pytest.mark.parametrize("mode,T,B", [(SEQ, 9, 2), (SEQ, 70, 1), (CHK, 150, 2), (SEG, 300, 2)],
+                         ids=["fused", "split", "chunked", "segmented"])
 def test_gqa_prefill_vs_oracle(H, Hk, mode, T, B):
+    """Every arm against the grouped-head oracle. The segmented case runs several
+    segments: its last segment writes the ring in the kernel, the q / k rows of a key head
+    by one of its value heads (the ring is compared exactly)."""
     cfg = CONFIGS["gdn_prefill"].with_(B=B, T=T, H=H, Hk=Hk, random_init=True)
     inp, dev = inputs_for(cfg)
     arm = kda.prefill_arm(cfg.B, cfg.T, cfg.H, cfg.D, kda.KDA_DTYPE_BF16, mode, gdn=True)
