@@ -110,6 +110,7 @@ struct C32Lds {
     } u;
     float gpos[2][GDN ? C : 1];    // GDN: e^{G_j} per row
     float gdec[2][GDN ? C : 1];    // GDN: e^{G_l - G_j} per row
+    uint32_t tcnt;                 // diagonal blocks T_00 finished (state wavefront 2)
 };
 
 __device__ __forceinline__ float lo_bf(uint32_t u) { return __uint_as_float(u << 16); }
@@ -627,6 +628,7 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
         for (int i = 0; i < 3; ++i) __builtin_amdgcn_raw_buffer_store_b128(zero, none, (int)eoff + 16 * i, 0, 0);
     }
 
+    if (tid == 0) sm.tcnt = 0u;  // before the barriers below; counted per chunk from here
     // step 0: the preparing group's first chunk
     lds_barrier();
     lds_barrier();
@@ -654,10 +656,10 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
                 *reinterpret_cast<bf16x4*>(&sm.vbt[c2 + e][swz(perm32(RW * w), c2 + e)]) = v4;
             }
         }
-        if (w == 2) {
+        if (w == 2 || w == 3) {
             __builtin_amdgcn_s_setprio(3);  // the longest chain of the phase
-            // T_aa = (I + A_aa)^-1 for both diagonal blocks, the two independent chains
-            // interleaved: forward substitution in column (axpy) order, all 64 lanes; lane
+            // T_aa = (I + A_aa)^-1, block a = w - 2 on this wavefront (the two blocks on two
+            // SIMDs): forward substitution in column (axpy) order, all 64 lanes; lane
             // (col = lane / 4, rg = lane % 4) holds rows 4 rg .. 4 rg + 3 of column col.
             // Step cc takes the pivot x[cc] from its owner in the quad (DPP broadcast) and
             // subtracts A[r][cc] x[cc] from every row r. A_aa is strictly lower triangular,
@@ -668,52 +670,60 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
             int ln = lane;
             asm volatile("" : "+v"(ln));
             const int col = ln >> 2, rg = ln & 3, bq4 = ln >> 4, bl16 = ln & 15;
-            float x[2][4];
+            const int bb = w - 2;
+            float x[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) x[0][i] = x[1][i] = (4 * rg + i == col) ? 1.0f : 0.0f;
-            f32x4v nxt[2] = {ld4f(&sm.ltd[0][4 * rg]), ld4f(&sm.ltd[1][4 * rg])};
+            for (int i = 0; i < 4; ++i) x[i] = (4 * rg + i == col) ? 1.0f : 0.0f;
+            f32x4v nxt = ld4f(&sm.ltd[bb][4 * rg]);
 #pragma unroll
             for (int cc = 0; cc < 15; ++cc) {
-                const f32x4v cur[2] = {nxt[0], nxt[1]};
-                if (cc + 1 < 15) {
-                    nxt[0] = ld4f(&sm.ltd[0][(cc + 1) * LDT + 4 * rg]);
-                    nxt[1] = ld4f(&sm.ltd[1][(cc + 1) * LDT + 4 * rg]);
-                }
+                const f32x4v cur = nxt;
+                if (cc + 1 < 15) nxt = ld4f(&sm.ltd[bb][(cc + 1) * LDT + 4 * rg]);
+                const float piv = quad_bcast(x[cc & 3], cc >> 2);  // from the quad lane owning row cc
 #pragma unroll
-                for (int bb = 0; bb < 2; ++bb) {
-                    const float piv = quad_bcast(x[bb][cc & 3], cc >> 2);  // from the quad lane owning row cc
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) x[bb][i] = fmaf(-cur[bb][i], piv, x[bb][i]);
-                }
+                for (int i = 0; i < 4; ++i) x[i] = fmaf(-cur[i], piv, x[i]);
             }
 #pragma unroll
-            for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sm.tdiag[bb][4 * rg + i][col] = x[bb][i];
+            for (int i = 0; i < 4; ++i) sm.tdiag[bb][4 * rg + i][col] = x[i];
             lds_wave_sync();  // the reads below cross lanes of this wavefront
-            // T_10 = -T_11 A_10 T_00, formed transposed in registers: Y = A_10^T T_11^T
-            // (slot k = 4 kk + q4), then T_10^T = T_00^T Y (negated) with Y fed back as
-            // the B operand (slot k = 4 q4 + kk); the lane ends with T_10[l16][4 q4 + r].
-            float la[4], lb[4], lc[4];
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                la[kk] = sm.lf10[4 * kk + bq4][bl16];
-                lb[kk] = sm.tdiag[1][bl16][4 * kk + bq4];
-                lc[kk] = sm.tdiag[0][4 * bq4 + kk][bl16];
-            }
-            const f32x4v t00 = ld4f(&sm.tdiag[0][bl16][4 * bq4]), t11 = ld4f(&sm.tdiag[1][bl16][4 * bq4]);
-            f32x4v y = zero4();
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) y = mfma_f32(la[kk], lb[kk], y);
-            f32x4v t10 = zero4();
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) t10 = mfma_f32(lc[kk], y[kk], t10);
             // T as the A fragments of every state wavefront (lane: rows 16 mt + l16; slots
             // e < 4 -> column 4 q4 + e, e >= 4 -> column 16 + 4 q4 + e - 4)
             const __bf16 z = (__bf16)0.0f;
-            sm.tfrag[0][ln] = bf16x8{(__bf16)t00[0], (__bf16)t00[1], (__bf16)t00[2], (__bf16)t00[3], z, z, z, z};
-            sm.tfrag[1][ln] = bf16x8{(__bf16)(-t10[0]), (__bf16)(-t10[1]), (__bf16)(-t10[2]), (__bf16)(-t10[3]),
-                                       (__bf16)t11[0], (__bf16)t11[1], (__bf16)t11[2], (__bf16)t11[3]};
+            if (bb == 0) {
+                const f32x4v t00 = ld4f(&sm.tdiag[0][bl16][4 * bq4]);
+                sm.tfrag[0][ln] = bf16x8{(__bf16)t00[0], (__bf16)t00[1], (__bf16)t00[2], (__bf16)t00[3], z, z, z, z};
+                // T_00 is in place (the wait above): wavefront 3 may read it
+                if (ln == 0) __hip_atomic_fetch_add(&sm.tcnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            } else {
+                // T_10 = -T_11 A_10 T_00, formed transposed in registers: Y = A_10^T T_11^T
+                // (slot k = 4 kk + q4), then T_10^T = T_00^T Y (negated) with Y fed back
+                // as the B operand (slot k = 4 q4 + kk); the lane ends with T_10[l16][4 q4 + r].
+                float la[4], lb[4], lc[4];
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    la[kk] = sm.lf10[4 * kk + bq4][bl16];
+                    lb[kk] = sm.tdiag[1][bl16][4 * kk + bq4];
+                }
+                const f32x4v t11 = ld4f(&sm.tdiag[1][bl16][4 * bq4]);
+                f32x4v y = zero4();
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) y = mfma_f32(la[kk], lb[kk], y);
+                // T_00 of this chunk from wavefront 2: its count of finished blocks
+                // reaches c + 1 (bounded wait; the two solves take the same time)
+                for (int it = 0; it < (1 << 16); ++it) {
+                    const uint32_t done = __builtin_amdgcn_readfirstlane(*static_cast<volatile uint32_t*>(&sm.tcnt));
+                    if (done > (uint32_t)c) break;
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                asm volatile("" ::: "memory");
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) lc[kk] = sm.tdiag[0][4 * bq4 + kk][bl16];
+                f32x4v t10 = zero4();
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) t10 = mfma_f32(lc[kk], y[kk], t10);
+                sm.tfrag[1][ln] = bf16x8{(__bf16)(-t10[0]), (__bf16)(-t10[1]), (__bf16)(-t10[2]), (__bf16)(-t10[3]),
+                                           (__bf16)t11[0], (__bf16)t11[1], (__bf16)t11[2], (__bf16)t11[3]};
+            }
             __builtin_amdgcn_s_setprio(2);
         }
         // this chunk's output gates (for phase 3), then the next chunk's v rows
