@@ -24,12 +24,12 @@
 // Work layout: wavefronts 8..15 (two per SIMD) prepare chunk c+1 while wavefronts 0..7
 // (two per SIMD) run chunk c's state-dependent work, so every SIMD holds VALU-heavy
 // and MFMA-heavy wavefronts at once, two of each to hide each other's latencies. The
-// state group's work is the longer chain in every phase; it issues first (older
-// wavefronts, raised priority). A step has three phases between workgroup barriers:
+// state group carries the longer chains; it issues first (older wavefronts, raised
+// priority). A step has two phases between workgroup barriers:
 //   phase  preparing group (chunk c+1)             state group (chunk c)
-//   1      conv + SiLU of q, k, l2 norms, gates    v conv, diagonal blocks of T, Q+ S, K+ S
-//   2      decay factors, operand tiles            T_10, Ub, O, state update
-//   3      L and P (MFMA)                          gated RMSNorm and stores
+//   1      conv + SiLU of q, k, l2 norms, gates    v conv, L and P (MFMA), T, Q+ S, K+ S
+//   2      decay factors, operand tiles            Ub, O, state update; gated RMSNorm
+//                                                  and stores of chunk c-1
 // The preparing wavefront w convolves rows 4w .. 4w+3, two channels per lane, straight
 // from registers: each lane reads its channels of its rows and of the 3 rows before
 // them (the conv history; the old ring before the sequence start), so no raw rows are
@@ -78,8 +78,8 @@ __device__ __forceinline__ int swz(int col, int row) { return col ^ (((row >> 4)
 
 template <bool GDN>
 struct C32Lds {
-    // written in phase 2 by the preparing group, read in phase 3 (and qp / kp by the
-    // state group in the next step's phase 1)
+    // written in phase 2 by the preparing group, read by the state group in the next
+    // step's phase 1
     alignas(16) __bf16 qa[C][LDR];             // KDA: q^ e^{gamma}; GDN: q^ (channels permuted)
     __bf16 ka[C][LDR];             // KDA: k^ e^{gamma}; GDN: k^
     __bf16 kb[GDN ? 1 : C][LDR];   // k^ e^{-gamma}
@@ -91,8 +91,8 @@ struct C32Lds {
     float beta[2][C];
     float ffn[2][GDN ? 4 : DK];    // KDA: e^{G_l} per key
     float gcum[2][C];              // GDN: G per row (log2 units)
-    // single-buffered (written in phase 3, read by the state group in the next step;
-    // v^T written and read by the state group within one step)
+    // the state group's own: L and P written in phase 1 (P read in phase 2), v^T
+    // written in phase 1 and read in phase 2
     __bf16 vbt[DK][LDJ];           // v^T (conv output, no beta)
     __bf16 pb[C][LDJ];             // P [s][j] (j permuted)
     float lf10[16][LDT];           // A_10 = diag(beta) L, rows 16.., columns 0..15
@@ -106,7 +106,7 @@ struct C32Lds {
     float normw[DK];               // norm weight (written by the state group, read back by each lane)
     union {
         float hist[3][HALO][DK];   // conv history before the sequence (first chunk)
-        float ost[C][DK + 4];      // O staging for the norm
+        float ost[2][C][DK + 4];   // O staging for the norm, by chunk parity
     } u;
     float gpos[2][GDN ? C : 1];    // GDN: e^{G_j} per row
     float gdec[2][GDN ? C : 1];    // GDN: e^{G_l - G_j} per row
@@ -505,64 +505,71 @@ __device__ __forceinline__ void c32_prepare(C32Lds<GDN>& sm, const MixerArgs& a,
         }
         lds_barrier();  // B2
 
-        // ---- phase 3: L and P, one 16 x 16 block product per wavefront 0..5:
-        // L(0,0), P(0,0), L(1,1), P(1,1), L(1,0), P(1,0) ----
-        if (w < 6) {
-            const bool doL = (w & 1) == 0;
-            const int ab = w < 2 ? 0 : 1, bb = (w == 2 || w == 3) ? 1 : 0;  // row block, column block
-            const int srow = 16 * ab + l16;
-            // the column operand: k^ (GDN); k^ e^{-gamma} of block bb, for block (1, 0) times e^{R_1}
-            const __bf16* brow_p = GDN ? &sm.ka[16 * bb + l16][0] : (w >= 4 ? &sm.kb1[l16][0] : &sm.kb[16 * bb + l16][0]);
-            const __bf16* arow_p = doL ? &sm.ka[srow][0] : &sm.qa[srow][0];
-            bf16x8 bo[4], ao[4];
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                bo[kk] = ld8(brow_p + 32 * kk + 8 * q4);
-                ao[kk] = ld8(arow_p + 32 * kk + 8 * q4);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            f32x4v acc = zero4();
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) acc = mfma_bf16(bo[kk], ao[kk], acc);  // lane: X[srow][16 bb + 4 q4 + r]
-            const int j0 = 16 * bb + 4 * q4;
-            if (doL) {
-                const float bs = sm.beta[par][srow];
-                f32x4v lv;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = j0 + r;
-                    float ef = 1.0f;
-                    if constexpr (GDN) ef = exp2_f(fminf(sm.gcum[par][srow] - sm.gcum[par][j], 0.0f));
-                    lv[r] = j < srow ? bs * (acc[r] * ef) : 0.0f;
-                }
-                if (ab == bb) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) sm.ltd[ab][(4 * q4 + r) * LDT + l16] = lv[r];
-                } else {
-                    *reinterpret_cast<f32x4v*>(&sm.lf10[l16][4 * q4]) = lv;
-                }
-            } else {
-                bf16x4 pv;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = j0 + r;
-                    float ef = 1.0f;
-                    if constexpr (GDN) ef = exp2_f(fminf(sm.gcum[par][srow] - sm.gcum[par][j], 0.0f));
-                    pv[r] = (__bf16)(j <= srow ? acc[r] * ef : 0.0f);
-                }
-                *reinterpret_cast<bf16x4*>(&sm.pb[srow][perm32(j0)]) = pv;
-                if (w == 1) {  // P block (0, 1) above the diagonal
-                    const __bf16 z = (__bf16)0.0f;
-                    *reinterpret_cast<bf16x4*>(&sm.pb[srow][perm32(16 + 4 * q4)]) = bf16x4{z, z, z, z};
-                }
-            }
-        }
-        lds_barrier();  // B3
     }
     // the state group's step for the last chunk
     lds_barrier();
     lds_barrier();
-    lds_barrier();
+}
+
+// One 16 x 16 block of L = diag(beta) strictly-lower(K+ K-^T) or P = lower(Q+ K-^T) of a
+// chunk (KDA: block-relative operands; GDN: k^ and q^ with the scalar decay applied per
+// entry), jw: 0 L(0,0), 1 P(0,0), 2 L(1,1), 3 P(1,1), 4 L(1,0), 5 P(1,0). L blocks go
+// to the solve's arrays (diagonal blocks transposed), P blocks to pb (its block (0,1)
+// above the diagonal stays zero from the start of the run).
+template <bool GDN>
+__device__ __forceinline__ void lp_block(C32Lds<GDN>& sm, int jw, int par, int lane) {
+    // the lane-derived LDS addresses are formed here, not held in registers across the
+    // caller's loop (the opaque copy keeps them from being hoisted)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int q4 = ln >> 4, l16 = ln & 15;
+    const bool doL = (jw & 1) == 0;
+    const int ab = jw < 2 ? 0 : 1, bb = (jw == 2 || jw == 3) ? 1 : 0;  // row block, column block
+    const int srow = 16 * ab + l16;
+    // the column operand: k^ (GDN); k^ e^{-gamma} of block bb, for block (1, 0) times e^{R_1}
+    const __bf16* brow_p = GDN ? &sm.ka[16 * bb + l16][0] : (jw >= 4 ? &sm.kb1[l16][0] : &sm.kb[16 * bb + l16][0]);
+    const __bf16* arow_p = doL ? &sm.ka[srow][0] : &sm.qa[srow][0];
+    f32x4v acc = zero4();  // lane: X[srow][16 bb + 4 q4 + r]
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {  // operands in two batches of two (registers are scarce here)
+        bf16x8 bo[2], ao[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            bo[i] = ld8(brow_p + 32 * (2 * kh + i) + 8 * q4);
+            ao[i] = ld8(arow_p + 32 * (2 * kh + i) + 8 * q4);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) acc = mfma_bf16(bo[i], ao[i], acc);
+    }
+    const int j0 = 16 * bb + 4 * q4;
+    if (doL) {
+        const float bs = sm.beta[par][srow];
+        f32x4v lv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j = j0 + r;
+            float ef = 1.0f;
+            if constexpr (GDN) ef = exp2_f(fminf(sm.gcum[par][srow] - sm.gcum[par][j], 0.0f));
+            lv[r] = j < srow ? bs * (acc[r] * ef) : 0.0f;
+        }
+        if (ab == bb) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sm.ltd[ab][(4 * q4 + r) * LDT + l16] = lv[r];
+        } else {
+            *reinterpret_cast<f32x4v*>(&sm.lf10[l16][4 * q4]) = lv;
+        }
+    } else {
+        bf16x4 pv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j = j0 + r;
+            float ef = 1.0f;
+            if constexpr (GDN) ef = exp2_f(fminf(sm.gcum[par][srow] - sm.gcum[par][j], 0.0f));
+            pv[r] = (__bf16)(j <= srow ? acc[r] * ef : 0.0f);
+        }
+        *reinterpret_cast<bf16x4*>(&sm.pb[srow][perm32(j0)]) = pv;
+    }
 }
 
 // ---------------------------------------------------------------------------------
@@ -605,10 +612,11 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
             for (int r = 0; r < 4; ++r) accS[kt][r] = 16 * kt + 4 * q4 + r == vcol ? one : 0.0f;
     }
     // The loop below waits for its prefetched v rows behind the three stores of the
-    // previous chunk's epilogue (vector-memory counters complete in order). Its entry
-    // must show the compiler the same order, or the merged count waits for everything:
-    // the state has landed (the empty asm reads it, and so everything requested before
-    // it has too) and three stores into an empty range (no memory access) follow.
+    // previous chunk's epilogue and one gate load (vector-memory counters complete in
+    // order). Its entry must show the compiler the same order, or the merged count waits
+    // for everything: the state has landed (the empty asm reads it, and so everything
+    // requested before it has too), then three stores and a load from an empty range (no
+    // memory access) follow.
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt) asm volatile("" ::"v"(accS[kt]));
     *reinterpret_cast<f32x4v*>(&sm.normw[c8]) = n0;
@@ -621,20 +629,65 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
     const uint32_t eoff = (uint32_t)(erow * qkv + c8) * 2u;
     const uint32_t orow = (uint32_t)(qkv * 2);  // bytes of one bf16 row
     const bool ocore = jb.readout && a.o_core;
+    bf16x8 zold;  // the output gates of the chunk whose epilogue runs next
     {
         const auto none = buf_rsrc(a.out, 0u);
         const u32x4v zero{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int i = 0; i < 3; ++i) __builtin_amdgcn_raw_buffer_store_b128(zero, none, (int)eoff + 16 * i, 0, 0);
+        // and, as each step ends with its gate load, one from an empty range (zeros)
+        zold = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(buf_rsrc(a.z, 0u), (int)eoff, 0, 0));
     }
 
     if (tid == 0) sm.tcnt = 0u;  // before the barriers below; counted per chunk from here
+    if (tid < 64) {  // P block (0, 1), above the diagonal: zero for the whole run
+        const __bf16 z = (__bf16)0.0f;
+        *reinterpret_cast<bf16x4*>(&sm.pb[tid & 15][perm32(16 + 4 * (tid >> 4))]) = bf16x4{z, z, z, z};
+    }
     // step 0: the preparing group's first chunk
     lds_barrier();
     lds_barrier();
-    lds_barrier();
-    bf16x8 zpre;
     f32x4v oacc[2], racc[2];  // [mt] O^T, K+ S
+    // Gated RMSNorm and stores of chunk ce (ce < 0: nothing stored) from its O staging;
+    // rows at or past the chunk's end fall outside the buffer's range (no access), and
+    // so does every store of a run without readout or of a null o_core.
+    auto epilogue = [&](int ce, const bf16x8& zg) {
+        const int ne = ce >= 0 ? min(C, jb.T - ce * C) : 0;
+        const size_t row0e = jb.rowb + (size_t)max(ce, 0) * C;
+        float o8[8], w8[8];
+        const f32x4v oa = ld4f(&sm.u.ost[ce & 1][erow][c8]), ob = ld4f(&sm.u.ost[ce & 1][erow][c8 + 4]);
+        const f32x4v wa = ld4f(&sm.normw[c8]), wb = ld4f(&sm.normw[c8 + 4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            w8[e] = wa[e];
+            w8[4 + e] = wb[e];
+        }
+        float ss = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            o8[e] = oa[e];
+            o8[4 + e] = ob[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = fmaf(o8[e], o8[e], ss);
+        ss = sum_row16(ss);  // the 16 lanes of a DPP row share erow
+        const float inv = rsqrtf(fmaf(ss, 1.0f / DK, a.rms_eps));
+        bf16x8 yb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float zf = (float)zg[e];
+            const float gate = GDN ? silu_f(zf) : sigmoid_f(zf);
+            yb[e] = (__bf16)(((o8[e] * inv) * w8[e]) * gate);
+        }
+        const uint32_t rows = jb.readout ? (uint32_t)ne : 0u;
+        const auto outr = buf_rsrc(static_cast<__bf16*>(a.out) + (row0e * qkv + hoff), rows * orow);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4v, yb), outr, (int)eoff, 0, 0);
+        const auto ocr = buf_rsrc(ocore ? a.o_core + (row0e * qkv + hoff) : nullptr, ocore ? (uint32_t)ne * 2u * orow : 0u);
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4v{__float_as_uint(o8[0]), __float_as_uint(o8[1]), __float_as_uint(o8[2]), __float_as_uint(o8[3])},
+                                               ocr, (int)(2u * eoff), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4v{__float_as_uint(o8[4]), __float_as_uint(o8[5]), __float_as_uint(o8[6]), __float_as_uint(o8[7])},
+                                               ocr, (int)(2u * eoff + 16u), 0, 0);
+    };
     for (int c = 0; c < nch; ++c) {
         const int par = c & 1, c0 = c * C, n = min(C, jb.T - c0);
         const size_t row0 = jb.rowb + c0;
@@ -658,6 +711,14 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
         }
         if (w == 2 || w == 3) {
             __builtin_amdgcn_s_setprio(3);  // the longest chain of the phase
+            // the diagonal block of L this wavefront inverts (wavefront 3 also L(1,0))
+            if (w == 2) {
+                lp_block<GDN>(sm, 0, par, lane);
+            } else {
+                lp_block<GDN>(sm, 2, par, lane);
+                lp_block<GDN>(sm, 4, par, lane);
+            }
+            lds_wave_sync();  // read back across lanes below
             // T_aa = (I + A_aa)^-1, block a = w - 2 on this wavefront (the two blocks on two
             // SIMDs): forward substitution in column (axpy) order, all 64 lanes; lane
             // (col = lane / 4, rg = lane % 4) holds rows 4 rg .. 4 rg + 3 of column col.
@@ -725,14 +786,11 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
                                            (__bf16)t11[0], (__bf16)t11[1], (__bf16)t11[2], (__bf16)t11[3]};
             }
             __builtin_amdgcn_s_setprio(2);
+        } else if (w == 0 || w == 1 || w == 5) {  // the blocks of P (read in phase 2)
+            lp_block<GDN>(sm, w == 0 ? 1 : (w == 1 ? 3 : 5), par, lane);
         }
-        // this chunk's output gates (for phase 3), then the next chunk's v rows
+        // the next chunk's v rows
         asm volatile("" ::: "memory");
-        {
-            const auto zr = buf_rsrc(static_cast<const __bf16*>(a.z) + (row0 * qkv + hoff), (uint32_t)n * orow);
-            const auto zv = __builtin_amdgcn_raw_buffer_load_b128(zr, (int)eoff, 0, 0);
-            zpre = __builtin_bit_cast(bf16x8, zv);
-        }
         load_rows(rv, a.v, vstride, hoff, lane_off, jb.vbytes, jb, c0 + C, w);
         // O^T (lane: O[16 mt + l16][16 w + 4 q4 + r]) and K+ S (lane: R[16 mt + 4 q4 + r]
         // [vcol]); the state packed to bf16 is the operand with its keys in the
@@ -831,50 +889,20 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
 #pragma unroll
                 for (int i = 0; i < 4; ++i) accS[4 * kh + i] = mfma_bf16(kd[i], ubs, accS[4 * kh + i]);
             }
+            // the previous chunk's epilogue while the matrix cores run the products above,
+            // then this chunk's output gates (used by the next step's epilogue)
+            epilogue(c - 1, zold);
+            {
+                const auto zr = buf_rsrc(static_cast<const __bf16*>(a.z) + (row0 * qkv + hoff), (uint32_t)n * orow);
+                zold = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(zr, (int)eoff, 0, 0));
+            }
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
-                *reinterpret_cast<f32x4v*>(&sm.u.ost[16 * mt + l16][16 * w + 4 * q4]) = a.scale * oacc[mt];
+                *reinterpret_cast<f32x4v*>(&sm.u.ost[par][16 * mt + l16][16 * w + 4 * q4]) = a.scale * oacc[mt];
         }
         lds_barrier();  // B2
-
-        // ---- phase 3: gated RMSNorm and stores ----
-        {
-            float o8[8], w8[8];
-            const f32x4v oa = ld4f(&sm.u.ost[erow][c8]), ob = ld4f(&sm.u.ost[erow][c8 + 4]);
-            const f32x4v wa = ld4f(&sm.normw[c8]), wb = ld4f(&sm.normw[c8 + 4]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                w8[e] = wa[e];
-                w8[4 + e] = wb[e];
-            }
-            float ss = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                o8[e] = oa[e];
-                o8[4 + e] = ob[e];
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ss = fmaf(o8[e], o8[e], ss);
-            ss = sum_row16(ss);  // the 16 lanes of a DPP row share erow
-            const float inv = rsqrtf(fmaf(ss, 1.0f / DK, a.rms_eps));
-            bf16x8 yb;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float zf = (float)zpre[e];
-                const float gate = GDN ? silu_f(zf) : sigmoid_f(zf);
-                yb[e] = (__bf16)(((o8[e] * inv) * w8[e]) * gate);
-            }
-            const uint32_t rows = jb.readout ? (uint32_t)n : 0u;
-            const auto outr = buf_rsrc(static_cast<__bf16*>(a.out) + (row0 * qkv + hoff), rows * orow);
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4v, yb), outr, (int)eoff, 0, 0);
-            const auto ocr = buf_rsrc(ocore ? a.o_core + (row0 * qkv + hoff) : nullptr, ocore ? (uint32_t)n * 2u * orow : 0u);
-            __builtin_amdgcn_raw_buffer_store_b128(u32x4v{__float_as_uint(o8[0]), __float_as_uint(o8[1]), __float_as_uint(o8[2]), __float_as_uint(o8[3])},
-                                                   ocr, (int)(2u * eoff), 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b128(u32x4v{__float_as_uint(o8[4]), __float_as_uint(o8[5]), __float_as_uint(o8[6]), __float_as_uint(o8[7])},
-                                                   ocr, (int)(2u * eoff + 16u), 0, 0);
-        }
-        lds_barrier();  // B3
     }
+    epilogue(nch - 1, zold);
 
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt)
