@@ -173,7 +173,11 @@ __device__ __forceinline__ void load_rows(uint32_t (&x)[NR], const void* base, s
 
 // conv + SiLU of the lane's two channels over its RW rows: the window starts from the
 // halo rows (or, for the first chunk of a run at the sequence start, from the ring
-// copy in LDS: `hist` non-null); wt[e][KT-1] multiplies the current input.
+// copy in LDS: `hist` non-null); wt[e][KT-1] multiplies the current input. With L2U
+// the taps carry a factor log2(e), so the conv output u is x log2(e) and the result
+// u sigmoid(x) = log2(e) SiLU(x) (for rows that are l2-normalised next, where the
+// factor cancels).
+template <bool L2U = false>
 __device__ __forceinline__ void conv_rows(const uint32_t (&x)[NR], const float* hist, const float (&wt)[2][KT],
                                           float (&y)[RW][2]) {
     float win[HALO][2];
@@ -198,7 +202,8 @@ __device__ __forceinline__ void conv_rows(const uint32_t (&x)[NR], const float* 
 #pragma unroll
             for (int t = 0; t < HALO; ++t) acc = fmaf(wt[e][t], win[t][e], acc);
             acc = fmaf(wt[e][KT - 1], xc[e], acc);
-            y[r][e] = silu_f(acc);
+            if constexpr (L2U) y[r][e] = acc * __builtin_amdgcn_rcpf(1.0f + exp2_f(-acc));
+            else y[r][e] = silu_f(acc);
         }
 #pragma unroll
         for (int t = 0; t < HALO - 1; ++t)
@@ -309,10 +314,14 @@ __device__ __forceinline__ void c32_prepare(C32Lds<GDN>& sm, const MixerArgs& a,
             else gate_log2_consts<GATE_SOFTPLUS>(gm, bias, &k1, &k0[e]);
         }
     }
+    // the q / k taps times log2(e): their conv outputs are l2-normalised, so the factor
+    // leaves the normalised rows as they are and saves a multiply in each SiLU
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-        *reinterpret_cast<f32x4v*>(&sm.taps[0][e][lane][0]) = f32x4v{wtq[e][0], wtq[e][1], wtq[e][2], wtq[e][3]};
-        *reinterpret_cast<f32x4v*>(&sm.taps[1][e][lane][0]) = f32x4v{wtk[e][0], wtk[e][1], wtk[e][2], wtk[e][3]};
+        *reinterpret_cast<f32x4v*>(&sm.taps[0][e][lane][0]) =
+            LOG2E * f32x4v{wtq[e][0], wtq[e][1], wtq[e][2], wtq[e][3]};
+        *reinterpret_cast<f32x4v*>(&sm.taps[1][e][lane][0]) =
+            LOG2E * f32x4v{wtk[e][0], wtk[e][1], wtk[e][2], wtk[e][3]};
     }
     if (hist0) {
 #pragma unroll
@@ -343,9 +352,9 @@ __device__ __forceinline__ void c32_prepare(C32Lds<GDN>& sm, const MixerArgs& a,
             {
                 float wt[2][KT];
                 taps_of(0, wt);
-                conv_rows(rq, from_hist ? &sm.u.hist[0][0][c2] : nullptr, wt, yq);
+                conv_rows<true>(rq, from_hist ? &sm.u.hist[0][0][c2] : nullptr, wt, yq);
                 taps_of(1, wt);
-                conv_rows(rk, from_hist ? &sm.u.hist[1][0][c2] : nullptr, wt, yk);
+                conv_rows<true>(rk, from_hist ? &sm.u.hist[1][0][c2] : nullptr, wt, yk);
             }
             float ps[8];
 #pragma unroll
@@ -380,7 +389,13 @@ __device__ __forceinline__ void c32_prepare(C32Lds<GDN>& sm, const MixerArgs& a,
             if (lane < RW) sm.beta[par][brow] = brow < n ? bval : 0.0f;
             // l2 norms: lane l gets plane (l >> 3) / RW, row (l >> 3) % RW of this wavefront
             const float ss = sum8x64(ps, lane);
-            if ((lane & 7) == 0) sm.nrm[w][lane >> 3] = rsqrtf(ss + L2_EPS);
+            // the rows carry log2(e) (the taps), and the eps its square, so the result is
+            // the plain l2 norm's; the q rows also take the attention scale, which O then
+            // inherits through Q+ and P
+            if ((lane & 7) == 0) {
+                const float inv = rsqrtf(ss + L2_EPS * (LOG2E * LOG2E));
+                sm.nrm[w][lane >> 3] = lane < 32 ? inv * a.scale : inv;
+            }
             // the next chunk's rows (the registers above are consumed)
             asm volatile("" ::: "memory");
             load_chunk(c0 + C);
@@ -898,7 +913,7 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
             }
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
-                *reinterpret_cast<f32x4v*>(&sm.u.ost[par][16 * mt + l16][16 * w + 4 * q4]) = a.scale * oacc[mt];
+                *reinterpret_cast<f32x4v*>(&sm.u.ost[par][16 * mt + l16][16 * w + 4 * q4]) = oacc[mt];
         }
         lds_barrier();  // B2
     }
