@@ -1,5 +1,7 @@
-"""GPU parity of the chunked prefill arm (D = 128, chunks of 64, bf16 MFMA operands)
-against the fp64 oracle and against the sequential arm on identical inputs."""
+"""GPU parity of the chunked prefill arm (D = 128, bf16 MFMA operands) against the fp64
+oracle and against the sequential arm on identical inputs. Conv kernels of up to 4 taps
+run the 32-row chunk kernel (kda_c32.hip), wider ones the 64-row kernel with its column
+splits (kda_chunk.hip)."""
 import numpy as np
 import pytest
 import torch
@@ -33,12 +35,12 @@ def _vs_sequential(cfg, dev, got, keys=("out", "o_core", "state", "ring"), tol=T
     return errs
 
 
-@pytest.mark.parametrize("T", [1, 37, 64, 65, 200])
+@pytest.mark.parametrize("T", [1, 32, 33, 37, 64, 65, 200])
 @pytest.mark.parametrize("gdn", [False, True])
 @pytest.mark.parametrize("B,H", [(2, 3), (1, 200), (2, 160)])
 def test_small_vs_oracle(T, gdn, B, H):
-    """Ragged T (partial chunks, T < K-1), every column-split variant (B*H < 128 -> 4
-    splits, 128..255 -> 2, >= 256 -> 1), random state and ring."""
+    """Ragged T (partial chunks, T < K-1) and exact multiples of the 32-row chunk (the
+    pipeline's one-, two- and seven-step runs), random state and ring."""
     cfg = CONFIGS["kda_decode"].with_(B=B, H=H, T=T, gdn=gdn)
     _print("case", cfg)
     inp, dev = inputs_for(cfg)
