@@ -785,11 +785,14 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) y = mfma_f32(la[kk], lb[kk], y);
                 // T_00 of this chunk from wavefront 2: its count of finished blocks
-                // reaches c + 1 (bounded wait; the two solves take the same time)
-                for (int it = 0; it < (1 << 16); ++it) {
+                // reaches c + 1. The two solves take the same time; the wait is bounded
+                // (about 2 ms of polling), and a wait that ran out poisons T_10 with NaN so
+                // the outputs show it instead of holding silently wrong values.
+                bool ready = false;
+                for (int it = 0; it < (1 << 16) && !ready; ++it) {
                     const uint32_t done = __builtin_amdgcn_readfirstlane(*static_cast<volatile uint32_t*>(&sm.tcnt));
-                    if (done > (uint32_t)c) break;
-                    __builtin_amdgcn_s_sleep(1);
+                    ready = done > (uint32_t)c;
+                    if (!ready) __builtin_amdgcn_s_sleep(1);
                 }
                 asm volatile("" ::: "memory");
 #pragma unroll
@@ -797,6 +800,7 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
                 f32x4v t10 = zero4();
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) t10 = mfma_f32(lc[kk], y[kk], t10);
+                if (!ready) t10 = f32x4v{NAN, NAN, NAN, NAN};
                 sm.tfrag[1][ln] = bf16x8{(__bf16)(-t10[0]), (__bf16)(-t10[1]), (__bf16)(-t10[2]), (__bf16)(-t10[3]),
                                            (__bf16)t11[0], (__bf16)t11[1], (__bf16)t11[2], (__bf16)t11[3]};
             }
