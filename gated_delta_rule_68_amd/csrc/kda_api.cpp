@@ -51,15 +51,18 @@ int check_shape(int B, int T, int H, int D, int K) {
 // at T = 32, against 0.27 ms at T = 24).
 // Few (b, h) pairs leave most compute units idle in the chunked arm. AUTO takes the
 // segmented arm (kda_internal.h, seg_plan) when its plan, with segments of at least
-// kSegAutoChunks chunks, shortens the critical path to at most 85% of the chunk
-// count. The explicit mode accepts segments of one chunk.
+// kSegAutoChunks 64-row units, shortens the critical path to at most 85% of the
+// chunked arm's (the margin covers the higher clock the chip holds with few units
+// busy). The explicit mode plans by chunk counts alone and accepts segments of one
+// unit, so it also cuts sequences too short for segments to pay.
 constexpr int kSegAutoChunks = 8;
 kda::SegPlan plan_for(int B, int T, int H, int mode) {
-    return kda::seg_plan((long)B * H, T, mode == KDA_MODE_SEGMENTED ? 1 : kSegAutoChunks);
+    return mode == KDA_MODE_SEGMENTED ? kda::seg_plan((long)B * H, T, 1, false)
+                                      : kda::seg_plan((long)B * H, T, kSegAutoChunks, true);
 }
 bool segments_pay(int B, int T, int H) {
     const kda::SegPlan p = plan_for(B, T, H, KDA_MODE_AUTO);
-    return p.n >= 3 && (long)p.cost * 100 <= 85 * (((long)T + 63) / 64);
+    return p.n >= 3 && p.cost * 100 <= 85 * kda::seg_chunked_cost(T);
 }
 
 //

@@ -235,9 +235,11 @@ __device__ __forceinline__ void kda_gate_prefix(const uint32_t (&g)[RW], int row
 }
 
 // ---------------------------------------------------------------------------------
-// Wavefronts 8..15: the state-independent preparation of each chunk.
+// Wavefronts 8..15: the state-independent preparation of each chunk. RO = false (the
+// segmented arm's runs without readout, which only carry the state) leaves out every
+// query-side step: the q rows, their conv, SiLU and norm, and the Q+ tiles.
 // ---------------------------------------------------------------------------------
-template <bool GDN, bool ACT>
+template <bool GDN, bool ACT, bool RO>
 __device__ __forceinline__ void c32_prepare(C32Lds<GDN>& sm, const MixerArgs& a, const C32Job& jb, int w,
                                             int lane) {
     const int q4 = lane >> 4, l16 = lane & 15, c2 = 2 * lane, K = a.K, H = a.H, h = jb.h;
@@ -252,7 +254,7 @@ __device__ __forceinline__ void c32_prepare(C32Lds<GDN>& sm, const MixerArgs& a,
     uint32_t rbeta = 0, rgs = 0;
     const uint32_t lane_off = 4u * lane;  // the lane's two channels, in bytes
     auto load_chunk = [&](int c0) {
-        load_rows(rq, a.q, kw, khead, lane_off, BUF_ALL, jb, c0, w);
+        if constexpr (RO) load_rows(rq, a.q, kw, khead, lane_off, BUF_ALL, jb, c0, w);
         load_rows(rk, a.k, kw, khead, lane_off, BUF_ALL, jb, c0, w);
         const int gb = min(c0 + pr0, jb.T - 1);  // the wavefront's first row, clamped
         if constexpr (!GDN) {
@@ -279,8 +281,8 @@ __device__ __forceinline__ void c32_prepare(C32Lds<GDN>& sm, const MixerArgs& a,
     // planes of the first chunk, state wavefront 0 the v plane in the next step) and the
     // gate-activation constants.
     load_chunk(0);
-    float wtq[2][KT], wtk[2][KT];
-    load_taps<KT, 2>(wtq, a.conv_w, khead + c2, K);
+    float wtq[2][KT] = {}, wtk[2][KT];
+    if constexpr (RO) load_taps<KT, 2>(wtq, a.conv_w, khead + c2, K);
     load_taps<KT, 2>(wtk, a.conv_w, kw + khead + c2, K);
     const bool hist0 = jb.ring_start && w == 0;
     float hv[3][HALO][2];
@@ -351,8 +353,13 @@ __device__ __forceinline__ void c32_prepare(C32Lds<GDN>& sm, const MixerArgs& a,
             const bool from_hist = jb.ring_start && s == 0 && w == 0;
             {
                 float wt[2][KT];
-                taps_of(0, wt);
-                conv_rows<true>(rq, from_hist ? &sm.u.hist[0][0][c2] : nullptr, wt, yq);
+                if constexpr (RO) {
+                    taps_of(0, wt);
+                    conv_rows<true>(rq, from_hist ? &sm.u.hist[0][0][c2] : nullptr, wt, yq);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < RW; ++r) yq[r][0] = yq[r][1] = 0.0f;
+                }
                 taps_of(1, wt);
                 conv_rows<true>(rk, from_hist ? &sm.u.hist[1][0][c2] : nullptr, wt, yk);
             }
@@ -453,11 +460,11 @@ __device__ __forceinline__ void c32_prepare(C32Lds<GDN>& sm, const MixerArgs& a,
                             const float e1 = exp2_f(gam), e2 = exp2_f(-gam);
                             const float qh = yq[r][e] * nr[r], kh = yk[r][e] * nr[RW + r];
                             const float qa = qh * e1, ka = kh * e1, kbv = kh * e2;
-                            oqa[e] = (__bf16)qa;
+                            if constexpr (RO) oqa[e] = (__bf16)qa;
                             oka[e] = (__bf16)ka;
                             okb[e] = (__bf16)kbv;
                             if constexpr (blk1) {
-                                oqp[e] = (__bf16)(qa * er1[e]);
+                                if constexpr (RO) oqp[e] = (__bf16)(qa * er1[e]);
                                 okp[e] = (__bf16)(ka * er1[e]);
                             } else {
                                 okb1[e] = (__bf16)(kbv * er1[e]);
@@ -465,14 +472,14 @@ __device__ __forceinline__ void c32_prepare(C32Lds<GDN>& sm, const MixerArgs& a,
                             kd[e][r] = kbv * fl[e];
                         }
                         const int row = pr0 + r;
-                        st2(&sm.qa[row][pc], oqa);
+                        if constexpr (RO) st2(&sm.qa[row][pc], oqa);
                         st2(&sm.ka[row][pc], oka);
                         st2(&sm.kb[row][pc], okb);
                         if constexpr (blk1) {
-                            st2(&sm.qp[row][pc], oqp);
+                            if constexpr (RO) st2(&sm.qp[row][pc], oqp);
                             st2(&sm.kp[row][pc], okp);
                         } else {
-                            st2(&sm.qp[row][pc], oqa);
+                            if constexpr (RO) st2(&sm.qp[row][pc], oqa);
                             st2(&sm.kp[row][pc], oka);
                             st2(&sm.kb1[row][pc], okb1);
                         }
@@ -508,7 +515,7 @@ __device__ __forceinline__ void c32_prepare(C32Lds<GDN>& sm, const MixerArgs& a,
                         kk[e][r] = yk[r][e] * nr[RW + r];
                         ok[e] = (__bf16)kk[e][r];
                     }
-                    st2(&sm.qa[pr0 + r][pc], oq);
+                    if constexpr (RO) st2(&sm.qa[pr0 + r][pc], oq);
                     st2(&sm.ka[pr0 + r][pc], ok);
                 }
 #pragma unroll
@@ -589,9 +596,10 @@ __device__ __forceinline__ void lp_block(C32Lds<GDN>& sm, int jw, int par, int l
 
 // ---------------------------------------------------------------------------------
 // Wavefronts 0..7: the state; in step s the v conv and the state-dependent work of
-// chunk s-1.
+// chunk s-1. RO = false (runs without readout) carries only the state: no P blocks,
+// Q+ S, O, gated norm or output stores.
 // ---------------------------------------------------------------------------------
-template <bool GDN>
+template <bool GDN, bool RO>
 __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, const C32Job& jb, int w,
                                           int lane) {
     const int tid = w * 64 + lane;  // 0..511 within the group
@@ -611,7 +619,11 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
     const size_t vstride = (size_t)a.H * DK;
     uint32_t rv[NR];
     load_rows(rv, a.v, vstride, hoff, lane_off, jb.vbytes, jb, 0, w);
-    const f32x4v n0 = ld4f(&a.norm_w[c8]), n1 = ld4f(&a.norm_w[c8 + 4]);
+    f32x4v n0 = zero4(), n1 = zero4();
+    if constexpr (RO) {
+        n0 = ld4f(&a.norm_w[c8]);
+        n1 = ld4f(&a.norm_w[c8 + 4]);
+    }
     float wt[2][KT];
     load_taps<KT, 2>(wt, a.conv_w, 2 * kw + hoff + c2, K);
     // ---- state: accS[kt] holds keys 16 kt + 4 q4 .. +3 of value column vcol ----
@@ -634,8 +646,10 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
     // memory access) follow.
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt) asm volatile("" ::"v"(accS[kt]));
-    *reinterpret_cast<f32x4v*>(&sm.normw[c8]) = n0;
-    *reinterpret_cast<f32x4v*>(&sm.normw[c8 + 4]) = n1;
+    if constexpr (RO) {
+        *reinterpret_cast<f32x4v*>(&sm.normw[c8]) = n0;
+        *reinterpret_cast<f32x4v*>(&sm.normw[c8 + 4]) = n1;
+    }
 #pragma unroll
     for (int e = 0; e < 2; ++e) *reinterpret_cast<f32x4v*>(&sm.taps[2][e][lane][0]) = f32x4v{wt[e][0], wt[e][1], wt[e][2], wt[e][3]};
     // the epilogue's z loads and out / o_core stores: row erow of the chunk, columns
@@ -644,8 +658,8 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
     const uint32_t eoff = (uint32_t)(erow * qkv + c8) * 2u;
     const uint32_t orow = (uint32_t)(qkv * 2);  // bytes of one bf16 row
     const bool ocore = jb.readout && a.o_core;
-    bf16x8 zold;  // the output gates of the chunk whose epilogue runs next
-    {
+    bf16x8 zold{};  // the output gates of the chunk whose epilogue runs next
+    if constexpr (RO) {
         const auto none = buf_rsrc(a.out, 0u);
         const u32x4v zero{0u, 0u, 0u, 0u};
 #pragma unroll
@@ -655,7 +669,7 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
     }
 
     if (tid == 0) sm.tcnt = 0u;  // before the barriers below; counted per chunk from here
-    if (tid < 64) {  // P block (0, 1), above the diagonal: zero for the whole run
+    if (RO && tid < 64) {  // P block (0, 1), above the diagonal: zero for the whole run
         const __bf16 z = (__bf16)0.0f;
         *reinterpret_cast<bf16x4*>(&sm.pb[tid & 15][perm32(16 + 4 * (tid >> 4))]) = bf16x4{z, z, z, z};
     }
@@ -805,7 +819,7 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
                                            (__bf16)t11[0], (__bf16)t11[1], (__bf16)t11[2], (__bf16)t11[3]};
             }
             __builtin_amdgcn_s_setprio(2);
-        } else if (w == 0 || w == 1 || w == 5) {  // the blocks of P (read in phase 2)
+        } else if (RO && (w == 0 || w == 1 || w == 5)) {  // the blocks of P (read in phase 2)
             lp_block<GDN>(sm, w == 0 ? 1 : (w == 1 ? 3 : 5), par, lane);
         }
         // the next chunk's v rows
@@ -832,13 +846,13 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
                         const int off = (16 * mt + l16) * LDR + 32 * (2 * kh + i) + 8 * q4;
-                        qf[i] = ld8(qsrc + off);
+                        if constexpr (RO) qf[i] = ld8(qsrc + off);
                         kf[i] = ld8(ksrc + off);
                     }
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
-                        oacc[mt] = mfma_bf16(sbop[2 * kh + i], qf[i], oacc[mt]);
+                        if constexpr (RO) oacc[mt] = mfma_bf16(sbop[2 * kh + i], qf[i], oacc[mt]);
                         racc[mt] = mfma_bf16(kf[i], sbop[2 * kh + i], racc[mt]);
                     }
                 }
@@ -889,7 +903,7 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
                 ubs = pack2(ub0 * d0, ub1 * d1);
             }
             // O^T = (Q+ S)^T + Ub^T P^T (GDN: Q+ S is q S with rows times e^{G_s})
-            {
+            if constexpr (RO) {
                 const bf16x8 p0 = ld8(&sm.pb[l16][8 * q4]), p1 = ld8(&sm.pb[16 + l16][8 * q4]);
                 if constexpr (GDN) {
                     oacc[0] *= sm.gpos[par][l16];
@@ -910,18 +924,18 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
             }
             // the previous chunk's epilogue while the matrix cores run the products above,
             // then this chunk's output gates (used by the next step's epilogue)
-            epilogue(c - 1, zold);
-            {
+            if constexpr (RO) {
+                epilogue(c - 1, zold);
                 const auto zr = buf_rsrc(static_cast<const __bf16*>(a.z) + (row0 * qkv + hoff), (uint32_t)n * orow);
                 zold = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(zr, (int)eoff, 0, 0));
-            }
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-                *reinterpret_cast<f32x4v*>(&sm.u.ost[par][16 * mt + l16][16 * w + 4 * q4]) = oacc[mt];
+                for (int mt = 0; mt < 2; ++mt)
+                    *reinterpret_cast<f32x4v*>(&sm.u.ost[par][16 * mt + l16][16 * w + 4 * q4]) = oacc[mt];
+            }
         }
         lds_barrier();  // B2
     }
-    epilogue(nch - 1, zold);
+    if constexpr (RO) epilogue(nch - 1, zold);
 
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt)
@@ -982,10 +996,13 @@ __global__ __launch_bounds__(NT) void c32_kernel(MixerArgs a) {
     // holds the older wavefronts (the SIMD arbiter favours them) and a raised priority,
     // and the preparing group fills the issue slots it leaves.
     if (wave >= NW) {
-        c32_prepare<GDN, ACT>(sm, a, jb, wave - NW, lane);
+        // the segmented arm's runs without readout take the state-only specialisation
+        if (!SEG || jb.readout) c32_prepare<GDN, ACT, true>(sm, a, jb, wave - NW, lane);
+        else c32_prepare<GDN, ACT, false>(sm, a, jb, wave - NW, lane);
     } else {
         __builtin_amdgcn_s_setprio(2);
-        c32_state<GDN>(sm, a, jb, wave, lane);
+        if (!SEG || jb.readout) c32_state<GDN, true>(sm, a, jb, wave, lane);
+        else c32_state<GDN, false>(sm, a, jb, wave, lane);
         // The segmented arm's last segment writes the new conv ring (the last K-1 input
         // rows, T >= K-1 there): only pass 1 read the old one, and it has finished. The
         // value head's v rows here; a key head's q / k rows by its first value head only.

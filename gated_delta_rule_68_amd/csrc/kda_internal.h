@@ -76,31 +76,59 @@ struct MixerArgs {
 // One workgroup fills a compute unit. Pass 3 must fit one wave over the 256 units,
 // (n-1) pairs <= 256. In pass 1 the pairs' segment-0 runs hold `pairs` units and the
 // 2 (n-2) pairs middle runs take the other 256 - pairs units in r rounds (workgroups
-// start in index order as units free up, the segment-0 runs first), so segment 0
-// can be r times as long as the others. The plan minimises the chunk times of the
-// critical path, max(len0, r len) + len, over n <= kSegMax and segment lengths of at
-// least min_chunks chunks.
+// start in index order as units free up, the segment-0 runs first). The plan
+// minimises the time of the critical path, pass 1 (the longer of segment 0 and r
+// rounds of middle runs), the scan and pass 3, over n <= kSegMax and segment lengths
+// (in 64-row units) of at least min_chunks units.
+// - timed (AUTO): the cost model below, in hundredths of the time of one 32-row chunk
+//   with readout on a fully loaded chip (measured on the 32-row kernel, KDA and GDN
+//   alike). A run costs its chunks plus kSegRunFixed (its state load, the pipeline's
+//   fill and drain and the final stores: about 3.7 chunk times); a chunk of a run
+//   without readout costs kSegNoReadout of one with readout (the kernel leaves out the
+//   query side, P, O and the gated norm there); a scan step costs kSegScanStep, and a
+//   second round of middle runs starts kSegGap after the first round's runs end.
+// - untimed (the explicit mode): 64-row units of the critical path, max(len0, r len)
+//   + len, with no fixed costs, so short sequences still take several segments.
+// The 64-row kernel (conv kernels of more than 4 taps) shares the plan.
 constexpr int kSegMax = 32;
 constexpr int kSegCUs = 256;
+constexpr int kSegRunFixed = 370, kSegNoReadout = 69, kSegScanStep = 140, kSegGap = 40;
 struct SegPlan {
     int n, len0, len;  // segment count; rows of segment 0 and of the others
-    int cost;          // chunk times of the critical path (the chunk count when n == 1)
+    long cost;         // critical path (timed: hundredths of a 32-row chunk time; untimed: 64-row units)
 };
-__host__ __device__ inline SegPlan seg_plan(long pairs, int T, int min_chunks) {
-    const int nch = (int)(((long)T + 63) / 64);
-    SegPlan best{1, T, 0, nch};
+// Critical path of the unsegmented chunked arm (one run of T rows) in the timed units.
+__host__ __device__ inline long seg_chunked_cost(int T) { return (((long)T + 31) / 32) * 100 + kSegRunFixed; }
+__host__ __device__ inline SegPlan seg_plan(long pairs, int T, int min_chunks, bool timed) {
+    const long nch = ((long)T + 63) / 64;  // 64-row units
+    SegPlan best{1, T, 0, timed ? seg_chunked_cost(T) : nch};
     if (min_chunks < 1) min_chunks = 1;
     if (pairs >= kSegCUs) return best;
     const long free_cu = kSegCUs - pairs;
     for (int n = 3; n <= kSegMax && (long)(n - 1) * pairs <= kSegCUs; ++n) {
         const long mid = 2 * pairs * (n - 2);
-        const int r = (int)((mid + free_cu - 1) / free_cu);
-        const int x0 = nch / (r + n - 1);
-        for (int x = x0; x <= x0 + 1; ++x) {
-            const int l0 = nch - (n - 1) * x;
+        const long r = (mid + free_cu - 1) / free_cu;
+        if (!timed) {
+            const long x0 = nch / (r + n - 1);
+            for (long x = x0; x <= x0 + 1; ++x) {
+                const long l0 = nch - (n - 1) * x;
+                if (x < min_chunks || l0 < 1) continue;
+                const long cost = (l0 > r * x ? l0 : r * x) + x;
+                if (cost < best.cost) best = SegPlan{n, (int)(l0 * 64), (int)(x * 64), cost};
+            }
+            continue;
+        }
+        // x (units per segment after the first) that balances the two sides of pass 1
+        const long x0 = (200 * nch + kSegRunFixed - r * kSegRunFixed - (r - 1) * kSegGap) /
+                        (200 * (n - 1) + 2 * r * kSegNoReadout);
+        for (long i = 0; i < 5; ++i) {  // around the balance, and the shortest segments
+            const long x = i < 4 ? x0 - 1 + i : min_chunks;
+            const long l0 = nch - (n - 1) * x;
             if (x < min_chunks || l0 < 1) continue;
-            const int cost = (l0 > r * x ? l0 : r * x) + x;
-            if (cost < best.cost) best = SegPlan{n, l0 * 64, x * 64, cost};
+            const long seg0 = 200 * l0 + kSegRunFixed;
+            const long mids = r * (2 * kSegNoReadout * x + kSegRunFixed) + (r - 1) * kSegGap;
+            const long cost = (seg0 > mids ? seg0 : mids) + (long)kSegScanStep * (n - 2) + 200 * x + kSegRunFixed;
+            if (cost < best.cost) best = SegPlan{n, (int)(l0 * 64), (int)(x * 64), cost};
         }
     }
     return best;

@@ -176,8 +176,8 @@ def test_auto_arm_boundaries():
 
 
 def test_segmented_queries():
-    # AUTO takes the segmented arm when its plan (segments of at least eight chunks)
-    # shortens the critical path to 85% of the chunk count or less
+    # AUTO takes the segmented arm when its timed plan (segments of at least eight
+    # 64-row units) shortens the critical path to 85% of the chunked arm's or less
     assert kda.prefill_arm(1, 4626, 64, 128, 1, 0) == 4  # 64 pairs, 73 chunks: 5 segments
     assert kda.prefill_arm(2, 4626, 64, 128, 1, 0) == 4  # 128 pairs: 3 segments
     assert kda.prefill_arm(4, 8192, 32, 128, 1, 0, gdn=True) == 4

@@ -155,9 +155,9 @@ def test_prefill_workload_auto_is_segmented():
 
 
 def test_gdn_workload_auto_is_segmented():
-    """GDN prefill B = 4, T = 8192, H = 32 (128 pairs): AUTO takes three segments, the
-    first twice as long as the others. Sampled heads against the oracle, everything
-    against the sequential arm."""
+    """GDN prefill B = 4, T = 8192, H = 32 (128 pairs): AUTO takes three segments
+    (3456, 2368 and 2368 rows). Sampled heads against the oracle, everything against
+    the sequential arm."""
     cfg = CONFIGS["gdn_prefill"]
     assert kda.prefill_arm(cfg.B, cfg.T, cfg.H, cfg.D, kda.KDA_DTYPE_BF16, kda.KDA_MODE_AUTO, gdn=True) == 4
     inp, dev = inputs_for(cfg)
@@ -172,8 +172,8 @@ def test_gdn_workload_auto_is_segmented():
 
 
 def test_segmented_gdn_few_pairs_auto():
-    """GDN, one sequence of 2048 rows, 16 heads: AUTO takes four segments of eight
-    chunks; checked against the sequential arm."""
+    """GDN, one sequence of 2048 rows, 16 heads: AUTO takes four segments (320 rows,
+    then 576); checked against the sequential arm."""
     cfg = CONFIGS["gdn_prefill"].with_(B=1, T=2048, H=16)
     assert kda.prefill_arm(cfg.B, cfg.T, cfg.H, cfg.D, kda.KDA_DTYPE_BF16, kda.KDA_MODE_AUTO, gdn=True) == 4
     inp, dev = inputs_for(cfg)
