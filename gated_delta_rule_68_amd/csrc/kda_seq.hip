@@ -209,28 +209,40 @@ __global__ __launch_bounds__(SHORT_THREADS, 6) void seq_short_kernel(MixerArgs a
     const int grp = (tid >> 6) * 8 + (lane >> 3), s = lane & 7;
     const size_t kw = (size_t)a.Hk * D, khead = (size_t)(h % a.Hk) * D;
 
-    float S[CPT][KPL];
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) load_keys<D>(S[c], a.state_in + ((size_t)bh * D + grp + c * NG) * D, s);
-
     const GateCol gp = gate_col(a, h, GDN ? (size_t)h : head_off + tid % D);
     size_t row0;
     int Tspan;
     seq_span(a, b, &row0, &Tspan);
     const int T = TM == 1 ? 1 : Tspan;  // 1 <= T <= TM (the launch checks it)
 
-    if (tid < 3 * D) {  // conv + SiLU of plane tid / D, channel tid % D
-        const int plane = tid / D, ch = tid % D;
-        const size_t prow = plane < 2 ? plane * kw + khead + ch : 2 * kw + head_off + ch;
-        float* ring_row = a.ring + ((size_t)b * ring_rows(a) + prow) * (K - 1);
-        ConvChannel cc;
-        conv_window_from_ring(cc, ring_row, K);
-        conv_load_taps(cc, a.conv_w + prow * K, K);
-        const void* xsrc = plane == 0 ? a.q : (plane == 1 ? a.k : a.v);
-        const size_t xw = plane < 2 ? kw : qkv, xc = (plane < 2 ? khead : head_off) + ch;
-        float x[TM];
+    // The conv inputs are requested before the state (vector-memory loads complete in
+    // order), so the conv, gates and l2 norms run while the state streams in. Every
+    // thread requests valid elements (threads tid >= 3 D those of plane 2, unused), so
+    // no branch stands between the requests and the state's.
+    // Conv + SiLU of plane tid / D, channel tid % D.
+    const int plane = min(tid / D, 2), ch = tid % D;
+    const size_t prow = plane < 2 ? plane * kw + khead + ch : 2 * kw + head_off + ch;
+    float* ring_row = a.ring + ((size_t)b * ring_rows(a) + prow) * (K - 1);
+    ConvChannel cc;
+    conv_window_from_ring(cc, ring_row, K);
+    conv_load_taps(cc, a.conv_w + prow * K, K);
+    const void* xsrc = plane == 0 ? a.q : (plane == 1 ? a.k : a.v);
+    const size_t xw = plane < 2 ? kw : qkv, xc = (plane < 2 ? khead : head_off) + ch;
+    float x[TM];
 #pragma unroll
-        for (int t = 0; t < TM; ++t) x[t] = ld_act<BF>(xsrc, (row0 + min(t, T - 1)) * xw + xc);
+    for (int t = 0; t < TM; ++t) x[t] = ld_act<BF>(xsrc, (row0 + min(t, T - 1)) * xw + xc);
+    // gate and beta of row min(tid / EW, T - 1), entry tid % EW (KDA: one channel per
+    // thread and row for T <= SHORT_THREADS / D rows, the rest below)
+    constexpr int GR = GDN ? TM : (TM * D <= SHORT_THREADS ? TM : SHORT_THREADS / D);
+    const int gt = min(GDN ? tid : tid / D, T - 1);
+    const float graw = ld_act<BF>(a.g, GDN ? (row0 + gt) * a.H + h : (row0 + gt) * qkv + head_off + tid % D);
+    const float braw = ld_act<BF>(a.beta, (row0 + min(tid, T - 1)) * a.H + h);
+    asm volatile("" ::: "memory");
+    float S[CPT][KPL];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) load_keys<D>(S[c], a.state_in + ((size_t)bh * D + grp + c * NG) * D, s);
+    asm volatile("" ::: "memory");
+    if (tid < 3 * D) {
 #pragma unroll
         for (int t = 0; t < TM; ++t)
             if (t < T) pre[plane][t][ch] = silu_f(conv_push(cc, x[t]));
@@ -238,15 +250,16 @@ __global__ __launch_bounds__(SHORT_THREADS, 6) void seq_short_kernel(MixerArgs a
     }
     if constexpr (GDN) {
         if (tid < T) {
-            es[tid][0] = exp_f(gate_in(a, gp, ld_act<BF>(a.g, (row0 + tid) * a.H + h)));
-            bs[tid] = beta_in(a, ld_act<BF>(a.beta, (row0 + tid) * a.H + h));
+            es[tid][0] = exp_f(gate_in(a, gp, graw));
+            bs[tid] = beta_in(a, braw);
         }
     } else {
-        for (int idx = tid; idx < T * D; idx += SHORT_THREADS) {
+        if (tid < GR * D && tid / D < T) es[tid / D][tid % D] = exp_f(gate_in(a, gp, graw));
+        for (int idx = GR * D + tid; idx < T * D; idx += SHORT_THREADS) {
             const int t = idx / D, i = idx % D;
             es[t][i] = exp_f(gate_in(a, gp, ld_act<BF>(a.g, (row0 + t) * qkv + head_off + i)));
         }
-        if (tid < T) bs[tid] = beta_in(a, ld_act<BF>(a.beta, (row0 + tid) * a.H + h));
+        if (tid < T) bs[tid] = beta_in(a, braw);
     }
     __syncthreads();
     for (int t = wave; t < T; t += NW) l2_qk_row<D>(pre[0][t], pre[1][t], lane, &kqs[t]);
