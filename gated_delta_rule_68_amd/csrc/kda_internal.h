@@ -83,7 +83,8 @@ struct MixerArgs {
 // - timed (AUTO): the cost model below, in hundredths of the time of one 32-row chunk
 //   with readout on a fully loaded chip (measured on the 32-row kernel, KDA and GDN
 //   alike). A run costs its chunks plus kSegRunFixed (its state load, the pipeline's
-//   fill and drain and the final stores: about 3.7 chunk times); a chunk of a run
+//   fill and drain and the final stores: 3 to 3.7 chunk times measured; the plans of
+//   the measured workloads are the same anywhere in 2.5 .. 3.7); a chunk of a run
 //   without readout costs kSegNoReadout of one with readout (the kernel leaves out the
 //   query side, P, O and the gated norm there); a scan step costs kSegScanStep, and a
 //   second round of middle runs starts kSegGap after the first round's runs end.
