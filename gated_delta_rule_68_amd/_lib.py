@@ -67,6 +67,13 @@ def lib() -> ctypes.CDLL:
 def bind(path: str) -> ctypes.CDLL:
     """Load the build of the library at `path` and declare every export's argument and
     result types."""
+    # torch brings its own copy of the HIP runtime under another file name. Loaded
+    # first, it is the one the library binds to; loaded after the library, it would be a
+    # second runtime in the process, and calls through the library then fail (no device).
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     l = ctypes.CDLL(path)
     for n in ("kda_prefill", "gdn_prefill"):
         getattr(l, n).argtypes = _PREFILL_ARGS

@@ -162,3 +162,32 @@ def test_gated_chunk_modes_refuse_unbounded_gates(arena, what, over, kw, rc, gdn
     a.update(over)
     assert call_gated(a, gdn, False, **kw) == rc
     assert outputs_untouched(arena) is None
+
+
+def test_library_bound_before_torch_import():
+    """A process that binds the library before importing torch itself still runs on
+    one HIP runtime: the binding loads torch's runtime first. A fresh interpreter binds
+    the library, then imports torch and runs a small decode (zero inputs, zero output)."""
+    import os
+    import subprocess
+    import sys
+    code = (
+        "import gated_delta_rule_68_amd as kda\n"
+        "kda.lib()\n"
+        "import torch\n"
+        "B, H, D, K = 2, 2, 16, 4\n"
+        "f = dict(dtype=torch.float32, device='cuda:0')\n"
+        "x = {n: torch.zeros(B, 1, H * D, **f) for n in ('q', 'k', 'v', 'g', 'z')}\n"
+        "beta = torch.zeros(B, 1, H, **f)\n"
+        "conv_w = torch.zeros(3 * H * D, K, **f)\n"
+        "ring = torch.zeros(B, 3 * H * D, K - 1, **f)\n"
+        "state = torch.zeros(B, H, D, D, **f)\n"
+        "out = torch.full((B, 1, H * D), 7.0, **f)\n"
+        "kda.kda_decode(x['q'], x['k'], x['v'], x['g'], beta, conv_w, ring, state, state, x['z'],\n"
+        "               torch.ones(D, **f), out, None, scale=D ** -0.5, rms_eps=1e-5)\n"
+        "torch.cuda.synchronize()\n"
+        "assert float(out.abs().max()) == 0.0\n"
+        "print('bound before torch: ok')\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=100)
+    assert r.returncode == 0 and "ok" in r.stdout, r.stdout + r.stderr
