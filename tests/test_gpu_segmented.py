@@ -185,6 +185,26 @@ def test_segmented_gdn_few_pairs_auto():
     assert max(errs.values()) <= TOL and errs["ring"] == 0.0
 
 
+@pytest.mark.parametrize("H,nseg", [(32, 9), (8, 10)])
+def test_auto_plans_with_few_heads_slow_gates(H, nseg):
+    """A single sequence of 4626 rows with 32 and with 8 heads: AUTO's timed plan takes
+    nine segments (576 rows, then 512) and ten (a first segment of 64 rows, then 512).
+    Slow gates, so every segment's entry state carries the history through its
+    transition M; every head against the sequential arm under the same gates."""
+    from tests.test_abi_host import _segments_from_workspace
+    cfg = CONFIGS["kda_prefill"].with_(H=H, random_init=True)
+    assert kda.prefill_arm(cfg.B, cfg.T, cfg.H, cfg.D, kda.KDA_DTYPE_BF16, kda.KDA_MODE_AUTO) == 4
+    assert _segments_from_workspace(cfg.B, cfg.T, cfg.H, kda.KDA_MODE_AUTO) == nseg
+    inp, dev = inputs_for(cfg)
+    ga, gb, _, _ = _slow_gates(inp, dev)
+    got = run_gated(cfg, dev, ga, gb, kda.KDA_GATE_SOFTPLUS, mode=kda.KDA_MODE_AUTO)
+    ref = run_gated(cfg, dev, ga, gb, kda.KDA_GATE_SOFTPLUS, mode=SEQ)
+    torch.cuda.synchronize()
+    errs = {k: oracle.rel_linf(to_f64(got[k]), to_f64(ref[k])) for k in ("out", "o_core", "state", "ring")}
+    _print("vs sequential", errs)
+    assert max(errs.values()) <= TOL and errs["ring"] == 0.0
+
+
 def test_without_o_core_same_outputs():
     """o_core = NULL: the same out, ring and state bit for bit as with it."""
     cfg = CONFIGS["kda_decode"].with_(B=1, H=2, T=300)
