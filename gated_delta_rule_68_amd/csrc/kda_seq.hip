@@ -492,13 +492,20 @@ __global__ __launch_bounds__(SHORT_THREADS, 4) void seq_short_pair_kernel(MixerA
 #pragma unroll
                 for (int c = 0; c < CPT; ++c) os[t][g * D + grp + c * NG] = o[c];
             }
+            if (TM == 1) {  // a one-token call stores head 0's state while head 1 is scanned
+#pragma unroll
+                for (int c = 0; c < CPT; ++c)
+                    store_keys<D>(a.state_out + ((size_t)(b * a.H + vhead(g)) * D + grp + c * NG) * D, S[g][c], s);
+            }
         }
     }
+    if (TM > 1) {
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+        for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int c = 0; c < CPT; ++c)
-            store_keys<D>(a.state_out + ((size_t)(b * a.H + vhead(g)) * D + grp + c * NG) * D, S[g][c], s);
+            for (int c = 0; c < CPT; ++c)
+                store_keys<D>(a.state_out + ((size_t)(b * a.H + vhead(g)) * D + grp + c * NG) * D, S[g][c], s);
+    }
     if (!a.readout) return;
     __syncthreads();
     for (int idx = wave; idx < T * G; idx += NW) {
