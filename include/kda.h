@@ -95,14 +95,16 @@ extern "C" {
  * the library cannot see device values), and gated calls with gate_lb < -5 are refused with KDA_ERR_DTYPE_MODE. */
 #define KDA_MODE_AUTO 0       /* library picks sequential, chunked or segmented from the shape */
 #define KDA_MODE_SEQUENTIAL 1 /* token-by-token scan (bit-identical to chained decodes) */
-#define KDA_MODE_CHUNKED 2    /* chunk-64 WY form, bf16 MFMA operands, fp32 state (D = 128, bf16) */
+#define KDA_MODE_CHUNKED 2    /* chunked WY form (32-row chunks for convs of up to 4 taps, 64-row
+                               * beyond), bf16 MFMA operands, fp32 state (D = 128, bf16) */
 /* The chunked form with every sequence cut into segments that run in parallel (D = 128,
  * equal-length sequences; not for packed batches). A run of tokens maps its entry state
  * affinely, S_out = M S_in + B: the decay and the delta-rule update of stage 5 above act
  * on the key index by left multiplication. The segments' M and B are computed in
  * parallel, a scan forms each segment's entry state, and the segments run again from
- * it with readout. AUTO takes it for few (b, h) pairs and long sequences; this mode
- * forces it, with segments as short as one chunk. Same accuracy contract as
+ * it with readout. AUTO takes it for few (b, h) pairs and long sequences, with
+ * segment lengths from a timed cost model; this mode forces it, with segments as
+ * short as 64 rows. Same accuracy contract as
  * KDA_MODE_CHUNKED. */
 #define KDA_MODE_SEGMENTED 3
 
