@@ -42,6 +42,10 @@
 // meets an accumulator are stored with that index permuted within each 32-wide slice
 // (perm32), so every MFMA fragment is one 16-byte LDS read. Tiles that one group
 // writes while the other reads the previous chunk's are double-buffered.
+//
+// The segmented arm's runs without readout (from zero and from the identity: only
+// their final state is used) take a specialisation of both groups chosen once per
+// workgroup: no q rows, q conv or Q+ tiles, no P blocks, Q+ S, O, gated norm or stores.
 #include <type_traits>
 
 #include "kda_chunk_common.h"
