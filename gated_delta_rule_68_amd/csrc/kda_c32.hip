@@ -87,8 +87,8 @@ struct C32Lds {
     alignas(16) __bf16 qa[C][LDR];             // KDA: q^ e^{gamma}; GDN: q^ (channels permuted)
     __bf16 ka[C][LDR];             // KDA: k^ e^{gamma}; GDN: k^
     __bf16 kb[GDN ? 1 : C][LDR];   // k^ e^{-gamma}
-    __bf16 qp[GDN ? 1 : C][LDR];   // Q+
-    __bf16 kp[GDN ? 1 : C][LDR];   // K+
+    __bf16 qp[GDN ? 1 : C][LDR];   // Q+, rows 16..31 (block 0's rows are those of qa)
+    __bf16 kp[GDN ? 1 : C][LDR];   // K+, rows 16..31 (block 0's rows are those of ka)
     __bf16 kb1[GDN ? 1 : C / 2][LDR];  // rows 0..15: k^ e^{-gamma} e^{R_1} (L, P block (1, 0))
     // double-buffered by chunk parity
     __bf16 kdt[2][DK][LDJ];        // KDA: K_dec^T; GDN: k^T  ([key][row], rows permuted)
@@ -465,8 +465,9 @@ __device__ __forceinline__ void c32_prepare(C32Lds<GDN>& sm, const MixerArgs& a,
                 for (int e = 0; e < 2; ++e) er1[e] = exp2_f(r1[e]);
                 if (w == 0) *reinterpret_cast<float2*>(&sm.ffn[par][c2]) = make_float2(exp2_f(acc[0]), exp2_f(acc[1]));
                 // Block a's rows: gamma = G - R_a; Q+ and K+ are the block-relative tiles
-                // times e^{R_a} (R_0 = 0, so block 0 stores them unscaled), and block 0
-                // also stores k e^{-gamma} e^{R_1}, the operand of the L and P block (1, 0).
+                // times e^{R_a} (R_0 = 0, so block 0's are its qa and ka rows and only
+                // block 1 stores them), and block 0 also stores k e^{-gamma} e^{R_1}, the
+                // operand of the L and P block (1, 0).
                 auto tiles = [&](auto blk1c) {
                     constexpr bool blk1 = decltype(blk1c)::value;
                     float kd[2][RW], fl[2];  // fl: e^{G_l - R_a}
@@ -499,9 +500,7 @@ __device__ __forceinline__ void c32_prepare(C32Lds<GDN>& sm, const MixerArgs& a,
                         if constexpr (blk1) {
                             if constexpr (RO) st2(&sm.qp[row][pc], oqp);
                             st2(&sm.kp[row][pc], okp);
-                        } else {
-                            if constexpr (RO) st2(&sm.qp[row][pc], oqa);
-                            st2(&sm.kp[row][pc], oka);
+                        } else {  // block 0: Q+ and K+ are qa and ka themselves (R_0 = 0)
                             st2(&sm.kb1[row][pc], okb1);
                         }
                     }
@@ -853,8 +852,11 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
             bf16x8 sbop[4];
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) sbop[kk] = pack2(accS[2 * kk], accS[2 * kk + 1]);
-            const __bf16* qsrc = GDN ? &sm.qa[0][0] : &sm.qp[0][0];
-            const __bf16* ksrc = GDN ? &sm.ka[0][0] : &sm.kp[0][0];
+            // (KDA: block 0's rows of Q+ and K+ are qa and ka, R_0 = 0; block 1's are qp, kp)
+            const __bf16* qsrc0 = &sm.qa[0][0];
+            const __bf16* ksrc0 = &sm.ka[0][0];
+            const __bf16* qsrc1 = GDN ? &sm.qa[0][0] : &sm.qp[0][0];
+            const __bf16* ksrc1 = GDN ? &sm.ka[0][0] : &sm.kp[0][0];
             // LDS operands in batches issued together (a scheduling fence keeps the
             // reads ahead of their uses, so each batch costs one round trip)
 #pragma unroll
@@ -867,8 +869,8 @@ __device__ __forceinline__ void c32_state(C32Lds<GDN>& sm, const MixerArgs& a, c
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
                         const int off = (16 * mt + l16) * LDR + 32 * (2 * kh + i) + 8 * q4;
-                        if constexpr (RO) qf[i] = ld8(qsrc + off);
-                        kf[i] = ld8(ksrc + off);
+                        if constexpr (RO) qf[i] = ld8((mt == 0 ? qsrc0 : qsrc1) + off);
+                        kf[i] = ld8((mt == 0 ? ksrc0 : ksrc1) + off);
                     }
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
